@@ -1,0 +1,343 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix (no GPU).
+
+Each test ties one oracle function to something other than itself: hand-derived
+golden bytes, closed forms, brute force on tiny inputs, library routines for special
+cases, or invariants.  Pages cited:
+  [AT] aratech.ae BitNet b1.58 article: "Ternary weights {-1, 0, +1}", "BitLinear: the
+       building block", and the information-content paragraph on log2(3) ~ 1.58 bits.
+  [BH] bhfrc.com news 56965: section 1.1 (add / subtract / skip; ~10x vs fp16) and
+       section 4.1 (2-bit code table).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bitlinear_fwd_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load_json(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------ exact rounding helper
+def test_round_rational_ieee_cases():
+    f = oracle.round_rational_to_f32
+    assert f(1, 1) == np.float32(1.0)
+    assert f(1, 3) == np.float32(1.0 / 3.0)
+    # exactly half-way between 1 and 1+2^-23: ties to the even significand (1.0)
+    assert f((1 << 24) + 1, 1 << 24) == np.float32(1.0)
+    # half-way between 1+2^-23 (odd) and 1+2^-22 (even) -> 1+2^-22
+    assert f((1 << 24) + 3, 1 << 24) == np.float32(1.0 + 2.0 ** -22)
+    # just above half-way rounds up
+    assert f((1 << 25) + 3, 1 << 25) == np.float32(1.0 + 2.0 ** -23)
+    # subnormals: 2^-150 is half of the smallest step -> 0 (even); 3*2^-150 -> 2^-148
+    assert f(1, 1 << 150) == np.float32(0.0)
+    assert f(3, 1 << 150) == np.float32(2.0 ** -148)
+    assert f(1, 1 << 149) == np.float32(2.0 ** -149)
+    assert f(0, 7) == np.float32(0.0)
+
+
+# ------------------------------------------------------------------ P2: gamma = mean|W|
+def test_gamma_bruteforce_tiny_wide_range():
+    rng = _rng(1)
+    for trial in range(40):
+        n = int(rng.integers(1, 40))
+        w = (rng.standard_normal(n) * 10.0 ** rng.uniform(-40, 30, n)).astype(np.float32)
+        if trial % 5 == 0:
+            w[: n // 2] = np.float32(1e-45) * rng.integers(1, 100, n // 2)  # subnormals
+        g = oracle.gamma_absmean(w)
+        assert g == oracle.gamma_bruteforce(w)
+
+
+def test_gamma_is_nearest_float_to_exact_mean():
+    from fractions import Fraction
+    rng = _rng(2)
+    for _ in range(20):
+        w = rng.standard_normal(33).astype(np.float32) * np.float32(0.02)
+        g = oracle.gamma_absmean(w)
+        mean = sum(Fraction(abs(float(v))) for v in w) / len(w)
+        err = abs(Fraction(float(g)) - mean)
+        for nb in (np.nextafter(g, np.float32(np.inf)), np.nextafter(g, np.float32(0))):
+            assert err <= abs(Fraction(float(nb)) - mean)
+
+
+def test_gamma_closed_forms():
+    assert oracle.gamma_absmean(np.full((3, 5), -0.375, np.float32)) == np.float32(0.375)
+    assert oracle.gamma_absmean(np.array([[1.0, -3.0]], np.float32)) == np.float32(2.0)
+    assert oracle.gamma_absmean(np.zeros((4, 4), np.float32)) == np.float32(0.0)
+    w = np.array([1.0, 2.0, 4.0], np.float32)  # 7/3
+    assert oracle.gamma_absmean(w) == np.float32(7.0 / 3.0)
+
+
+def test_gamma_matches_float64_library_mean():
+    w = synth.latent_weights(256, 1024, seed=7).numpy()
+    g = oracle.gamma_absmean(w)
+    assert g == np.float32(np.mean(np.abs(w), dtype=np.float64))
+
+
+def test_gamma_gaussian_expectation():
+    # E|W| = sigma * sqrt(2/pi) for W ~ N(0, sigma^2); std error sigma*sqrt(1-2/pi)/sqrt(n)
+    w = synth.latent_weights(512, 2048, seed=11).numpy()
+    g = float(oracle.gamma_absmean(w))
+    sigma = synth.SIGMA_W
+    mu = sigma * math.sqrt(2 / math.pi)
+    se = sigma * math.sqrt(1 - 2 / math.pi) / math.sqrt(w.size)
+    assert abs(g - mu) < 5 * se
+
+
+# ------------------------------------------------------------------ P1/P3: ternary codes
+def test_ternary_values_and_golden():
+    for case in _load_json("quant_examples.json")["weights"]:
+        w = np.array(case["W"], np.float32)
+        g, q, _ = oracle.quantize_weights(w)
+        assert g == np.float32(case["gamma"]), case
+        assert q.tolist() == case["q"], case
+
+
+def test_ternary_distribution_closed_form():
+    # t = W / gamma ~ N(0, pi/2) for Gaussian W; q = 0 iff |t| <= 1/2:
+    # P0 = erf(1 / (2 sqrt(pi))) = 0.3101, P(+1) = P(-1) = (1 - P0) / 2.
+    w = synth.latent_weights(1024, 2048, seed=13).numpy()
+    g, q, _ = oracle.quantize_weights(w)
+    assert set(np.unique(q).tolist()) <= {-1, 0, 1}
+    n = q.size
+    p0 = math.erf(1 / (2 * math.sqrt(math.pi)))
+    f0 = float(np.mean(q == 0))
+    fp = float(np.mean(q == 1))
+    fm = float(np.mean(q == -1))
+    assert abs(f0 - p0) < 5 * math.sqrt(p0 * (1 - p0) / n)
+    p1 = (1 - p0) / 2
+    for f in (fp, fm):
+        assert abs(f - p1) < 5 * math.sqrt(p1 * (1 - p1) / n)
+    # entropy of the code distribution stays below log2(3) ~ 1.585 bits ([AT], [BH] 1.1)
+    h = -sum(p * math.log2(p) for p in (f0, fp, fm))
+    assert 1.57 < h <= math.log2(3)
+    assert abs(math.log2(3) - 1.58496) < 1e-5
+
+
+def test_ternarise_metamorphic():
+    w = synth.latent_weights(64, 512, seed=17).numpy()
+    g, q, _ = oracle.quantize_weights(w)
+    g2, q2, _ = oracle.quantize_weights(-w)  # RNE is symmetric
+    assert g2 == g and np.array_equal(q2, -q)
+    for j in (-3, 5):  # exact power-of-two scaling leaves every code unchanged
+        g3, q3, _ = oracle.quantize_weights(w * np.float32(2.0 ** j))
+        assert g3 == g * np.float32(2.0 ** j) and np.array_equal(q3, q)
+
+
+# ------------------------------------------------------------------ packing layout
+def _golden_q(case):
+    q = np.full((case["N"], case["K"]), case["fill"], np.int8)
+    for n, k, v in case["set"]:
+        q[n, k] = v
+    return q
+
+
+def test_pack_golden_bytes():
+    for case in _load_json("pack_layout.json")["cases"]:
+        p = oracle.pack(_golden_q(case))
+        assert p.size == case["expect_size"], case["name"]
+        if "expect_all_bytes" in case:
+            assert np.all(p == case["expect_all_bytes"]), case["name"]
+            continue
+        seen = np.zeros(p.size, bool)
+        for off, vals in case["expect_bytes"].items():
+            off = int(off)
+            assert p[off:off + 4].tolist() == vals, (case["name"], off)
+            seen[off:off + 4] = True
+        if "expect_other_bytes" in case:
+            assert np.all(p[~seen] == case["expect_other_bytes"]), case["name"]
+
+
+def test_pack_roundtrip_and_padding_codes():
+    rng = _rng(3)
+    for n, k in [(1, 1), (16, 256), (17, 300), (33, 513), (40, 1000)]:
+        q = rng.integers(-1, 2, (n, k)).astype(np.int8)
+        p = oracle.pack(q)
+        assert p.size == oracle.n_pad(n) * oracle.k_pad(k) // 4
+        assert np.array_equal(oracle.unpack(p, n, k), q)
+        codes = oracle.unpack_codes(p, n, k)
+        inner = codes[:n, :k]
+        assert not np.any(inner == 3)  # no padding code inside the matrix
+        assert np.all(codes[n:, :] == 3) and np.all(codes[:, k:] == 3)
+        # code table: 00 -> 0, 01 -> +1, 10 -> -1 ([BH] 4.1)
+        assert np.array_equal(inner == 0, q == 0)
+        assert np.array_equal(inner == 1, q == 1)
+        assert np.array_equal(inner == 2, q == -1)
+
+
+def test_pack_rejects_non_ternary():
+    with pytest.raises(ValueError):
+        oracle.pack(np.array([[2]], np.int8))
+
+
+def test_packed_size_closed_forms():
+    # 100B-class matrix 28672 x 8192 at 2 bits/weight
+    assert oracle.packed_bytes(28672, 8192) == 58_720_256
+    assert oracle.packed_bytes(8192, 28672) == 58_720_256
+    assert oracle.packed_bytes(6912, 2560) == 4_423_680
+    assert oracle.packed_bytes(512, 256) == 32_768
+    # 2e9 weights at 2 bits are 0.5 GB, inside [BH] 5.1's 0.4-0.6 GB for a 2B model;
+    # at the log2(3) information bound they would be ~396 MB ([AT]: ~400 MB)
+    assert 0.4e9 <= 2e9 * 2 / 8 <= 0.6e9
+    assert abs(2e9 * math.log2(3) / 8 / 1e6 - 396.2) < 0.5
+    # 1000 trits carry ~1585 bits ([AT]); fp16 -> ~1.58 bits is ~10x ([BH] 1.1)
+    assert round(1000 * math.log2(3)) == 1585
+    assert round(16 / math.log2(3)) == 10
+
+
+# ------------------------------------------------------------------ P4: activation quant
+def test_act_quant_golden():
+    for case in _load_json("quant_examples.json")["acts"]:
+        x = np.array([case["x"]], np.float32)
+        xq, a = oracle.quant_acts(x)
+        assert a[0] == np.float32(case["absmax"])
+        assert xq[0, : x.shape[1]].tolist() == case["xq"], case
+        assert np.all(xq[0, x.shape[1]:] == 0)
+
+
+def test_act_quant_invariants():
+    x = synth.activations(37, 700, seed=19, dtype=torch.float32, outlier_p=0.01, outlier_mult=20.0).numpy()
+    x[5] = 0.0
+    xq, a = oracle.quant_acts(x)
+    assert xq.shape == (37, 768)
+    assert np.all(np.abs(xq.astype(np.int32)) <= 127)
+    assert np.all(xq[:, 700:] == 0)
+    assert np.all(xq[5] == 0) and a[5] == 0
+    for m in range(37):
+        if m == 5:
+            continue
+        assert a[m] == np.max(np.abs(x[m]))
+        j = int(np.argmax(np.abs(x[m])))
+        assert abs(int(xq[m, j])) == 127 and np.sign(xq[m, j]) == np.sign(x[m, j])
+        # quantisation error bound: |xq * a/127 - x| <= a/254 (+ fp32 slack)
+        err = np.abs(xq[m, :700].astype(np.float64) * a[m] / 127 - x[m])
+        assert np.all(err <= a[m] / 254 * (1 + 1e-5))
+        # monotone in x within a row
+        order = np.argsort(x[m], kind="stable")
+        assert np.all(np.diff(xq[m, order].astype(np.int32)) >= 0)
+    xq_neg, a_neg = oracle.quant_acts(-x)
+    assert np.array_equal(xq_neg, -xq) and np.array_equal(a_neg, a)
+    xq_s, _ = oracle.quant_acts(x * np.float32(8.0))
+    assert np.array_equal(xq_s, xq)
+
+
+def test_act_quant_exhaustive_bf16_rounding():
+    # every finite bf16 value, quantised against a row maximum a: the code is the integer
+    # nearest to the fp32 product x * fl32(127 / a), with ties going to the even integer
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_bits_to_f32(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    finite = np.isfinite(ref)
+    assert np.array_equal(vals[finite].view(np.uint32), ref[finite].view(np.uint32))
+    vals = vals[finite]
+    for a in (np.float32(3.0), np.float32(1.0), np.float32(1e-3), np.float32(6.5e4)):
+        row = vals[np.abs(vals) <= a]
+        row = np.concatenate([row, [a]]).astype(np.float32)
+        xq, amax = oracle.quant_acts(row[None, :])
+        assert amax[0] == a
+        s = np.float32(127.0) / a
+        prod = (row * s).astype(np.float64)  # fp32 product, exact in float64
+        code = xq[0, : row.size].astype(np.float64)
+        diff = prod - code
+        assert np.all(np.abs(diff) <= 0.5)
+        tie = np.abs(diff) == 0.5
+        assert np.all(code[tie] % 2 == 0)
+
+
+# ------------------------------------------------------------------ P5/P6: contraction
+def test_matmul_special_cases():
+    # [BH] 1.1: +1 adds the activation, -1 subtracts it, 0 skips it
+    k = 300
+    xq = _rng(5).integers(-127, 128, (3, 512)).astype(np.int8)
+    xq[:, k:] = 0
+    q = np.zeros((5, k), np.int8)
+    q[0] = 1
+    q[1] = -1
+    q[3, 17] = 1  # one-hot row picks one activation
+    q[4, ::2] = 1
+    q[4, 1::2] = -1
+    acc = oracle.matmul(q, xq, k)
+    s = xq[:, :k].astype(np.int64).sum(1)
+    assert acc.shape == (3, 5)
+    assert np.array_equal(acc[:, 0], s)
+    assert np.array_equal(acc[:, 1], -s)
+    assert np.all(acc[:, 2] == 0)
+    assert np.array_equal(acc[:, 3], xq[:, 17].astype(np.int64))
+    alt = xq[:, :k:2].astype(np.int64).sum(1) - xq[:, 1:k:2].astype(np.int64).sum(1)
+    assert np.array_equal(acc[:, 4], alt)
+    # one-hot activation picks one column of the codes
+    qr = _rng(6).integers(-1, 2, (7, k)).astype(np.int8)
+    xo = np.zeros((2, k), np.int8)
+    xo[1, 42] = 1
+    acc = oracle.matmul(qr, xo, k)
+    assert np.all(acc[0] == 0) and np.array_equal(acc[1], qr[:, 42].astype(np.int32))
+
+
+def test_matmul_vs_numpy_int64():
+    rng = _rng(8)
+    for m, n, k in [(1, 7, 5), (4, 33, 257), (9, 64, 1000)]:
+        q = rng.integers(-1, 2, (n, k)).astype(np.int8)
+        xq = rng.integers(-127, 128, (m, oracle.k_pad(k))).astype(np.int8)
+        ref = xq[:, :k].astype(np.int64) @ q.astype(np.int64).T
+        assert np.array_equal(oracle.matmul(q, xq, k), ref)
+
+
+def test_matmul_extreme_range_fits_int32():
+    # |acc| <= 127 * K; the largest K of the workloads stays below 2^24, so the int32 ->
+    # fp32 conversion in the rescale is exact
+    assert 127 * 28672 < 2 ** 24
+    k = 28672
+    q = np.ones((2, k), np.int8)
+    q[1] = -1
+    xq = np.full((1, k), 127, np.int8)
+    acc = oracle.matmul(q, xq, k)
+    assert acc.tolist() == [[127 * k, -127 * k]]
+
+
+def test_matmul_permutation_invariance():
+    rng = _rng(9)
+    k = 200
+    q = rng.integers(-1, 2, (6, k)).astype(np.int8)
+    xq = rng.integers(-127, 128, (3, k)).astype(np.int8)
+    perm = rng.permutation(k)
+    assert np.array_equal(oracle.matmul(q, xq, k), oracle.matmul(q[:, perm].copy(), xq[:, perm].copy(), k))
+
+
+# ------------------------------------------------------------------ P7: brute-force float
+def test_forward_within_quantisation_error_tiny():
+    for seed, (m, n, k) in enumerate([(1, 8, 16), (3, 64, 256), (4, 17, 100)]):
+        w = synth.latent_weights(n, k, seed=100 + seed).numpy()
+        x = synth.activations(m, k, seed=600 + seed, dtype=torch.float32,
+                              outlier_p=0.05, outlier_mult=20.0).numpy()
+        g, q, packed = oracle.quantize_weights(w)
+        xq, a = oracle.quant_acts(x)
+        acc, y = oracle.forward(oracle.unpack(packed, n, k), g, xq, a, k)
+        g64 = float(g)
+        x64 = x.astype(np.float64)
+        # against the dequantised weights: only activation rounding, |dx| <= a/254
+        yq = x64 @ (g64 * q.astype(np.float64)).T
+        bound_a = (a.astype(np.float64)[:, None] / 254) * g64 * np.abs(q).sum(1)[None, :]
+        assert np.all(np.abs(y - yq) <= bound_a * (1 + 1e-6) + 1e-12)
+        # against the latent weights: add the weight rounding term sum |W - gamma q| |x|
+        yl = x64 @ w.astype(np.float64).T
+        bound_w = np.abs(x64) @ np.abs(w.astype(np.float64) - g64 * q).T
+        assert np.all(np.abs(y - yl) <= (bound_a + bound_w) * (1 + 1e-6) + 1e-12)
+
+
+def test_rescale_closed_form():
+    acc = np.array([[127, -254, 0]], np.int32)
+    y = oracle.rescale(acc, np.float32(0.5), np.array([2.0], np.float32))
+    assert y.tolist() == [[1.0, -2.0, 0.0]]
