@@ -1,0 +1,273 @@
+"""Benchmark of the BitLinear forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 1] [--no-cpu-baseline]
+
+A step is one pass of the hot path over one batch of synthetic input: for every matrix of
+the workload, the per-token int8 activation quantiser and the forward (packed-ternary x
+int8 contraction, exact int32 accumulation, fp32 rescale).  The weights are quantised and
+packed once, before timing, as at model load; their quantiser is timed separately.
+
+Headline (default workload 1): 2B-class decode at M = 1, gate/up 2560->6912 and down
+6912->2560, cycling through 48 distinct weight sets (637 MB of packed weights, more than
+twice the 256 MB Infinity Cache) so every step streams its weights from HBM.  value =
+packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
+  roofline     the decode kernel's algorithmic bytes per launch / its mean launch
+               duration (HIP events around each launch) against 8 TB/s;
+  legs         the other workloads: M = 16 full layer, M = 2048 prefill (int8 TOPS vs
+               5.0 POPS dense int8 MFMA), 100B-class M = 1 and M = 8 sweeps;
+  cpu_baseline the CPU oracle on the host, on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
+I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA (no sparsity)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--legs", default="2,3,4", help="other workloads to time into 'legs' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    return ap.parse_args()
+
+
+class Matrix:
+    """One quantised weight matrix with its pre-drawn activations and output buffers."""
+
+    def __init__(self, bl, synth, wl, layer, midx, k, n, m, dev):
+        import torch
+
+        w = synth.latent_weights(n, k, seed=synth.weight_seed(wl.index, layer, midx), device=dev)
+        self.packed, self.gamma = bl.quantize_weights(w)
+        del w
+        self.x = synth.activations(m, k, seed=synth.act_seed(wl.index, layer, midx), dtype=wl.act_dtype,
+                                   device=dev, outlier_p=wl.outlier_p, outlier_mult=wl.outlier_mult)
+        self.n, self.k, self.m = n, k, m
+        self.bytes = bl.packed_bytes(n, k)
+
+
+class Workload:
+    def __init__(self, bl, synth, idx, m, dev):
+        import torch
+
+        self.wl = synth.WORKLOADS[idx]
+        self.m = m
+        self.bl = bl
+        sets = self.wl.layers if self.wl.layers > 1 else self.wl.rotate_sets
+        self.sets = []
+        for s in range(sets):
+            self.sets.append([Matrix(bl, synth, self.wl, s, i, k, n, m, dev)
+                              for i, (_, k, n) in enumerate(self.wl.matrices)])
+        torch.cuda.synchronize()
+        # output buffers shared by all sets (same shapes)
+        self.bufs = {}
+        for mat in self.sets[0]:
+            key = (mat.k, mat.n)
+            if key not in self.bufs:
+                self.bufs[key] = (torch.empty((m, bl.k_pad(mat.k)), dtype=torch.int8, device=dev),
+                                  torch.empty(m, dtype=torch.float32, device=dev),
+                                  torch.empty((m, mat.n), dtype=torch.float32, device=dev))
+        self.sweep = self.wl.layers > 1  # a step sweeps every layer instead of one set
+        self.cursor = 0
+
+    def step_sets(self):
+        if self.sweep:
+            return self.sets
+        s = self.sets[self.cursor]
+        self.cursor = (self.cursor + 1) % len(self.sets)
+        return [s]
+
+    def bytes_per_step(self):
+        n = len(self.sets) if self.sweep else 1
+        return n * sum(mat.bytes for mat in self.sets[0])
+
+    def ops_per_step(self):
+        n = len(self.sets) if self.sweep else 1
+        return n * sum(2 * self.m * mat.n * mat.k for mat in self.sets[0])
+
+    def run_step(self, events=None):
+        bl = self.bl
+        for s in self.step_sets():
+            for mat in s:
+                xq, a, y = self.bufs[(mat.k, mat.n)]
+                bl.quantize_acts(mat.x, xq, a)
+                if events is not None:
+                    e0, e1 = events.pop()
+                    e0.record()
+                    bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
+                    e1.record()
+                    events_done.append((e0, e1, mat.bytes, 2 * self.m * mat.n * mat.k))
+                else:
+                    bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
+
+
+events_done = []
+
+
+def time_steps(w: Workload, steps: int, warmup: int):
+    import torch
+
+    for _ in range(warmup):
+        w.run_step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        w.run_step()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per step
+
+
+def time_forward_launches(w: Workload, steps: int):
+    """Mean duration of the forward kernel launches (event pair around each launch)."""
+    import torch
+
+    per_step = sum(len(s) for s in (w.sets if w.sweep else w.sets[:1]))
+    n_ev = steps * per_step
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    events_done.clear()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        w.run_step(events=evs)
+    torch.cuda.synchronize()
+    tot_ms = sum(e0.elapsed_time(e1) for e0, e1, _, _ in events_done)
+    tot_bytes = sum(b for _, _, b, _ in events_done)
+    tot_ops = sum(o for _, _, _, o in events_done)
+    return tot_ms / len(events_done), tot_bytes / len(events_done), tot_ops / len(events_done)
+
+
+def cpu_baseline(w: Workload, budget_s: float):
+    """The oracle on the host over a bounded sample of the same workload (1 thread)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    def acts_host_f32(x):
+        if x.dtype == torch.bfloat16:
+            return oracle.bf16_bits_to_f32(x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+        return x.float().cpu().numpy()
+
+    done_bytes, done_ops, t_used, mats = 0, 0, 0.0, 0
+    for s in w.sets:
+        for mat in s:
+            packed = mat.packed.cpu().numpy()
+            x = acts_host_f32(mat.x)
+            g = np.float32(mat.gamma.cpu().numpy()[0])
+            t0 = time.perf_counter()
+            xq, a = oracle.quant_acts(x)
+            q = oracle.unpack(packed, mat.n, mat.k)
+            oracle.forward(q, g, xq, a, mat.k)
+            t_used += time.perf_counter() - t0
+            done_bytes += mat.bytes
+            done_ops += 2 * w.m * mat.n * mat.k
+            mats += 1
+            if t_used >= budget_s:
+                break
+        if t_used >= budget_s:
+            break
+    return done_bytes, done_ops, t_used, mats
+
+
+def leg_summary(w: Workload, ms: float, launch_ms: float, launch_bytes: float, launch_ops: float):
+    gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9
+    tops = w.ops_per_step() / (ms * 1e-3) / 1e12
+    return {
+        "workload": w.wl.name, "M": w.m, "ms_per_step": round(ms, 5),
+        "packed_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "int8_TOPS": round(tops, 2), "mfma_frac": round(tops / I8_PEAK_TOPS, 4),
+        "tokens_per_s_eq": round(w.m / (ms * 1e-3), 1),  # every matrix of the step applied once per token
+        "forward_launch_us": round(launch_ms * 1e3, 3),
+        "forward_launch_GBps": round(launch_bytes / (launch_ms * 1e-3) / 1e9, 1),
+        "forward_launch_TOPS": round(launch_ops / (launch_ms * 1e-3) / 1e12, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bitlinear_fwd_amd as bl
+    from bitlinear_fwd_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bl.lib()
+    m_head = synth.WORKLOADS[args.workload].m_list[0]
+    head = Workload(bl, synth, args.workload, m_head, dev)
+    ms = time_steps(head, args.steps, args.warmup)
+    launch_ms, launch_bytes, launch_ops = time_forward_launches(head, max(2, min(args.steps, 48)))
+    decode = m_head <= 16
+    value = head.bytes_per_step() / (ms * 1e-3) / 1e9 if decode else head.ops_per_step() / (ms * 1e-3) / 1e12
+    if decode:
+        achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_gemv_mfma", "launch_us": round(launch_ms * 1e3, 3),
+                "algorithmic_bytes_per_launch": int(launch_bytes)}
+    else:
+        achieved = launch_ops / (launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": I8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / I8_PEAK_TOPS, 4), "traffic": None,
+                "kernel": "k_gemm_mfma", "launch_us": round(launch_ms * 1e3, 3),
+                "algorithmic_ops_per_launch": int(launch_ops)}
+    legs = {}
+    for tok in [t for t in args.legs.split(",") if t.strip()]:
+        idx = int(tok)
+        if idx == args.workload:
+            continue
+        for m in synth.WORKLOADS[idx].m_list:
+            w = Workload(bl, synth, idx, m, dev)
+            steps = max(3, args.steps // (20 if w.sweep else 1))
+            lms = time_steps(w, steps, max(1, args.warmup // 4))
+            l_ms, l_b, l_o = time_forward_launches(w, 2 if w.sweep else max(2, min(steps, 32)))
+            legs[f"w{idx}_m{m}"] = leg_summary(w, lms, l_ms, l_b, l_o)
+            del w
+            torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline:
+        b, o, t, mats = cpu_baseline(head, args.cpu_seconds)
+        cpu = {"value": round(b / t / 1e9, 4) if decode else round(o / t / 1e12, 6),
+               "unit": "GB/s" if decode else "TOPS", "cores": 1, "kind": "oracle",
+               "sample": f"{mats} matrices of the same workload (act quant + unpack + int matmul + rescale), "
+                         f"{t:.1f} s, single-threaded scalar C"}
+    out = {
+        "metric": "BitLinear decode packed-weight GB/s (% HBM peak); prefill int8 TOPS (% MFMA)",
+        "value": round(value, 1 if decode else 2),
+        "unit": "GB/s" if decode else "TOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8", "data": "synthetic",
+        "config": {"workload": head.wl.name, "M": m_head,
+                   "matrices": [list(x) for x in head.wl.matrices],
+                   "distinct_weight_sets": len(head.sets),
+                   "packed_bytes_per_step": head.bytes_per_step(),
+                   "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "legs": legs,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+"""MI355X-native BitNet b1.58 BitLinear forward: thin Python binding of libbitlinear.so.
+
+The binding only marshals arguments: every step of the path (weight absmean + ternarise
++ pack, per-token absmax int8 activation quantisation, the packed-ternary x int8
+contraction with exact int32 accumulation, and the fp32 rescale) runs in the HIP kernels
+behind the C ABI declared in ``include/bitlinear.h``.  PyTorch supplies device memory
+and the current stream.  There is no CPU fallback: if the library is missing or a call
+fails, an exception is raised.
+
+The method follows the aratech.ae article "BitNet b1.58: Microsoft's 1-bit LLM that runs
+a 100B model on one CPU" (sub-sections "Ternary weights {-1, 0, +1}" and "BitLinear: the
+building block") and the 2-bit code table of bhfrc.com news 56965, section 4.1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+BL_OK, BL_ERR_INVALID_ARG, BL_ERR_UNSUPPORTED, BL_ERR_HIP = 0, -1, -2, -3
+BL_F32, BL_BF16 = 0, 1
+
+_lib = None
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbitlinear.so (built by ``python -m bitlinear_fwd_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bitlinear_fwd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, p, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.bitlinear_version.restype = c_int
+        L.bitlinear_version.argtypes = []
+        L.bitlinear_status_string.restype = ctypes.c_char_p
+        L.bitlinear_status_string.argtypes = [c_int]
+        for name in ("bitlinear_n_pad", "bitlinear_k_pad"):
+            getattr(L, name).restype = i64
+            getattr(L, name).argtypes = [i64]
+        for name in ("bitlinear_packed_bytes", "bitlinear_wq_workspace_bytes"):
+            getattr(L, name).restype = i64
+            getattr(L, name).argtypes = [i64, i64]
+        L.bitlinear_quantize_weights.restype = c_int
+        L.bitlinear_quantize_weights.argtypes = [p, i64, i64, p, p, p, i64, p]
+        L.bitlinear_quantize_acts.restype = c_int
+        L.bitlinear_quantize_acts.argtypes = [p, c_int, i64, i64, p, p, p]
+        L.bitlinear_forward.restype = c_int
+        L.bitlinear_forward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p]
+        _lib = L
+    return _lib
+
+
+EXPORTED_SYMBOLS = (
+    "bitlinear_version", "bitlinear_status_string", "bitlinear_n_pad", "bitlinear_k_pad",
+    "bitlinear_packed_bytes", "bitlinear_wq_workspace_bytes", "bitlinear_quantize_weights",
+    "bitlinear_quantize_acts", "bitlinear_forward",
+)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != BL_OK:
+        raise BitLinearError(fn, status, lib().bitlinear_status_string(status).decode())
+
+
+def status_string(status: int) -> str:
+    return lib().bitlinear_status_string(status).decode()
+
+
+def version() -> int:
+    return lib().bitlinear_version()
+
+
+def n_pad(n: int) -> int:
+    return int(lib().bitlinear_n_pad(n))
+
+
+def k_pad(k: int) -> int:
+    return int(lib().bitlinear_k_pad(k))
+
+
+def packed_bytes(n: int, k: int) -> int:
+    return int(lib().bitlinear_packed_bytes(n, k))
+
+
+def wq_workspace_bytes(n: int, k: int) -> int:
+    return int(lib().bitlinear_wq_workspace_bytes(n, k))
+
+
+def _stream(device) -> int:
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require_cuda(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize_weights(W, packed=None, gamma=None, workspace=None):
+    """Ternarise + pack latent weights W[N][K] (fp32, out x in) on the GPU.
+
+    Returns ``(packed uint8 [packed_bytes(N, K)], gamma fp32 [1])``."""
+    import torch
+
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float32 tensor")
+    n, k = W.shape
+    dev = W.device
+    if packed is None:
+        packed = torch.empty(packed_bytes(n, k), dtype=torch.uint8, device=dev)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(wq_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+    _check("bitlinear_quantize_weights", lib().bitlinear_quantize_weights(
+        W.data_ptr(), n, k, packed.data_ptr(), gamma.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(dev)))
+    return packed, gamma
+
+
+def quantize_acts(x, xq=None, absmax=None):
+    """Per-token absmax int8 quantisation of x[M][K] (fp32 or bf16) on the GPU.
+
+    Returns ``(xq int8 [M][K_pad], absmax fp32 [M])``."""
+    import torch
+
+    _require_cuda(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [tokens, features]")
+    if x.dtype == torch.float32:
+        dt = BL_F32
+    elif x.dtype == torch.bfloat16:
+        dt = BL_BF16
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    m, k = x.shape
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((m, k_pad(k)), dtype=torch.int8, device=dev)
+    if absmax is None:
+        absmax = torch.empty(m, dtype=torch.float32, device=dev)
+    _check("bitlinear_quantize_acts", lib().bitlinear_quantize_acts(
+        x.data_ptr(), dt, m, k, xq.data_ptr(), absmax.data_ptr(), _stream(dev)))
+    return xq, absmax
+
+
+def forward(packed, gamma, xq, absmax, n: int, k: int, y=None, acc=None, want_y: bool = True,
+            want_acc: bool = False):
+    """y[M][N] (fp32) and/or acc[M][N] (int32) of the packed-ternary x int8 product.
+
+    Returns y, acc or (y, acc) depending on ``want_y`` / ``want_acc``."""
+    import torch
+
+    for t, name in ((packed, "packed"), (gamma, "gamma"), (xq, "xq"), (absmax, "absmax")):
+        _require_cuda(t, name)
+    m = xq.shape[0]
+    dev = xq.device
+    if want_y and y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    if want_acc and acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    _check("bitlinear_forward", lib().bitlinear_forward(
+        packed.data_ptr(), gamma.data_ptr(), xq.data_ptr(), absmax.data_ptr(), m, n, k,
+        y.data_ptr() if y is not None else None, acc.data_ptr() if acc is not None else None,
+        _stream(dev)))
+    if want_y and want_acc:
+        return y, acc
+    return y if want_y else acc
+
+
+class BitLinear:
+    """Inference-time BitLinear: weights quantised once, forward per token batch."""
+
+    def __init__(self, W):
+        self.n, self.k = W.shape
+        self.packed, self.gamma = quantize_weights(W)
+
+    def __call__(self, x):
+        xq, a = quantize_acts(x)
+        return forward(self.packed, self.gamma, xq, a, self.n, self.k)

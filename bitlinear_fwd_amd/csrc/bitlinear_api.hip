@@ -1,0 +1,78 @@
+// C ABI of libbitlinear.so: argument validation, kernel selection, launch on the caller's
+// stream.  Declarations and the contract of each call are in include/bitlinear.h.
+#include "../../include/bitlinear.h"
+
+#include "bl_internal.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+constexpr int64_t kMaxCount = int64_t(1) << 40;  // exactness bound of the gamma bins
+constexpr int64_t kMaxK = int64_t(1) << 24;      // |acc| <= 127 K < 2^31, and exact in fp32 for K < 2^17
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+constexpr int kDecodeMaxM = 16;                  // tokens handled by the decode kernel
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_version(void) { return kVersion; }
+
+const char* bitlinear_status_string(int status) {
+  switch (status) {
+    case BL_OK: return "ok";
+    case BL_ERR_INVALID_ARG: return "invalid argument (null pointer, size, alignment or workspace)";
+    case BL_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case BL_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int64_t bitlinear_n_pad(int64_t N) { return N < 1 ? -1 : bl::n_pad(N); }
+int64_t bitlinear_k_pad(int64_t K) { return K < 1 ? -1 : bl::k_pad(K); }
+int64_t bitlinear_packed_bytes(int64_t N, int64_t K) {
+  return (N < 1 || K < 1) ? -1 : bl::n_pad(N) * bl::k_pad(K) / 4;
+}
+int64_t bitlinear_wq_workspace_bytes(int64_t N, int64_t K) {
+  return (N < 1 || K < 1) ? -1 : bl::kWqWorkspaceBytes;
+}
+
+int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                               void* workspace, int64_t ws_bytes, void* stream) {
+  if (!W || !packed || !gamma || !workspace) return BL_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim) return BL_ERR_INVALID_ARG;
+  if (N > kMaxCount / K) return BL_ERR_UNSUPPORTED;
+  if (ws_bytes < bl::kWqWorkspaceBytes) return BL_ERR_INVALID_ARG;
+  if (!aligned(W, 4) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 8))
+    return BL_ERR_INVALID_ARG;
+  return hip_status(bl::launch_weight_quant(W, N, K, packed, gamma, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_quantize_acts(const void* X, int dt, int64_t M, int64_t K, int8_t* Xq, float* absmax,
+                            void* stream) {
+  if (!X || !Xq || !absmax) return BL_ERR_INVALID_ARG;
+  if (M < 1 || K < 1 || M >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
+  if (!aligned(X, dt == BL_F32 ? 4 : 2) || !aligned(Xq, 16) || !aligned(absmax, 4)) return BL_ERR_INVALID_ARG;
+  return hip_status(
+      bl::launch_act_quant(X, dt == BL_BF16 ? 1 : 0, M, K, Xq, absmax, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
+                      int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream) {
+  if (!packed || !gamma || !Xq || !absmax || (!Y && !acc)) return BL_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (!aligned(packed, 16) || !aligned(Xq, 16) || !aligned(gamma, 4) || !aligned(absmax, 4) ||
+      (Y && !aligned(Y, 4)) || (acc && !aligned(acc, 4)))
+    return BL_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= kDecodeMaxM) return hip_status(bl::launch_gemv(packed, gamma, Xq, absmax, M, N, K, Y, acc, s));
+  if (M > 65535LL * 128) return BL_ERR_UNSUPPORTED;  // grid.y limit of the prefill launch
+  return hip_status(bl::launch_gemm(packed, gamma, Xq, absmax, M, N, K, Y, acc, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal declarations shared by the HIP sources of libbitlinear.so (not installed).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kTileRows = 16;      // rows (output features) per packed tile
+constexpr int kTileCols = 256;     // columns (input features) per packed tile
+constexpr int kTileBytes = 1024;   // 16 x 256 codes at 2 bits
+constexpr int kWqBins = 256;       // one exact bin per fp32 exponent field
+// quantiser workspace: 256 uint64 bins, then fp32 1/gamma
+constexpr int64_t kWqWorkspaceBytes = kWqBins * 8 + 256;
+
+// Decode one packed 32-bit word (16 consecutive codes, layout of bitlinear.h) into 16
+// int8 values in column order, four per dword.  Code table: 00 -> 0, 01 -> +1,
+// 10 -> -1, 11 -> 0 (padding).  Fields 0 and 2 use the low two bits of each byte as a
+// v_perm_b32 selector into the bytes {00, 01, FF, 00}; fields 1 and 3 keep the selector
+// in bits 2-3 (values 0, 4, 8, 12), which v_perm_b32 maps to byte 0 of the low source
+// (0x00), byte 0 of the high source (0x01), the sign of byte 1 of the low source (0x80
+// -> 0xFF) and the constant 0x00.  One shift, four ANDs and four permutes per 16 weights.
+__device__ __forceinline__ v4i decode16(uint32_t w) {
+  const uint32_t hi = w >> 4;
+  v4i r;
+  r.x = (int)__builtin_amdgcn_perm(0u, 0x00FF0100u, w & 0x03030303u);
+  r.y = (int)__builtin_amdgcn_perm(0x00000001u, 0x00008000u, w & 0x0C0C0C0Cu);
+  r.z = (int)__builtin_amdgcn_perm(0u, 0x00FF0100u, hi & 0x03030303u);
+  r.w = (int)__builtin_amdgcn_perm(0x00000001u, 0x00008000u, hi & 0x0C0C0C0Cu);
+  return r;
+}
+
+__device__ __forceinline__ v4i as_v4i(uint4 u) {
+  v4i r;
+  r.x = (int)u.x;
+  r.y = (int)u.y;
+  r.z = (int)u.z;
+  r.w = (int)u.w;
+  return r;
+}
+
+// Launchers (return hipSuccess or the launch error).  All sizes are validated by the
+// C ABI before these are called.
+hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                               void* workspace, hipStream_t s);
+hipError_t launch_act_quant(const void* X, int bf16, int64_t M, int64_t K, int8_t* Xq, float* absmax,
+                            hipStream_t s);
+hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
+                       int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
+hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
+                       int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
+
+inline int64_t n_pad(int64_t n) { return (n + kTileRows - 1) / kTileRows * kTileRows; }
+inline int64_t k_pad(int64_t k) { return (k + kTileCols - 1) / kTileCols * kTileCols; }
+
+}  // namespace bl

@@ -1,0 +1,122 @@
+/*
+ * bitlinear.h - C ABI of libbitlinear.so, the MI355X (gfx950) BitNet b1.58 BitLinear
+ * forward.
+ *
+ * The operation (pages: aratech.ae "BitNet b1.58: Microsoft's 1-bit LLM that runs a
+ * 100B model on one CPU", sub-sections "Ternary weights {-1, 0, +1}" and "BitLinear:
+ * the building block"; bhfrc.com news 56965, sections 1.1 and 4.1):
+ *
+ *   1. weights W[N][K] (out x in) -> gamma = mean |W| over the whole tensor, codes
+ *      q = clamp(round(W / gamma), -1, 1) in {-1, 0, +1}, packed at 2 bits per weight
+ *      with the code table 00 -> 0, 01 -> +1, 10 -> -1, 11 -> padding;
+ *   2. activations x[M][K] -> per token (row) a[m] = max_k |x[m][k]|, int8 codes
+ *      xq = clamp(round(x * 127 / a), -127, 127);
+ *   3. acc[m][n] = sum_k xq[m][k] * q[n][k], exact in int32 (each term adds, subtracts
+ *      or skips an activation);
+ *   4. y[m][n] = acc[m][n] * gamma * a[m] / 127 in fp32.
+ *
+ * Numeric conventions fixed by this library (the pages leave them open):
+ *   - gamma is the exact mean of |W| rounded to the nearest fp32 (ties to even); it
+ *     does not depend on summation order, so it is reproducible bit for bit.
+ *   - "round" is round-half-to-even; the ternarise decision is t = fl32(W * fl32(1/gamma)),
+ *     the activation decision t = fl32(x * fl32(127/a)); gamma == 0 gives all-zero codes,
+ *     a zero row gives zero codes and a[m] = 0.
+ *   - The packed layout (below) is designed for gfx950 loads; it is not a file format
+ *     from the pages.
+ *
+ * Packed weight layout.  N_pad = roundup(N, 16), K_pad = roundup(K, 256).  The buffer
+ * holds N_pad*K_pad/4 bytes as 1024-byte tiles; tile (nb, c) starts at byte
+ * (nb*(K_pad/256) + c)*1024 and covers rows 16nb..16nb+15, columns 256c..256c+255.  In a
+ * tile, row r and column offset kk sit in the little-endian 32-bit word at byte
+ * 16*(16*(kk/64) + r) + 4*((kk%64)/16), bits 8*(kk%4) + 2*((kk%16)/4) (+1).  So each
+ * 16-byte slot is 64 consecutive columns of one row, one 64-lane wave load covers a
+ * whole tile, and (word >> 2f) & 0x03030303 yields four consecutive codes, one per byte.
+ * Entries outside N x K hold the padding code 11 (decoded as 0).
+ *
+ * Activation layout.  xq is int8 [M][K_pad], row-major, padding columns zero.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers (HIP global memory) owned by the caller;
+ *     the library allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work
+ *     and return; completion is observed through the stream.
+ *   - Arguments are validated on the host before anything is enqueued; errors are
+ *     returned synchronously as a negative bl_status and nothing is launched.  A failed
+ *     launch returns BL_ERR_HIP.  Device data (NaN/Inf) is never inspected: inputs must
+ *     be finite.
+ *   - Work enqueued on one stream may run concurrently with work on another; buffers
+ *     shared between streams are the caller's responsibility.
+ */
+#ifndef BITLINEAR_H_
+#define BITLINEAR_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BL_OK = 0,
+  BL_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad alignment, small workspace */
+  BL_ERR_UNSUPPORTED = -2, /* a shape or dtype this build does not handle */
+  BL_ERR_HIP = -3          /* a HIP runtime call or kernel launch failed */
+} bl_status;
+
+typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int bitlinear_version(void);
+
+/* Static text for a bl_status value (never NULL). */
+const char* bitlinear_status_string(int status);
+
+/* Host-only size helpers; return -1 for arguments < 1. */
+int64_t bitlinear_n_pad(int64_t N);                         /* roundup(N, 16)            */
+int64_t bitlinear_k_pad(int64_t K);                         /* roundup(K, 256)           */
+int64_t bitlinear_packed_bytes(int64_t N, int64_t K);       /* N_pad * K_pad / 4         */
+int64_t bitlinear_wq_workspace_bytes(int64_t N, int64_t K); /* scratch for the quantiser */
+
+/*
+ * Step 1 - weight quantiser (aratech.ae, "Ternary weights {-1, 0, +1}"; code table from
+ * bhfrc.com section 4.1).
+ *   W         [N][K] fp32, row-major, N = out_features, K = in_features. 4-byte aligned.
+ *   packed    out: bitlinear_packed_bytes(N, K) bytes in the layout above, 16-byte aligned.
+ *   gamma     out: one fp32, the absmean scale (written on the device).
+ *   workspace device scratch of at least bitlinear_wq_workspace_bytes(N, K) bytes,
+ *             8-byte aligned; it is initialised by the call itself.
+ * Requires 1 <= N, K and N*K < 2^40.  Not safe to run concurrently on one workspace.
+ */
+int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                               void* workspace, int64_t ws_bytes, void* stream);
+
+/*
+ * Step 2 - per-token absmax int8 activation quantiser (aratech.ae, "BitLinear: the
+ * building block": the largest magnitude of each token maps to 127).
+ *   X       [M][K] fp32 (dt = BL_F32) or bf16 (dt = BL_BF16), row-major, element-aligned.
+ *   Xq      out: int8 [M][K_pad], 16-byte aligned; columns K..K_pad-1 are set to 0.
+ *   absmax  out: fp32 [M], a[m] = max_k |X[m][k]|.
+ */
+int bitlinear_quantize_acts(const void* X, int dt, int64_t M, int64_t K, int8_t* Xq, float* absmax,
+                            void* stream);
+
+/*
+ * Steps 3 + 4 - packed-ternary x int8 contraction with exact int32 accumulation
+ * (bhfrc.com section 1.1: add / subtract / skip) and the rescale to fp32.
+ *   packed  from bitlinear_quantize_weights for the same N, K; 16-byte aligned.
+ *   gamma   device pointer to the fp32 weight scale.
+ *   Xq      int8 [M][K_pad] and absmax fp32 [M] from bitlinear_quantize_acts.
+ *   Y       out (nullable): fp32 [M][N], y = acc * gamma * absmax[m] / 127.
+ *   acc     out (nullable): int32 [M][N], the exact accumulators.
+ * At least one of Y and acc must be non-null.  M = 1..16 runs the decode kernel
+ * (HBM-streaming, MFMA on in-register decoded weights); larger M runs the prefill GEMM
+ * (weights decoded into LDS, int8 MFMA).  |acc| <= 127*K must fit int32: K <= 2^24.
+ */
+int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
+                      int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H_ */

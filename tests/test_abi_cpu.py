@@ -1,0 +1,113 @@
+"""The C ABI library loads and exports every symbol include/bitlinear.h declares; host-only
+helpers and argument validation behave as documented.  No compute call reaches a GPU:
+every call here is rejected on the host before anything is enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bitlinear_fwd_amd as bl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+def test_library_present():
+    assert os.path.exists(bl.LIB_PATH), "build with `python -m bitlinear_fwd_amd.build`"
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert set(declared) == set(bl.EXPORTED_SYMBOLS)
+    L = bl.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    # and they are real dynamic symbols of the shared object
+    out = subprocess.run(["nm", "-D", "--defined-only", bl.LIB_PATH], capture_output=True, text=True).stdout
+    for name in declared:
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_host_size_helpers():
+    assert bl.n_pad(1) == 16 and bl.n_pad(16) == 16 and bl.n_pad(17) == 32
+    assert bl.k_pad(1) == 256 and bl.k_pad(256) == 256 and bl.k_pad(257) == 512
+    assert bl.packed_bytes(28672, 8192) == 58_720_256
+    assert bl.packed_bytes(6912, 2560) == 4_423_680
+    assert bl.packed_bytes(17, 300) == 32 * 512 // 4
+    assert bl.packed_bytes(0, 5) == -1 and bl.k_pad(0) == -1
+    assert bl.wq_workspace_bytes(100, 100) >= 256 * 8 + 4
+    assert bl.version() >= 10000
+
+
+def test_status_strings():
+    for s in (bl.BL_OK, bl.BL_ERR_INVALID_ARG, bl.BL_ERR_UNSUPPORTED, bl.BL_ERR_HIP, 7):
+        assert isinstance(bl.status_string(s), str) and bl.status_string(s)
+
+
+FAKE = 0x10000  # 64 KiB-aligned non-null address; never dereferenced (calls are rejected first)
+
+
+def test_forward_argument_validation():
+    L = bl.lib()
+    ok = dict(packed=FAKE, gamma=FAKE, xq=FAKE, a=FAKE, M=1, N=16, K=256, y=FAKE, acc=None)
+
+    def call(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return L.bitlinear_forward(d["packed"], d["gamma"], d["xq"], d["a"], d["M"], d["N"], d["K"], d["y"],
+                                   d["acc"], None)
+
+    assert call(packed=None) == bl.BL_ERR_INVALID_ARG
+    assert call(gamma=None) == bl.BL_ERR_INVALID_ARG
+    assert call(xq=None) == bl.BL_ERR_INVALID_ARG
+    assert call(a=None) == bl.BL_ERR_INVALID_ARG
+    assert call(y=None, acc=None) == bl.BL_ERR_INVALID_ARG
+    assert call(M=0) == bl.BL_ERR_INVALID_ARG
+    assert call(N=0) == bl.BL_ERR_INVALID_ARG
+    assert call(K=-3) == bl.BL_ERR_INVALID_ARG
+    assert call(K=(1 << 24) + 1) == bl.BL_ERR_INVALID_ARG
+    assert call(packed=FAKE + 8) == bl.BL_ERR_INVALID_ARG  # packed must be 16-byte aligned
+    assert call(xq=FAKE + 4) == bl.BL_ERR_INVALID_ARG
+    assert call(y=FAKE + 2) == bl.BL_ERR_INVALID_ARG
+
+
+def test_quantize_argument_validation():
+    L = bl.lib()
+    ws = bl.wq_workspace_bytes(16, 256)
+    assert L.bitlinear_quantize_weights(None, 16, 256, FAKE, FAKE, FAKE, ws, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_weights(FAKE, 16, 256, FAKE, FAKE, FAKE, ws - 1, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_weights(FAKE, 0, 256, FAKE, FAKE, FAKE, ws, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_weights(FAKE, 16, 256, FAKE + 4, FAKE, FAKE, ws, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_weights(FAKE, 1 << 21, 1 << 20, FAKE, FAKE, FAKE, ws, None) == bl.BL_ERR_UNSUPPORTED
+    assert L.bitlinear_quantize_acts(FAKE, 5, 1, 16, FAKE, FAKE, None) == bl.BL_ERR_UNSUPPORTED
+    assert L.bitlinear_quantize_acts(None, bl.BL_F32, 1, 16, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_acts(FAKE, bl.BL_F32, 0, 16, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_acts(FAKE + 2, bl.BL_F32, 1, 16, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_acts(FAKE, bl.BL_BF16, 1, 16, FAKE + 8, FAKE, None) == bl.BL_ERR_INVALID_ARG
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    with pytest.raises(ValueError):
+        bl.quantize_weights(torch.zeros(4, 4))
+    with pytest.raises(ValueError):
+        bl.quantize_acts(torch.zeros(4, 4))
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "bitlinear_fwd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src, f
+                assert "liboracle" not in src and "bitlinear_oracle" not in src, f

@@ -1,0 +1,245 @@
+"""GPU parity of every step against the CPU oracle, through the C ABI (ctypes binding).
+
+Stage-wise: each kernel is fed bytes the oracle also consumes (device tensors copied to
+the host), so a mismatch names the stage.  End-to-end cases live in test_gpu_workloads.py.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import bitlinear_fwd_amd as bl
+import oracle
+from bitlinear_fwd_amd import synth
+from gpu_helpers import acts_host_f32, check_equal, check_y, gamma_bits, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _announce(*a):
+    print("case:", *a, flush=True)
+
+
+# ------------------------------------------------------------------ weight quantiser
+def _wq_check(w_dev: torch.Tensor, tag: str):
+    packed, gamma = bl.quantize_weights(w_dev)
+    torch.cuda.synchronize()
+    w = host(w_dev)
+    g_ref, q_ref, p_ref = oracle.quantize_weights(w)
+    assert gamma_bits(host(gamma)) == gamma_bits(g_ref), (tag, float(host(gamma)[0]), float(g_ref))
+    check_equal(host(packed), p_ref, f"packed {tag}")
+    return packed, gamma, q_ref, g_ref
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (16, 256), (17, 300), (33, 513), (512, 256), (100, 1000),
+                                 (64, 4103), (3, 70000), (1000, 3)])
+def test_weight_quant_random(n, k):
+    _announce("weight_quant", n, k)
+    _wq_check(synth.latent_weights(n, k, seed=n * 7 + k, device=DEV), f"{n}x{k}")
+
+
+def test_weight_quant_golden_ties():
+    with open(os.path.join(GOLDEN, "quant_examples.json")) as f:
+        cases = json.load(f)["weights"]
+    for c in cases:
+        _announce("weight_quant golden", c["W"])
+        w = torch.tensor(c["W"], dtype=torch.float32, device=DEV)
+        packed, gamma, q_ref, _ = _wq_check(w, str(c["W"]))
+        assert float(host(gamma)[0]) == c["gamma"]
+        n, k = w.shape
+        assert oracle.unpack(host(packed), n, k).tolist() == c["q"]
+
+
+def test_weight_quant_wide_range_and_subnormals():
+    rng = np.random.default_rng(5)
+    for trial in range(6):
+        _announce("weight_quant wide", trial)
+        n, k = int(rng.integers(1, 40)), int(rng.integers(1, 700))
+        w = (rng.standard_normal((n, k)) * 10.0 ** rng.uniform(-44, 37, (n, k))).astype(np.float32)
+        if trial == 3:
+            w[:] = np.float32(1e-45) * rng.integers(0, 5, (n, k))  # subnormal-only tensor
+        _wq_check(torch.from_numpy(w).to(DEV), f"wide{trial}")
+
+
+def test_weight_quant_special_tensors():
+    for name, w in [("zeros", np.zeros((16, 256), np.float32)),
+                    ("const", np.full((20, 300), -0.03125, np.float32)),
+                    ("one_hot", np.eye(17, 260, dtype=np.float32))]:
+        _announce("weight_quant", name)
+        _wq_check(torch.from_numpy(w).to(DEV), name)
+
+
+def test_weight_quant_unaligned_source():
+    _announce("weight_quant unaligned")
+    base = synth.latent_weights(1, 33 * 256 + 1, seed=3, device=DEV).reshape(-1)
+    w = base[1:].view(33, 256)  # 4-byte aligned, not 16-byte aligned: scalar load path
+    assert w.data_ptr() % 16 != 0
+    _wq_check(w, "unaligned")
+
+
+def test_weight_quant_deterministic():
+    w = synth.latent_weights(700, 2560, seed=99, device=DEV)
+    p1, g1 = bl.quantize_weights(w)
+    p2, g2 = bl.quantize_weights(w)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2) and torch.equal(g1, g2)
+
+
+# ------------------------------------------------------------------ activation quantiser
+def _aq_check(x_dev: torch.Tensor, tag: str):
+    xq, a = bl.quantize_acts(x_dev)
+    torch.cuda.synchronize()
+    xq_ref, a_ref = oracle.quant_acts(acts_host_f32(x_dev))
+    check_equal(host(a).view(np.uint32), a_ref.view(np.uint32), f"absmax {tag}")
+    check_equal(host(xq), xq_ref, f"xq {tag}")
+    return xq, a, xq_ref, a_ref
+
+
+@pytest.mark.parametrize("m,k,dtype", [(1, 256, torch.float32), (3, 300, torch.float32), (5, 2560, torch.bfloat16),
+                                       (16, 6912, torch.bfloat16), (7, 1000, torch.bfloat16),
+                                       (4, 999, torch.bfloat16), (2, 28672, torch.bfloat16),
+                                       (9, 12000, torch.float32), (300, 64, torch.bfloat16)])
+def test_act_quant(m, k, dtype):
+    _announce("act_quant", m, k, dtype)
+    x = synth.activations(m, k, seed=m * 131 + k, dtype=dtype, device=DEV, outlier_p=0.01, outlier_mult=20.0)
+    _aq_check(x, f"{m}x{k}")
+
+
+def test_act_quant_golden_and_zero_rows():
+    with open(os.path.join(GOLDEN, "quant_examples.json")) as f:
+        cases = json.load(f)["acts"]
+    for c in cases:
+        _announce("act_quant golden", c["x"])
+        x = torch.tensor([c["x"]], dtype=torch.float32, device=DEV)
+        xq, a, _, _ = _aq_check(x, str(c["x"]))
+        assert host(xq)[0, : len(c["x"])].tolist() == c["xq"]
+    x = synth.activations(6, 512, seed=1, dtype=torch.bfloat16, device=DEV)
+    x[2] = 0
+    _aq_check(x, "zero row")
+
+
+def test_act_quant_unaligned_source():
+    for dtype in (torch.float32, torch.bfloat16):
+        _announce("act_quant unaligned", dtype)
+        flat = synth.activations(1, 4 * 512 + 1, seed=4, dtype=dtype, device=DEV).reshape(-1)
+        x = flat[1:].view(4, 512)
+        assert x.data_ptr() % 16 != 0
+        _aq_check(x, f"unaligned {dtype}")
+
+
+def test_act_quant_every_bf16_value():
+    # one token holding every finite bf16 value, plus rows scaled so the maximum varies
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_bits_to_f32(bits)
+    keep = bits[np.isfinite(vals)]
+    keep = keep[: len(keep) // 8 * 8]
+    row = torch.from_numpy(keep.view(np.int16)).to(DEV).view(torch.bfloat16)
+    small = row[(row.float().abs() <= 3.0)]
+    small = small[: small.numel() // 8 * 8]
+    for tag, x in [("all", row[None, :]), ("le3", small[None, :])]:
+        _announce("act_quant bf16 sweep", tag)
+        _aq_check(x.contiguous(), tag)
+
+
+def test_act_quant_deterministic():
+    x = synth.activations(64, 6912, seed=8, dtype=torch.bfloat16, device=DEV, outlier_p=0.005, outlier_mult=30.0)
+    a1 = bl.quantize_acts(x)
+    a2 = bl.quantize_acts(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a1[0], a2[0]) and torch.equal(a1[1], a2[1])
+
+
+# ------------------------------------------------------------------ forward (contraction + rescale)
+def _fwd_check(m, n, k, seed, want=("y", "acc")):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-1, 2, (n, k)).astype(np.int8)
+    packed = oracle.pack(q)
+    x = synth.activations(m, k, seed=seed, dtype=torch.float32, outlier_p=0.01, outlier_mult=20.0).numpy()
+    if m > 2:
+        x[m // 2] = 0  # a zero token
+    xq, a = oracle.quant_acts(x)
+    gamma = np.float32(0.0159577)
+    acc_ref, y_ref = oracle.forward(q, gamma, xq, a, k)
+    d = lambda arr: torch.from_numpy(arr).to(DEV)
+    y, acc = bl.forward(d(packed), d(np.array([gamma], np.float32)), d(xq), d(a), n, k,
+                        want_y=True, want_acc=True)
+    torch.cuda.synchronize()
+    check_equal(host(acc), acc_ref, f"acc m={m} n={n} k={k}")
+    check_y(host(y), y_ref, f"y m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 15, 16])
+@pytest.mark.parametrize("n,k", [(16, 256), (17, 300), (512, 256), (130, 1000), (48, 2304), (1, 1)])
+def test_forward_decode(m, n, k):
+    _announce("forward decode", m, n, k)
+    _fwd_check(m, n, k, seed=m * 1000 + n + k)
+
+
+@pytest.mark.parametrize("m", [17, 31, 64, 100, 128, 129, 257])
+@pytest.mark.parametrize("n,k", [(16, 256), (17, 300), (130, 1000), (300, 2304), (1, 1), (129, 513)])
+def test_forward_prefill(m, n, k):
+    _announce("forward prefill", m, n, k)
+    _fwd_check(m, n, k, seed=m * 1000 + n + k)
+
+
+def test_forward_extreme_accumulators():
+    # all +1 / all -1 rows against all +127 activations: |acc| = 127 K, the int32 range
+    # the path guarantees for the largest K of the workloads
+    k = 28672
+    for m in (1, 16, 40):
+        _announce("forward extreme", m)
+        q = np.ones((32, k), np.int8)
+        q[1::2] = -1
+        xq = np.full((m, k), 127, np.int8)
+        a = np.full(m, 127.0, np.float32)
+        d = lambda arr: torch.from_numpy(arr).to(DEV)
+        y, acc = bl.forward(d(oracle.pack(q)), d(np.array([1.0], np.float32)), d(xq), d(a), 32, k,
+                            want_y=True, want_acc=True)
+        torch.cuda.synchronize()
+        exp = np.tile(np.array([127 * k, -127 * k], np.int64), 16)
+        assert np.array_equal(host(acc), np.broadcast_to(exp, (m, 32)))
+        check_y(host(y), np.broadcast_to(exp.astype(np.float64), (m, 32)), "extreme y")
+
+
+def test_forward_only_acc_or_only_y():
+    m, n, k = 3, 40, 512
+    rng = np.random.default_rng(1)
+    q = rng.integers(-1, 2, (n, k)).astype(np.int8)
+    xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
+    a = np.ones(m, np.float32)
+    d = lambda arr: torch.from_numpy(arr).to(DEV)
+    acc = bl.forward(d(oracle.pack(q)), d(np.array([0.5], np.float32)), d(xq), d(a), n, k, want_y=False,
+                     want_acc=True)
+    y = bl.forward(d(oracle.pack(q)), d(np.array([0.5], np.float32)), d(xq), d(a), n, k)
+    torch.cuda.synchronize()
+    acc_ref = oracle.matmul(q, xq, k)
+    check_equal(host(acc), acc_ref, "acc only")
+    check_y(host(y), oracle.rescale(acc_ref, np.float32(0.5), a), "y only")
+
+
+def test_forward_deterministic():
+    n, k = 2560, 6912
+    for m in (1, 16, 300):
+        w = synth.latent_weights(n, k, seed=5, device=DEV)
+        packed, gamma = bl.quantize_weights(w)
+        xq, a = bl.quantize_acts(synth.activations(m, k, seed=6, device=DEV))
+        r1 = bl.forward(packed, gamma, xq, a, n, k, want_acc=True)
+        r2 = bl.forward(packed, gamma, xq, a, n, k, want_acc=True)
+        torch.cuda.synchronize()
+        assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
+
+def test_binding_errors_are_raised():
+    w = torch.zeros(4, 4, device=DEV, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        bl.quantize_weights(w)
+    xq = torch.zeros((1, 256), dtype=torch.int8, device=DEV)
+    a = torch.zeros(1, dtype=torch.float32, device=DEV)
+    g = torch.zeros(1, dtype=torch.float32, device=DEV)
+    packed = torch.zeros(bl.packed_bytes(16, 256) + 16, dtype=torch.uint8, device=DEV)[8:]  # misaligned
+    with pytest.raises(bl.BitLinearError):
+        bl.forward(packed, g, xq, a, 16, 256)

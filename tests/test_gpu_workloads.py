@@ -1,0 +1,82 @@
+"""End-to-end parity at the workloads' full sizes, in the launch configuration the
+benchmark times (the same C ABI calls, M decides decode or prefill kernel).
+
+Weights and activations are drawn on the GPU with the seeded generators, the whole path
+runs on the GPU (weight quantiser, activation quantiser, forward), and the oracle runs on
+host copies of the same inputs.  Every stage is compared bit-exactly (gamma, packed
+bytes, xq, absmax, int32 acc) and y within 1e-5 relative.  Where the oracle would take
+minutes (prefill at M = 2048) it computes a sample of token rows, chosen to cover the
+first and last rows and the ragged edges of the 128-row tiles."""
+import numpy as np
+import pytest
+import torch
+
+import bitlinear_fwd_amd as bl
+import oracle
+from bitlinear_fwd_amd import synth
+from gpu_helpers import acts_host_f32, check_equal, check_y, gamma_bits, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(workload: int, layer: int, midx: int, k: int, n: int, m: int, rows=None):
+    wl = synth.WORKLOADS[workload]
+    print(f"case: workload {workload} layer {layer} matrix {midx} K={k} N={n} M={m}", flush=True)
+    w_dev = synth.latent_weights(n, k, seed=synth.weight_seed(workload, layer, midx), device=DEV)
+    x_dev = synth.activations(m, k, seed=synth.act_seed(workload, layer, midx), dtype=wl.act_dtype, device=DEV,
+                              outlier_p=wl.outlier_p, outlier_mult=wl.outlier_mult)
+    packed, gamma = bl.quantize_weights(w_dev)
+    xq, a = bl.quantize_acts(x_dev)
+    y, acc = bl.forward(packed, gamma, xq, a, n, k, want_y=True, want_acc=True)
+    torch.cuda.synchronize()
+    w = host(w_dev)
+    del w_dev
+    g_ref = oracle.gamma_absmean(w)
+    assert gamma_bits(host(gamma)) == gamma_bits(g_ref)
+    q_ref = oracle.ternarise(w, g_ref)
+    del w
+    check_equal(host(packed), oracle.pack(q_ref), "packed")
+    x = acts_host_f32(x_dev)
+    if rows is not None:
+        x = x[rows]
+    xq_ref, a_ref = oracle.quant_acts(x)
+    xq_h, a_h, acc_h, y_h = host(xq), host(a), host(acc), host(y)
+    if rows is not None:
+        xq_h, a_h, acc_h, y_h = xq_h[rows], a_h[rows], acc_h[rows], y_h[rows]
+    check_equal(xq_h, xq_ref, "xq")
+    check_equal(a_h.view(np.uint32), a_ref.view(np.uint32), "absmax")
+    acc_ref, y_ref = oracle.forward(q_ref, g_ref, xq_ref, a_ref, k)
+    check_equal(acc_h, acc_ref, "acc")
+    check_y(y_h, y_ref)
+
+
+def test_workload0_single_bitlinear():
+    _run(0, 0, 0, 256, 512, 1)
+
+
+@pytest.mark.parametrize("midx", [0, 1, 2])
+def test_workload1_2b_decode_m1(midx):
+    _, k, n = synth.WORKLOADS[1].matrices[midx]
+    _run(1, 0, midx, k, n, 1)
+
+
+@pytest.mark.parametrize("midx", range(7))
+def test_workload2_2b_layer_m16(midx):
+    _, k, n = synth.WORKLOADS[2].matrices[midx]
+    _run(2, 0, midx, k, n, 16)
+
+
+@pytest.mark.parametrize("midx", [0, 1])
+def test_workload3_prefill_m2048_sampled(midx):
+    _, k, n = synth.WORKLOADS[3].matrices[midx]
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, 1023, 1024, 2046, 2047],
+                                     np.random.default_rng(midx).integers(0, 2048, 23)]))
+    _run(3, 0, midx, k, n, 2048, rows=rows)
+
+
+@pytest.mark.parametrize("m", [1, 8])
+@pytest.mark.parametrize("midx", [0, 1])
+def test_workload4_100b_decode(midx, m):
+    _, k, n = synth.WORKLOADS[4].matrices[midx]
+    _run(4, 0, midx, k, n, m)
