@@ -1,18 +1,22 @@
 """Benchmark of the BitLinear forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 1] [--legs 2,3,4]
+                    [--no-graph] [--no-cpu-baseline]
 
 A step is one pass of the hot path over one batch of synthetic input: for every matrix of
 the workload, the per-token int8 activation quantiser and the forward (packed-ternary x
-int8 contraction, exact int32 accumulation, fp32 rescale).  The weights are quantised and
-packed once, before timing, as at model load; their quantiser is timed separately.
+int8 contraction, exact int32 accumulation, fp32 rescale).  For a few tokens with short
+rows the two run as one fused kernel (bitlinear_forward_fused); otherwise as two kernels.
+Weights are quantised and packed once, before timing, as at model load.  Each step is
+replayed from a HIP graph captured beforehand (one graph per distinct weight set), so the
+timed region holds only GPU work.
 
 Headline (default workload 1): 2B-class decode at M = 1, gate/up 2560->6912 and down
 6912->2560, cycling through 48 distinct weight sets (637 MB of packed weights, more than
 twice the 256 MB Infinity Cache) so every step streams its weights from HBM.  value =
 packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
-  roofline     the decode kernel's algorithmic bytes per launch / its mean launch
-               duration (HIP events around each launch) against 8 TB/s;
+  roofline     the decode kernel: algorithmic bytes per launch / mean launch duration
+               (HIP event pair around each launch, eager) against 8 TB/s;
   legs         the other workloads: M = 16 full layer, M = 2048 prefill (int8 TOPS vs
                5.0 POPS dense int8 MFMA), 100B-class M = 1 and M = 8 sweeps;
   cpu_baseline the CPU oracle on the host, on a bounded sample of the same workload.
@@ -36,21 +40,20 @@ I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA (no sparsity)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
-    ap.add_argument("--legs", default="2,3,4", help="other workloads to time into 'legs' ('' for none)")
+    ap.add_argument("--legs", default="2,3,4", help="other workloads timed into 'legs' ('' for none)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     return ap.parse_args()
 
 
 class Matrix:
-    """One quantised weight matrix with its pre-drawn activations and output buffers."""
+    """One quantised weight matrix with its pre-drawn activations."""
 
     def __init__(self, bl, synth, wl, layer, midx, k, n, m, dev):
-        import torch
-
         w = synth.latent_weights(n, k, seed=synth.weight_seed(wl.index, layer, midx), device=dev)
         self.packed, self.gamma = bl.quantize_weights(w)
         del w
@@ -58,6 +61,7 @@ class Matrix:
                                    device=dev, outlier_p=wl.outlier_p, outlier_mult=wl.outlier_mult)
         self.n, self.k, self.m = n, k, m
         self.bytes = bl.packed_bytes(n, k)
+        self.ops = 2 * m * n * k
 
 
 class Workload:
@@ -67,13 +71,11 @@ class Workload:
         self.wl = synth.WORKLOADS[idx]
         self.m = m
         self.bl = bl
-        sets = self.wl.layers if self.wl.layers > 1 else self.wl.rotate_sets
-        self.sets = []
-        for s in range(sets):
-            self.sets.append([Matrix(bl, synth, self.wl, s, i, k, n, m, dev)
-                              for i, (_, k, n) in enumerate(self.wl.matrices)])
+        self.sweep = self.wl.layers > 1  # a step sweeps every layer instead of one set
+        nsets = self.wl.layers if self.sweep else self.wl.rotate_sets
+        self.sets = [[Matrix(bl, synth, self.wl, s, i, k, n, m, dev) for i, (_, k, n) in enumerate(self.wl.matrices)]
+                     for s in range(nsets)]
         torch.cuda.synchronize()
-        # output buffers shared by all sets (same shapes)
         self.bufs = {}
         for mat in self.sets[0]:
             key = (mat.k, mat.n)
@@ -81,41 +83,60 @@ class Workload:
                 self.bufs[key] = (torch.empty((m, bl.k_pad(mat.k)), dtype=torch.int8, device=dev),
                                   torch.empty(m, dtype=torch.float32, device=dev),
                                   torch.empty((m, mat.n), dtype=torch.float32, device=dev))
-        self.sweep = self.wl.layers > 1  # a step sweeps every layer instead of one set
+        self.fused = {key: bl.forward_plan(m, key[1], key[0])["kernel"] == "decode" and m <= 4
+                      for key in self.bufs}
         self.cursor = 0
+        self.graphs = None
 
-    def step_sets(self):
-        if self.sweep:
-            return self.sets
-        s = self.sets[self.cursor]
-        self.cursor = (self.cursor + 1) % len(self.sets)
-        return [s]
+    def step_groups(self):
+        """The matrix lists of the distinct steps (one per weight set, or one sweep)."""
+        return [sum(self.sets, [])] if self.sweep else self.sets
+
+    def launch(self, mat, timing=None):
+        bl = self.bl
+        xq, a, y = self.bufs[(mat.k, mat.n)]
+        if self.fused[(mat.k, mat.n)]:
+            if timing is not None:
+                timing[0].record()
+            bl.forward_fused(mat.packed, mat.gamma, mat.x, mat.n, mat.k, y=y, xq=xq, absmax=a)
+        else:
+            bl.quantize_acts(mat.x, xq, a)
+            if timing is not None:
+                timing[0].record()
+            bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
+        if timing is not None:
+            timing[1].record()
+
+    def capture(self):
+        import torch
+
+        self.graphs = []
+        for group in self.step_groups():
+            for mat in group:  # warm the kernels once outside capture
+                self.launch(mat)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for mat in group:
+                    self.launch(mat)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_step(self):
+        groups = self.step_groups()
+        i = self.cursor
+        self.cursor = (self.cursor + 1) % len(groups)
+        if self.graphs is not None:
+            self.graphs[i].replay()
+        else:
+            for mat in groups[i]:
+                self.launch(mat)
 
     def bytes_per_step(self):
-        n = len(self.sets) if self.sweep else 1
-        return n * sum(mat.bytes for mat in self.sets[0])
+        return sum(mat.bytes for mat in self.step_groups()[0])
 
     def ops_per_step(self):
-        n = len(self.sets) if self.sweep else 1
-        return n * sum(2 * self.m * mat.n * mat.k for mat in self.sets[0])
-
-    def run_step(self, events=None):
-        bl = self.bl
-        for s in self.step_sets():
-            for mat in s:
-                xq, a, y = self.bufs[(mat.k, mat.n)]
-                bl.quantize_acts(mat.x, xq, a)
-                if events is not None:
-                    e0, e1 = events.pop()
-                    e0.record()
-                    bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
-                    e1.record()
-                    events_done.append((e0, e1, mat.bytes, 2 * self.m * mat.n * mat.k))
-                else:
-                    bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
-
-
-events_done = []
+        return sum(mat.ops for mat in self.step_groups()[0])
 
 
 def time_steps(w: Workload, steps: int, warmup: int):
@@ -133,26 +154,26 @@ def time_steps(w: Workload, steps: int, warmup: int):
     return start.elapsed_time(stop) / steps  # ms per step
 
 
-def time_forward_launches(w: Workload, steps: int):
-    """Mean duration of the forward kernel launches (event pair around each launch)."""
+def time_forward_launches(w: Workload, passes: int):
+    """Mean duration of the forward kernel launches: an event pair around each launch
+    (eager, on the stream the kernels run on), over `passes` passes of every step group."""
     import torch
 
-    per_step = sum(len(s) for s in (w.sets if w.sweep else w.sets[:1]))
-    n_ev = steps * per_step
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
-    events_done.clear()
+    recs = []
     torch.cuda.synchronize()
-    for _ in range(steps):
-        w.run_step(events=evs)
+    for _ in range(passes):
+        for group in w.step_groups():
+            for mat in group:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                w.launch(mat, timing=ev)
+                recs.append((ev, mat))
     torch.cuda.synchronize()
-    tot_ms = sum(e0.elapsed_time(e1) for e0, e1, _, _ in events_done)
-    tot_bytes = sum(b for _, _, b, _ in events_done)
-    tot_ops = sum(o for _, _, _, o in events_done)
-    return tot_ms / len(events_done), tot_bytes / len(events_done), tot_ops / len(events_done)
+    tot_ms = sum(ev[0].elapsed_time(ev[1]) for ev, _ in recs)
+    return tot_ms / len(recs), sum(m.bytes for _, m in recs) / len(recs), sum(m.ops for _, m in recs) / len(recs)
 
 
 def cpu_baseline(w: Workload, budget_s: float):
-    """The oracle on the host over a bounded sample of the same workload (1 thread)."""
+    """The oracle on the host over a bounded sample of the same workload (one thread)."""
     import numpy as np
     import torch
 
@@ -164,21 +185,18 @@ def cpu_baseline(w: Workload, budget_s: float):
         return x.float().cpu().numpy()
 
     done_bytes, done_ops, t_used, mats = 0, 0, 0.0, 0
-    for s in w.sets:
-        for mat in s:
-            packed = mat.packed.cpu().numpy()
-            x = acts_host_f32(mat.x)
-            g = np.float32(mat.gamma.cpu().numpy()[0])
-            t0 = time.perf_counter()
-            xq, a = oracle.quant_acts(x)
-            q = oracle.unpack(packed, mat.n, mat.k)
-            oracle.forward(q, g, xq, a, mat.k)
-            t_used += time.perf_counter() - t0
-            done_bytes += mat.bytes
-            done_ops += 2 * w.m * mat.n * mat.k
-            mats += 1
-            if t_used >= budget_s:
-                break
+    for mat in sum(w.sets, []):
+        packed = mat.packed.cpu().numpy()
+        x = acts_host_f32(mat.x)
+        g = np.float32(mat.gamma.cpu().numpy()[0])
+        t0 = time.perf_counter()
+        xq, a = oracle.quant_acts(x)
+        q = oracle.unpack(packed, mat.n, mat.k)
+        oracle.forward(q, g, xq, a, mat.k)
+        t_used += time.perf_counter() - t0
+        done_bytes += mat.bytes
+        done_ops += mat.ops
+        mats += 1
         if t_used >= budget_s:
             break
     return done_bytes, done_ops, t_used, mats
@@ -213,22 +231,23 @@ def main():
     bl.lib()
     m_head = synth.WORKLOADS[args.workload].m_list[0]
     head = Workload(bl, synth, args.workload, m_head, dev)
+    if not args.no_graph:
+        head.capture()
     ms = time_steps(head, args.steps, args.warmup)
-    launch_ms, launch_bytes, launch_ops = time_forward_launches(head, max(2, min(args.steps, 48)))
+    launch_ms, launch_bytes, launch_ops = time_forward_launches(head, 1 if head.sweep else 2)
     decode = m_head <= 16
     value = head.bytes_per_step() / (ms * 1e-3) / 1e9 if decode else head.ops_per_step() / (ms * 1e-3) / 1e12
     if decode:
         achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_gemv_mfma", "launch_us": round(launch_ms * 1e3, 3),
-                "algorithmic_bytes_per_launch": int(launch_bytes)}
+                "kernel": "k_gemv_lds (fused quantise + decode)" if all(head.fused.values()) else "k_gemv",
+                "launch_us": round(launch_ms * 1e3, 3), "algorithmic_bytes_per_launch": int(launch_bytes)}
     else:
         achieved = launch_ops / (launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": I8_PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / I8_PEAK_TOPS, 4), "traffic": None,
-                "kernel": "k_gemm_mfma", "launch_us": round(launch_ms * 1e3, 3),
-                "algorithmic_ops_per_launch": int(launch_ops)}
+                "frac": round(achieved / I8_PEAK_TOPS, 4), "traffic": None, "kernel": "k_gemm_mfma",
+                "launch_us": round(launch_ms * 1e3, 3), "algorithmic_ops_per_launch": int(launch_ops)}
     legs = {}
     for tok in [t for t in args.legs.split(",") if t.strip()]:
         idx = int(tok)
@@ -236,9 +255,11 @@ def main():
             continue
         for m in synth.WORKLOADS[idx].m_list:
             w = Workload(bl, synth, idx, m, dev)
-            steps = max(3, args.steps // (20 if w.sweep else 1))
-            lms = time_steps(w, steps, max(1, args.warmup // 4))
-            l_ms, l_b, l_o = time_forward_launches(w, 2 if w.sweep else max(2, min(steps, 32)))
+            if not args.no_graph:
+                w.capture()
+            steps = max(3, args.steps // (40 if w.sweep else 1))
+            lms = time_steps(w, steps, max(1, args.warmup // (40 if w.sweep else 4)))
+            l_ms, l_b, l_o = time_forward_launches(w, 1 if w.sweep else 2)
             legs[f"w{idx}_m{m}"] = leg_summary(w, lms, l_ms, l_b, l_o)
             del w
             torch.cuda.empty_cache()
@@ -261,6 +282,7 @@ def main():
                    "matrices": [list(x) for x in head.wl.matrices],
                    "distinct_weight_sets": len(head.sets),
                    "packed_bytes_per_step": head.bytes_per_step(),
+                   "graph": not args.no_graph,
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None},
         "roofline": roof,
         "cpu_baseline": cpu,

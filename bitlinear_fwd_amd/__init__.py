@@ -53,6 +53,10 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_quantize_weights.argtypes = [p, i64, i64, p, p, p, i64, p]
         L.bitlinear_quantize_acts.restype = c_int
         L.bitlinear_quantize_acts.argtypes = [p, c_int, i64, i64, p, p, p]
+        L.bitlinear_forward_fused.restype = c_int
+        L.bitlinear_forward_fused.argtypes = [p, p, p, c_int, i64, i64, i64, p, p, p, p, p]
+        L.bitlinear_forward_plan.restype = c_int
+        L.bitlinear_forward_plan.argtypes = [i64, i64, i64, p]
         L.bitlinear_forward.restype = c_int
         L.bitlinear_forward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p]
         _lib = L
@@ -62,7 +66,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED_SYMBOLS = (
     "bitlinear_version", "bitlinear_status_string", "bitlinear_n_pad", "bitlinear_k_pad",
     "bitlinear_packed_bytes", "bitlinear_wq_workspace_bytes", "bitlinear_quantize_weights",
-    "bitlinear_quantize_acts", "bitlinear_forward",
+    "bitlinear_quantize_acts", "bitlinear_forward", "bitlinear_forward_fused", "bitlinear_forward_plan",
 )
 
 
@@ -93,6 +97,17 @@ def packed_bytes(n: int, k: int) -> int:
 
 def wq_workspace_bytes(n: int, k: int) -> int:
     return int(lib().bitlinear_wq_workspace_bytes(n, k))
+
+
+def forward_plan(m: int, n: int, k: int) -> dict:
+    """The launch bitlinear_forward makes for (M, N, K), computed on the host."""
+    out = (ctypes.c_int32 * 6)()
+    _check("bitlinear_forward_plan", lib().bitlinear_forward_plan(m, n, k, out))
+    if out[0] == 1:
+        return {"kernel": "decode", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
+                "lds_acts": bool(out[4]), "lds_bytes": out[5]}
+    return {"kernel": "prefill", "workgroups": out[1], "threads": out[2], "tile_m": out[3], "tile_n": out[4],
+            "lds_bytes": out[5]}
 
 
 def _stream(device) -> int:
@@ -181,6 +196,41 @@ def forward(packed, gamma, xq, absmax, n: int, k: int, y=None, acc=None, want_y:
     return y if want_y else acc
 
 
+def forward_fused(packed, gamma, x, n: int, k: int, y=None, acc=None, xq=None, absmax=None, want_y: bool = True,
+                  want_acc: bool = False):
+    """Quantise x[M][K] (fp32/bf16) per token and apply the packed weights in one call.
+
+    Returns (y and/or acc, xq, absmax)."""
+    import torch
+
+    for t, name in ((packed, "packed"), (gamma, "gamma"), (x, "x")):
+        _require_cuda(t, name)
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [tokens, K]")
+    if x.dtype == torch.float32:
+        dt = BL_F32
+    elif x.dtype == torch.bfloat16:
+        dt = BL_BF16
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    m = x.shape[0]
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((m, k_pad(k)), dtype=torch.int8, device=dev)
+    if absmax is None:
+        absmax = torch.empty(m, dtype=torch.float32, device=dev)
+    if want_y and y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    if want_acc and acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    _check("bitlinear_forward_fused", lib().bitlinear_forward_fused(
+        packed.data_ptr(), gamma.data_ptr(), x.data_ptr(), dt, m, n, k,
+        y.data_ptr() if y is not None else None, acc.data_ptr() if acc is not None else None,
+        xq.data_ptr(), absmax.data_ptr(), _stream(dev)))
+    out = (y, acc) if (want_y and want_acc) else (y if want_y else acc)
+    return out, xq, absmax
+
+
 class BitLinear:
     """Inference-time BitLinear: weights quantised once, forward per token batch."""
 
@@ -189,5 +239,5 @@ class BitLinear:
         self.packed, self.gamma = quantize_weights(W)
 
     def __call__(self, x):
-        xq, a = quantize_acts(x)
-        return forward(self.packed, self.gamma, xq, a, self.n, self.k)
+        y, _, _ = forward_fused(self.packed, self.gamma, x.contiguous(), self.n, self.k)
+        return y

@@ -18,11 +18,6 @@ constexpr int kMaxVecPerThread = 4;  // 256 threads x 4 x 8 bf16 = 8192 elements
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-__device__ __forceinline__ int8_t qcode(float x, float s) {
-  float r = rintf(x * s);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int8_t)(int)r;
-}
 
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
@@ -86,8 +81,8 @@ __global__ __launch_bounds__(kThreads) void k_act_quant_vec(const void* __restri
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        lo |= (uint32_t)(uint8_t)qcode(v[j][e], s) << (8 * e);
-        hi |= (uint32_t)(uint8_t)qcode(v[j][4 + e], s) << (8 * e);
+        lo |= (uint32_t)(uint8_t)quant_code(v[j][e], s) << (8 * e);
+        hi |= (uint32_t)(uint8_t)quant_code(v[j][4 + e], s) << (8 * e);
       }
       reinterpret_cast<uint2*>(out)[gi] = make_uint2(lo, hi);
     }
@@ -97,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void k_act_quant_vec(const void* __restri
     for (int e = 0; e < 8; ++e) {
       const float x = kBf16 ? bf16_to_f32(static_cast<const uint16_t*>(X)[m * K + 8 * gi + e])
                             : static_cast<const float*>(X)[m * K + 8 * gi + e];
-      const uint32_t c = (uint32_t)(uint8_t)qcode(x, s);
+      const uint32_t c = (uint32_t)(uint8_t)quant_code(x, s);
       if (e < 4) lo |= c << (8 * e); else hi |= c << (8 * (e - 4));
     }
     reinterpret_cast<uint2*>(out)[gi] = make_uint2(lo, hi);
@@ -122,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void k_act_quant_scalar(const void* __res
   const float s = a > 0.0f ? 127.0f / a : 0.0f;
   if (threadIdx.x == 0) absmax[m] = a;
   int8_t* out = Xq + m * K_pad;
-  for (int64_t k = threadIdx.x; k < K_pad; k += kThreads) out[k] = k < K ? qcode(load(k), s) : (int8_t)0;
+  for (int64_t k = threadIdx.x; k < K_pad; k += kThreads) out[k] = k < K ? quant_code(load(k), s) : (int8_t)0;
 }
 
 }  // namespace

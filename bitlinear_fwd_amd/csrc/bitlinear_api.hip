@@ -75,4 +75,47 @@ int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* X
   return hip_status(bl::launch_gemm(packed, gamma, Xq, absmax, M, N, K, Y, acc, s));
 }
 
+int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const void* X, int dt, int64_t M, int64_t N,
+                            int64_t K, float* Y, int32_t* acc, int8_t* Xq, float* absmax, void* stream) {
+  if (!packed || !gamma || !X || !Xq || !absmax || (!Y && !acc)) return BL_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
+  if (!aligned(packed, 16) || !aligned(Xq, 16) || !aligned(gamma, 4) || !aligned(absmax, 4) ||
+      !aligned(X, dt == BL_F32 ? 4 : 2) || (Y && !aligned(Y, 4)) || (acc && !aligned(acc, 4)))
+    return BL_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int src = dt == BL_BF16 ? 1 : 2;
+  if (M <= kDecodeMaxM && aligned(X, 16)) {
+    const bl::GemvPlan p = bl::plan_gemv(M, N, K, src);
+    if (p.lds_act && p.ok)
+      return hip_status(bl::launch_gemv_fused(packed, gamma, X, dt == BL_BF16, M, N, K, Y, acc, Xq, absmax, s));
+  }
+  // general case: the activation quantiser, then the forward, both on the stream
+  hipError_t e = bl::launch_act_quant(X, dt == BL_BF16 ? 1 : 0, M, K, Xq, absmax, s);
+  if (e != hipSuccess) return BL_ERR_HIP;
+  return bitlinear_forward(packed, gamma, Xq, absmax, M, N, K, Y, acc, stream);
+}
+
+int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]) {
+  if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (M <= kDecodeMaxM) {
+    const bl::GemvPlan p = bl::plan_gemv(M, N, K, 0);
+    out[0] = 1;
+    out[1] = (int32_t)p.groups;
+    out[2] = p.waves * 64;
+    out[3] = p.rb;
+    out[4] = p.lds_act ? 1 : 0;
+    out[5] = p.lds_act ? (int32_t)(M * (bl::k_pad(K) + 16)) : 0;
+  } else {
+    const bl::GemmPlan p = bl::plan_gemm(M, N, K);
+    out[0] = 2;
+    out[1] = (int32_t)p.groups;
+    out[2] = p.threads;
+    out[3] = p.bm;
+    out[4] = p.bn;
+    out[5] = 0;
+  }
+  return BL_OK;
+}
+
 }  // extern "C"

@@ -40,6 +40,35 @@ __device__ __forceinline__ v4i as_v4i(uint4 u) {
   return r;
 }
 
+// Activation code of one element: clamp(rint(x * s), -127, 127) with s = fl32(127 / a)
+// (0 for an all-zero row); round-half-to-even.  Shared by the standalone activation
+// quantiser and the fused decode kernel so both produce identical codes.
+__device__ __forceinline__ int8_t quant_code(float x, float s) {
+  float r = rintf(x * s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int8_t)(int)r;
+}
+
+// Launch plan of the decode kernel for one shape (exposed for tests and the benchmark).
+struct GemvPlan {
+  int waves = 1;        // waves per workgroup; they split the K tiles into contiguous runs
+  int rb = 1;           // 16-row output blocks per workgroup
+  bool lds_act = false; // activations staged in LDS (small M*K) or loaded per tile
+  int stage = 0;        // LDS staging: 16-byte activation pieces per thread
+  bool ok = true;       // the requested activation source is supported by this plan
+  int64_t groups = 0;   // workgroups
+};
+// src: 0 = int8 activations (bitlinear_forward), 1 = bf16 x, 2 = fp32 x (fused form)
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src);
+
+// Launch plan of the prefill kernel.
+struct GemmPlan {
+  int bm = 128, bn = 128;  // output tile
+  int threads = 256;
+  int64_t groups = 0;
+};
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+
 // Launchers (return hipSuccess or the launch error).  All sizes are validated by the
 // C ABI before these are called.
 hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
@@ -48,6 +77,8 @@ hipError_t launch_act_quant(const void* X, int bf16, int64_t M, int64_t K, int8_
                             hipStream_t s);
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
+hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const void* X, int bf16, int64_t M, int64_t N,
+                             int64_t K, float* Y, int32_t* acc, int8_t* Xq_out, float* absmax_out, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
 

@@ -1,115 +1,462 @@
-// Decode kernel (M = 1..16 tokens): packed-ternary x int8 with exact int32 accumulation
+// Decode kernels (M = 1..16 tokens): packed-ternary x int8 with exact int32 accumulation
 // and the fp32 rescale in the epilogue.
 //
 // bhfrc.com news 56965, section 1.1: a ternary weight times an activation adds it,
 // subtracts it or skips it; section 4.1: the weights travel as 2-bit codes so that one
-// load carries many of them.  aratech.ae BitNet b1.58 article, "BitLinear": y is the
-// int8 x ternary product rescaled by both scales.
+// load carries many of them.  aratech.ae BitNet b1.58 article, "BitLinear": activations
+// are int8 with a per-token absmax scale; y is the product rescaled by both scales.
 //
-// The decode regime is HBM-bound (0.25 byte of weights per multiply-add at M = 1), so
-// the kernel is built around streaming the packed matrix once:
-//   * a workgroup owns one 16-row block of outputs; its waves split the 1 KiB tiles of
-//     that block along K, so every wave-wide 16-byte-per-lane load is one contiguous
-//     tile;
+// Decode is HBM-bound (0.25 byte of weights per multiply-add at M = 1), so both kernels
+// are built as a streaming read of the packed matrix:
+//   * a workgroup owns RB 16-row output blocks; its W waves split the K tiles of those
+//     blocks into contiguous runs; each wave streams whole 1 KiB tiles with one
+//     16-byte-per-lane non-temporal load per tile, through a ring of NB batches of U
+//     tiles (NB-1 batches stay in flight while one is computed);
+//   * every load in the steady-state loop is unconditional (indices past the wave's run
+//     are clamped to a valid tile and their codes zeroed) and each batch is fenced with
+//     a scheduling barrier, so the compiler emits exact vmcnt waits instead of draining
+//     the whole load queue;
 //   * each lane's 16 bytes are 64 consecutive codes of one row, decoded in registers
-//     (decode16) straight into the B operand of v_mfma_i32_16x16x64_i8; the A operand
-//     is the matching 16 int8 activations of token lane%16 (zero for lanes >= M), so
-//     the matrix core does the dot products and the VALU only decodes;
-//   * partial 16x16 int32 tiles of the waves are summed through LDS (exact), and the
-//     first wave rescales and stores.
+//     (decode16) straight into the B operand of v_mfma_i32_16x16x64_i8; the A operand is
+//     the matching 16 int8 activations of token lane%16;
+//   * rows of A beyond M repeat row M-1; they only feed output rows that are not stored;
+//   * partial 16x16 int32 tiles of the waves are summed in LDS in wave order (exact) and
+//     rescaled by y = acc * gamma * a[m] / 127.
+//
+// Activations reach the A operand in one of two ways:
+//   k_gemv_lds  (M <= 4, small K): the workgroup stages the M rows once in LDS - copied
+//               from int8 xq, or (fused form) quantised in the kernel from bf16/fp32 x
+//               with the same arithmetic as the standalone activation quantiser - using
+//               an exact, compile-time number of 16-byte pieces per thread issued before
+//               the weight loads (vector-memory loads retire in order, so their wait
+//               does not wait for the weights);
+//   k_gemv_reg  (larger M*K): each wave loads the 16-byte fragments of a tile index with
+//               the weights of that batch and reuses them for its RB row blocks.
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
 
-template <int kWaves, int kUnroll>
-__global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __restrict__ packed,
-                                                            const float* __restrict__ gamma,
-                                                            const int8_t* __restrict__ Xq,
-                                                            const float* __restrict__ absmax, int M, int N,
-                                                            int K_pad, int chunks, float* __restrict__ Y,
-                                                            int32_t* __restrict__ acc_out) {
-  __shared__ v4i red[kWaves][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+constexpr int kMaxLdsActBytes = 48 * 1024;
+
+__device__ __forceinline__ uint32_t word_of(const uint4& w, int i) {
+  return i == 0 ? w.x : (i == 1 ? w.y : (i == 2 ? w.z : w.w));
+}
+
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p)));
+}
+
+// Sum the W waves' partial tiles (red[w][j][lane]) and write y / acc for row block j.
+template <int W, int RB>
+__device__ __forceinline__ void gemv_epilogue(const v4i* red, int wave, int lane, int rb0, int rblocks, int M, int N,
+                                              float gm, const float* absmax, float* Y, int32_t* acc_out) {
   const int r = lane & 15, g = lane >> 4;
-  const int nb = blockIdx.x;
-  const uint4* wp = reinterpret_cast<const uint4*>(packed + (size_t)nb * chunks * kTileBytes) + lane;
-  const bool has_row = r < M;
-  const int8_t* xrow = Xq + (size_t)(has_row ? r : 0) * K_pad + 64 * g;
-  v4i c = {0, 0, 0, 0};
-  int ch = wave;
-  for (; ch + (kUnroll - 1) * kWaves < chunks; ch += kUnroll * kWaves) {
-    uint4 wv[kUnroll];
+  for (int j = wave; j < RB; j += W) {
+    if (rb0 + j >= rblocks) continue;
+    v4i s = red[j * 64 + lane];
+    for (int w = 1; w < W; ++w) s += red[(w * RB + j) * 64 + lane];
+    // lane holds D[4g + v][r]: token m = 4g + v, output n = 16*(rb0 + j) + r
+    const int n = (rb0 + j) * kTileRows + r;
+    if (n >= N) continue;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) wv[u] = wp[(size_t)(ch + u * kWaves) * 64];
-    uint4 av[kUnroll][4];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (has_row) {
-        const uint4* ap = reinterpret_cast<const uint4*>(xrow + (size_t)(ch + u * kWaves) * kTileCols);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) av[u][i] = ap[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) av[u][i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * g + v;
+      if (m < M) {
+        if (acc_out) acc_out[(size_t)m * N + n] = s[v];
+        if (Y) Y[(size_t)m * N + n] = (float)s[v] * gm * absmax[m] * (1.0f / 127.0f);
       }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(av[u][0]), decode16(wv[u].x), c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(av[u][1]), decode16(wv[u].y), c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(av[u][2]), decode16(wv[u].z), c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(av[u][3]), decode16(wv[u].w), c, 0, 0, 0);
-    }
-  }
-  for (; ch < chunks; ch += kWaves) {
-    const uint4 wv = wp[(size_t)ch * 64];
-    uint4 av[4];
-    if (has_row) {
-      const uint4* ap = reinterpret_cast<const uint4*>(xrow + (size_t)ch * kTileCols);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = ap[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(av[0]), decode16(wv.x), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(av[1]), decode16(wv.y), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(av[2]), decode16(wv.z), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(av[3]), decode16(wv.w), c, 0, 0, 0);
-  }
-  if (kWaves > 1) {
-    red[wave][lane] = c;
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) c += red[w][lane];
-  }
-  // lane holds D[4*g + v][r] for v = 0..3: token m = 4g + v, output n = 16*nb + r
-  const int n = nb * kTileRows + r;
-  if (n >= N) return;
-  const float gm = gamma[0];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int m = 4 * g + v;
-    if (m < M) {
-      const int32_t a = c[v];
-      if (acc_out) acc_out[(size_t)m * N + n] = a;
-      if (Y) Y[(size_t)m * N + n] = (float)a * gm * absmax[m] * (1.0f / 127.0f);
     }
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// k_gemv_lds: activations staged in LDS.  kSrc: 0 = int8 xq (K_pad columns), 1 = bf16 x,
+// 2 = fp32 x (K columns, quantised here).  S = 16-byte pieces per thread (exact: the
+// launcher picks S = ceil(pieces / threads)).
+template <int W, int U, int NB, int S, int kSrc>
+__global__ __launch_bounds__(W * 64) void k_gemv_lds(const uint8_t* __restrict__ packed,
+                                                     const float* __restrict__ gamma, const void* __restrict__ X,
+                                                     const float* __restrict__ absmax_in, int M, int N, int K,
+                                                     int K_pad, int chunks, int rblocks, float* __restrict__ Y,
+                                                     int32_t* __restrict__ acc_out, int8_t* __restrict__ xq_out,
+                                                     float* __restrict__ absmax_out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];  // [M][K_pad + 16] int8
+  __shared__ v4i red[W * 64];
+  __shared__ float amax_red[W][4];
+  __shared__ float row_scale[4], row_amax[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int rb0 = blockIdx.x;
+  const int tpw = (chunks + W - 1) / W;
+  const int c0 = wave * tpw;
+  const int c1 = min(chunks, c0 + tpw);
+  const int row = min(r, M - 1);
+  const int lds_stride = K_pad + 16;
+  const uint4* wsrc = reinterpret_cast<const uint4*>(packed) + (size_t)rb0 * chunks * 64 + lane;
+
+  // activation pieces: int8 source -> 16 codes; bf16 -> 8 elements; fp32 -> 4 elements
+  constexpr int kElems = kSrc == 0 ? 16 : (kSrc == 1 ? 8 : 4);
+  constexpr int kElemBytes = kSrc == 0 ? 1 : (kSrc == 1 ? 2 : 4);
+  const int row_elems = kSrc == 0 ? K_pad : K;
+  const int per_row = row_elems / kElems;
+  const int pieces = M * per_row;
+  uint4 st[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    const int idx = min((int)threadIdx.x + j * W * 64, pieces - 1);
+    const int m = idx / per_row, p = idx - m * per_row;
+    const uint8_t* base = static_cast<const uint8_t*>(X) + (size_t)m * row_elems * kElemBytes;
+    st[j] = reinterpret_cast<const uint4*>(base)[p];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // activation loads are issued before the weights
+
+  uint4 w[NB][U];
+  auto load = [&](int b, int cb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[b][u] = load_nt(wsrc + (size_t)min(cb + u, c1 - 1) * 64);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Unconditional: a wave without tiles re-reads a valid tile (c1 - 1 >= 0) and never
+  // computes, so the waits below count exactly the loads issued after each one.
+#pragma unroll
+  for (int b = 0; b < NB; ++b) load(b, c0 + b * U);
+
+  if (kSrc == 0) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const int idx = (int)threadIdx.x + j * W * 64;
+      if (idx < pieces) {
+        const int m = idx / per_row, p = idx - m * per_row;
+        *reinterpret_cast<uint4*>(act_lds + m * lds_stride + 16 * p) = st[j];
+      }
+    }
+  } else {
+    // fused activation quantiser: per-row absmax, s = 127/a, xq = clamp(rint(x*s))
+    float v[S][kElems];
+    float pm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const int idx = (int)threadIdx.x + j * W * 64;
+      if (kSrc == 1) {
+        const uint32_t q4[4] = {st[j].x, st[j].y, st[j].z, st[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[j][2 * e] = __uint_as_float(q4[e] << 16);
+          v[j][2 * e + 1] = __uint_as_float(q4[e] & 0xFFFF0000u);
+        }
+      } else {
+        v[j][0] = __uint_as_float(st[j].x);
+        v[j][1] = __uint_as_float(st[j].y);
+        v[j][2] = __uint_as_float(st[j].z);
+        v[j][3] = __uint_as_float(st[j].w);
+      }
+      if (idx < pieces) {
+        const int m = idx / per_row;
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) a = fmaxf(a, fabsf(v[j][e]));
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+          if (m == mm) pm[mm] = fmaxf(pm[mm], a);
+      }
+    }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      float a = pm[mm];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+      if (lane == 0) amax_red[wave][mm] = a;
+    }
+    __syncthreads();
+    if (threadIdx.x < 4) {
+      float a = 0.0f;
+      for (int ww = 0; ww < W; ++ww) a = fmaxf(a, amax_red[ww][threadIdx.x]);
+      row_amax[threadIdx.x] = a;
+      row_scale[threadIdx.x] = a > 0.0f ? 127.0f / a : 0.0f;
+      if (blockIdx.x == 0 && (int)threadIdx.x < M) absmax_out[threadIdx.x] = a;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const int idx = (int)threadIdx.x + j * W * 64;
+      if (idx < pieces) {
+        const int m = idx / per_row, p = idx - m * per_row;
+        const float s = row_scale[m];
+        uint32_t packed_q[kElems / 4];
+#pragma unroll
+        for (int e4 = 0; e4 < kElems / 4; ++e4) {
+          uint32_t q = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q |= (uint32_t)(uint8_t)quant_code(v[j][4 * e4 + e], s) << (8 * e);
+          packed_q[e4] = q;
+        }
+        uint8_t* dst = act_lds + m * lds_stride + kElems * p;
+        if (kSrc == 1) *reinterpret_cast<uint2*>(dst) = make_uint2(packed_q[0], packed_q[1]);
+        else *reinterpret_cast<uint32_t*>(dst) = packed_q[0];
+        if (blockIdx.x == 0) {
+          int8_t* gdst = xq_out + (size_t)m * K_pad + kElems * p;
+          if (kSrc == 1) *reinterpret_cast<uint2*>(gdst) = make_uint2(packed_q[0], packed_q[1]);
+          else *reinterpret_cast<uint32_t*>(gdst) = packed_q[0];
+        }
+      }
+    }
+    // padding columns K .. K_pad-1 are zero (K is a multiple of 4 here)
+    const int per_pad = (K_pad - K) / 4;
+    for (int idx = threadIdx.x; idx < M * per_pad; idx += W * 64) {
+      const int m = idx / per_pad, p = idx - m * per_pad;
+      *reinterpret_cast<uint32_t*>(act_lds + m * lds_stride + K + 4 * p) = 0u;
+      if (blockIdx.x == 0) *reinterpret_cast<uint32_t*>(xq_out + (size_t)m * K_pad + K + 4 * p) = 0u;
+    }
+  }
+  __syncthreads();
+
+  v4i c = {0, 0, 0, 0};
+  auto compute = [&](int b, int cb, bool tail) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(cb + u, c1 - 1);
+      const bool live = !tail || cb + u < c1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t word = word_of(w[b][u], i);
+        if (tail) word = live ? word : 0u;  // code 00 decodes to 0
+        const v4i av = *reinterpret_cast<const v4i*>(act_lds + row * lds_stride + t * kTileCols + 64 * g + 16 * i);
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, decode16(word), c, 0, 0, 0);
+      }
+    }
+  };
+  if (c0 < c1) {
+    const int nbat = (c1 - c0 + U - 1) / U;
+    int j = 0;
+    for (; j + 2 * NB <= nbat; j += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        compute(b, c0 + (j + b) * U, false);
+        load(b, c0 + (j + b + NB) * U);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (j + b < nbat) compute(b, c0 + (j + b) * U, true);
+      if (j + b + NB < nbat) load(b, c0 + (j + b + NB) * U);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (j + NB + b < nbat) compute(b, c0 + (j + NB + b) * U, true);
+  }
+
+  red[wave * 64 + lane] = c;
+  __syncthreads();
+  const float* am = kSrc == 0 ? absmax_in : row_amax;
+  gemv_epilogue<W, 1>(red, wave, lane, rb0, rblocks, M, N, gamma[0], am, Y, acc_out);
+}
+
+// ---------------------------------------------------------------------------------------
+// k_gemv_reg: activation fragments in registers, loaded per tile index with the weights
+// of that batch and shared by the RB row blocks of the workgroup.
+template <int W, int RB, int U, int NB>
+__global__ __launch_bounds__(W * 64) void k_gemv_reg(const uint8_t* __restrict__ packed,
+                                                     const float* __restrict__ gamma, const int8_t* __restrict__ Xq,
+                                                     const float* __restrict__ absmax, int M, int N, int K_pad,
+                                                     int chunks, int rblocks, float* __restrict__ Y,
+                                                     int32_t* __restrict__ acc_out) {
+  __shared__ v4i red[W * RB * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int rb0 = blockIdx.x * RB;
+  const int tpw = (chunks + W - 1) / W;
+  const int c0 = wave * tpw;
+  const int c1 = min(chunks, c0 + tpw);
+  const int row = min(r, M - 1);
+  const uint4* wsrc[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j)
+    wsrc[j] = reinterpret_cast<const uint4*>(packed) + (size_t)min(rb0 + j, rblocks - 1) * chunks * 64 + lane;
+  const int8_t* xrow = Xq + (size_t)row * K_pad + 64 * g;
+  uint4 w[NB][U][RB];
+  uint4 a[NB][U][4];
+  auto load = [&](int b, int cb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(cb + u, c1 - 1);
+#pragma unroll
+      for (int j = 0; j < RB; ++j) w[b][u][j] = load_nt(wsrc[j] + (size_t)t * 64);
+      const uint4* p = reinterpret_cast<const uint4*>(xrow + (size_t)t * kTileCols);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[b][u][i] = p[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  v4i c[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) c[j] = (v4i){0, 0, 0, 0};
+  auto compute = [&](int b, int cb, bool tail) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = !tail || cb + u < c1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v4i av = as_v4i(a[b][u][i]);
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          uint32_t word = word_of(w[b][u][j], i);
+          if (tail) word = live ? word : 0u;
+          c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, decode16(word), c[j], 0, 0, 0);
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int b = 0; b < NB; ++b) load(b, c0 + b * U);
+  if (c0 < c1) {
+    const int nbat = (c1 - c0 + U - 1) / U;
+    int j = 0;
+    for (; j + 2 * NB <= nbat; j += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        compute(b, c0 + (j + b) * U, false);
+        load(b, c0 + (j + b + NB) * U);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (j + b < nbat) compute(b, c0 + (j + b) * U, true);
+      if (j + b + NB < nbat) load(b, c0 + (j + b + NB) * U);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (j + NB + b < nbat) compute(b, c0 + (j + NB + b) * U, true);
+  }
+  // a missing row block (past rblocks) re-read a valid block's codes: never stored
+#pragma unroll
+  for (int j = 0; j < RB; ++j) red[(wave * RB + j) * 64 + lane] = c[j];
+  __syncthreads();
+  gemv_epilogue<W, RB>(red, wave, lane, rb0, rblocks, M, N, gamma[0], absmax, Y, acc_out);
+}
+
+// ---------------------------------------------------------------------------------------
+struct Args {
+  const uint8_t* packed;
+  const float* gamma;
+  const void* X;
+  const float* absmax;
+  int M, N, K, K_pad, chunks, rblocks;
+  float* Y;
+  int32_t* acc;
+  int8_t* xq_out;
+  float* absmax_out;
+};
+
+template <int W, int U, int NB, int S, int kSrc>
+hipError_t launch_lds(const Args& a, hipStream_t s) {
+  const size_t lds = (size_t)a.M * (a.K_pad + 16);
+  hipLaunchKernelGGL((k_gemv_lds<W, U, NB, S, kSrc>), dim3(a.rblocks), dim3(W * 64), lds, s, a.packed, a.gamma, a.X,
+                     a.absmax, a.M, a.N, a.K, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc, a.xq_out, a.absmax_out);
+  return hipGetLastError();
+}
+
+template <int W, int U, int NB, int kSrc>
+hipError_t launch_lds_s(int S, const Args& a, hipStream_t s) {
+  switch (S) {
+    case 1: return launch_lds<W, U, NB, 1, kSrc>(a, s);
+    case 2: return launch_lds<W, U, NB, 2, kSrc>(a, s);
+    case 3: return launch_lds<W, U, NB, 3, kSrc>(a, s);
+    default: return launch_lds<W, U, NB, 4, kSrc>(a, s);
+  }
+}
+
+template <int kSrc>
+hipError_t launch_lds_w(int W, int S, const Args& a, hipStream_t s) {
+  switch (W) {
+    case 16: return launch_lds_s<16, 1, 3, kSrc>(S, a, s);
+    case 8: return launch_lds_s<8, 2, 2, kSrc>(S, a, s);
+    case 4: return launch_lds_s<4, 2, 3, kSrc>(S, a, s);
+    case 2: return launch_lds_s<2, 2, 3, kSrc>(S, a, s);
+    default: return launch_lds_s<1, 2, 3, kSrc>(S, a, s);
+  }
+}
+
+template <int W, int RB, int U, int NB>
+hipError_t launch_reg(const Args& a, hipStream_t s) {
+  const unsigned groups = (unsigned)((a.rblocks + RB - 1) / RB);
+  hipLaunchKernelGGL((k_gemv_reg<W, RB, U, NB>), dim3(groups), dim3(W * 64), 0, s, a.packed, a.gamma,
+                     static_cast<const int8_t*>(a.X), a.absmax, a.M, a.N, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc);
+  return hipGetLastError();
+}
+
+template <int RB, int U, int NB>
+hipError_t launch_reg_w(int W, const Args& a, hipStream_t s) {
+  switch (W) {
+    case 16: return launch_reg<16, RB, U, NB>(a, s);
+    case 8: return launch_reg<8, RB, U, NB>(a, s);
+    case 4: return launch_reg<4, RB, U, NB>(a, s);
+    case 2: return launch_reg<2, RB, U, NB>(a, s);
+    default: return launch_reg<1, RB, U, NB>(a, s);
+  }
+}
+
+// waves per workgroup: enough waves in flight without splitting K finer than ~2 tiles
+// per wave, and at most ~32 waves per compute unit overall
+int pick_waves(int64_t chunks, int64_t groups) {
+  int w = 16;
+  while (w > 1 && (2 * w > chunks || groups * w > 256 * 32)) w /= 2;
+  return w;
+}
+
 }  // namespace
+
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
+  GemvPlan p;
+  const int64_t K_pad = k_pad(K);
+  const int64_t chunks = K_pad / kTileCols;
+  const int64_t rblocks = n_pad(N) / kTileRows;
+  const bool small = M <= 4 && M * (K_pad + 16) <= kMaxLdsActBytes;
+  // fused quantisation needs whole 16-byte pieces of x in every row
+  const bool src_ok = src == 0 || (src == 1 && K % 8 == 0) || (src == 2 && K % 4 == 0);
+  if (small && src_ok) {
+    p.lds_act = true;
+    p.rb = 1;
+    p.groups = rblocks;
+    p.waves = pick_waves(chunks, rblocks);
+    const int64_t elems = src == 0 ? 16 : (src == 1 ? 8 : 4);
+    const int64_t pieces = M * (src == 0 ? K_pad : K) / elems;
+    // every piece must be covered by at most 4 loads per thread
+    while (p.waves < 16 && pieces > 4 * 64 * p.waves) p.waves *= 2;
+    p.stage = (int)((pieces + 64 * p.waves - 1) / (64 * p.waves));
+    p.ok = p.stage <= 4;
+    return p;
+  }
+  p.lds_act = false;
+  p.rb = 1;
+  if (M > 4 && rblocks >= 4 * 256) p.rb = 4;
+  else if (M > 4 && rblocks >= 2 * 256) p.rb = 2;
+  p.groups = (rblocks + p.rb - 1) / p.rb;
+  p.waves = pick_waves(chunks, p.groups);
+  p.ok = src == 0;  // the register path reads int8 activations only
+  return p;
+}
 
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s) {
-  const int64_t K_pad = k_pad(K);
-  const int chunks = (int)(K_pad / kTileCols);
-  const unsigned blocks = (unsigned)(n_pad(N) / kTileRows);
-  hipLaunchKernelGGL((k_gemv_mfma<4, 2>), dim3(blocks), dim3(256), 0, s, packed, gamma, Xq, absmax, (int)M,
-                     (int)N, (int)K_pad, chunks, Y, acc);
-  return hipGetLastError();
+  const GemvPlan p = plan_gemv(M, N, K, 0);
+  Args a{packed, gamma, Xq, absmax, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
+         (int)(n_pad(N) / kTileRows), Y, acc, nullptr, nullptr};
+  if (p.lds_act) return launch_lds_w<0>(p.waves, p.stage, a, s);
+  if (p.rb == 4) return launch_reg_w<4, 1, 2>(p.waves, a, s);
+  if (p.rb == 2) return launch_reg_w<2, 1, 2>(p.waves, a, s);
+  return launch_reg_w<1, 2, 2>(p.waves, a, s);
+}
+
+hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const void* X, int bf16, int64_t M, int64_t N,
+                             int64_t K, float* Y, int32_t* acc, int8_t* Xq_out, float* absmax_out, hipStream_t s) {
+  const GemvPlan p = plan_gemv(M, N, K, bf16 ? 1 : 2);
+  Args a{packed, gamma, X, nullptr, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
+         (int)(n_pad(N) / kTileRows), Y, acc, Xq_out, absmax_out};
+  if (bf16) return launch_lds_w<1>(p.waves, p.stage, a, s);
+  return launch_lds_w<2>(p.waves, p.stage, a, s);
 }
 
 }  // namespace bl

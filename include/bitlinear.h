@@ -115,6 +115,31 @@ int bitlinear_quantize_acts(const void* X, int dt, int64_t M, int64_t K, int8_t*
 int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                       int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream);
 
+/*
+ * Steps 2 + 3 + 4 in one call: per-token activation quantisation, contraction and
+ * rescale, for inference on un-quantised activations.
+ *   X       [M][K] fp32 (dt = BL_F32) or bf16 (dt = BL_BF16), row-major.
+ *   Xq      out: int8 [M][K_pad] codes, 16-byte aligned (as bitlinear_quantize_acts).
+ *   absmax  out: fp32 [M] (as bitlinear_quantize_acts).
+ *   Y, acc  as bitlinear_forward (at least one non-null).
+ * Results are identical to bitlinear_quantize_acts followed by bitlinear_forward.  For a
+ * few tokens (M <= 4) with a short row (M*K_pad <= 48 KiB), K a multiple of 8 (bf16) or
+ * 4 (fp32) and a 16-byte aligned X, one kernel launch does all three steps (each
+ * workgroup quantises the rows into LDS); otherwise the two kernels run back to back.
+ */
+int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const void* X, int dt, int64_t M, int64_t N,
+                            int64_t K, float* Y, int32_t* acc, int8_t* Xq, float* absmax, void* stream);
+
+/*
+ * Host-only description of the launch bitlinear_forward would make for (M, N, K); no
+ * device work.  out[0] = kernel (1 = decode, 2 = prefill), out[1] = workgroups,
+ * out[2] = threads per workgroup, out[3] = decode: 16-row output blocks per workgroup,
+ * prefill: output tile rows, out[4] = decode: 1 if activations are staged in LDS,
+ * prefill: output tile columns, out[5] = dynamic LDS bytes.  Returns BL_OK or
+ * BL_ERR_INVALID_ARG (same size rules as bitlinear_forward, null out).
+ */
+int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]);
+
 #ifdef __cplusplus
 }
 #endif

@@ -179,6 +179,20 @@ def test_forward_decode(m, n, k):
     _fwd_check(m, n, k, seed=m * 1000 + n + k)
 
 
+@pytest.mark.parametrize("m,n,k,rb,lds", [
+    (1, 512, 256, 1, True), (1, 16400, 300, 1, True), (3, 130, 7000, 1, True), (2, 8200, 12000, 1, True),
+    (1, 300, 40000, 1, True), (2, 70, 5000, 1, True),
+    (4, 100, 16000, 1, False), (5, 8200, 300, 2, False), (16, 16400, 256, 4, False), (8, 2560, 6912, 1, False),
+    (12, 16400, 1000, 4, False), (7, 9000, 4100, 2, False), (16, 4200, 9000, 1, False)])
+def test_forward_decode_variants(m, n, k, rb, lds):
+    # every decode-kernel variant (activations in LDS or registers, 1/2/4 row blocks per
+    # workgroup, 1..16 waves splitting K) against the oracle, including ragged N and K
+    plan = bl.forward_plan(m, n, k)
+    _announce("forward decode variant", m, n, k, plan)
+    assert plan["kernel"] == "decode" and plan["row_blocks"] == rb and plan["lds_acts"] == lds
+    _fwd_check(m, n, k, seed=m * 7 + n * 3 + k)
+
+
 @pytest.mark.parametrize("m", [17, 31, 64, 100, 128, 129, 257])
 @pytest.mark.parametrize("n,k", [(16, 256), (17, 300), (130, 1000), (300, 2304), (1, 1), (129, 513)])
 def test_forward_prefill(m, n, k):
@@ -243,3 +257,45 @@ def test_binding_errors_are_raised():
     packed = torch.zeros(bl.packed_bytes(16, 256) + 16, dtype=torch.uint8, device=DEV)[8:]  # misaligned
     with pytest.raises(bl.BitLinearError):
         bl.forward(packed, g, xq, a, 16, 256)
+
+
+# ------------------------------------------------------------------ fused quantise + forward
+def _fused_check(m, n, k, dtype, seed, unaligned=False):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-1, 2, (n, k)).astype(np.int8)
+    packed = torch.from_numpy(oracle.pack(q)).to(DEV)
+    if unaligned:
+        flat = synth.activations(1, m * k + 1, seed=seed, dtype=dtype, device=DEV,
+                                 outlier_p=0.01, outlier_mult=20.0).reshape(-1)
+        x = flat[1:].view(m, k)
+    else:
+        x = synth.activations(m, k, seed=seed, dtype=dtype, device=DEV, outlier_p=0.01, outlier_mult=20.0)
+    if m > 2:
+        x[1] = 0
+    gamma = np.float32(0.0159577)
+    (y, acc), xq, a = bl.forward_fused(packed, torch.tensor([gamma], device=DEV), x, n, k, want_y=True, want_acc=True)
+    torch.cuda.synchronize()
+    xq_ref, a_ref = oracle.quant_acts(acts_host_f32(x))
+    check_equal(host(xq), xq_ref, f"fused xq m={m} k={k}")
+    check_equal(host(a).view(np.uint32), a_ref.view(np.uint32), f"fused absmax m={m} k={k}")
+    acc_ref, y_ref = oracle.forward(q, gamma, xq_ref, a_ref, k)
+    check_equal(host(acc), acc_ref, f"fused acc m={m} n={n} k={k}")
+    check_y(host(y), y_ref, f"fused y m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("m,n,k", [(1, 512, 256), (1, 700, 2560), (2, 130, 6912), (3, 48, 1000), (4, 520, 4096),
+                                   (1, 33, 8), (1, 16400, 512), (2, 100, 12000)])
+def test_forward_fused_single_kernel(m, n, k, dtype):
+    # shapes the one-kernel path takes (M <= 4, short rows, K a multiple of 8)
+    _announce("forward fused", m, n, k, dtype)
+    _fused_check(m, n, k, dtype, seed=m * 31 + n + k)
+
+
+@pytest.mark.parametrize("m,n,k,dtype,unaligned", [(5, 64, 512, torch.bfloat16, False), (1, 64, 300, torch.bfloat16, False),
+                                                   (2, 64, 1002, torch.float32, False), (3, 40, 512, torch.bfloat16, True),
+                                                   (1, 40, 30000, torch.bfloat16, False), (40, 72, 700, torch.float32, False)])
+def test_forward_fused_fallback(m, n, k, dtype, unaligned):
+    # shapes outside the one-kernel path: the quantiser kernel then the forward kernel
+    _announce("forward fused fallback", m, n, k, dtype, unaligned)
+    _fused_check(m, n, k, dtype, seed=m * 17 + n + k, unaligned=unaligned)

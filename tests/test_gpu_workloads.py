@@ -51,6 +51,35 @@ def _run(workload: int, layer: int, midx: int, k: int, n: int, m: int, rows=None
     check_y(y_h, y_ref)
 
 
+def _run_fused(workload: int, layer: int, midx: int, k: int, n: int, m: int):
+    # the one-call quantise + forward path on the same inputs as _run
+    wl = synth.WORKLOADS[workload]
+    print(f"case: fused workload {workload} layer {layer} matrix {midx} K={k} N={n} M={m}", flush=True)
+    w_dev = synth.latent_weights(n, k, seed=synth.weight_seed(workload, layer, midx), device=DEV)
+    x_dev = synth.activations(m, k, seed=synth.act_seed(workload, layer, midx), dtype=wl.act_dtype, device=DEV,
+                              outlier_p=wl.outlier_p, outlier_mult=wl.outlier_mult)
+    packed, gamma = bl.quantize_weights(w_dev)
+    (y, acc), xq, a = bl.forward_fused(packed, gamma, x_dev, n, k, want_y=True, want_acc=True)
+    torch.cuda.synchronize()
+    w = host(w_dev)
+    del w_dev
+    g_ref = oracle.gamma_absmean(w)
+    q_ref = oracle.ternarise(w, g_ref)
+    del w
+    xq_ref, a_ref = oracle.quant_acts(acts_host_f32(x_dev))
+    check_equal(host(xq), xq_ref, "fused xq")
+    check_equal(host(a).view(np.uint32), a_ref.view(np.uint32), "fused absmax")
+    acc_ref, y_ref = oracle.forward(q_ref, g_ref, xq_ref, a_ref, k)
+    check_equal(host(acc), acc_ref, "fused acc")
+    check_y(host(y), y_ref)
+
+
+@pytest.mark.parametrize("midx", [0, 2])
+def test_workload1_fused_m1(midx):
+    _, k, n = synth.WORKLOADS[1].matrices[midx]
+    _run_fused(1, 0, midx, k, n, 1)
+
+
 def test_workload0_single_bitlinear():
     _run(0, 0, 0, 256, 512, 1)
 
