@@ -3,6 +3,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -29,6 +32,27 @@ __device__ __forceinline__ v4i decode16(uint32_t w) {
   r.z = (int)__builtin_amdgcn_perm(0u, 0x00FF0100u, hi & 0x03030303u);
   r.w = (int)__builtin_amdgcn_perm(0x00000001u, 0x00008000u, hi & 0x0C0C0C0Cu);
   return r;
+}
+
+// Direct global -> LDS load of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane
+// i of the wave writes lds_base + 16 i, so one wave instruction fills 1 KiB of LDS.
+// lds_base must be the same for the whole wave.  Completion is counted by vmcnt; the
+// compiler does not order later LDS reads after it, so callers wait explicitly.  (Kept
+// in a plain function: inside a kernel template in an anonymous namespace the builtin
+// stops clang from emitting the kernel's host launch stub.)
+__device__ __forceinline__ void load_g2lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// static_for<N>(f): calls f(std::integral_constant<int, k>{}) for k = 0 .. N-1, so the
+// body can use k where a constant expression is required (template arguments).
+template <typename F, int... ks>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, ks...>) {
+  (f(std::integral_constant<int, ks>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ v4i as_v4i(uint4 u) {

@@ -1,94 +1,228 @@
-// Prefill kernel (M > 16 tokens): a dense int8 x ternary contraction on the matrix
-// cores.  The packed ternary tiles are decoded once per workgroup into LDS as int8 and
-// fed, together with the int8 activations, to v_mfma_i32_16x16x64_i8; accumulation is
-// exact int32 and the fp32 rescale (y = acc * gamma * a[m] / 127) is the epilogue.
+// Prefill kernel (M > 16 tokens): a dense int8 x ternary contraction on the matrix cores,
+// exact int32 accumulation and the fp32 rescale (y = acc * gamma * a[m] / 127) in the
+// epilogue.
 //
 // bhfrc.com news 56965, section 1.1 (ternary x activation = add / subtract / skip) and
 // section 4.1 (2-bit codes); aratech.ae BitNet b1.58 article, "BitLinear".
 //
-// Workgroup tile 128 (tokens) x 128 (outputs), K step 128 (half a packed tile column):
-// 256 threads = 4 waves in a 2 x 2 grid, each wave a 64 x 64 block of 4 x 4 MFMA tiles.
+// Structure (workgroup = 4 waves in a GM x GN grid, each wave a WM x WN block of 16 x 16
+// v_mfma_i32_16x16x64_i8 tiles; K advances half a 256-column packed chunk per stage):
+//   * activations (A): each half-stage's BM x 128-byte slab (the pieces two MFMA steps
+//     use) goes straight from global memory into LDS (direct global -> LDS loads, no
+//     registers) through a ring of D slabs, so D - 1 half-stages are in flight while
+//     one computes; the wait at the end of a half-stage counts only the loads still
+//     allowed to be outstanding, and one barrier per half-stage hands the slab over;
+//   * weights (B): every wave loads its own 16-byte slots of the packed tiles (a 1 KiB
+//     tile is one coalesced wave load) into a register ring of the same depth and
+//     decodes them straight into the B operand - the packed layout is the MFMA lane
+//     layout, and 2-bit codes are 4x fewer bytes through the cache than int8;
+//   * one 16-byte word of a slot feeds one MFMA step; with WM = 128 each decoded word
+//     serves 8 MFMAs, which keeps the decode VALU well below the matrix-core time;
+//   * tile order is XCD-aware: consecutive workgroup ids go to different XCDs, so each
+//     XCD gets a contiguous run of output tiles (sharing activation rows in its L2).
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int LDS_STRIDE = BK + 16;  // bytes per LDS row; the pad staggers 16-byte reads
+// Activation staging.  MFMA step i of a 256-column chunk uses, in lane group g, the
+// 16-byte piece 4g + i of each activation row (columns 64g + 16i .. +15), so steps
+// {2h, 2h+1} need only the 8 pieces 4g + 2h + i' (g = 0..3, i' = 0..1): a half-stage.
+// A half-stage slab is BM rows x 128 bytes in LDS; row r keeps its local piece
+// lp = 2g + i' in slot lp ^ ((r >> 1) & 7), which puts the 16 lanes of a fragment read
+// (16 consecutive rows, one piece) on 16 distinct 16-byte bank groups.  One direct-load
+// wave instruction fills 1 KiB of LDS contiguously (lane i at +16 i), i.e. 8 rows; the
+// swizzle is applied by choosing which global piece each lane fetches.
+__device__ __forceinline__ int a_slot(int row, int lp) { return lp ^ ((row >> 1) & 7); }
 
+// s_waitcnt that waits only for vmcnt <= n (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Work-group barrier for the LDS ring.  Unlike __syncthreads() it carries no release
+// fence, so it does not drain the direct global->LDS loads still in flight for later ring
+// slots; the caller has already waited (wait_vmcnt) for the slot the next half-stage reads.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Vector-memory instructions a wave issues in half-stage hs: the activation slab, plus
+// the weight slots of a chunk at its first half-stage.
+template <int kDma, int NB>
+constexpr int loads_at(int hs) { return kDma + ((hs & 1) == 0 ? NB : 0); }
+
+// Number of loads issued in half-stages (a, b] (a < b), for the ring wait counts.
+template <int kDma, int NB>
+constexpr int loads_between(int a, int b) {
+  int n = 0;
+  for (int h = a + 1; h <= b; ++h) n += loads_at<kDma, NB>(h);
+  return n;
+}
+
+template <int GM, int GN, int WM, int WN, int D>
 __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ packed, const float* __restrict__ gamma,
                                                    const int8_t* __restrict__ Xq, const float* __restrict__ absmax,
-                                                   int M, int N, int n_blocks, int K_pad, int chunks,
-                                                   float* __restrict__ Y, int32_t* __restrict__ acc_out) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[BN * LDS_STRIDE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                                   int M, int N, int n_blocks, int K_pad, int chunks, int tiles_m,
+                                                   int tiles_n, float* __restrict__ Y, int32_t* __restrict__ acc_out) {
+  static_assert(GM * GN == 4, "four waves");
+  static_assert(D % 2 == 0 && D >= 2, "ring of whole chunks");
+  constexpr int BM = GM * WM, BN = GN * WN;
+  constexpr int MB = WM / 16, NB = WN / 16;
+  constexpr int kHalf = kTileCols / 2;        // bytes per activation row in a half-stage
+  constexpr int kDma = BM / 32;               // direct loads per wave per half-stage (8 rows each, 4 waves)
+  constexpr int P = D - 1;                    // prefetch distance in half-stages
+  constexpr int CB = D / 2 + 1;               // weight register ring (chunks)
+  // one LDS object per ring slot: distinct objects let the compiler see that the direct
+  // loads into one slot do not alias reads of another (otherwise it waits for all of them)
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[BM * kHalf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[BM * kHalf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As2[D > 2 ? BM * kHalf : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t As3[D > 3 ? BM * kHalf : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t As4[D > 4 ? BM * kHalf : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t As5[D > 5 ? BM * kHalf : 16];
+  static_assert(D <= 6, "ring of at most 6 slots");
+  auto slab = [&](auto sc) -> uint8_t* {
+    constexpr int sl = decltype(sc)::value;
+    if constexpr (sl == 0) return As0;
+    else if constexpr (sl == 1) return As1;
+    else if constexpr (sl == 2) return As2;
+    else if constexpr (sl == 3) return As3;
+    else if constexpr (sl == 4) return As4;
+    else return As5;
+  };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  v4i acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+  const int wm = wave / GN, wn = wave % GN;
 
-  for (int step = 0; step < 2 * chunks; ++step) {
-    const int ch = step >> 1, half = step & 1;
-    const int kbase = ch * kTileCols + half * BK;
-    // A: 128 rows x 128 bytes = 1024 16-byte pieces, 4 per thread
+  // XCD-aware tile order: workgroup b runs on XCD b % 8; give XCD x the x-th contiguous
+  // run of tiles in row-major (m, n) order
+  const int tiles = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int per_xcd = (tiles + 7) / 8;
+  const int full = tiles - 8 * (per_xcd - 1);  // XCDs holding per_xcd tiles (the rest hold one fewer)
+  const int t = xcd < full ? xcd * per_xcd + slot : full * per_xcd + (xcd - full) * (per_xcd - 1) + slot;
+  if (slot >= (xcd < full ? per_xcd : per_xcd - 1)) return;
+  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+  const int hstages = 2 * chunks;
+
+  // this lane's source for each direct load: row 8 (4 j + wave) + lane / 8, LDS slot
+  // lane % 8 holding local piece lp = slot ^ swizzle, global piece 4 (lp >> 1) + 2h + (lp & 1)
+  // (rows past M repeat row M-1: their outputs are never stored)
+  const int8_t* asrc[kDma];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + 256 * j;
-      const int row = idx >> 3, piece = idx & 7;
-      const int m = m0 + row;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (m < M) v = *reinterpret_cast<const uint4*>(Xq + (size_t)m * K_pad + kbase + 16 * piece);
-      *reinterpret_cast<uint4*>(&As[row * LDS_STRIDE + 16 * piece]) = v;
-    }
-    // B: 8 row blocks x 32 slots (the half tile) = 256 slots, one per thread
-    {
-      const int nbl = tid >> 5, slot = 32 * half + (tid & 31);
-      const int nb = n0 / kTileRows + nbl;
-      uint4 wv = make_uint4(0u, 0u, 0u, 0u);  // code 00 decodes to 0
-      if (nb < n_blocks) wv = reinterpret_cast<const uint4*>(packed + ((size_t)nb * chunks + ch) * kTileBytes)[slot];
-      const int row = nbl * kTileRows + (slot & 15);
-      const int col = 64 * ((slot >> 4) & 1);  // 64 columns per slot inside the half tile
-      uint8_t* dst = &Bs[row * LDS_STRIDE + col];
-      *reinterpret_cast<v4i*>(dst + 0) = decode16(wv.x);
-      *reinterpret_cast<v4i*>(dst + 16) = decode16(wv.y);
-      *reinterpret_cast<v4i*>(dst + 32) = decode16(wv.z);
-      *reinterpret_cast<v4i*>(dst + 48) = decode16(wv.w);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < BK / 64; ++ks) {
-      v4i a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const v4i*>(&As[(64 * wm + 16 * i + r) * LDS_STRIDE + 64 * ks + 16 * g]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const v4i*>(&Bs[(64 * wn + 16 * j + r) * LDS_STRIDE + 64 * ks + 16 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
+  for (int j = 0; j < kDma; ++j) {
+    const int row = 8 * (4 * j + wave) + (lane >> 3);
+    const int lp = a_slot(row, lane & 7);
+    asrc[j] = Xq + (size_t)min(m0 + row, M - 1) * K_pad + 16 * (4 * (lp >> 1) + (lp & 1));
   }
+  // weight slots of this wave's NB row blocks (blocks past the matrix re-read the last
+  // block: their outputs are never stored)
+  const uint4* bsrc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int nb = min(n0 / kTileRows + wn * NB + j, n_blocks - 1);
+    bsrc[j] = reinterpret_cast<const uint4*>(packed) + (size_t)nb * chunks * 64 + lane;
+  }
+  uint4 bw[CB][NB];
+
+  v4i acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+
+  // compute half-stage in ring slot s (steps 2h, 2h+1 of its chunk) with weights cb
+  auto compute = [&](auto sc, int half, const uint4 (&wcur)[NB]) {
+    const uint8_t* slabp = slab(sc);
+#pragma unroll
+    for (int ip = 0; ip < 2; ++ip) {
+      const int i = 2 * half + ip;
+      v4i bf[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint32_t word = i == 0 ? wcur[j].x : (i == 1 ? wcur[j].y : (i == 2 ? wcur[j].z : wcur[j].w));
+        bf[j] = decode16(word);
+      }
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi) {
+        const int row = wm * WM + 16 * mi + r;
+        const v4i af = *reinterpret_cast<const v4i*>(&slabp[row * kHalf + 16 * a_slot(row, 2 * g + ip)]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[mi][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[j], acc[mi][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // Ring: half-stage hs computes LDS slot hs % D and refills slot (hs + P) % D (last read
+  // at hs - 1); the weights of chunk c live in register slot c % CB from half-stage 2c - P
+  // (issue) to 2c + 1 (last use).  The loop body covers D half-stages, so every slot
+  // index below is a compile-time constant.
+  // Prologue: half-stages 0 .. P-1.
+  static_for<P>([&](auto hc) {
+    constexpr int hs = decltype(hc)::value;
+    const int c = min(hs, hstages - 1) >> 1;
+    uint8_t* dst = slab(std::integral_constant<int, hs>{});
+#pragma unroll
+    for (int j = 0; j < kDma; ++j)
+      load_g2lds16(asrc[j] + (size_t)c * kTileCols + 32 * (min(hs, hstages - 1) & 1), &dst[8 * (4 * j + wave) * kHalf]);
+    if constexpr ((hs & 1) == 0) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bw[(hs / 2) % CB][j] = bsrc[j][(size_t)c * 64];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  wait_vmcnt<loads_between<kDma, NB>(0, P - 1)>();  // half-stage 0 has landed
+  ring_barrier();
+  // a do-while (there is always at least one chunk): a loop the compiler may skip lets it
+  // sink the prologue's weight loads below the barrier, which breaks the wait counts
+  int base = 0;
+  do {
+    // D * CB half-stages per trip keep both ring indices static
+    static_for<D * CB>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const int hs = base + k;
+      const int nh = hs + P;  // half-stage to issue
+      {
+        const int hc = min(nh, hstages - 1);
+        const int c = hc >> 1;
+        uint8_t* dst = slab(std::integral_constant<int, (k + P) % D>{});
+#pragma unroll
+        for (int j = 0; j < kDma; ++j)
+          load_g2lds16(asrc[j] + (size_t)c * kTileCols + 32 * (hc & 1), &dst[8 * (4 * j + wave) * kHalf]);
+        if constexpr (((k + P) & 1) == 0) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) bw[((k + P) / 2) % CB][j] = bsrc[j][(size_t)c * 64];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (hs < hstages) compute(std::integral_constant<int, k % D>{}, k & 1, bw[(k / 2) % CB]);
+      // half-stage hs + 1 has landed: loads issued after it are those of hs + 2 .. hs + P
+      wait_vmcnt<loads_between<kDma, NB>(k + 1, k + P)>();
+      ring_barrier();
+    });
+    base += D * CB;
+  } while (base < hstages);
+
   const float gm = gamma[0];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int mi = 0; mi < MB; ++mi) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int m = m0 + 64 * wm + 16 * i + 4 * g + v;
+      const int m = m0 + wm * WM + 16 * mi + 4 * g + v;
       if (m >= M) continue;
       const float sc = gm * absmax[m] * (1.0f / 127.0f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 64 * wn + 16 * j + r;
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + wn * WN + 16 * j + r;
         if (n < N) {
-          const int32_t a = acc[i][j][v];
+          const int32_t a = acc[mi][j][v];
           if (acc_out) acc_out[(size_t)m * N + n] = a;
           if (Y) Y[(size_t)m * N + n] = (float)a * sc;
         }
@@ -97,27 +231,40 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
   }
 }
 
+template <int GM, int GN, int WM, int WN, int D>
+hipError_t launch(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax, int64_t M,
+                  int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s) {
+  const int64_t K_pad = k_pad(K);
+  const int chunks = (int)(K_pad / kTileCols);
+  const int n_blocks = (int)(n_pad(N) / kTileRows);
+  constexpr int BM = GM * WM, BN = GN * WN;
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  const int tiles = tiles_m * tiles_n;
+  const int grid = 8 * ((tiles + 7) / 8);
+  hipLaunchKernelGGL((k_gemm_mfma<GM, GN, WM, WN, D>), dim3(grid), dim3(256), 0, s, packed, gamma, Xq, absmax, (int)M,
+                     (int)N, n_blocks, (int)K_pad, chunks, tiles_m, tiles_n, Y, acc);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   (void)K;
   GemmPlan p;
-  p.bm = BM;
-  p.bn = BN;
   p.threads = 256;
-  p.groups = ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+  // 128 x 128 tiles, four waves of 64 x 64, two-slot ring: 32 KiB of LDS and 152 VGPRs give
+  // three workgroups per compute unit.  Deeper rings (64 KiB) and wider wave tiles (more
+  // registers) drop to one or two per CU and measured slower on 2048..8192-row shapes.
+  p.bm = 128;
+  p.bn = 128;
+  const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+  p.groups = 8 * ((tiles + 7) / 8);
   return p;
 }
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s) {
-  const int64_t K_pad = k_pad(K);
-  const int chunks = (int)(K_pad / kTileCols);
-  const int n_blocks = (int)(n_pad(N) / kTileRows);
-  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  hipLaunchKernelGGL(k_gemm_mfma, grid, dim3(256), 0, s, packed, gamma, Xq, absmax, (int)M, (int)N, n_blocks,
-                     (int)K_pad, chunks, Y, acc);
-  return hipGetLastError();
+  return launch<2, 2, 64, 64, 2>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
 }
 
 }  // namespace bl

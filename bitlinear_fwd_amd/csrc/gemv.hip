@@ -38,6 +38,7 @@ namespace bl {
 namespace {
 
 constexpr int kMaxLdsActBytes = 48 * 1024;
+constexpr int64_t kMaxFusedElems = 8192;  // M*K limit of the one-kernel quantise + decode
 
 __device__ __forceinline__ uint32_t word_of(const uint4& w, int i) {
   return i == 0 ? w.x : (i == 1 ? w.y : (i == 2 ? w.z : w.w));
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_lds(const uint8_t* __restrict__
   extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];  // [M][K_pad + 16] int8
   __shared__ v4i red[W * 64];
   __shared__ float amax_red[W][4];
-  __shared__ float row_scale[4], row_amax[4];
+  __shared__ float row_amax[4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
@@ -164,26 +165,34 @@ __global__ __launch_bounds__(W * 64) void k_gemv_lds(const uint8_t* __restrict__
     }
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
-      float a = pm[mm];
+      if (mm < M) {
+        float a = pm[mm];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
-      if (lane == 0) amax_red[wave][mm] = a;
+        for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+        if (lane == 0) amax_red[wave][mm] = a;
+      }
     }
     __syncthreads();
-    if (threadIdx.x < 4) {
+    // every thread forms the row maxima and scales itself (no second barrier); the
+    // epilogue reads row_amax after the reduction barrier further down
+    float scale[4];
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
       float a = 0.0f;
-      for (int ww = 0; ww < W; ++ww) a = fmaxf(a, amax_red[ww][threadIdx.x]);
-      row_amax[threadIdx.x] = a;
-      row_scale[threadIdx.x] = a > 0.0f ? 127.0f / a : 0.0f;
-      if (blockIdx.x == 0 && (int)threadIdx.x < M) absmax_out[threadIdx.x] = a;
+      if (mm < M)
+        for (int ww = 0; ww < W; ++ww) a = fmaxf(a, amax_red[ww][mm]);
+      scale[mm] = a > 0.0f ? 127.0f / a : 0.0f;
+      if ((int)threadIdx.x == mm) {
+        row_amax[mm] = a;
+        if (blockIdx.x == 0 && mm < M) absmax_out[mm] = a;
+      }
     }
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < S; ++j) {
       const int idx = (int)threadIdx.x + j * W * 64;
       if (idx < pieces) {
         const int m = idx / per_row, p = idx - m * per_row;
-        const float s = row_scale[m];
+        const float s = m == 0 ? scale[0] : (m == 1 ? scale[1] : (m == 2 ? scale[2] : scale[3]));
         uint32_t packed_q[kElems / 4];
 #pragma unroll
         for (int e4 = 0; e4 < kElems / 4; ++e4) {
@@ -414,8 +423,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   const int64_t chunks = K_pad / kTileCols;
   const int64_t rblocks = n_pad(N) / kTileRows;
   const bool small = M <= 4 && M * (K_pad + 16) <= kMaxLdsActBytes;
-  // fused quantisation needs whole 16-byte pieces of x in every row
-  const bool src_ok = src == 0 || (src == 1 && K % 8 == 0) || (src == 2 && K % 4 == 0);
+  // fused quantisation needs whole 16-byte pieces of x in every row, and pays off only
+  // for short rows: every workgroup re-reads and re-quantises all M*K activations
+  const bool src_ok = src == 0 || (M * K <= kMaxFusedElems && ((src == 1 && K % 8 == 0) || (src == 2 && K % 4 == 0)));
   if (small && src_ok) {
     p.lds_act = true;
     p.rb = 1;

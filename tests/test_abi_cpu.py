@@ -24,6 +24,14 @@ def test_library_present():
     assert os.path.exists(bl.LIB_PATH), "build with `python -m bitlinear_fwd_amd.build`"
 
 
+def test_library_loads_without_unresolved_symbols():
+    # dlopen with immediate binding: every referenced symbol (kernel launch stubs
+    # included) must resolve
+    out = subprocess.run(["nm", "-D", "--undefined-only", bl.LIB_PATH], capture_output=True, text=True).stdout
+    assert "__device_stub__" not in out, out
+    ctypes.CDLL(bl.LIB_PATH, mode=os.RTLD_NOW)
+
+
 def test_exports_every_declared_symbol():
     declared = _declared_functions()
     assert set(declared) == set(bl.EXPORTED_SYMBOLS)
