@@ -1,22 +1,28 @@
 """Benchmark of the BitLinear forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 1] [--legs 2,3,4]
-                    [--no-graph] [--no-cpu-baseline]
+                    [--no-graph] [--no-cpu-baseline] [--copy-calibration MIB]
 
 A step is one pass of the hot path over one batch of synthetic input: for every matrix of
 the workload, the per-token int8 activation quantiser and the forward (packed-ternary x
 int8 contraction, exact int32 accumulation, fp32 rescale).  For a few tokens with short
 rows the two run as one fused kernel (bitlinear_forward_fused); otherwise as two kernels.
-Weights are quantised and packed once, before timing, as at model load.  Each step is
-replayed from a HIP graph captured beforehand (one graph per distinct weight set), so the
-timed region holds only GPU work.
+Weights are quantised and packed once, before timing, as at model load.  Each step's
+launches are C-ABI calls whose arguments were marshalled beforehand (one foreign call per
+kernel, a microsecond or so of host time), so the host stays ahead of the GPU and the
+timed region is the GPU's back-to-back execution.  --graph replays one captured HIP graph
+per step instead; on this stack a graph adds about a microsecond per kernel node over
+back-to-back stream launches, so it is the slower of the two for microsecond kernels.
 
 Headline (default workload 1): 2B-class decode at M = 1, gate/up 2560->6912 and down
 6912->2560, cycling through 48 distinct weight sets (637 MB of packed weights, more than
 twice the 256 MB Infinity Cache) so every step streams its weights from HBM.  value =
 packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
-  roofline     the decode kernel: algorithmic bytes per launch / mean launch duration
-               (HIP event pair around each launch, eager) against 8 TB/s;
+  roofline     the dominant kernel: algorithmic bytes (decode) or int8 ops (prefill) per
+               launch / mean launch duration, against 8 TB/s or 5.0 POPS.  The duration
+               comes from HIP events on the replay stream: the timed region over its
+               launches when the step is nothing but that kernel, else graph replays of the
+               forward launches alone.  traffic: measured HBM bytes per launch (see TRAFFIC);
   legs         the other workloads: M = 16 full layer, M = 2048 prefill (int8 TOPS vs
                5.0 POPS dense int8 MFMA), 100B-class M = 1 and M = 8 sweeps;
   cpu_baseline the CPU oracle on the host, on a bounded sample of the same workload.
@@ -44,9 +50,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--legs", default="2,3,4", help="other workloads timed into 'legs' ('' for none)")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured HIP graph instead of pre-marshalled eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device-to-device three times (the reference kernel of "
+                         "known size for scaling FETCH_SIZE / WRITE_SIZE counter runs)")
     return ap.parse_args()
 
 
@@ -87,25 +97,35 @@ class Workload:
                       for key in self.bufs}
         self.cursor = 0
         self.graphs = None
+        self.calls = [self.prepared(group, False) for group in self.step_groups()]
 
     def step_groups(self):
         """The matrix lists of the distinct steps (one per weight set, or one sweep)."""
         return [sum(self.sets, [])] if self.sweep else self.sets
 
-    def launch(self, mat, timing=None):
+    def launch(self, mat, forward_only=False):
         bl = self.bl
         xq, a, y = self.bufs[(mat.k, mat.n)]
         if self.fused[(mat.k, mat.n)]:
-            if timing is not None:
-                timing[0].record()
             bl.forward_fused(mat.packed, mat.gamma, mat.x, mat.n, mat.k, y=y, xq=xq, absmax=a)
         else:
-            bl.quantize_acts(mat.x, xq, a)
-            if timing is not None:
-                timing[0].record()
+            if not forward_only:
+                bl.quantize_acts(mat.x, xq, a)
             bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
-        if timing is not None:
-            timing[1].record()
+
+    def prepared(self, group, forward_only):
+        """The step's launches as pre-marshalled C-ABI calls (one foreign call each)."""
+        bl = self.bl
+        calls = []
+        for mat in group:
+            xq, a, y = self.bufs[(mat.k, mat.n)]
+            if self.fused[(mat.k, mat.n)]:
+                calls.append(bl.prepare_forward_fused(mat.packed, mat.gamma, mat.x, mat.n, mat.k, y, xq, a))
+            else:
+                if not forward_only:
+                    calls.append(bl.prepare_quantize_acts(mat.x, xq, a))
+                calls.append(bl.prepare_forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y))
+        return calls
 
     def capture(self):
         import torch
@@ -129,14 +149,70 @@ class Workload:
         if self.graphs is not None:
             self.graphs[i].replay()
         else:
-            for mat in groups[i]:
-                self.launch(mat)
+            for call in self.calls[i]:
+                call()
 
     def bytes_per_step(self):
         return sum(mat.bytes for mat in self.step_groups()[0])
 
     def ops_per_step(self):
         return sum(mat.ops for mat in self.step_groups()[0])
+
+
+# HBM traffic per launch of the dominant kernel, from two rocprofv3 --pmc runs of this script
+# (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, averaged over the step's launches), each
+# scaled by what the same counter reads for a device-to-device copy of known size run in the
+# same process (--copy-calibration).  A figure holds only for the kernel source it was taken
+# on: the sha256 of the kernel's source files is stored with it, and a mismatch reports null.
+KERNEL_SOURCES = {
+    "decode": ("bitlinear_fwd_amd/csrc/gemv.hip", "bitlinear_fwd_amd/csrc/bl_internal.h"),
+    "prefill": ("bitlinear_fwd_amd/csrc/gemm.hip", "bitlinear_fwd_amd/csrc/bl_internal.h"),
+}
+TRAFFIC = {
+    # (workload, M): {"bytes_per_launch": B, "fetch": F, "write": W, "sha": "..."}
+}
+
+
+def source_sha(kind: str) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: int, m: int):
+    rec = TRAFFIC.get((workload, m))
+    if rec is None:
+        return None
+    kind = "prefill" if kernel.startswith("k_gemm") else "decode"
+    return rec["bytes_per_launch"] if rec["sha"] == source_sha(kind) else None
+
+
+def copy_calibration(mib: int):
+    import torch
+
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def dominant_kernel(w: Workload) -> str:
+    """Name of the kernel that takes the step's time, as the launch plan picks it."""
+    m = w.m
+    key = max(w.bufs, key=lambda kn: kn[0] * kn[1])
+    plan = w.bl.forward_plan(m, key[1], key[0])
+    if plan["kernel"] == "prefill":
+        return "k_gemm_mfma (prefill, %dx%d tiles)" % (plan["tile_m"], plan["tile_n"])
+    if w.fused[key]:
+        return "k_gemv_lds (fused activation quantise + decode)"
+    return "k_gemv_lds (decode, activations in LDS)" if plan["lds_acts"] else "k_gemv_reg (decode)"
 
 
 def time_steps(w: Workload, steps: int, warmup: int):
@@ -154,22 +230,44 @@ def time_steps(w: Workload, steps: int, warmup: int):
     return start.elapsed_time(stop) / steps  # ms per step
 
 
-def time_forward_launches(w: Workload, passes: int):
-    """Mean duration of the forward kernel launches: an event pair around each launch
-    (eager, on the stream the kernels run on), over `passes` passes of every step group."""
+def time_forward_only(w: Workload, reps: int):
+    """Mean duration of one forward-kernel launch: HIP events on the stream the kernels run
+    on, around `reps` passes over the step groups that issue only the forward launches
+    (activations quantised beforehand where the step uses two kernels), launched the way
+    the timed steps are (pre-marshalled eager calls, or graph replays)."""
     import torch
 
-    recs = []
+    groups = w.step_groups()
+    for group in groups:
+        for mat in group:
+            w.launch(mat)  # leaves each matrix's quantised activations in place
     torch.cuda.synchronize()
-    for _ in range(passes):
-        for group in w.step_groups():
-            for mat in group:
-                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                w.launch(mat, timing=ev)
-                recs.append((ev, mat))
+    if w.graphs is not None:
+        runs = []
+        for group in groups:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for mat in group:
+                    w.launch(mat, forward_only=True)
+            runs.append(g.replay)
+        keep = runs
+    else:
+        keep = [w.prepared(group, True) for group in groups]
+        runs = [(lambda calls=calls: [c() for c in calls]) for calls in keep]
+    for r in runs:  # warm
+        r()
     torch.cuda.synchronize()
-    tot_ms = sum(ev[0].elapsed_time(ev[1]) for ev, _ in recs)
-    return tot_ms / len(recs), sum(m.bytes for _, m in recs) / len(recs), sum(m.ops for _, m in recs) / len(recs)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for r in range(reps):
+        runs[r % len(runs)]()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    mats = [mat for r in range(reps) for mat in groups[r % len(groups)]]
+    del keep, runs
+    return (start.elapsed_time(stop) / len(mats), sum(m.bytes for m in mats) / len(mats),
+            sum(m.ops for m in mats) / len(mats))
 
 
 def cpu_baseline(w: Workload, budget_s: float):
@@ -231,23 +329,38 @@ def main():
     bl.lib()
     m_head = synth.WORKLOADS[args.workload].m_list[0]
     head = Workload(bl, synth, args.workload, m_head, dev)
-    if not args.no_graph:
+    if args.graph:
         head.capture()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
     ms = time_steps(head, args.steps, args.warmup)
-    launch_ms, launch_bytes, launch_ops = time_forward_launches(head, 1 if head.sweep else 2)
     decode = m_head <= 16
+    mats = head.step_groups()[0]
+    if all(head.fused.values()):
+        # the step holds nothing but launches of the fused kernel: its mean launch duration
+        # is the timed region (HIP events on the replay stream) over the launches in it
+        launch_ms = ms / len(mats)
+        launch_bytes, launch_ops = head.bytes_per_step() / len(mats), head.ops_per_step() / len(mats)
+        launch_timing = "timed region / launches (the step is only this kernel)"
+    else:
+        launch_ms, launch_bytes, launch_ops = time_forward_only(head, 3 if head.sweep else 4 * len(head.sets))
+        launch_timing = "graph replays of the forward launches alone"
     value = head.bytes_per_step() / (ms * 1e-3) / 1e9 if decode else head.ops_per_step() / (ms * 1e-3) / 1e12
+    kernel = dominant_kernel(head)
+    traffic = measured_traffic(kernel, args.workload, m_head)
     if decode:
         achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_gemv_lds (fused quantise + decode)" if all(head.fused.values()) else "k_gemv",
-                "launch_us": round(launch_ms * 1e3, 3), "algorithmic_bytes_per_launch": int(launch_bytes)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": kernel, "launch_us": round(launch_ms * 1e3, 3), "launch_timing": launch_timing,
+                "algorithmic_bytes_per_launch": int(launch_bytes)}
     else:
+        # int8 contraction: TOPS against the dense int8 MFMA peak (unit kept as the contract's)
         achieved = launch_ops / (launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": I8_PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / I8_PEAK_TOPS, 4), "traffic": None, "kernel": "k_gemm_mfma",
-                "launch_us": round(launch_ms * 1e3, 3), "algorithmic_ops_per_launch": int(launch_ops)}
+                "frac": round(achieved / I8_PEAK_TOPS, 4), "traffic": traffic, "kernel": kernel,
+                "launch_us": round(launch_ms * 1e3, 3), "launch_timing": launch_timing,
+                "algorithmic_ops_per_launch": int(launch_ops)}
     legs = {}
     for tok in [t for t in args.legs.split(",") if t.strip()]:
         idx = int(tok)
@@ -255,11 +368,11 @@ def main():
             continue
         for m in synth.WORKLOADS[idx].m_list:
             w = Workload(bl, synth, idx, m, dev)
-            if not args.no_graph:
+            if args.graph:
                 w.capture()
             steps = max(3, args.steps // (40 if w.sweep else 1))
             lms = time_steps(w, steps, max(1, args.warmup // (40 if w.sweep else 4)))
-            l_ms, l_b, l_o = time_forward_launches(w, 1 if w.sweep else 2)
+            l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
             legs[f"w{idx}_m{m}"] = leg_summary(w, lms, l_ms, l_b, l_o)
             del w
             torch.cuda.empty_cache()
@@ -282,7 +395,7 @@ def main():
                    "matrices": [list(x) for x in head.wl.matrices],
                    "distinct_weight_sets": len(head.sets),
                    "packed_bytes_per_step": head.bytes_per_step(),
-                   "graph": not args.no_graph,
+                   "launch": "hip graph replay" if args.graph else "pre-marshalled eager C-ABI calls",
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -231,6 +231,56 @@ def forward_fused(packed, gamma, x, n: int, k: int, y=None, acc=None, xq=None, a
     return out, xq, absmax
 
 
+class PreparedCall:
+    """One C-ABI call with its arguments marshalled once: raw device pointers, sizes and the
+    stream handle, converted to ctypes values up front.  Calling it re-issues the same
+    launch for the cost of one foreign call, for launch loops where the per-call Python
+    work of the functions above would take longer than the kernel itself.  The caller keeps
+    the tensors the pointers came from alive."""
+
+    def __init__(self, fn: str, *args):
+        self._name = fn
+        self._fn = getattr(lib(), fn)
+        self._args = tuple(t(a) for t, a in zip(self._fn.argtypes, args))
+        if len(self._args) != len(self._fn.argtypes):
+            raise ValueError(f"{fn} takes {len(self._fn.argtypes)} arguments")
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != BL_OK:
+            _check(self._name, st)
+
+
+def prepare_forward_fused(packed, gamma, x, n: int, k: int, y, xq, absmax) -> PreparedCall:
+    """bitlinear_forward_fused on these tensors (y fp32 output), marshalled once."""
+    import torch
+
+    for t, name in ((packed, "packed"), (gamma, "gamma"), (x, "x"), (y, "y"), (xq, "xq"), (absmax, "absmax")):
+        _require_cuda(t, name)
+    dt = BL_BF16 if x.dtype == torch.bfloat16 else BL_F32
+    return PreparedCall("bitlinear_forward_fused", packed.data_ptr(), gamma.data_ptr(), x.data_ptr(), dt,
+                        x.shape[0], n, k, y.data_ptr(), None, xq.data_ptr(), absmax.data_ptr(), _stream(x.device))
+
+
+def prepare_quantize_acts(x, xq, absmax) -> PreparedCall:
+    """bitlinear_quantize_acts on these tensors, marshalled once."""
+    import torch
+
+    for t, name in ((x, "x"), (xq, "xq"), (absmax, "absmax")):
+        _require_cuda(t, name)
+    dt = BL_BF16 if x.dtype == torch.bfloat16 else BL_F32
+    return PreparedCall("bitlinear_quantize_acts", x.data_ptr(), dt, x.shape[0], x.shape[1], xq.data_ptr(),
+                        absmax.data_ptr(), _stream(x.device))
+
+
+def prepare_forward(packed, gamma, xq, absmax, n: int, k: int, y) -> PreparedCall:
+    """bitlinear_forward on these tensors (y fp32 output), marshalled once."""
+    for t, name in ((packed, "packed"), (gamma, "gamma"), (xq, "xq"), (absmax, "absmax"), (y, "y")):
+        _require_cuda(t, name)
+    return PreparedCall("bitlinear_forward", packed.data_ptr(), gamma.data_ptr(), xq.data_ptr(), absmax.data_ptr(),
+                        xq.shape[0], n, k, y.data_ptr(), None, _stream(xq.device))
+
+
 class BitLinear:
     """Inference-time BitLinear: weights quantised once, forward per token batch."""
 
