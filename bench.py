@@ -93,11 +93,19 @@ class Workload:
                 self.bufs[key] = (torch.empty((m, bl.k_pad(mat.k)), dtype=torch.int8, device=dev),
                                   torch.empty(m, dtype=torch.float32, device=dev),
                                   torch.empty((m, mat.n), dtype=torch.float32, device=dev))
-        self.fused = {key: bl.forward_plan(m, key[1], key[0])["kernel"] == "decode" and m <= 4
+        # forward_fused for a few tokens (one kernel when the library fuses the shape, else
+        # quantiser + forward); quantiser + forward otherwise
+        self.use_fused = m <= 4
+        self.fused = {key: m <= 4 and bl.forward_fused_plan(m, key[1], key[0], self._dt())["kernel"] == "fused"
                       for key in self.bufs}
         self.cursor = 0
         self.graphs = None
         self.calls = [self.prepared(group, False) for group in self.step_groups()]
+
+    def _dt(self):
+        import torch
+
+        return "bf16" if self.wl.act_dtype == torch.bfloat16 else "f32"
 
     def step_groups(self):
         """The matrix lists of the distinct steps (one per weight set, or one sweep)."""
@@ -106,7 +114,7 @@ class Workload:
     def launch(self, mat, forward_only=False):
         bl = self.bl
         xq, a, y = self.bufs[(mat.k, mat.n)]
-        if self.fused[(mat.k, mat.n)]:
+        if self.fused[(mat.k, mat.n)] or (self.use_fused and not forward_only):
             bl.forward_fused(mat.packed, mat.gamma, mat.x, mat.n, mat.k, y=y, xq=xq, absmax=a)
         else:
             if not forward_only:
@@ -119,7 +127,7 @@ class Workload:
         calls = []
         for mat in group:
             xq, a, y = self.bufs[(mat.k, mat.n)]
-            if self.fused[(mat.k, mat.n)]:
+            if self.fused[(mat.k, mat.n)] or (self.use_fused and not forward_only):
                 calls.append(bl.prepare_forward_fused(mat.packed, mat.gamma, mat.x, mat.n, mat.k, y, xq, a))
             else:
                 if not forward_only:
@@ -169,7 +177,12 @@ KERNEL_SOURCES = {
     "prefill": ("bitlinear_fwd_amd/csrc/gemm.hip", "bitlinear_fwd_amd/csrc/bl_internal.h"),
 }
 TRAFFIC = {
-    # (workload, M): {"bytes_per_launch": B, "fetch": F, "write": W, "sha": "..."}
+    # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
+    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.3 KiB (x1.99980),
+    # WRITE_SIZE 262144.0 KiB (x1.0).
+    (1, 1): {"bytes_per_launch": 4688235, "fetch_kib": 2276.77, "write_kib": 25.27, "sha": "5ee5fd4cbea92a19"},
+    (4, 1): {"bytes_per_launch": 59143507, "fetch_kib": 28843.55, "write_kib": 76.0, "sha": "5ee5fd4cbea92a19"},
+    (3, 2048): {"bytes_per_launch": 91587936, "fetch_kib": 25779.25, "write_kib": 37888.0, "sha": "2ee8480095a9aa9f"},
 }
 
 
@@ -212,6 +225,8 @@ def dominant_kernel(w: Workload) -> str:
         return "k_gemm_mfma (prefill, %dx%d tiles)" % (plan["tile_m"], plan["tile_n"])
     if w.fused[key]:
         return "k_gemv_lds (fused activation quantise + decode)"
+    if plan["acts"] == "registers":
+        return "k_gemv_dpp (decode, activations broadcast across lanes)"
     return "k_gemv_lds (decode, activations in LDS)" if plan["lds_acts"] else "k_gemv_reg (decode)"
 
 
@@ -374,6 +389,8 @@ def main():
             lms = time_steps(w, steps, max(1, args.warmup // (40 if w.sweep else 4)))
             l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
             legs[f"w{idx}_m{m}"] = leg_summary(w, lms, l_ms, l_b, l_o)
+            legs[f"w{idx}_m{m}"]["kernel"] = dominant_kernel(w)
+            legs[f"w{idx}_m{m}"]["traffic_bytes_per_launch"] = measured_traffic(dominant_kernel(w), idx, m)
             del w
             torch.cuda.empty_cache()
     cpu = None

@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward_fused.argtypes = [p, p, p, c_int, i64, i64, i64, p, p, p, p, p]
         L.bitlinear_forward_plan.restype = c_int
         L.bitlinear_forward_plan.argtypes = [i64, i64, i64, p]
+        L.bitlinear_forward_fused_plan.restype = c_int
+        L.bitlinear_forward_fused_plan.argtypes = [i64, i64, i64, c_int, p]
         L.bitlinear_forward.restype = c_int
         L.bitlinear_forward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p]
         _lib = L
@@ -67,6 +69,7 @@ EXPORTED_SYMBOLS = (
     "bitlinear_version", "bitlinear_status_string", "bitlinear_n_pad", "bitlinear_k_pad",
     "bitlinear_packed_bytes", "bitlinear_wq_workspace_bytes", "bitlinear_quantize_weights",
     "bitlinear_quantize_acts", "bitlinear_forward", "bitlinear_forward_fused", "bitlinear_forward_plan",
+    "bitlinear_forward_fused_plan",
 )
 
 
@@ -99,15 +102,33 @@ def wq_workspace_bytes(n: int, k: int) -> int:
     return int(lib().bitlinear_wq_workspace_bytes(n, k))
 
 
+def _plan_dict(out) -> dict:
+    if out[0] == 3:
+        return {"kernel": "fused", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
+                "acts": "lds", "lds_acts": True, "lds_bytes": out[5], "tiles_per_wave": 0}
+    if out[0] == 1:
+        acts = {0: "per-tile loads", 1: "lds", 2: "registers"}[out[4]]
+        return {"kernel": "decode", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
+                "acts": acts, "lds_acts": out[4] == 1, "lds_bytes": out[5] if out[4] == 1 else 0,
+                "tiles_per_wave": out[5] if out[4] == 2 else 0}
+    return {"kernel": "prefill", "workgroups": out[1], "threads": out[2], "tile_m": out[3], "tile_n": out[4],
+            "lds_bytes": out[5]}
+
+
 def forward_plan(m: int, n: int, k: int) -> dict:
     """The launch bitlinear_forward makes for (M, N, K), computed on the host."""
     out = (ctypes.c_int32 * 6)()
     _check("bitlinear_forward_plan", lib().bitlinear_forward_plan(m, n, k, out))
-    if out[0] == 1:
-        return {"kernel": "decode", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
-                "lds_acts": bool(out[4]), "lds_bytes": out[5]}
-    return {"kernel": "prefill", "workgroups": out[1], "threads": out[2], "tile_m": out[3], "tile_n": out[4],
-            "lds_bytes": out[5]}
+    return _plan_dict(out)
+
+
+def forward_fused_plan(m: int, n: int, k: int, dtype: str = "bf16") -> dict:
+    """What bitlinear_forward_fused does for (M, N, K): kernel "fused" (one launch) or the
+    forward launch that follows the activation quantiser."""
+    out = (ctypes.c_int32 * 6)()
+    dt = BL_BF16 if dtype == "bf16" else BL_F32
+    _check("bitlinear_forward_fused_plan", lib().bitlinear_forward_fused_plan(m, n, k, dt, out))
+    return _plan_dict(out)
 
 
 def _stream(device) -> int:

@@ -96,6 +96,24 @@ int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const voi
   return bitlinear_forward(packed, gamma, Xq, absmax, M, N, K, Y, acc, stream);
 }
 
+int bitlinear_forward_fused_plan(int64_t M, int64_t N, int64_t K, int dt, int32_t out[6]) {
+  if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
+  if (M <= kDecodeMaxM) {
+    const bl::GemvPlan p = bl::plan_gemv(M, N, K, dt == BL_BF16 ? 1 : 2);
+    if (p.lds_act && p.ok) {
+      out[0] = 3;
+      out[1] = (int32_t)p.groups;
+      out[2] = p.waves * 64;
+      out[3] = p.rb;
+      out[4] = 1;
+      out[5] = (int32_t)(M * (bl::k_pad(K) + 16));
+      return BL_OK;
+    }
+  }
+  return bitlinear_forward_plan(M, N, K, out);
+}
+
 int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]) {
   if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
   if (M <= kDecodeMaxM) {
@@ -104,8 +122,8 @@ int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]) {
     out[1] = (int32_t)p.groups;
     out[2] = p.waves * 64;
     out[3] = p.rb;
-    out[4] = p.lds_act ? 1 : 0;
-    out[5] = p.lds_act ? (int32_t)(M * (bl::k_pad(K) + 16)) : 0;
+    out[4] = p.dpp ? 2 : (p.lds_act ? 1 : 0);
+    out[5] = p.dpp ? p.run : (p.lds_act ? (int32_t)(M * (bl::k_pad(K) + 16)) : 0);
   } else {
     const bl::GemmPlan p = bl::plan_gemm(M, N, K);
     out[0] = 2;

@@ -34,6 +34,8 @@
 //               the weights of that batch and reuses them for its RB row blocks.
 #include "bl_internal.h"
 
+#include <algorithm>
+
 namespace bl {
 namespace {
 
@@ -347,6 +349,117 @@ __global__ __launch_bounds__(W * 64) void k_gemv_reg(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------
+// k_gemv_dpp (M = MM <= 4 tokens, int8 activations): no LDS staging and no barrier before
+// the contraction.  A workgroup owns one 16-row block; wave w owns tiles [w T, w T + T)
+// of it (T a compile-time run length; tiles past the matrix re-read the last tile and
+// decode as zeros) and issues every one of its loads at once, so the whole matrix is in
+// flight from the start.  Activations travel in registers: with UA = 16 / (4 MM) tiles
+// per activation load, lane (r, g) loads the 16 bytes of token r % MM, step (r / MM) % 4,
+// tile r / (4 MM) of its group, at columns 64 g + 16 step; the A operand of step i of
+// tile u is that register shifted down MM (4 u + i) lanes inside each 16-lane row (DPP
+// row_shl), which puts the piece of token m in lane m.  Lanes r >= MM receive other
+// pieces: they feed output rows of tokens that do not exist and are never stored.
+template <int s>
+__device__ __forceinline__ int row_shl(int v) {
+  if constexpr (s == 0) return v;
+  else return __builtin_amdgcn_mov_dpp(v, 0x100 + s, 0xF, 0xF, true);
+}
+
+// One token: the A operand of step (u, i) only needs piece 4 u + i in lane 0 of each row,
+// and a 64-bit DPP row_newbcast copies that lane to the whole row in two moves.
+template <int n>
+__device__ __forceinline__ uint64_t row_bcast64(uint64_t v) {
+  return (uint64_t)__builtin_amdgcn_update_dpp((long)0, (long)v, 0x150 + n, 0xF, 0xF, false);
+}
+
+template <int T, int MM, bool kExact>
+__global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ packed,
+                                                  const float* __restrict__ gamma, const int8_t* __restrict__ Xq,
+                                                  const float* __restrict__ absmax, int M, int N, int K_pad,
+                                                  int chunks, int rblocks, float* __restrict__ Y,
+                                                  int32_t* __restrict__ acc_out) {
+  static_assert(MM >= 1 && MM <= 4, "one to four tokens");
+  constexpr int UA = 16 / (4 * MM);      // tiles covered by one activation load
+  constexpr int NA = (T + UA - 1) / UA;  // activation loads per wave
+  __shared__ v4i red[16 * 64];
+  const int W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int rb0 = blockIdx.x;
+  const int c0 = wave * T;
+  const uint4* wsrc = reinterpret_cast<const uint4*>(packed) + (size_t)rb0 * chunks * 64 + lane;
+  const int pm = r % MM, pq = r / MM;
+  const int pu = min(pq / 4, UA - 1), pi = pq % 4;
+  const int8_t* asrc = Xq + (size_t)pm * K_pad + 64 * g + 16 * pi;
+
+  uint4 w[T];
+  uint4 a[NA];
+  static_for<NA>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    a[j] = *reinterpret_cast<const uint4*>(asrc + (size_t)min(c0 + j * UA + pu, chunks - 1) * kTileCols);
+    static_for<UA>([&](auto uc) {
+      constexpr int t = j * UA + decltype(uc)::value;
+      if constexpr (t < T) w[t] = load_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
+    });
+  });
+  __builtin_amdgcn_sched_barrier(0);
+
+  v4i c = {0, 0, 0, 0};
+  static_for<NA>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    static_for<UA>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int t = j * UA + u;
+      if constexpr (t < T) {
+        // kExact: W T == chunks, every tile is live; else tiles past the matrix decode as 0
+        const bool live = kExact || c0 + t < chunks;
+        static_for<4>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          constexpr int sft = MM * (4 * u + i);
+          const uint32_t word = kExact ? word_of(w[t], i) : (live ? word_of(w[t], i) : 0u);
+          v4i av;
+          if constexpr (MM == 1) {
+            const uint64_t lo = row_bcast64<sft>((uint64_t)a[j].x | ((uint64_t)a[j].y << 32));
+            const uint64_t hi = row_bcast64<sft>((uint64_t)a[j].z | ((uint64_t)a[j].w << 32));
+            av.x = (int)(uint32_t)lo;
+            av.y = (int)(uint32_t)(lo >> 32);
+            av.z = (int)(uint32_t)hi;
+            av.w = (int)(uint32_t)(hi >> 32);
+          } else {
+            av.x = row_shl<sft>((int)a[j].x);
+            av.y = row_shl<sft>((int)a[j].y);
+            av.z = row_shl<sft>((int)a[j].z);
+            av.w = row_shl<sft>((int)a[j].w);
+          }
+          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, decode16(word), c, 0, 0, 0);
+        });
+      }
+    });
+  });
+
+  red[wave * 64 + lane] = c;
+  __syncthreads();
+  // sum the W partial tiles in wave order (exact) and store row block rb0
+  if (wave == 0) {
+    v4i sum = red[lane];
+    for (int w2 = 1; w2 < W; ++w2) sum += red[w2 * 64 + lane];
+    const int n = rb0 * kTileRows + r;
+    if (n < N) {
+      const float gm = gamma[0];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * g + v;
+        if (m < M) {
+          if (acc_out) acc_out[(size_t)m * N + n] = sum[v];
+          if (Y) Y[(size_t)m * N + n] = (float)sum[v] * gm * absmax[m] * (1.0f / 127.0f);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 struct Args {
   const uint8_t* packed;
   const float* gamma;
@@ -407,6 +520,53 @@ hipError_t launch_reg_w(int W, const Args& a, hipStream_t s) {
   }
 }
 
+template <int T, int MM>
+hipError_t launch_dpp(int W, const Args& a, hipStream_t s) {
+  if (W * T == a.chunks)
+    hipLaunchKernelGGL((k_gemv_dpp<T, MM, true>), dim3(a.rblocks), dim3(W * 64), 0, s, a.packed, a.gamma,
+                       static_cast<const int8_t*>(a.X), a.absmax, a.M, a.N, a.K_pad, a.chunks, a.rblocks, a.Y,
+                       a.acc);
+  else
+    hipLaunchKernelGGL((k_gemv_dpp<T, MM, false>), dim3(a.rblocks), dim3(W * 64), 0, s, a.packed, a.gamma,
+                     static_cast<const int8_t*>(a.X), a.absmax, a.M, a.N, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc);
+  return hipGetLastError();
+}
+
+// Supported dpp run lengths (K tiles per wave); returns the smallest one >= t, or 0.
+constexpr int kDppRuns[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
+int64_t dpp_run(int64_t t) {
+  for (int r : kDppRuns)
+    if (r >= t) return r;
+  return 0;
+}
+
+template <int T>
+hipError_t launch_dpp_m(int M, int W, const Args& a, hipStream_t s) {
+  switch (M) {
+    case 1: return launch_dpp<T, 1>(W, a, s);
+    case 2: return launch_dpp<T, 2>(W, a, s);
+    case 3: return launch_dpp<T, 3>(W, a, s);
+    default: return launch_dpp<T, 4>(W, a, s);
+  }
+}
+
+hipError_t launch_dpp_run(int T, int M, int W, const Args& a, hipStream_t s) {
+  switch (T) {
+    case 1: return launch_dpp_m<1>(M, W, a, s);
+    case 2: return launch_dpp_m<2>(M, W, a, s);
+    case 3: return launch_dpp_m<3>(M, W, a, s);
+    case 4: return launch_dpp_m<4>(M, W, a, s);
+    case 5: return launch_dpp_m<5>(M, W, a, s);
+    case 6: return launch_dpp_m<6>(M, W, a, s);
+    case 7: return launch_dpp_m<7>(M, W, a, s);
+    case 8: return launch_dpp_m<8>(M, W, a, s);
+    case 10: return launch_dpp_m<10>(M, W, a, s);
+    case 12: return launch_dpp_m<12>(M, W, a, s);
+    case 14: return launch_dpp_m<14>(M, W, a, s);
+    default: return launch_dpp_m<16>(M, W, a, s);
+  }
+}
+
 // waves per workgroup: enough waves in flight without splitting K finer than ~2 tiles
 // per wave, and at most ~32 waves per compute unit overall
 int pick_waves(int64_t chunks, int64_t groups) {
@@ -426,7 +586,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   // fused quantisation needs whole 16-byte pieces of x in every row, and pays off only
   // for short rows: every workgroup re-reads and re-quantises all M*K activations
   const bool src_ok = src == 0 || (M * K <= kMaxFusedElems && ((src == 1 && K % 8 == 0) || (src == 2 && K % 4 == 0)));
-  if (small && src_ok) {
+  if (src != 0 && small && src_ok) {
     p.lds_act = true;
     p.rb = 1;
     p.groups = rblocks;
@@ -441,11 +601,25 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   }
   p.lds_act = false;
   p.rb = 1;
+  p.ok = src == 0;  // the register paths read int8 activations only
+  if (M <= 4) {
+    // about 32 waves per compute unit over the launch, at least two tiles per wave, then
+    // the shortest supported run that covers the row block with at most 16 waves
+    int64_t w = std::min<int64_t>(16, std::max<int64_t>(1, 8192 / rblocks));
+    w = std::min<int64_t>(w, std::max<int64_t>(1, (chunks + 1) / 2));
+    const int64_t t = dpp_run((chunks + w - 1) / w);
+    if (t > 0 && (chunks + t - 1) / t <= 16) {
+      p.dpp = true;
+      p.run = (int)t;
+      p.waves = (int)((chunks + t - 1) / t);
+      p.groups = rblocks;
+      return p;
+    }
+  }
   if (M > 4 && rblocks >= 4 * 256) p.rb = 4;
   else if (M > 4 && rblocks >= 2 * 256) p.rb = 2;
   p.groups = (rblocks + p.rb - 1) / p.rb;
   p.waves = pick_waves(chunks, p.groups);
-  p.ok = src == 0;  // the register path reads int8 activations only
   return p;
 }
 
@@ -454,6 +628,7 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
   const GemvPlan p = plan_gemv(M, N, K, 0);
   Args a{packed, gamma, Xq, absmax, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
          (int)(n_pad(N) / kTileRows), Y, acc, nullptr, nullptr};
+  if (p.dpp) return launch_dpp_run(p.run, (int)M, p.waves, a, s);
   if (p.lds_act) return launch_lds_w<0>(p.waves, p.stage, a, s);
   if (p.rb == 4) return launch_reg_w<4, 1, 2>(p.waves, a, s);
   if (p.rb == 2) return launch_reg_w<2, 1, 2>(p.waves, a, s);

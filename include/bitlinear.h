@@ -134,11 +134,23 @@ int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const voi
  * Host-only description of the launch bitlinear_forward would make for (M, N, K); no
  * device work.  out[0] = kernel (1 = decode, 2 = prefill), out[1] = workgroups,
  * out[2] = threads per workgroup, out[3] = decode: 16-row output blocks per workgroup,
- * prefill: output tile rows, out[4] = decode: 1 if activations are staged in LDS,
- * prefill: output tile columns, out[5] = dynamic LDS bytes.  Returns BL_OK or
- * BL_ERR_INVALID_ARG (same size rules as bitlinear_forward, null out).
+ * prefill: output tile rows, out[4] = decode: where the activations live (0 = loaded with
+ * each weight tile, 1 = staged in LDS, 2 = held in registers and broadcast across lanes),
+ * prefill: output tile columns, out[5] = decode: dynamic LDS bytes (out[4] = 1) or K
+ * tiles per wave (out[4] = 2), else 0.  Returns BL_OK or BL_ERR_INVALID_ARG (same size
+ * rules as bitlinear_forward, null out).
  */
 int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]);
+
+/*
+ * Host-only description of what bitlinear_forward_fused does for (M, N, K) and activation
+ * type dt, for a 16-byte aligned X; no device work.  out[0] = 3 when one fused kernel
+ * quantises and contracts (out[1..3] as bitlinear_forward_plan, out[4] = 1, out[5] =
+ * dynamic LDS bytes); otherwise the activation quantiser runs first and out[] describes
+ * the forward launch exactly as bitlinear_forward_plan.  Returns BL_OK,
+ * BL_ERR_INVALID_ARG (as bitlinear_forward_plan) or BL_ERR_UNSUPPORTED (dt).
+ */
+int bitlinear_forward_fused_plan(int64_t M, int64_t N, int64_t K, int dt, int32_t out[6]);
 
 #ifdef __cplusplus
 }

@@ -179,17 +179,27 @@ def test_forward_decode(m, n, k):
     _fwd_check(m, n, k, seed=m * 1000 + n + k)
 
 
-@pytest.mark.parametrize("m,n,k,rb,lds", [
-    (1, 512, 256, 1, True), (1, 16400, 300, 1, True), (3, 130, 7000, 1, True), (2, 8200, 12000, 1, True),
-    (1, 300, 40000, 1, True), (2, 70, 5000, 1, True),
-    (4, 100, 16000, 1, False), (5, 8200, 300, 2, False), (16, 16400, 256, 4, False), (8, 2560, 6912, 1, False),
-    (12, 16400, 1000, 4, False), (7, 9000, 4100, 2, False), (16, 4200, 9000, 1, False)])
-def test_forward_decode_variants(m, n, k, rb, lds):
-    # every decode-kernel variant (activations in LDS or registers, 1/2/4 row blocks per
-    # workgroup, 1..16 waves splitting K) against the oracle, including ragged N and K
+@pytest.mark.parametrize("m,n,k,acts,rb,run", [
+    # M <= 4: activations in registers (DPP broadcast), every supported run length, exact
+    # and ragged wave tilings, one to four tokens
+    (1, 512, 256, "registers", 1, 1), (1, 16400, 300, "registers", 1, 2), (3, 130, 7000, "registers", 1, 2),
+    (1, 64, 10000, "registers", 1, 3), (2, 8200, 12000, "registers", 1, 4), (4, 100, 16000, "registers", 1, 4),
+    (1, 40, 17000, "registers", 1, 5), (2, 30, 22000, "registers", 1, 6), (1, 100, 27000, "registers", 1, 7),
+    (2, 50, 30000, "registers", 1, 8), (1, 300, 40000, "registers", 1, 10), (3, 33, 47000, "registers", 1, 12),
+    (1, 20, 55000, "registers", 1, 14), (4, 20, 62000, "registers", 1, 16), (2, 70, 5000, "registers", 1, 2),
+    (3, 1000, 2560, "registers", 1, 2),
+    # K beyond 16 waves x 16 tiles: activations loaded with each tile
+    (4, 40, 70000, "per-tile loads", 1, 0),
+    # M = 5..16: activations loaded with each tile, 1/2/4 row blocks per workgroup
+    (5, 8200, 300, "per-tile loads", 2, 0), (16, 16400, 256, "per-tile loads", 4, 0),
+    (8, 2560, 6912, "per-tile loads", 1, 0), (12, 16400, 1000, "per-tile loads", 4, 0),
+    (7, 9000, 4100, "per-tile loads", 2, 0), (16, 4200, 9000, "per-tile loads", 1, 0)])
+def test_forward_decode_variants(m, n, k, acts, rb, run):
+    # every decode-kernel variant against the oracle, including ragged N and K
     plan = bl.forward_plan(m, n, k)
     _announce("forward decode variant", m, n, k, plan)
-    assert plan["kernel"] == "decode" and plan["row_blocks"] == rb and plan["lds_acts"] == lds
+    assert plan["kernel"] == "decode" and plan["acts"] == acts and plan["row_blocks"] == rb
+    assert plan["tiles_per_wave"] == run
     _fwd_check(m, n, k, seed=m * 7 + n * 3 + k)
 
 
@@ -284,18 +294,24 @@ def _fused_check(m, n, k, dtype, seed, unaligned=False):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("m,n,k", [(1, 512, 256), (1, 700, 2560), (2, 130, 6912), (3, 48, 1000), (4, 520, 4096),
-                                   (1, 33, 8), (1, 16400, 512), (2, 100, 12000)])
+@pytest.mark.parametrize("m,n,k", [(1, 512, 256), (1, 700, 2560), (2, 130, 4096), (3, 48, 1000), (4, 520, 2048),
+                                   (1, 33, 8), (1, 16400, 512), (1, 64, 6912)])
 def test_forward_fused_single_kernel(m, n, k, dtype):
-    # shapes the one-kernel path takes (M <= 4, short rows, K a multiple of 8)
-    _announce("forward fused", m, n, k, dtype)
+    # shapes the one-kernel path takes (M <= 4, M*K <= 8192, K a multiple of 8)
+    plan = bl.forward_fused_plan(m, n, k, "bf16" if dtype == torch.bfloat16 else "f32")
+    _announce("forward fused", m, n, k, dtype, plan)
+    assert plan["kernel"] == "fused"
     _fused_check(m, n, k, dtype, seed=m * 31 + n + k)
 
 
 @pytest.mark.parametrize("m,n,k,dtype,unaligned", [(5, 64, 512, torch.bfloat16, False), (1, 64, 300, torch.bfloat16, False),
                                                    (2, 64, 1002, torch.float32, False), (3, 40, 512, torch.bfloat16, True),
-                                                   (1, 40, 30000, torch.bfloat16, False), (40, 72, 700, torch.float32, False)])
+                                                   (1, 40, 30000, torch.bfloat16, False), (40, 72, 700, torch.float32, False),
+                                                   (2, 130, 6912, torch.bfloat16, False), (4, 520, 4096, torch.float32, False),
+                                                   (2, 100, 12000, torch.bfloat16, False)])
 def test_forward_fused_fallback(m, n, k, dtype, unaligned):
     # shapes outside the one-kernel path: the quantiser kernel then the forward kernel
-    _announce("forward fused fallback", m, n, k, dtype, unaligned)
+    plan = bl.forward_fused_plan(m, n, k, "bf16" if dtype == torch.bfloat16 else "f32")
+    _announce("forward fused fallback", m, n, k, dtype, unaligned, plan)
+    assert unaligned or plan["kernel"] != "fused"
     _fused_check(m, n, k, dtype, seed=m * 17 + n + k, unaligned=unaligned)
