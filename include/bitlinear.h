@@ -123,9 +123,10 @@ int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* X
  *   absmax  out: fp32 [M] (as bitlinear_quantize_acts).
  *   Y, acc  as bitlinear_forward (at least one non-null).
  * Results are identical to bitlinear_quantize_acts followed by bitlinear_forward.  For a
- * few tokens (M <= 4) with a short row (M*K_pad <= 48 KiB), K a multiple of 8 (bf16) or
- * 4 (fp32) and a 16-byte aligned X, one kernel launch does all three steps (each
- * workgroup quantises the rows into LDS); otherwise the two kernels run back to back.
+ * few tokens with short rows (M <= 4, M*K <= 8192), K a multiple of 8 (bf16) or 4 (fp32)
+ * and a 16-byte aligned X, one kernel launch does all three steps (each workgroup
+ * quantises the rows into LDS); otherwise the two kernels run back to back
+ * (bitlinear_forward_fused_plan tells which).
  */
 int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const void* X, int dt, int64_t M, int64_t N,
                             int64_t K, float* Y, int32_t* acc, int8_t* Xq, float* absmax, void* stream);
