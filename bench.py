@@ -224,7 +224,10 @@ def dominant_kernel(w: Workload) -> str:
     if plan["kernel"] == "prefill":
         return "k_gemm_mfma (prefill, %dx%d tiles)" % (plan["tile_m"], plan["tile_n"])
     if w.fused[key]:
-        return "k_gemv_lds (fused activation quantise + decode)"
+        fplan = w.bl.forward_fused_plan(m, key[1], key[0], w._dt())
+        if fplan["acts"] == "registers":
+            return "k_gemv_dpp (fused activation quantise + decode, activations in registers)"
+        return "k_gemv_lds (fused activation quantise + decode, activations in LDS)"
     if plan["acts"] == "registers":
         return "k_gemv_dpp (decode, activations broadcast across lanes)"
     return "k_gemv_lds (decode, activations in LDS)" if plan["lds_acts"] else "k_gemv_reg (decode)"

@@ -105,7 +105,8 @@ def wq_workspace_bytes(n: int, k: int) -> int:
 def _plan_dict(out) -> dict:
     if out[0] == 3:
         return {"kernel": "fused", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
-                "acts": "lds", "lds_acts": True, "lds_bytes": out[5], "tiles_per_wave": 0}
+                "acts": "registers" if out[4] == 2 else "lds", "lds_acts": out[4] == 1,
+                "lds_bytes": out[5] if out[4] == 1 else 0, "tiles_per_wave": out[5] if out[4] == 2 else 0}
     if out[0] == 1:
         acts = {0: "per-tile loads", 1: "lds", 2: "registers"}[out[4]]
         return {"kernel": "decode", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],

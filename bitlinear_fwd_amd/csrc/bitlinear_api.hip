@@ -87,7 +87,7 @@ int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const voi
   const int src = dt == BL_BF16 ? 1 : 2;
   if (M <= kDecodeMaxM && aligned(X, 16)) {
     const bl::GemvPlan p = bl::plan_gemv(M, N, K, src);
-    if (p.lds_act && p.ok)
+    if ((p.lds_act || p.dpp) && p.ok)
       return hip_status(bl::launch_gemv_fused(packed, gamma, X, dt == BL_BF16, M, N, K, Y, acc, Xq, absmax, s));
   }
   // general case: the activation quantiser, then the forward, both on the stream
@@ -101,13 +101,13 @@ int bitlinear_forward_fused_plan(int64_t M, int64_t N, int64_t K, int dt, int32_
   if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
   if (M <= kDecodeMaxM) {
     const bl::GemvPlan p = bl::plan_gemv(M, N, K, dt == BL_BF16 ? 1 : 2);
-    if (p.lds_act && p.ok) {
+    if ((p.lds_act || p.dpp) && p.ok) {
       out[0] = 3;
       out[1] = (int32_t)p.groups;
       out[2] = p.waves * 64;
       out[3] = p.rb;
-      out[4] = 1;
-      out[5] = (int32_t)(M * (bl::k_pad(K) + 16));
+      out[4] = p.dpp ? 2 : 1;
+      out[5] = p.dpp ? p.run : (int32_t)(M * (bl::k_pad(K) + 16));
       return BL_OK;
     }
   }

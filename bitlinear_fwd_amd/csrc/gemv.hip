@@ -349,16 +349,23 @@ __global__ __launch_bounds__(W * 64) void k_gemv_reg(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------
-// k_gemv_dpp (M = MM <= 4 tokens, int8 activations): no LDS staging and no barrier before
-// the contraction.  A workgroup owns one 16-row block; wave w owns tiles [w T, w T + T)
-// of it (T a compile-time run length; tiles past the matrix re-read the last tile and
-// decode as zeros) and issues every one of its loads at once, so the whole matrix is in
-// flight from the start.  Activations travel in registers: with UA = 16 / (4 MM) tiles
-// per activation load, lane (r, g) loads the 16 bytes of token r % MM, step (r / MM) % 4,
-// tile r / (4 MM) of its group, at columns 64 g + 16 step; the A operand of step i of
-// tile u is that register shifted down MM (4 u + i) lanes inside each 16-lane row (DPP
-// row_shl), which puts the piece of token m in lane m.  Lanes r >= MM receive other
-// pieces: they feed output rows of tokens that do not exist and are never stored.
+// k_gemv_dpp (M = MM <= 4 tokens): no LDS staging of activations and no barrier in front
+// of the weight stream.  A workgroup owns one 16-row block; wave w owns tiles
+// [w T, w T + T) of it (T a compile-time run length; tiles past the matrix re-read the
+// last tile and decode as zeros) and issues every one of its loads at once, so the whole
+// matrix is in flight from the start.  Activations travel in registers: with
+// UA = 16 / (4 MM) tiles per activation piece, lane (r, g) holds the 16 activations of
+// token r % MM, step (r / MM) % 4, tile r / (4 MM) of its group, at columns 64 g + 16 step;
+// the A operand of step i of tile u is that register shifted down MM (4 u + i) lanes inside
+// each 16-lane row (DPP), which puts the piece of token m in lane m.  Lanes r >= MM
+// receive other pieces: they feed output rows of tokens that do not exist and are never
+// stored.
+//
+// kSrc = 0 reads int8 xq.  kSrc = 1 (bf16) / 2 (fp32) is the fused form: the pieces are
+// read from x itself, and since the pieces of a workgroup's waves cover every column of
+// every token, the per-token absmax is the maximum over them (wave reductions, then one
+// barrier across the waves); each lane then quantises its own pieces with the
+// arithmetic of the standalone quantiser, and workgroup 0 stores xq and absmax.
 template <int s>
 __device__ __forceinline__ int row_shl(int v) {
   if constexpr (s == 0) return v;
@@ -372,16 +379,32 @@ __device__ __forceinline__ uint64_t row_bcast64(uint64_t v) {
   return (uint64_t)__builtin_amdgcn_update_dpp((long)0, (long)v, 0x150 + n, 0xF, 0xF, false);
 }
 
-template <int T, int MM, bool kExact>
+// Work-group barrier that only orders LDS: unlike __syncthreads() it carries no release
+// fence, so it does not wait for the weight loads still in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int MM, int kSrc>
+struct DppShape {
+  static constexpr int UA = 16 / (4 * MM);                        // tiles per activation piece
+  static constexpr int kParts = kSrc == 0 ? 1 : (kSrc == 1 ? 2 : 4);  // 16-byte loads per piece
+};
+
+template <int T, int MM, int kSrc>
 __global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ packed,
-                                                  const float* __restrict__ gamma, const int8_t* __restrict__ Xq,
-                                                  const float* __restrict__ absmax, int M, int N, int K_pad,
-                                                  int chunks, int rblocks, float* __restrict__ Y,
-                                                  int32_t* __restrict__ acc_out) {
+                                                  const float* __restrict__ gamma, const void* __restrict__ X,
+                                                  const float* __restrict__ absmax_in, int M, int N, int K,
+                                                  int K_pad, int chunks, int rblocks, float* __restrict__ Y,
+                                                  int32_t* __restrict__ acc_out, int8_t* __restrict__ xq_out,
+                                                  float* __restrict__ absmax_out) {
   static_assert(MM >= 1 && MM <= 4, "one to four tokens");
-  constexpr int UA = 16 / (4 * MM);      // tiles covered by one activation load
-  constexpr int NA = (T + UA - 1) / UA;  // activation loads per wave
+  constexpr int UA = DppShape<MM, kSrc>::UA;
+  constexpr int NA = (T + UA - 1) / UA;    // activation pieces per lane
+  constexpr int kParts = DppShape<MM, kSrc>::kParts;
+  constexpr int kPartElems = 16 / kParts;  // elements per 16-byte load
   __shared__ v4i red[16 * 64];
+  __shared__ float amax_w[16][4];
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -391,17 +414,98 @@ __global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ p
   const uint4* wsrc = reinterpret_cast<const uint4*>(packed) + (size_t)rb0 * chunks * 64 + lane;
   const int pm = r % MM, pq = r / MM;
   const int pu = min(pq / 4, UA - 1), pi = pq % 4;
-  const int8_t* asrc = Xq + (size_t)pm * K_pad + 64 * g + 16 * pi;
 
-  uint4 w[T];
-  uint4 a[NA];
+  // every activation load first (their wait then does not wait for the weights), then
+  // every weight load of the run
+  uint4 raw[NA][kParts];
   static_for<NA>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    a[j] = *reinterpret_cast<const uint4*>(asrc + (size_t)min(c0 + j * UA + pu, chunks - 1) * kTileCols);
-    static_for<UA>([&](auto uc) {
-      constexpr int t = j * UA + decltype(uc)::value;
-      if constexpr (t < T) w[t] = load_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
+    const int col = min(c0 + j * UA + pu, chunks - 1) * kTileCols + 64 * g + 16 * pi;
+    if constexpr (kSrc == 0) {
+      raw[j][0] = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(X) + (size_t)pm * K_pad + col);
+    } else {
+      constexpr int kEB = kSrc == 1 ? 2 : 4;
+      static_for<kParts>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const int e = col + kPartElems * h;
+        const int es = e + kPartElems <= K ? e : K - kPartElems;  // columns past K: any valid load, zeroed below
+        raw[j][h] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(X) + ((size_t)pm * K + es) * kEB);
+      });
+    }
+  });
+  // The fused form issues its weight loads only after the absmax barrier: loads issued
+  // earlier by any wave of the compute unit delay the activation loads queued behind
+  // them, and with them the barrier (measured: up to 5 us on 58.7 MB matrices).
+  constexpr int kEarly = kSrc == 0 ? T : 0;
+  uint4 w[T];
+  static_for<kEarly>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    w[t] = load_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+
+  uint4 act[NA];
+  float am[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // fused form: absmax of tokens 0..MM-1
+  if constexpr (kSrc == 0) {
+    static_for<NA>([&](auto jc) { act[decltype(jc)::value] = raw[decltype(jc)::value][0]; });
+  } else {
+    float v[NA][16];
+    float lmax = 0.0f;
+    static_for<NA>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int col = min(c0 + j * UA + pu, chunks - 1) * kTileCols + 64 * g + 16 * pi;
+      static_for<kParts>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const bool in = col + kPartElems * h + kPartElems <= K;
+        const uint32_t d[4] = {raw[j][h].x, raw[j][h].y, raw[j][h].z, raw[j][h].w};
+#pragma unroll
+        for (int e = 0; e < kPartElems; ++e) {
+          float f;
+          if constexpr (kSrc == 1) f = __uint_as_float(e & 1 ? (d[e >> 1] & 0xFFFF0000u) : (d[e >> 1] << 16));
+          else f = __uint_as_float(d[e]);
+          f = in ? f : 0.0f;
+          v[j][kPartElems * h + e] = f;
+          lmax = fmaxf(lmax, fabsf(f));
+        }
+      });
     });
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      float x = pm == m ? lmax : 0.0f;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+      if (lane == 0) amax_w[wave][m] = x;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      float a = 0.0f;
+      for (int w2 = 0; w2 < W; ++w2) a = fmaxf(a, amax_w[w2][m]);
+      am[m] = a;
+    }
+    const float apm = pm == 0 ? am[0] : (pm == 1 ? am[1] : (pm == 2 ? am[2] : am[3]));
+    const float sc = apm > 0.0f ? 127.0f / apm : 0.0f;
+    static_for<NA>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      uint32_t q[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) word |= (uint32_t)(uint8_t)quant_code(v[j][4 * d + e], sc) << (8 * e);
+        q[d] = word;
+      }
+      act[j] = make_uint4(q[0], q[1], q[2], q[3]);
+      if (blockIdx.x == 0) {
+        const int col = min(c0 + j * UA + pu, chunks - 1) * kTileCols + 64 * g + 16 * pi;
+        *reinterpret_cast<uint4*>(xq_out + (size_t)pm * K_pad + col) = act[j];
+      }
+    });
+    if (blockIdx.x == 0 && threadIdx.x < MM) absmax_out[threadIdx.x] = am[threadIdx.x];
+  }
+  static_for<T>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    if constexpr (t >= kEarly) w[t] = load_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
   });
   __builtin_amdgcn_sched_barrier(0);
 
@@ -412,25 +516,24 @@ __global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ p
       constexpr int u = decltype(uc)::value;
       constexpr int t = j * UA + u;
       if constexpr (t < T) {
-        // kExact: W T == chunks, every tile is live; else tiles past the matrix decode as 0
-        const bool live = kExact || c0 + t < chunks;
+        const bool live = c0 + t < chunks;  // tiles past the matrix decode as 0
         static_for<4>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
           constexpr int sft = MM * (4 * u + i);
-          const uint32_t word = kExact ? word_of(w[t], i) : (live ? word_of(w[t], i) : 0u);
+          const uint32_t word = live ? word_of(w[t], i) : 0u;
           v4i av;
           if constexpr (MM == 1) {
-            const uint64_t lo = row_bcast64<sft>((uint64_t)a[j].x | ((uint64_t)a[j].y << 32));
-            const uint64_t hi = row_bcast64<sft>((uint64_t)a[j].z | ((uint64_t)a[j].w << 32));
+            const uint64_t lo = row_bcast64<sft>((uint64_t)act[j].x | ((uint64_t)act[j].y << 32));
+            const uint64_t hi = row_bcast64<sft>((uint64_t)act[j].z | ((uint64_t)act[j].w << 32));
             av.x = (int)(uint32_t)lo;
             av.y = (int)(uint32_t)(lo >> 32);
             av.z = (int)(uint32_t)hi;
             av.w = (int)(uint32_t)(hi >> 32);
           } else {
-            av.x = row_shl<sft>((int)a[j].x);
-            av.y = row_shl<sft>((int)a[j].y);
-            av.z = row_shl<sft>((int)a[j].z);
-            av.w = row_shl<sft>((int)a[j].w);
+            av.x = row_shl<sft>((int)act[j].x);
+            av.y = row_shl<sft>((int)act[j].y);
+            av.z = row_shl<sft>((int)act[j].z);
+            av.w = row_shl<sft>((int)act[j].w);
           }
           c = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, decode16(word), c, 0, 0, 0);
         });
@@ -451,8 +554,9 @@ __global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ p
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * g + v;
         if (m < M) {
+          const float a = kSrc == 0 ? absmax_in[m] : (m == 0 ? am[0] : (m == 1 ? am[1] : (m == 2 ? am[2] : am[3])));
           if (acc_out) acc_out[(size_t)m * N + n] = sum[v];
-          if (Y) Y[(size_t)m * N + n] = (float)sum[v] * gm * absmax[m] * (1.0f / 127.0f);
+          if (Y) Y[(size_t)m * N + n] = (float)sum[v] * gm * a * (1.0f / 127.0f);
         }
       }
     }
@@ -520,16 +624,22 @@ hipError_t launch_reg_w(int W, const Args& a, hipStream_t s) {
   }
 }
 
-template <int T, int MM>
+// Fused forms hold the raw activation pieces in registers until the barrier: limit them
+// to 8 sixteen-byte loads per lane.
+template <int T, int MM, int kSrc>
+constexpr bool dpp_fits() {
+  return kSrc == 0 || ((T + DppShape<MM, kSrc>::UA - 1) / DppShape<MM, kSrc>::UA) * DppShape<MM, kSrc>::kParts <= 8;
+}
+
+template <int T, int MM, int kSrc>
 hipError_t launch_dpp(int W, const Args& a, hipStream_t s) {
-  if (W * T == a.chunks)
-    hipLaunchKernelGGL((k_gemv_dpp<T, MM, true>), dim3(a.rblocks), dim3(W * 64), 0, s, a.packed, a.gamma,
-                       static_cast<const int8_t*>(a.X), a.absmax, a.M, a.N, a.K_pad, a.chunks, a.rblocks, a.Y,
-                       a.acc);
-  else
-    hipLaunchKernelGGL((k_gemv_dpp<T, MM, false>), dim3(a.rblocks), dim3(W * 64), 0, s, a.packed, a.gamma,
-                     static_cast<const int8_t*>(a.X), a.absmax, a.M, a.N, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc);
-  return hipGetLastError();
+  if constexpr (dpp_fits<T, MM, kSrc>()) {
+    hipLaunchKernelGGL((k_gemv_dpp<T, MM, kSrc>), dim3(a.rblocks), dim3(W * 64), 0, s, a.packed, a.gamma, a.X,
+                       a.absmax, a.M, a.N, a.K, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc, a.xq_out, a.absmax_out);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidConfiguration;  // not planned (dpp_fused_ok)
+  }
 }
 
 // Supported dpp run lengths (K tiles per wave); returns the smallest one >= t, or 0.
@@ -540,31 +650,39 @@ int64_t dpp_run(int64_t t) {
   return 0;
 }
 
-template <int T>
+template <int T, int kSrc>
 hipError_t launch_dpp_m(int M, int W, const Args& a, hipStream_t s) {
   switch (M) {
-    case 1: return launch_dpp<T, 1>(W, a, s);
-    case 2: return launch_dpp<T, 2>(W, a, s);
-    case 3: return launch_dpp<T, 3>(W, a, s);
-    default: return launch_dpp<T, 4>(W, a, s);
+    case 1: return launch_dpp<T, 1, kSrc>(W, a, s);
+    case 2: return launch_dpp<T, 2, kSrc>(W, a, s);
+    case 3: return launch_dpp<T, 3, kSrc>(W, a, s);
+    default: return launch_dpp<T, 4, kSrc>(W, a, s);
   }
 }
 
+template <int kSrc>
 hipError_t launch_dpp_run(int T, int M, int W, const Args& a, hipStream_t s) {
   switch (T) {
-    case 1: return launch_dpp_m<1>(M, W, a, s);
-    case 2: return launch_dpp_m<2>(M, W, a, s);
-    case 3: return launch_dpp_m<3>(M, W, a, s);
-    case 4: return launch_dpp_m<4>(M, W, a, s);
-    case 5: return launch_dpp_m<5>(M, W, a, s);
-    case 6: return launch_dpp_m<6>(M, W, a, s);
-    case 7: return launch_dpp_m<7>(M, W, a, s);
-    case 8: return launch_dpp_m<8>(M, W, a, s);
-    case 10: return launch_dpp_m<10>(M, W, a, s);
-    case 12: return launch_dpp_m<12>(M, W, a, s);
-    case 14: return launch_dpp_m<14>(M, W, a, s);
-    default: return launch_dpp_m<16>(M, W, a, s);
+    case 1: return launch_dpp_m<1, kSrc>(M, W, a, s);
+    case 2: return launch_dpp_m<2, kSrc>(M, W, a, s);
+    case 3: return launch_dpp_m<3, kSrc>(M, W, a, s);
+    case 4: return launch_dpp_m<4, kSrc>(M, W, a, s);
+    case 5: return launch_dpp_m<5, kSrc>(M, W, a, s);
+    case 6: return launch_dpp_m<6, kSrc>(M, W, a, s);
+    case 7: return launch_dpp_m<7, kSrc>(M, W, a, s);
+    case 8: return launch_dpp_m<8, kSrc>(M, W, a, s);
+    case 10: return launch_dpp_m<10, kSrc>(M, W, a, s);
+    case 12: return launch_dpp_m<12, kSrc>(M, W, a, s);
+    case 14: return launch_dpp_m<14, kSrc>(M, W, a, s);
+    default: return launch_dpp_m<16, kSrc>(M, W, a, s);
   }
+}
+
+// Host mirror of dpp_fits for the planner.
+bool dpp_fused_ok(int64_t T, int64_t M, int src) {
+  if (src == 0) return true;
+  const int64_t ua = 16 / (4 * M), parts = src == 1 ? 2 : 4;
+  return (T + ua - 1) / ua * parts <= 8;
 }
 
 // waves per workgroup: enough waves in flight without splitting K finer than ~2 tiles
@@ -582,17 +700,33 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   const int64_t K_pad = k_pad(K);
   const int64_t chunks = K_pad / kTileCols;
   const int64_t rblocks = n_pad(N) / kTileRows;
+  // the fused forms read x in whole 16-byte pieces
+  const bool k_ok = src == 0 || (src == 1 && K % 8 == 0) || (src == 2 && K % 4 == 0);
+  if (M <= 4 && k_ok) {
+    // about 32 waves per compute unit over the launch, at least two tiles per wave, then
+    // the shortest supported run that covers the row block with at most 16 waves
+    int64_t w = std::min<int64_t>(16, std::max<int64_t>(1, 8192 / rblocks));
+    w = std::min<int64_t>(w, std::max<int64_t>(1, (chunks + 1) / 2));
+    const int64_t t = dpp_run((chunks + w - 1) / w);
+    if (t > 0 && (chunks + t - 1) / t <= 16 && dpp_fused_ok(t, M, src)) {
+      p.dpp = true;
+      p.run = (int)t;
+      p.waves = (int)((chunks + t - 1) / t);
+      p.groups = rblocks;
+      p.ok = true;
+      return p;
+    }
+  }
+  // fused form for short rows when the register form does not fit: every workgroup
+  // quantises all M*K activations into LDS
   const bool small = M <= 4 && M * (K_pad + 16) <= kMaxLdsActBytes;
-  // fused quantisation needs whole 16-byte pieces of x in every row, and pays off only
-  // for short rows: every workgroup re-reads and re-quantises all M*K activations
-  const bool src_ok = src == 0 || (M * K <= kMaxFusedElems && ((src == 1 && K % 8 == 0) || (src == 2 && K % 4 == 0)));
-  if (src != 0 && small && src_ok) {
+  if (src != 0 && small && k_ok && M * K <= kMaxFusedElems) {
     p.lds_act = true;
     p.rb = 1;
     p.groups = rblocks;
     p.waves = pick_waves(chunks, rblocks);
-    const int64_t elems = src == 0 ? 16 : (src == 1 ? 8 : 4);
-    const int64_t pieces = M * (src == 0 ? K_pad : K) / elems;
+    const int64_t elems = src == 1 ? 8 : 4;
+    const int64_t pieces = M * K / elems;
     // every piece must be covered by at most 4 loads per thread
     while (p.waves < 16 && pieces > 4 * 64 * p.waves) p.waves *= 2;
     p.stage = (int)((pieces + 64 * p.waves - 1) / (64 * p.waves));
@@ -602,20 +736,6 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   p.lds_act = false;
   p.rb = 1;
   p.ok = src == 0;  // the register paths read int8 activations only
-  if (M <= 4) {
-    // about 32 waves per compute unit over the launch, at least two tiles per wave, then
-    // the shortest supported run that covers the row block with at most 16 waves
-    int64_t w = std::min<int64_t>(16, std::max<int64_t>(1, 8192 / rblocks));
-    w = std::min<int64_t>(w, std::max<int64_t>(1, (chunks + 1) / 2));
-    const int64_t t = dpp_run((chunks + w - 1) / w);
-    if (t > 0 && (chunks + t - 1) / t <= 16) {
-      p.dpp = true;
-      p.run = (int)t;
-      p.waves = (int)((chunks + t - 1) / t);
-      p.groups = rblocks;
-      return p;
-    }
-  }
   if (M > 4 && rblocks >= 4 * 256) p.rb = 4;
   else if (M > 4 && rblocks >= 2 * 256) p.rb = 2;
   p.groups = (rblocks + p.rb - 1) / p.rb;
@@ -628,8 +748,7 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
   const GemvPlan p = plan_gemv(M, N, K, 0);
   Args a{packed, gamma, Xq, absmax, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
          (int)(n_pad(N) / kTileRows), Y, acc, nullptr, nullptr};
-  if (p.dpp) return launch_dpp_run(p.run, (int)M, p.waves, a, s);
-  if (p.lds_act) return launch_lds_w<0>(p.waves, p.stage, a, s);
+  if (p.dpp) return launch_dpp_run<0>(p.run, (int)M, p.waves, a, s);
   if (p.rb == 4) return launch_reg_w<4, 1, 2>(p.waves, a, s);
   if (p.rb == 2) return launch_reg_w<2, 1, 2>(p.waves, a, s);
   return launch_reg_w<1, 2, 2>(p.waves, a, s);
@@ -640,6 +759,7 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const vo
   const GemvPlan p = plan_gemv(M, N, K, bf16 ? 1 : 2);
   Args a{packed, gamma, X, nullptr, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
          (int)(n_pad(N) / kTileRows), Y, acc, Xq_out, absmax_out};
+  if (p.dpp) return bf16 ? launch_dpp_run<1>(p.run, (int)M, p.waves, a, s) : launch_dpp_run<2>(p.run, (int)M, p.waves, a, s);
   if (bf16) return launch_lds_w<1>(p.waves, p.stage, a, s);
   return launch_lds_w<2>(p.waves, p.stage, a, s);
 }

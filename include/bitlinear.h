@@ -123,10 +123,11 @@ int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* X
  *   absmax  out: fp32 [M] (as bitlinear_quantize_acts).
  *   Y, acc  as bitlinear_forward (at least one non-null).
  * Results are identical to bitlinear_quantize_acts followed by bitlinear_forward.  For a
- * few tokens with short rows (M <= 4, M*K <= 8192), K a multiple of 8 (bf16) or 4 (fp32)
- * and a 16-byte aligned X, one kernel launch does all three steps (each workgroup
- * quantises the rows into LDS); otherwise the two kernels run back to back
- * (bitlinear_forward_fused_plan tells which).
+ * few tokens (M <= 4) with K a multiple of 8 (bf16) or 4 (fp32), a 16-byte aligned X and
+ * K up to a size limit that depends on M and dt (at least 8192), one kernel launch does
+ * all three steps: each workgroup computes the per-token absmax from the activation
+ * pieces its waves hold, and each lane quantises its own pieces; otherwise the two
+ * kernels run back to back (bitlinear_forward_fused_plan tells which).
  */
 int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const void* X, int dt, int64_t M, int64_t N,
                             int64_t K, float* Y, int32_t* acc, int8_t* Xq, float* absmax, void* stream);
@@ -146,8 +147,9 @@ int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]);
 /*
  * Host-only description of what bitlinear_forward_fused does for (M, N, K) and activation
  * type dt, for a 16-byte aligned X; no device work.  out[0] = 3 when one fused kernel
- * quantises and contracts (out[1..3] as bitlinear_forward_plan, out[4] = 1, out[5] =
- * dynamic LDS bytes); otherwise the activation quantiser runs first and out[] describes
+ * quantises and contracts (out[1..3] as bitlinear_forward_plan; out[4] = 2 with out[5] =
+ * K tiles per wave for the register form, or out[4] = 1 with out[5] = dynamic LDS bytes
+ * for the LDS form); otherwise the activation quantiser runs first and out[] describes
  * the forward launch exactly as bitlinear_forward_plan.  Returns BL_OK,
  * BL_ERR_INVALID_ARG (as bitlinear_forward_plan) or BL_ERR_UNSUPPORTED (dt).
  */

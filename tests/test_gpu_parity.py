@@ -295,20 +295,31 @@ def _fused_check(m, n, k, dtype, seed, unaligned=False):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("m,n,k", [(1, 512, 256), (1, 700, 2560), (2, 130, 4096), (3, 48, 1000), (4, 520, 2048),
-                                   (1, 33, 8), (1, 16400, 512), (1, 64, 6912)])
+                                   (1, 33, 8), (1, 16400, 512), (1, 64, 6912), (2, 130, 6912), (1, 40, 30000),
+                                   (2, 100, 12000), (4, 24, 4096)])
 def test_forward_fused_single_kernel(m, n, k, dtype):
-    # shapes the one-kernel path takes (M <= 4, M*K <= 8192, K a multiple of 8)
+    # shapes one fused kernel takes: activation pieces held in registers, per-token absmax
+    # across the workgroup's waves, ragged K, one to four tokens
     plan = bl.forward_fused_plan(m, n, k, "bf16" if dtype == torch.bfloat16 else "f32")
     _announce("forward fused", m, n, k, dtype, plan)
-    assert plan["kernel"] == "fused"
+    assert plan["kernel"] == "fused" and plan["acts"] == "registers"
     _fused_check(m, n, k, dtype, seed=m * 31 + n + k)
+
+
+@pytest.mark.parametrize("m,n,k,dtype", [(3, 65600, 768, torch.float32), (4, 70000, 1024, torch.float32)])
+def test_forward_fused_lds_form(m, n, k, dtype):
+    # many row blocks leave one wave per block; where its pieces would not fit in
+    # registers, short rows are quantised into LDS by every workgroup instead
+    plan = bl.forward_fused_plan(m, n, k, "bf16" if dtype == torch.bfloat16 else "f32")
+    _announce("forward fused lds", m, n, k, dtype, plan)
+    assert plan["kernel"] == "fused" and plan["acts"] == "lds"
+    _fused_check(m, n, k, dtype, seed=m * 13 + n + k)
 
 
 @pytest.mark.parametrize("m,n,k,dtype,unaligned", [(5, 64, 512, torch.bfloat16, False), (1, 64, 300, torch.bfloat16, False),
                                                    (2, 64, 1002, torch.float32, False), (3, 40, 512, torch.bfloat16, True),
-                                                   (1, 40, 30000, torch.bfloat16, False), (40, 72, 700, torch.float32, False),
-                                                   (2, 130, 6912, torch.bfloat16, False), (4, 520, 4096, torch.float32, False),
-                                                   (2, 100, 12000, torch.bfloat16, False)])
+                                                   (40, 72, 700, torch.float32, False), (3, 40, 12000, torch.float32, False),
+                                                   (4, 30, 20000, torch.bfloat16, False)])
 def test_forward_fused_fallback(m, n, k, dtype, unaligned):
     # shapes outside the one-kernel path: the quantiser kernel then the forward kernel
     plan = bl.forward_fused_plan(m, n, k, "bf16" if dtype == torch.bfloat16 else "f32")

@@ -109,3 +109,11 @@ def test_workload3_prefill_m2048_sampled(midx):
 def test_workload4_100b_decode(midx, m):
     _, k, n = synth.WORKLOADS[4].matrices[midx]
     _run(4, 0, midx, k, n, m)
+
+
+@pytest.mark.parametrize("midx", [0, 1])
+def test_workload4_fused_m1(midx):
+    # the benchmark's call for one token on the 100B-class shapes: one fused launch
+    _, k, n = synth.WORKLOADS[4].matrices[midx]
+    assert bl.forward_fused_plan(1, n, k, "bf16")["kernel"] == "fused"
+    _run_fused(4, 0, midx, k, n, 1)
