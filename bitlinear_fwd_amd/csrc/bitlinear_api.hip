@@ -71,7 +71,7 @@ int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* X
     return BL_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= kDecodeMaxM) return hip_status(bl::launch_gemv(packed, gamma, Xq, absmax, M, N, K, Y, acc, s));
-  if (M > 65535LL * 128) return BL_ERR_UNSUPPORTED;  // grid.y limit of the prefill launch
+  if (bl::plan_gemm(M, N, K).groups > (int64_t(1) << 30)) return BL_ERR_UNSUPPORTED;  // grid size
   return hip_status(bl::launch_gemm(packed, gamma, Xq, absmax, M, N, K, Y, acc, s));
 }
 

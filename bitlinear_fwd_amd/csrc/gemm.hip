@@ -16,11 +16,16 @@
 //     tile is one coalesced wave load) into a register ring of the same depth and
 //     decodes them straight into the B operand - the packed layout is the MFMA lane
 //     layout, and 2-bit codes are 4x fewer bytes through the cache than int8;
-//   * one 16-byte word of a slot feeds one MFMA step; with WM = 128 each decoded word
-//     serves 8 MFMAs, which keeps the decode VALU well below the matrix-core time;
+//   * one 16-byte word of a slot feeds one MFMA step and serves WM / 16 MFMAs, which
+//     keeps the decode VALU below the matrix-core time;
+//   * shapes: 64 x 256 output tiles (waves 1 x 4 of 64 x 64, three-slot ring) when there
+//     are enough of them to give every compute unit two; else 64 x 128 tiles (waves
+//     2 x 2 of 32 x 64, fewer registers, A reads issued a half-stage at a time);
 //   * tile order is XCD-aware: consecutive workgroup ids go to different XCDs, so each
 //     XCD gets a contiguous run of output tiles (sharing activation rows in its L2).
 #include "bl_internal.h"
+
+#include <numeric>
 
 namespace bl {
 namespace {
@@ -64,19 +69,20 @@ constexpr int loads_between(int a, int b) {
   return n;
 }
 
-template <int GM, int GN, int WM, int WN, int D>
+template <int GM, int GN, int WM, int WN, int D, int kPipe = 0>
 __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ packed, const float* __restrict__ gamma,
                                                    const int8_t* __restrict__ Xq, const float* __restrict__ absmax,
                                                    int M, int N, int n_blocks, int K_pad, int chunks, int tiles_m,
                                                    int tiles_n, float* __restrict__ Y, int32_t* __restrict__ acc_out) {
   static_assert(GM * GN == 4, "four waves");
-  static_assert(D % 2 == 0 && D >= 2, "ring of whole chunks");
+  static_assert(D >= 2, "at least two ring slots");
   constexpr int BM = GM * WM, BN = GN * WN;
   constexpr int MB = WM / 16, NB = WN / 16;
   constexpr int kHalf = kTileCols / 2;        // bytes per activation row in a half-stage
   constexpr int kDma = BM / 32;               // direct loads per wave per half-stage (8 rows each, 4 waves)
   constexpr int P = D - 1;                    // prefetch distance in half-stages
-  constexpr int CB = D / 2 + 1;               // weight register ring (chunks)
+  constexpr int CB = (P + 1) / 2 + 1;         // weight register ring (chunks live at once)
+  constexpr int kBody = std::lcm(D, 2 * CB);  // half-stages per trip: both ring indices static
   // one LDS object per ring slot: distinct objects let the compiler see that the direct
   // loads into one slot do not alias reads of another (otherwise it waits for all of them)
   __shared__ __attribute__((aligned(1024))) uint8_t As0[BM * kHalf];
@@ -141,6 +147,43 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
   // compute half-stage in ring slot s (steps 2h, 2h+1 of its chunk) with weights cb
   auto compute = [&](auto sc, int half, const uint4 (&wcur)[NB]) {
     const uint8_t* slabp = slab(sc);
+    if constexpr (kPipe == 1) {
+      // both steps' A fragments are read up front; step 1's weights are decoded while
+      // step 0's MFMAs run (interleaving requested from the scheduler)
+      v4i af[2][MB];
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi) {
+          const int row = wm * WM + 16 * mi + r;
+          af[ip][mi] = *reinterpret_cast<const v4i*>(&slabp[row * kHalf + 16 * a_slot(row, 2 * g + ip)]);
+        }
+      v4i bf[2][NB];
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip) {
+        const int i = 2 * half + ip;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const uint32_t word = i == 0 ? wcur[j].x : (i == 1 ? wcur[j].y : (i == 2 ? wcur[j].z : wcur[j].w));
+          bf[ip][j] = decode16(word);
+        }
+      }
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+        for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            acc[mi][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[ip][mi], bf[ip][j], acc[mi][j], 0, 0, 0);
+      // schedule: the A reads first, step 0's decode, then MFMAs interleaved with the rest
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * MB, 0);   // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x2, 9 * NB, 0);     // VALU: step 0 decode
+      static_for<MB * NB>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);        // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x2, 3, 0);        // ~3 VALU of step 1's decode
+      });
+      return;
+    }
 #pragma unroll
     for (int ip = 0; ip < 2; ++ip) {
       const int i = 2 * half + ip;
@@ -184,8 +227,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
   // sink the prologue's weight loads below the barrier, which breaks the wait counts
   int base = 0;
   do {
-    // D * CB half-stages per trip keep both ring indices static
-    static_for<D * CB>([&](auto kc) {
+    static_for<kBody>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       const int hs = base + k;
       const int nh = hs + P;  // half-stage to issue
@@ -207,7 +249,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
       wait_vmcnt<loads_between<kDma, NB>(k + 1, k + P)>();
       ring_barrier();
     });
-    base += D * CB;
+    base += kBody;
   } while (base < hstages);
 
   const float gm = gamma[0];
@@ -231,7 +273,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
   }
 }
 
-template <int GM, int GN, int WM, int WN, int D>
+template <int GM, int GN, int WM, int WN, int D, int kPipe = 0>
 hipError_t launch(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax, int64_t M,
                   int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s) {
   const int64_t K_pad = k_pad(K);
@@ -241,7 +283,7 @@ hipError_t launch(const uint8_t* packed, const float* gamma, const int8_t* Xq, c
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   const int tiles = tiles_m * tiles_n;
   const int grid = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL((k_gemm_mfma<GM, GN, WM, WN, D>), dim3(grid), dim3(256), 0, s, packed, gamma, Xq, absmax, (int)M,
+  hipLaunchKernelGGL((k_gemm_mfma<GM, GN, WM, WN, D, kPipe>), dim3(grid), dim3(256), 0, s, packed, gamma, Xq, absmax, (int)M,
                      (int)N, n_blocks, (int)K_pad, chunks, tiles_m, tiles_n, Y, acc);
   return hipGetLastError();
 }
@@ -252,11 +294,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   (void)K;
   GemmPlan p;
   p.threads = 256;
-  // 128 x 128 tiles, four waves of 64 x 64, two-slot ring: 32 KiB of LDS and 152 VGPRs give
-  // three workgroups per compute unit.  Deeper rings (64 KiB) and wider wave tiles (more
-  // registers) drop to one or two per CU and measured slower on 2048..8192-row shapes.
-  p.bm = 128;
-  p.bn = 128;
+  // 64 x 256 tiles (four waves side by side, 64 x 64 each, three-slot ring: 24 KiB of
+  // LDS, 152 VGPRs, three workgroups per CU) when they give at least two per CU;
+  // otherwise 64 x 128 tiles of four 32 x 64 waves (124 VGPRs, four per CU) so that
+  // short-N shapes still fill the chip.
+  const int64_t wide = ((M + 63) / 64) * ((N + 255) / 256);
+  p.bm = 64;
+  p.bn = wide >= 512 ? 256 : 128;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   p.groups = 8 * ((tiles + 7) / 8);
   return p;
@@ -264,7 +308,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s) {
-  return launch<2, 2, 64, 64, 2>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
+  const GemmPlan p = plan_gemm(M, N, K);
+  if (p.bn == 256) return launch<1, 4, 64, 64, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
+  return launch<2, 2, 32, 64, 3, 1>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
 }
 
 }  // namespace bl

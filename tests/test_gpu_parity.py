@@ -210,6 +210,28 @@ def test_forward_prefill(m, n, k):
     _fwd_check(m, n, k, seed=m * 1000 + n + k)
 
 
+@pytest.mark.parametrize("m,n,k,tile_n", [(2048, 4100, 1000, 256), (1000, 3000, 777, 128), (333, 24000, 2600, 256)])
+def test_forward_prefill_tile_shapes(m, n, k, tile_n):
+    # both prefill tile shapes (64 x 256 when there are enough tiles, else 64 x 128) with
+    # ragged M, N and K; the oracle checks a sample of token rows covering tile edges
+    plan = bl.forward_plan(m, n, k)
+    _announce("forward prefill tiles", m, n, k, plan)
+    assert plan["kernel"] == "prefill" and plan["tile_m"] == 64 and plan["tile_n"] == tile_n
+    rng = np.random.default_rng(m + n + k)
+    q = rng.integers(-1, 2, (n, k)).astype(np.int8)
+    x = synth.activations(m, k, seed=m + k, dtype=torch.float32, outlier_p=0.01, outlier_mult=20.0).numpy()
+    xq, a = oracle.quant_acts(x)
+    gamma = np.float32(0.0159577)
+    d = lambda arr: torch.from_numpy(arr).to(DEV)
+    y, acc = bl.forward(d(oracle.pack(q)), d(np.array([gamma], np.float32)), d(xq), d(a), n, k,
+                        want_y=True, want_acc=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, m // 2, m - 2, m - 1], rng.integers(0, m, 12)]))
+    acc_ref, y_ref = oracle.forward(q, gamma, xq[rows], a[rows], k)
+    check_equal(host(acc)[rows], acc_ref, f"acc m={m} n={n} k={k}")
+    check_y(host(y)[rows], y_ref, f"y m={m} n={n} k={k}")
+
+
 def test_forward_extreme_accumulators():
     # all +1 / all -1 rows against all +127 activations: |acc| = 127 K, the int32 range
     # the path guarantees for the largest K of the workloads
