@@ -102,7 +102,10 @@ def _aq_check(x_dev: torch.Tensor, tag: str):
 @pytest.mark.parametrize("m,k,dtype", [(1, 256, torch.float32), (3, 300, torch.float32), (5, 2560, torch.bfloat16),
                                        (16, 6912, torch.bfloat16), (7, 1000, torch.bfloat16),
                                        (4, 999, torch.bfloat16), (2, 28672, torch.bfloat16),
-                                       (9, 12000, torch.float32), (300, 64, torch.bfloat16)])
+                                       (9, 12000, torch.float32), (300, 64, torch.bfloat16),
+                                       # 256 / 1024 threads per row, registers exactly full, re-read tail
+                                       (1, 8192, torch.bfloat16), (2, 8200, torch.float32), (1, 32768, torch.bfloat16),
+                                       (3, 32776, torch.bfloat16), (2, 40000, torch.float32)])
 def test_act_quant(m, k, dtype):
     _announce("act_quant", m, k, dtype)
     x = synth.activations(m, k, seed=m * 131 + k, dtype=dtype, device=DEV, outlier_p=0.01, outlier_mult=20.0)
