@@ -78,7 +78,8 @@ struct GemvPlan {
   int waves = 1;        // waves per workgroup; they split the K tiles into contiguous runs
   int rb = 1;           // 16-row output blocks per workgroup
   bool lds_act = false; // activations staged in LDS (fused quantise + decode)
-  bool dpp = false;     // activations held in registers, broadcast by DPP (M <= 4)
+  bool dpp = false;     // activations held in registers, shifted into place by DPP (M <= 4,
+                        // or 9..16 tokens on rows of at most 4096 elements)
   int run = 0;          // dpp: K tiles per wave (all loads of a wave issued at once)
   int stage = 0;        // LDS staging: 16-byte activation pieces per thread
   bool ok = true;       // the requested activation source is supported by this plan

@@ -564,6 +564,92 @@ __global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------------------
+// k_gemv_dppm (5..16 tokens, int8 activations): the register-run structure of k_gemv_dpp
+// for a token group of MM = 8 or 16 (tokens M..MM-1 repeat token M-1; their rows are
+// never stored).  A tile needs 4 MM activation pieces per 16-lane row, i.e. RA = MM / 4
+// registers: register q of lane (r, g) holds piece p = 16 q + r = token p % MM of step
+// p / MM; step i reads register MM i / 16 shifted down (MM i) % 16 lanes.  Each wave
+// covers RB row blocks over its run of T tiles, so one set of activation registers
+// feeds RB weight tiles.
+template <int T, int MM, int RB>
+__global__ __launch_bounds__(1024) void k_gemv_dppm(const uint8_t* __restrict__ packed,
+                                                   const float* __restrict__ gamma, const int8_t* __restrict__ Xq,
+                                                   const float* __restrict__ absmax, int M, int N, int K_pad,
+                                                   int chunks, int rblocks, float* __restrict__ Y,
+                                                   int32_t* __restrict__ acc_out) {
+  static_assert(MM == 8 || MM == 16, "token group of 8 or 16");
+  constexpr int RA = MM / 4;
+  __shared__ v4i red[16 * 64];  // W * RB <= 16 partial tiles
+  const int W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int rb0 = blockIdx.x * RB;
+  const int c0 = wave * T;
+  const uint4* wsrc[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j)
+    wsrc[j] = reinterpret_cast<const uint4*>(packed) + (size_t)min(rb0 + j, rblocks - 1) * chunks * 64 + lane;
+
+  uint4 a[T][RA];
+  uint4 w[T][RB];
+  static_for<T>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    const int tile = min(c0 + t, chunks - 1);
+#pragma unroll
+    for (int q = 0; q < RA; ++q) {
+      const int p = 16 * q + r;
+      const int m = min(p % MM, M - 1), i = p / MM;
+      a[t][q] = *reinterpret_cast<const uint4*>(Xq + (size_t)m * K_pad + tile * kTileCols + 64 * g + 16 * i);
+    }
+#pragma unroll
+    for (int j = 0; j < RB; ++j) w[t][j] = load_nt(wsrc[j] + (size_t)tile * 64);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+
+  v4i c[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) c[j] = (v4i){0, 0, 0, 0};
+  static_for<T>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    const bool live = c0 + t < chunks;  // tiles past the matrix decode as 0
+    static_for<4>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int q = MM * i / 16, sft = (MM * i) % 16;
+      v4i av;
+      av.x = row_shl<sft>((int)a[t][q].x);
+      av.y = row_shl<sft>((int)a[t][q].y);
+      av.z = row_shl<sft>((int)a[t][q].z);
+      av.w = row_shl<sft>((int)a[t][q].w);
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        const uint32_t word = live ? word_of(w[t][j], i) : 0u;
+        c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, decode16(word), c[j], 0, 0, 0);
+      }
+    });
+  });
+#pragma unroll
+  for (int j = 0; j < RB; ++j) red[(wave * RB + j) * 64 + lane] = c[j];
+  __syncthreads();
+  const float gm = gamma[0];
+  for (int j = wave; j < RB; j += W) {
+    if (rb0 + j >= rblocks) continue;
+    v4i sum = red[j * 64 + lane];
+    for (int w2 = 1; w2 < W; ++w2) sum += red[(w2 * RB + j) * 64 + lane];
+    const int n = (rb0 + j) * kTileRows + r;
+    if (n >= N) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * g + v;
+      if (m < M) {
+        if (acc_out) acc_out[(size_t)m * N + n] = sum[v];
+        if (Y) Y[(size_t)m * N + n] = (float)sum[v] * gm * absmax[m] * (1.0f / 127.0f);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 struct Args {
   const uint8_t* packed;
   const float* gamma;
@@ -678,6 +764,14 @@ hipError_t launch_dpp_run(int T, int M, int W, const Args& a, hipStream_t s) {
   }
 }
 
+template <int T, int MM, int RB>
+hipError_t launch_dppm(int W, const Args& a, hipStream_t s) {
+  const unsigned groups = (unsigned)((a.rblocks + RB - 1) / RB);
+  hipLaunchKernelGGL((k_gemv_dppm<T, MM, RB>), dim3(groups), dim3(W * 64), 0, s, a.packed, a.gamma,
+                     static_cast<const int8_t*>(a.X), a.absmax, a.M, a.N, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc);
+  return hipGetLastError();
+}
+
 // Host mirror of dpp_fits for the planner.
 bool dpp_fused_ok(int64_t T, int64_t M, int src) {
   if (src == 0) return true;
@@ -736,6 +830,16 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   p.lds_act = false;
   p.rb = 1;
   p.ok = src == 0;  // the register paths read int8 activations only
+  if (M > 8 && chunks <= 16) {
+    // 9..16 tokens on short rows: two-tile register runs, activation registers shared by
+    // two row blocks once there are enough blocks to fill the chip
+    p.dpp = true;
+    p.run = 2;
+    p.rb = rblocks >= 384 ? 2 : 1;
+    p.waves = (int)((chunks + 1) / 2);
+    p.groups = (rblocks + p.rb - 1) / p.rb;
+    return p;
+  }
   if (M > 4 && rblocks >= 4 * 256) p.rb = 4;
   else if (M > 4 && rblocks >= 2 * 256) p.rb = 2;
   p.groups = (rblocks + p.rb - 1) / p.rb;
@@ -748,6 +852,7 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
   const GemvPlan p = plan_gemv(M, N, K, 0);
   Args a{packed, gamma, Xq, absmax, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
          (int)(n_pad(N) / kTileRows), Y, acc, nullptr, nullptr};
+  if (p.dpp && M > 4) return p.rb == 2 ? launch_dppm<2, 16, 2>(p.waves, a, s) : launch_dppm<2, 16, 1>(p.waves, a, s);
   if (p.dpp) return launch_dpp_run<0>(p.run, (int)M, p.waves, a, s);
   if (p.rb == 4) return launch_reg_w<4, 1, 2>(p.waves, a, s);
   if (p.rb == 2) return launch_reg_w<2, 1, 2>(p.waves, a, s);
