@@ -180,9 +180,10 @@ TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
     # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.3 KiB (x1.99980),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4688235, "fetch_kib": 2276.77, "write_kib": 25.27, "sha": "5ee5fd4cbea92a19"},
-    (4, 1): {"bytes_per_launch": 59143507, "fetch_kib": 28843.55, "write_kib": 76.0, "sha": "5ee5fd4cbea92a19"},
-    (3, 2048): {"bytes_per_launch": 91587936, "fetch_kib": 25779.25, "write_kib": 37888.0, "sha": "2ee8480095a9aa9f"},
+    (1, 1): {"bytes_per_launch": 4592518, "fetch_kib": 2230.03, "write_kib": 25.27, "sha": "accc5a11c597c96a"},
+    (2, 16): {"bytes_per_launch": 3159765, "fetch_kib": 1441.29, "write_kib": 203.43, "sha": "accc5a11c597c96a"},
+    (3, 2048): {"bytes_per_launch": 107258282, "fetch_kib": 33431.6, "write_kib": 37888.0, "sha": "3a955bb30b5ef120"},
+    (4, 1): {"bytes_per_launch": 59234959, "fetch_kib": 28881.25, "write_kib": 90.0, "sha": "accc5a11c597c96a"},
 }
 
 
