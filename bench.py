@@ -24,7 +24,9 @@ packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
                launches when the step is nothing but that kernel, else graph replays of the
                forward launches alone.  traffic: measured HBM bytes per launch (see TRAFFIC);
   legs         the other workloads: M = 16 full layer, M = 2048 prefill (int8 TOPS vs
-               5.0 POPS dense int8 MFMA), 100B-class M = 1 and M = 8 sweeps;
+               5.0 POPS dense int8 MFMA), 100B-class M = 1 and M = 8 sweeps, and the 2B
+               decode workloads with the projections of one input (gate/up, Q/K/V) grouped
+               into one bitlinear_forward_grouped call ("1g", "2g");
   cpu_baseline the CPU oracle on the host, on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -49,7 +51,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
-    ap.add_argument("--legs", default="2,3,4", help="other workloads timed into 'legs' ('' for none)")
+    ap.add_argument("--legs", default="1g,2,2g,3,4",
+                    help="other workloads timed into 'legs' ('' for none); a trailing g times the workload "
+                         "with the projections of one input grouped into one call")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph instead of pre-marshalled eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -121,9 +125,34 @@ class Workload:
                 bl.quantize_acts(mat.x, xq, a)
             bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
 
+    def set_grouping(self, grouping):
+        """Projections of one input launched as one grouped call: ``grouping`` lists the
+        matrix indices of each group (a group's matrices take the first one's input).
+        Every matrix gets its own output buffer."""
+        import torch
+
+        self.grouping = grouping
+        self.group_y = [[torch.empty((self.m, mat.n), dtype=torch.float32, device=mat.x.device) for mat in st]
+                        for st in self.sets]
+        self.calls = [self.prepared(group, False) for group in self.step_groups()]
+
     def prepared(self, group, forward_only):
         """The step's launches as pre-marshalled C-ABI calls (one foreign call each)."""
         bl = self.bl
+        if getattr(self, "grouping", None) and not forward_only:
+            si = next(i for i, st in enumerate(self.sets) if st[0] is group[0])
+            calls = []
+            for idxs in self.grouping:
+                first = group[idxs[0]]
+                xq, a, _ = self.bufs[(first.k, first.n)]
+                if len(idxs) == 1:
+                    calls.append(bl.prepare_forward_fused(first.packed, first.gamma, first.x, first.n, first.k,
+                                                          self.group_y[si][idxs[0]], xq, a))
+                else:
+                    calls.append(bl.prepare_forward_grouped(
+                        [(group[i].packed, group[i].gamma, group[i].n, self.group_y[si][i]) for i in idxs],
+                        first.x, first.k, xq, a))
+            return calls
         calls = []
         for mat in group:
             xq, a, y = self.bufs[(mat.k, mat.n)]
@@ -203,6 +232,11 @@ def measured_traffic(kernel: str, workload: int, m: int):
         return None
     kind = "prefill" if kernel.startswith("k_gemm") else "decode"
     return rec["bytes_per_launch"] if rec["sha"] == source_sha(kind) else None
+
+
+# Projections that share one input in a transformer layer, by matrix index of the workload:
+# gate/up (2B decode, workload 1); Q/K/V and gate/up (2B layer, workload 2).
+GROUPINGS = {1: [[0, 1], [2]], 2: [[0, 1, 2], [3], [4, 5], [6]]}
 
 
 def copy_calibration(mib: int):
@@ -321,18 +355,20 @@ def cpu_baseline(w: Workload, budget_s: float):
     return done_bytes, done_ops, t_used, mats
 
 
-def leg_summary(w: Workload, ms: float, launch_ms: float, launch_bytes: float, launch_ops: float):
+def leg_summary(w: Workload, ms: float, launch_ms, launch_bytes, launch_ops):
     gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9
     tops = w.ops_per_step() / (ms * 1e-3) / 1e12
-    return {
+    out = {
         "workload": w.wl.name, "M": w.m, "ms_per_step": round(ms, 5),
         "packed_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "int8_TOPS": round(tops, 2), "mfma_frac": round(tops / I8_PEAK_TOPS, 4),
         "tokens_per_s_eq": round(w.m / (ms * 1e-3), 1),  # every matrix of the step applied once per token
-        "forward_launch_us": round(launch_ms * 1e3, 3),
-        "forward_launch_GBps": round(launch_bytes / (launch_ms * 1e-3) / 1e9, 1),
-        "forward_launch_TOPS": round(launch_ops / (launch_ms * 1e-3) / 1e12, 2),
     }
+    if launch_ms is not None:
+        out["forward_launch_us"] = round(launch_ms * 1e3, 3)
+        out["forward_launch_GBps"] = round(launch_bytes / (launch_ms * 1e-3) / 1e9, 1)
+        out["forward_launch_TOPS"] = round(launch_ops / (launch_ms * 1e-3) / 1e12, 2)
+    return out
 
 
 def main():
@@ -383,20 +419,32 @@ def main():
                 "launch_us": round(launch_ms * 1e3, 3), "launch_timing": launch_timing,
                 "algorithmic_ops_per_launch": int(launch_ops)}
     legs = {}
-    for tok in [t for t in args.legs.split(",") if t.strip()]:
-        idx = int(tok)
-        if idx == args.workload:
+    for tok in [t.strip() for t in args.legs.split(",") if t.strip()]:
+        grouped = tok.endswith("g")
+        idx = int(tok.rstrip("g"))
+        if idx == args.workload and not grouped:
+            continue
+        if grouped and idx not in GROUPINGS:
             continue
         for m in synth.WORKLOADS[idx].m_list:
             w = Workload(bl, synth, idx, m, dev)
+            if grouped:
+                w.set_grouping(GROUPINGS[idx])
             if args.graph:
                 w.capture()
             steps = max(3, args.steps // (40 if w.sweep else 1))
             lms = time_steps(w, steps, max(1, args.warmup // (40 if w.sweep else 4)))
-            l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
-            legs[f"w{idx}_m{m}"] = leg_summary(w, lms, l_ms, l_b, l_o)
-            legs[f"w{idx}_m{m}"]["kernel"] = dominant_kernel(w)
-            legs[f"w{idx}_m{m}"]["traffic_bytes_per_launch"] = measured_traffic(dominant_kernel(w), idx, m)
+            key = f"w{idx}{'g' if grouped else ''}_m{m}"
+            if grouped:
+                legs[key] = leg_summary(w, lms, None, None, None)
+                legs[key]["grouping"] = [[w.wl.matrices[i][0] for i in g] for g in GROUPINGS[idx]]
+                legs[key]["note"] = ("projections of one input in one bitlinear_forward_grouped call (shared "
+                                     "activation quantisation); per-step bytes and ops as the ungrouped workload")
+            else:
+                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
+                legs[key] = leg_summary(w, lms, l_ms, l_b, l_o)
+                legs[key]["kernel"] = dominant_kernel(w)
+                legs[key]["traffic_bytes_per_launch"] = measured_traffic(dominant_kernel(w), idx, m)
             del w
             torch.cuda.empty_cache()
     cpu = None

@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward_fused_plan.argtypes = [i64, i64, i64, c_int, p]
         L.bitlinear_forward.restype = c_int
         L.bitlinear_forward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p]
+        L.bitlinear_forward_grouped.restype = c_int
+        L.bitlinear_forward_grouped.argtypes = [p, c_int, p, c_int, i64, i64, p, p, p]
         _lib = L
     return _lib
 
@@ -69,8 +71,16 @@ EXPORTED_SYMBOLS = (
     "bitlinear_version", "bitlinear_status_string", "bitlinear_n_pad", "bitlinear_k_pad",
     "bitlinear_packed_bytes", "bitlinear_wq_workspace_bytes", "bitlinear_quantize_weights",
     "bitlinear_quantize_acts", "bitlinear_forward", "bitlinear_forward_fused", "bitlinear_forward_plan",
-    "bitlinear_forward_fused_plan",
+    "bitlinear_forward_fused_plan", "bitlinear_forward_grouped",
 )
+
+MAX_GROUP = 8
+
+
+class BlMatrix(ctypes.Structure):
+    """bl_matrix of bitlinear.h: one weight matrix of a grouped call."""
+    _fields_ = [("packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("Y", ctypes.c_void_p), ("acc", ctypes.c_void_p)]
 
 
 def _check(fn: str, status: int) -> None:
@@ -253,6 +263,49 @@ def forward_fused(packed, gamma, x, n: int, k: int, y=None, acc=None, xq=None, a
     return out, xq, absmax
 
 
+def _group_array(mats):
+    """Host bl_matrix array for [(packed, gamma, n, y, acc), ...] (y / acc may be None)."""
+    if not 1 <= len(mats) <= MAX_GROUP:
+        raise ValueError(f"a group holds 1..{MAX_GROUP} matrices")
+    arr = (BlMatrix * len(mats))()
+    for i, (packed, gamma, n, y, acc) in enumerate(mats):
+        for t, name in ((packed, "packed"), (gamma, "gamma")):
+            _require_cuda(t, name)
+        arr[i] = BlMatrix(packed.data_ptr(), gamma.data_ptr(), n, y.data_ptr() if y is not None else None,
+                          acc.data_ptr() if acc is not None else None)
+    return arr
+
+
+def forward_grouped(mats, x, k: int, xq=None, absmax=None, want_y: bool = True, want_acc: bool = False):
+    """Several projections of one input x[M][K] (fp32/bf16): ``mats`` is a list of
+    (packed, gamma, n).  The activations are quantised once.  Returns (outs, xq, absmax)
+    with outs[i] = y_i, acc_i or (y_i, acc_i) as for forward_fused."""
+    import torch
+
+    _require_cuda(x, "x")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [tokens, K]")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    dt = BL_BF16 if x.dtype == torch.bfloat16 else BL_F32
+    m = x.shape[0]
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((m, k_pad(k)), dtype=torch.int8, device=dev)
+    if absmax is None:
+        absmax = torch.empty(m, dtype=torch.float32, device=dev)
+    full, outs = [], []
+    for packed, gamma, n in mats:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev) if want_y else None
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev) if want_acc else None
+        full.append((packed, gamma, n, y, acc))
+        outs.append((y, acc) if (want_y and want_acc) else (y if want_y else acc))
+    arr = _group_array(full)
+    _check("bitlinear_forward_grouped", lib().bitlinear_forward_grouped(
+        ctypes.addressof(arr), len(full), x.data_ptr(), dt, m, k, xq.data_ptr(), absmax.data_ptr(), _stream(dev)))
+    return outs, xq, absmax
+
+
 class PreparedCall:
     """One C-ABI call with its arguments marshalled once: raw device pointers, sizes and the
     stream handle, converted to ctypes values up front.  Calling it re-issues the same
@@ -282,6 +335,21 @@ def prepare_forward_fused(packed, gamma, x, n: int, k: int, y, xq, absmax) -> Pr
     dt = BL_BF16 if x.dtype == torch.bfloat16 else BL_F32
     return PreparedCall("bitlinear_forward_fused", packed.data_ptr(), gamma.data_ptr(), x.data_ptr(), dt,
                         x.shape[0], n, k, y.data_ptr(), None, xq.data_ptr(), absmax.data_ptr(), _stream(x.device))
+
+
+def prepare_forward_grouped(mats, x, k: int, xq, absmax) -> PreparedCall:
+    """bitlinear_forward_grouped on these tensors: ``mats`` is a list of
+    (packed, gamma, n, y) with fp32 outputs y, marshalled once."""
+    import torch
+
+    for t, name in ((x, "x"), (xq, "xq"), (absmax, "absmax")):
+        _require_cuda(t, name)
+    arr = _group_array([(pk, g, n, y, None) for pk, g, n, y in mats])
+    dt = BL_BF16 if x.dtype == torch.bfloat16 else BL_F32
+    call = PreparedCall("bitlinear_forward_grouped", ctypes.addressof(arr), len(mats), x.data_ptr(), dt,
+                        x.shape[0], k, xq.data_ptr(), absmax.data_ptr(), _stream(x.device))
+    call._keep = arr  # the host descriptor array must outlive the call object
+    return call
 
 
 def prepare_quantize_acts(x, xq, absmax) -> PreparedCall:

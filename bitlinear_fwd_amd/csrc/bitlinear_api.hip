@@ -96,6 +96,38 @@ int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const voi
   return bitlinear_forward(packed, gamma, Xq, absmax, M, N, K, Y, acc, stream);
 }
 
+int bitlinear_forward_grouped(const bl_matrix* mats, int count, const void* X, int dt, int64_t M, int64_t K,
+                              int8_t* Xq, float* absmax, void* stream) {
+  if (!mats || !X || !Xq || !absmax) return BL_ERR_INVALID_ARG;
+  if (count < 1 || count > bl::kMaxGroup) return BL_ERR_INVALID_ARG;
+  if (M < 1 || K < 1 || M >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
+  if (!aligned(Xq, 16) || !aligned(absmax, 4) || !aligned(X, dt == BL_F32 ? 4 : 2)) return BL_ERR_INVALID_ARG;
+  bl::GroupMat gm[bl::kMaxGroup];
+  for (int j = 0; j < count; ++j) {
+    const bl_matrix& m = mats[j];
+    if (!m.packed || !m.gamma || (!m.Y && !m.acc)) return BL_ERR_INVALID_ARG;
+    if (m.N < 1 || m.N >= kMaxDim) return BL_ERR_INVALID_ARG;
+    if (!aligned(m.packed, 16) || !aligned(m.gamma, 4) || (m.Y && !aligned(m.Y, 4)) || (m.acc && !aligned(m.acc, 4)))
+      return BL_ERR_INVALID_ARG;
+    gm[j] = bl::GroupMat{m.packed, m.gamma, m.N, m.Y, m.acc};
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (aligned(X, 16)) {
+    bool launched = false;
+    const hipError_t e = bl::launch_gemv_grouped(gm, count, X, dt == BL_BF16, M, K, Xq, absmax, s, &launched);
+    if (launched || e != hipSuccess) return hip_status(e);
+  }
+  // general case: one activation quantisation, then one forward per matrix
+  if (bl::launch_act_quant(X, dt == BL_BF16 ? 1 : 0, M, K, Xq, absmax, s) != hipSuccess) return BL_ERR_HIP;
+  for (int j = 0; j < count; ++j) {
+    const int st = bitlinear_forward(mats[j].packed, mats[j].gamma, Xq, absmax, M, mats[j].N, K, mats[j].Y,
+                                     mats[j].acc, stream);
+    if (st != BL_OK) return st;
+  }
+  return BL_OK;
+}
+
 int bitlinear_forward_fused_plan(int64_t M, int64_t N, int64_t K, int dt, int32_t out[6]) {
   if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
   if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;

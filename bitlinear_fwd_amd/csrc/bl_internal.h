@@ -14,6 +14,7 @@ constexpr int kTileRows = 16;      // rows (output features) per packed tile
 constexpr int kTileCols = 256;     // columns (input features) per packed tile
 constexpr int kTileBytes = 1024;   // 16 x 256 codes at 2 bits
 constexpr int kWqBins = 256;       // one exact bin per fp32 exponent field
+constexpr int kMaxGroup = 8;       // matrices sharing one activation input in a grouped call
 // quantiser workspace: 256 uint64 bins, then fp32 1/gamma
 constexpr int64_t kWqWorkspaceBytes = kWqBins * 8 + 256;
 
@@ -106,6 +107,18 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const void* X, int bf16, int64_t M, int64_t N,
                              int64_t K, float* Y, int32_t* acc, int8_t* Xq_out, float* absmax_out, hipStream_t s);
+// One matrix of a grouped call (matrices sharing one activation input).
+struct GroupMat {
+  const uint8_t* packed;
+  const float* gamma;
+  int64_t N;
+  float* Y;
+  int32_t* acc;
+};
+// One fused launch for the whole group when the register form of the decode kernel
+// covers it (M <= 4): *launched tells whether it did (nothing is enqueued otherwise).
+hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, int bf16, int64_t M, int64_t K,
+                               int8_t* Xq_out, float* absmax_out, hipStream_t s, bool* launched);
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
 

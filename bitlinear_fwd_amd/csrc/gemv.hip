@@ -366,6 +366,18 @@ __global__ __launch_bounds__(W * 64) void k_gemv_reg(const uint8_t* __restrict__
 // every token, the per-token absmax is the maximum over them (wave reductions, then one
 // barrier across the waves); each lane then quantises its own pieces with the
 // arithmetic of the standalone quantiser, and workgroup 0 stores xq and absmax.
+// Matrices that share one activation input (bitlinear_forward_grouped); a single forward
+// is a group of one.  rb_end[j] = row blocks of matrices 0..j.
+struct MatGroup {
+  int count;
+  int rb_end[kMaxGroup];
+  int N[kMaxGroup];
+  const uint8_t* packed[kMaxGroup];
+  const float* gamma[kMaxGroup];
+  float* Y[kMaxGroup];
+  int32_t* acc[kMaxGroup];
+};
+
 template <int s>
 __device__ __forceinline__ int row_shl(int v) {
   if constexpr (s == 0) return v;
@@ -392,12 +404,11 @@ struct DppShape {
 };
 
 template <int T, int MM, int kSrc>
-__global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ packed,
-                                                  const float* __restrict__ gamma, const void* __restrict__ X,
-                                                  const float* __restrict__ absmax_in, int M, int N, int K,
-                                                  int K_pad, int chunks, int rblocks, float* __restrict__ Y,
-                                                  int32_t* __restrict__ acc_out, int8_t* __restrict__ xq_out,
-                                                  float* __restrict__ absmax_out) {
+__device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed, const float* __restrict__ gamma,
+                                              int N, float* __restrict__ Y, int32_t* __restrict__ acc_out, int rb0,
+                                              const void* __restrict__ X, const float* __restrict__ absmax_in, int M,
+                                              int K, int K_pad, int chunks, int8_t* __restrict__ xq_out,
+                                              float* __restrict__ absmax_out) {
   static_assert(MM >= 1 && MM <= 4, "one to four tokens");
   constexpr int UA = DppShape<MM, kSrc>::UA;
   constexpr int NA = (T + UA - 1) / UA;    // activation pieces per lane
@@ -409,7 +420,6 @@ __global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ p
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int rb0 = blockIdx.x;
   const int c0 = wave * T;
   const uint4* wsrc = reinterpret_cast<const uint4*>(packed) + (size_t)rb0 * chunks * 64 + lane;
   const int pm = r % MM, pq = r / MM;
@@ -561,6 +571,45 @@ __global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ p
       }
     }
   }
+}
+
+template <int T, int MM, int kSrc>
+__global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ packed,
+                                                  const float* __restrict__ gamma, const void* __restrict__ X,
+                                                  const float* __restrict__ absmax_in, int M, int N, int K,
+                                                  int K_pad, int chunks, float* __restrict__ Y,
+                                                  int32_t* __restrict__ acc_out, int8_t* __restrict__ xq_out,
+                                                  float* __restrict__ absmax_out) {
+  gemv_dpp_body<T, MM, kSrc>(packed, gamma, N, Y, acc_out, (int)blockIdx.x, X, absmax_in, M, K, K_pad, chunks,
+                             xq_out, absmax_out);
+}
+
+// Grouped form: workgroups take the row blocks of the group's matrices one after another.
+template <int T, int MM, int kSrc>
+__global__ __launch_bounds__(1024) void k_gemv_dpp_group(const MatGroup grp, const void* __restrict__ X, int M,
+                                                        int K, int K_pad, int chunks, int8_t* __restrict__ xq_out,
+                                                        float* __restrict__ absmax_out) {
+  int mat = 0;  // uniform
+#pragma unroll
+  for (int k = 0; k + 1 < kMaxGroup; ++k)
+    if (k + 1 < grp.count && (int)blockIdx.x >= grp.rb_end[k]) mat = k + 1;
+  const uint8_t* packed = grp.packed[0];
+  const float* gamma = grp.gamma[0];
+  float* Y = grp.Y[0];
+  int32_t* acc_out = grp.acc[0];
+  int N = grp.N[0], rb_base = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxGroup; ++k)
+    if (mat == k) {
+      packed = grp.packed[k];
+      gamma = grp.gamma[k];
+      Y = grp.Y[k];
+      acc_out = grp.acc[k];
+      N = grp.N[k];
+      rb_base = grp.rb_end[k - 1];
+    }
+  gemv_dpp_body<T, MM, kSrc>(packed, gamma, N, Y, acc_out, (int)blockIdx.x - rb_base, X, nullptr, M, K, K_pad,
+                             chunks, xq_out, absmax_out);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -717,11 +766,20 @@ constexpr bool dpp_fits() {
   return kSrc == 0 || ((T + DppShape<MM, kSrc>::UA - 1) / DppShape<MM, kSrc>::UA) * DppShape<MM, kSrc>::kParts <= 8;
 }
 
+
 template <int T, int MM, int kSrc>
-hipError_t launch_dpp(int W, const Args& a, hipStream_t s) {
+hipError_t launch_dpp(int W, const Args& a, hipStream_t s, const MatGroup* grp = nullptr) {
   if constexpr (dpp_fits<T, MM, kSrc>()) {
+    if (grp) {
+      if constexpr (kSrc != 0) {
+        hipLaunchKernelGGL((k_gemv_dpp_group<T, MM, kSrc>), dim3(grp->rb_end[grp->count - 1]), dim3(W * 64), 0, s,
+                           *grp, a.X, a.M, a.K, a.K_pad, a.chunks, a.xq_out, a.absmax_out);
+        return hipGetLastError();
+      }
+      return hipErrorInvalidConfiguration;  // groups are formed by the fused (x input) call only
+    }
     hipLaunchKernelGGL((k_gemv_dpp<T, MM, kSrc>), dim3(a.rblocks), dim3(W * 64), 0, s, a.packed, a.gamma, a.X,
-                       a.absmax, a.M, a.N, a.K, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc, a.xq_out, a.absmax_out);
+                       a.absmax, a.M, a.N, a.K, a.K_pad, a.chunks, a.Y, a.acc, a.xq_out, a.absmax_out);
     return hipGetLastError();
   } else {
     return hipErrorInvalidConfiguration;  // not planned (dpp_fused_ok)
@@ -737,30 +795,30 @@ int64_t dpp_run(int64_t t) {
 }
 
 template <int T, int kSrc>
-hipError_t launch_dpp_m(int M, int W, const Args& a, hipStream_t s) {
+hipError_t launch_dpp_m(int M, int W, const Args& a, hipStream_t s, const MatGroup* grp) {
   switch (M) {
-    case 1: return launch_dpp<T, 1, kSrc>(W, a, s);
-    case 2: return launch_dpp<T, 2, kSrc>(W, a, s);
-    case 3: return launch_dpp<T, 3, kSrc>(W, a, s);
-    default: return launch_dpp<T, 4, kSrc>(W, a, s);
+    case 1: return launch_dpp<T, 1, kSrc>(W, a, s, grp);
+    case 2: return launch_dpp<T, 2, kSrc>(W, a, s, grp);
+    case 3: return launch_dpp<T, 3, kSrc>(W, a, s, grp);
+    default: return launch_dpp<T, 4, kSrc>(W, a, s, grp);
   }
 }
 
 template <int kSrc>
-hipError_t launch_dpp_run(int T, int M, int W, const Args& a, hipStream_t s) {
+hipError_t launch_dpp_run(int T, int M, int W, const Args& a, hipStream_t s, const MatGroup* grp = nullptr) {
   switch (T) {
-    case 1: return launch_dpp_m<1, kSrc>(M, W, a, s);
-    case 2: return launch_dpp_m<2, kSrc>(M, W, a, s);
-    case 3: return launch_dpp_m<3, kSrc>(M, W, a, s);
-    case 4: return launch_dpp_m<4, kSrc>(M, W, a, s);
-    case 5: return launch_dpp_m<5, kSrc>(M, W, a, s);
-    case 6: return launch_dpp_m<6, kSrc>(M, W, a, s);
-    case 7: return launch_dpp_m<7, kSrc>(M, W, a, s);
-    case 8: return launch_dpp_m<8, kSrc>(M, W, a, s);
-    case 10: return launch_dpp_m<10, kSrc>(M, W, a, s);
-    case 12: return launch_dpp_m<12, kSrc>(M, W, a, s);
-    case 14: return launch_dpp_m<14, kSrc>(M, W, a, s);
-    default: return launch_dpp_m<16, kSrc>(M, W, a, s);
+    case 1: return launch_dpp_m<1, kSrc>(M, W, a, s, grp);
+    case 2: return launch_dpp_m<2, kSrc>(M, W, a, s, grp);
+    case 3: return launch_dpp_m<3, kSrc>(M, W, a, s, grp);
+    case 4: return launch_dpp_m<4, kSrc>(M, W, a, s, grp);
+    case 5: return launch_dpp_m<5, kSrc>(M, W, a, s, grp);
+    case 6: return launch_dpp_m<6, kSrc>(M, W, a, s, grp);
+    case 7: return launch_dpp_m<7, kSrc>(M, W, a, s, grp);
+    case 8: return launch_dpp_m<8, kSrc>(M, W, a, s, grp);
+    case 10: return launch_dpp_m<10, kSrc>(M, W, a, s, grp);
+    case 12: return launch_dpp_m<12, kSrc>(M, W, a, s, grp);
+    case 14: return launch_dpp_m<14, kSrc>(M, W, a, s, grp);
+    default: return launch_dpp_m<16, kSrc>(M, W, a, s, grp);
   }
 }
 
@@ -867,6 +925,33 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const vo
   if (p.dpp) return bf16 ? launch_dpp_run<1>(p.run, (int)M, p.waves, a, s) : launch_dpp_run<2>(p.run, (int)M, p.waves, a, s);
   if (bf16) return launch_lds_w<1>(p.waves, p.stage, a, s);
   return launch_lds_w<2>(p.waves, p.stage, a, s);
+}
+
+hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, int bf16, int64_t M, int64_t K,
+                               int8_t* Xq_out, float* absmax_out, hipStream_t s, bool* launched) {
+  *launched = false;
+  if (count < 1 || count > kMaxGroup || M > 4) return hipSuccess;
+  int64_t rb_total = 0;
+  for (int j = 0; j < count; ++j) rb_total += n_pad(mats[j].N) / kTileRows;
+  const GemvPlan p = plan_gemv(M, rb_total * kTileRows, K, bf16 ? 1 : 2);
+  if (!(p.dpp && p.ok)) return hipSuccess;
+  *launched = true;
+  MatGroup g{};
+  g.count = count;
+  int end = 0;
+  for (int j = 0; j < count; ++j) {
+    end += (int)(n_pad(mats[j].N) / kTileRows);
+    g.rb_end[j] = end;
+    g.N[j] = (int)mats[j].N;
+    g.packed[j] = mats[j].packed;
+    g.gamma[j] = mats[j].gamma;
+    g.Y[j] = mats[j].Y;
+    g.acc[j] = mats[j].acc;
+  }
+  Args a{nullptr, nullptr, X, nullptr, (int)M, 0, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols), 0,
+         nullptr, nullptr, Xq_out, absmax_out};
+  if (bf16) return launch_dpp_run<1>(p.run, (int)M, p.waves, a, s, &g);
+  return launch_dpp_run<2>(p.run, (int)M, p.waves, a, s, &g);
 }
 
 }  // namespace bl

@@ -132,6 +132,29 @@ int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* X
 int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const void* X, int dt, int64_t M, int64_t N,
                             int64_t K, float* Y, int32_t* acc, int8_t* Xq, float* absmax, void* stream);
 
+/* One weight matrix of a grouped call: device pointers as in bitlinear_forward. */
+typedef struct {
+  const uint8_t* packed; /* from bitlinear_quantize_weights for (N, K); 16-byte aligned */
+  const float* gamma;    /* its fp32 weight scale                                      */
+  int64_t N;             /* its output features                                        */
+  float* Y;              /* out (nullable): fp32 [M][N]                                */
+  int32_t* acc;          /* out (nullable): int32 [M][N]; Y or acc must be non-null    */
+} bl_matrix;
+
+/*
+ * Several projections of one input (for instance Q, K and V, or gate and up), each with
+ * its own packed weights and scale: the activation quantisation runs once and the
+ * contractions of all matrices share its codes.  mats is a HOST array of count
+ * descriptors (1 <= count <= 8), all with in_features K; X, dt, M, K, Xq and absmax as
+ * bitlinear_forward_fused.  Results are identical to bitlinear_forward_fused on each
+ * matrix.  For M <= 4 with a 16-byte aligned X, when bitlinear_forward_fused_plan(M,
+ * sum of N_pad, K, dt) reports a fused kernel with activations in registers, the whole
+ * group is one kernel launch (workgroups take the row blocks of the matrices in order);
+ * otherwise the quantiser runs once, then one forward per matrix.
+ */
+int bitlinear_forward_grouped(const bl_matrix* mats, int count, const void* X, int dt, int64_t M, int64_t K,
+                              int8_t* Xq, float* absmax, void* stream);
+
 /*
  * Host-only description of the launch bitlinear_forward would make for (M, N, K); no
  * device work.  out[0] = kernel (1 = decode, 2 = prefill), out[1] = workgroups,

@@ -119,3 +119,31 @@ def test_product_path_does_not_import_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
                 assert "liboracle" not in src and "bitlinear_oracle" not in src, f
+
+
+def test_grouped_argument_validation():
+    L = bl.lib()
+    one = (bl.BlMatrix * 9)(*[bl.BlMatrix(FAKE, FAKE, 16, FAKE, None) for _ in range(9)])
+    addr = ctypes.addressof(one)
+    ok = dict(mats=addr, count=2, x=FAKE, dt=bl.BL_BF16, M=1, K=256, xq=FAKE, a=FAKE)
+
+    def call(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return L.bitlinear_forward_grouped(d["mats"], d["count"], d["x"], d["dt"], d["M"], d["K"], d["xq"], d["a"],
+                                           None)
+
+    assert call(mats=None) == bl.BL_ERR_INVALID_ARG
+    assert call(count=0) == bl.BL_ERR_INVALID_ARG
+    assert call(count=9) == bl.BL_ERR_INVALID_ARG
+    assert call(x=None) == bl.BL_ERR_INVALID_ARG
+    assert call(M=0) == bl.BL_ERR_INVALID_ARG
+    assert call(K=(1 << 24) + 1) == bl.BL_ERR_INVALID_ARG
+    assert call(dt=7) == bl.BL_ERR_UNSUPPORTED
+    assert call(xq=FAKE + 4) == bl.BL_ERR_INVALID_ARG
+    bad = (bl.BlMatrix * 2)(bl.BlMatrix(FAKE, FAKE, 16, FAKE, None), bl.BlMatrix(FAKE + 8, FAKE, 16, FAKE, None))
+    assert call(mats=ctypes.addressof(bad)) == bl.BL_ERR_INVALID_ARG  # misaligned packed
+    bad[1] = bl.BlMatrix(FAKE, FAKE, 0, FAKE, None)
+    assert call(mats=ctypes.addressof(bad)) == bl.BL_ERR_INVALID_ARG  # N = 0
+    bad[1] = bl.BlMatrix(FAKE, FAKE, 16, None, None)
+    assert call(mats=ctypes.addressof(bad)) == bl.BL_ERR_INVALID_ARG  # no output

@@ -354,3 +354,40 @@ def test_forward_fused_fallback(m, n, k, dtype, unaligned):
     _announce("forward fused fallback", m, n, k, dtype, unaligned, plan)
     assert unaligned or plan["kernel"] != "fused"
     _fused_check(m, n, k, dtype, seed=m * 17 + n + k, unaligned=unaligned)
+
+
+# ------------------------------------------------------------------ grouped projections
+def _grouped_check(m, ns, k, dtype, seed):
+    rng = np.random.default_rng(seed)
+    qs = [rng.integers(-1, 2, (n, k)).astype(np.int8) for n in ns]
+    gammas = [np.float32(0.01 + 0.001 * i) for i in range(len(ns))]
+    x = synth.activations(m, k, seed=seed, dtype=dtype, device=DEV, outlier_p=0.01, outlier_mult=20.0)
+    if m > 2:
+        x[1] = 0
+    mats = [(torch.from_numpy(oracle.pack(q)).to(DEV), torch.tensor([g], device=DEV), n)
+            for q, g, n in zip(qs, gammas, ns)]
+    outs, xq, a = bl.forward_grouped(mats, x, k, want_y=True, want_acc=True)
+    torch.cuda.synchronize()
+    xq_ref, a_ref = oracle.quant_acts(acts_host_f32(x))
+    check_equal(host(xq), xq_ref, f"grouped xq m={m} k={k}")
+    check_equal(host(a).view(np.uint32), a_ref.view(np.uint32), f"grouped absmax m={m} k={k}")
+    for i, ((y, acc), q, g) in enumerate(zip(outs, qs, gammas)):
+        acc_ref, y_ref = oracle.forward(q, g, xq_ref, a_ref, k)
+        check_equal(host(acc), acc_ref, f"grouped acc {i} m={m} k={k}")
+        check_y(host(y), y_ref, f"grouped y {i} m={m} k={k}")
+
+
+@pytest.mark.parametrize("m,ns,k,dtype", [
+    (1, [6912, 6912], 2560, torch.bfloat16),           # gate + up of a 2B-class layer
+    (1, [2560, 640, 640], 2560, torch.bfloat16),       # Q, K, V
+    (2, [17, 300, 1000], 1000, torch.float32),         # ragged rows and columns
+    (3, [16, 33, 48, 64, 80, 96, 112, 130], 512, torch.bfloat16),  # eight matrices
+    (4, [700, 900], 4096, torch.float32),
+    (1, [512], 256, torch.float32),                    # a group of one
+    (8, [300, 100], 2560, torch.bfloat16),             # more tokens: quantiser once, then forwards
+    (40, [130, 64], 1000, torch.float32),              # prefill sizes
+    (1, [100, 200], 300, torch.bfloat16),              # K not a multiple of 8: quantiser path
+])
+def test_forward_grouped(m, ns, k, dtype):
+    _announce("forward grouped", m, ns, k, dtype)
+    _grouped_check(m, ns, k, dtype, seed=m * 71 + sum(ns) + k)
