@@ -27,6 +27,10 @@ packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
                5.0 POPS dense int8 MFMA), 100B-class M = 1 and M = 8 sweeps, and the 2B
                decode workloads with the projections of one input (gate/up, Q/K/V) grouped
                into one bitlinear_forward_grouped call ("1g", "2g");
+  ceilings     measured on this GPU by the library's probes: HBM read rate with the decode
+               access pattern at 58.7 MB and 4.4 MB per launch, and the int8 MFMA rate;
+               roofline.frac_of_measured_ceiling sets the dominant kernel against the
+               one that matches its size;
   cpu_baseline the CPU oracle on the host, on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -251,6 +255,55 @@ def copy_calibration(mib: int):
     del src, dst
 
 
+def measure_ceilings(bl, dev):
+    """Measured ceilings on this GPU (library probes, back-to-back launches timed with HIP
+    events): HBM read rate for the decode access pattern at the two matrix sizes (the
+    buffers rotate through 2 GiB, so every launch reads from HBM), and the int8 MFMA rate
+    with no memory traffic."""
+    import torch
+
+    pool_bytes = 2 << 30
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    pool.fill_(0x5A)
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, nbytes in (("58.7MB", 58_720_256), ("4.4MB", 4_423_680)):
+        copies = pool_bytes // nbytes
+        words = int(bl.lib().bitlinear_probe_stream_words(nbytes))
+        sink = torch.empty(words, dtype=torch.int32, device=dev)
+        calls = [bl.PreparedCall("bitlinear_probe_stream", pool.data_ptr() + i * nbytes, nbytes, sink.data_ptr(),
+                                 words, stream) for i in range(copies)]
+        reps = 400 if nbytes < 10_000_000 else 200
+        for i in range(20):
+            calls[i % copies]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            calls[i % copies]()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[f"stream_{name}_us"] = round(us, 3)
+        out[f"stream_{name}_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    del pool
+    torch.cuda.empty_cache()
+    # about 5 ms per launch; the first launch brings the clocks up, the best of three counts
+    groups, iters = 512, 16000
+    sink = torch.empty(groups, dtype=torch.int32, device=dev)
+    best = 0.0
+    for rep in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bl.probe_mfma(iters, groups, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        if rep:
+            best = max(best, 2.0 * 16 * 16 * 64 * 16 * iters * groups * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    out["mfma_int8_TOPS"] = round(best, 1)
+    return out
+
+
 def dominant_kernel(w: Workload) -> str:
     """Name of the kernel that takes the step's time, as the launch plan picks it."""
     m = w.m
@@ -418,6 +471,13 @@ def main():
                 "frac": round(achieved / I8_PEAK_TOPS, 4), "traffic": traffic, "kernel": kernel,
                 "launch_us": round(launch_ms * 1e3, 3), "launch_timing": launch_timing,
                 "algorithmic_ops_per_launch": int(launch_ops)}
+    ceilings = measure_ceilings(bl, dev)
+    if decode:
+        ceil = ceilings["stream_4.4MB_GBps"] if head.bytes_per_step() / len(mats) < 20e6 else ceilings["stream_58.7MB_GBps"]
+    else:
+        ceil = ceilings["mfma_int8_TOPS"]
+    roof["measured_ceiling"] = ceil
+    roof["frac_of_measured_ceiling"] = round(roof["achieved"] / ceil, 4)
     legs = {}
     for tok in [t.strip() for t in args.legs.split(",") if t.strip()]:
         grouped = tok.endswith("g")
@@ -469,6 +529,7 @@ def main():
                    "launch": "hip graph replay" if args.graph else "pre-marshalled eager C-ABI calls",
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None},
         "roofline": roof,
+        "ceilings": ceilings,
         "cpu_baseline": cpu,
         "legs": legs,
     }

@@ -61,6 +61,12 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward_fused_plan.argtypes = [i64, i64, i64, c_int, p]
         L.bitlinear_forward.restype = c_int
         L.bitlinear_forward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p]
+        L.bitlinear_probe_stream_words.restype = i64
+        L.bitlinear_probe_stream_words.argtypes = [i64]
+        L.bitlinear_probe_stream.restype = c_int
+        L.bitlinear_probe_stream.argtypes = [p, i64, p, i64, p]
+        L.bitlinear_probe_mfma.restype = c_int
+        L.bitlinear_probe_mfma.argtypes = [i64, i64, p, p]
         L.bitlinear_forward_grouped.restype = c_int
         L.bitlinear_forward_grouped.argtypes = [p, c_int, p, c_int, i64, i64, p, p, p]
         _lib = L
@@ -71,7 +77,8 @@ EXPORTED_SYMBOLS = (
     "bitlinear_version", "bitlinear_status_string", "bitlinear_n_pad", "bitlinear_k_pad",
     "bitlinear_packed_bytes", "bitlinear_wq_workspace_bytes", "bitlinear_quantize_weights",
     "bitlinear_quantize_acts", "bitlinear_forward", "bitlinear_forward_fused", "bitlinear_forward_plan",
-    "bitlinear_forward_fused_plan", "bitlinear_forward_grouped",
+    "bitlinear_forward_fused_plan", "bitlinear_forward_grouped", "bitlinear_probe_stream_words",
+    "bitlinear_probe_stream", "bitlinear_probe_mfma",
 )
 
 MAX_GROUP = 8
@@ -304,6 +311,32 @@ def forward_grouped(mats, x, k: int, xq=None, absmax=None, want_y: bool = True, 
     _check("bitlinear_forward_grouped", lib().bitlinear_forward_grouped(
         ctypes.addressof(arr), len(full), x.data_ptr(), dt, m, k, xq.data_ptr(), absmax.data_ptr(), _stream(dev)))
     return outs, xq, absmax
+
+
+def probe_stream(buf, out=None):
+    """Read the uint8 device tensor ``buf`` with the decode access pattern (measurement
+    probe); returns the per-32-KiB-block XOR checksums (uint32 device tensor)."""
+    import torch
+
+    _require_cuda(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    words = int(lib().bitlinear_probe_stream_words(nbytes))
+    if words < 0:
+        raise ValueError("probe_stream needs a multiple of 1024 bytes")
+    if out is None:
+        out = torch.empty(words, dtype=torch.int32, device=buf.device)
+    _check("bitlinear_probe_stream", lib().bitlinear_probe_stream(buf.data_ptr(), nbytes, out.data_ptr(),
+                                                                  out.numel(), _stream(buf.device)))
+    return out
+
+
+def probe_mfma(iters: int, workgroups: int, out):
+    """Matrix-core probe: workgroups x 4 waves x 16 independent int8 MFMAs per iteration."""
+    _require_cuda(out, "out")
+    if out.numel() < workgroups:
+        raise ValueError("out needs one word per workgroup")
+    _check("bitlinear_probe_mfma", lib().bitlinear_probe_mfma(iters, workgroups, out.data_ptr(), _stream(out.device)))
+    return out
 
 
 class PreparedCall:

@@ -128,6 +128,24 @@ int bitlinear_forward_grouped(const bl_matrix* mats, int count, const void* X, i
   return BL_OK;
 }
 
+int64_t bitlinear_probe_stream_words(int64_t bytes) {
+  return (bytes < bl::kTileBytes || bytes % bl::kTileBytes) ? -1 : bl::probe_stream_groups(bytes);
+}
+
+int bitlinear_probe_stream(const void* buf, int64_t bytes, uint32_t* out, int64_t out_words, void* stream) {
+  if (!buf || !out || bytes < bl::kTileBytes || bytes % bl::kTileBytes || bytes >= (int64_t(1) << 40))
+    return BL_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(out, 4) || out_words < bl::probe_stream_groups(bytes)) return BL_ERR_INVALID_ARG;
+  return hip_status(bl::launch_probe_stream(buf, bytes, out, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_probe_mfma(int64_t iters, int64_t workgroups, uint32_t* out, void* stream) {
+  if (!out || iters < 1 || iters > (int64_t(1) << 32) || workgroups < 1 || workgroups > (int64_t(1) << 20) ||
+      !aligned(out, 4))
+    return BL_ERR_INVALID_ARG;
+  return hip_status(bl::launch_probe_mfma(iters, workgroups, out, static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_forward_fused_plan(int64_t M, int64_t N, int64_t K, int dt, int32_t out[6]) {
   if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
   if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;

@@ -122,6 +122,11 @@ hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, i
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
 
+// Measurement probes (probes.hip).
+int64_t probe_stream_groups(int64_t bytes);
+hipError_t launch_probe_stream(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
+hipError_t launch_probe_mfma(int64_t iters, int64_t groups, uint32_t* out, hipStream_t s);
+
 inline int64_t n_pad(int64_t n) { return (n + kTileRows - 1) / kTileRows * kTileRows; }
 inline int64_t k_pad(int64_t k) { return (k + kTileCols - 1) / kTileCols * kTileCols; }
 

@@ -178,6 +178,25 @@ int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]);
  */
 int bitlinear_forward_fused_plan(int64_t M, int64_t N, int64_t K, int dt, int32_t out[6]);
 
+/*
+ * Measurement probes: not steps of the method, the ceilings a benchmark holds the
+ * kernels above against.
+ *
+ * bitlinear_probe_stream reads `bytes` (a multiple of 1024, at least 1024) of device
+ * memory at `buf` (16-byte aligned) with the decode kernels' access pattern (1 KiB tiles,
+ * 16 bytes per lane, non-temporal, each wave's 8-tile run in flight at once) and does no
+ * other work.  out[i] (device, uint32, out_words >= bitlinear_probe_stream_words(bytes))
+ * receives the XOR of the 32-bit words of the i-th 32 KiB block (the last block may be
+ * shorter).  bitlinear_probe_stream_words returns -1 for an invalid size.
+ *
+ * bitlinear_probe_mfma runs `workgroups` x 4 waves, each issuing 16 independent
+ * v_mfma_i32_16x16x64_i8 per iteration for `iters` iterations (32768 int8 operations
+ * each), with no memory traffic; out[workgroups] (device) receives checksums.
+ */
+int64_t bitlinear_probe_stream_words(int64_t bytes);
+int bitlinear_probe_stream(const void* buf, int64_t bytes, uint32_t* out, int64_t out_words, void* stream);
+int bitlinear_probe_mfma(int64_t iters, int64_t workgroups, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

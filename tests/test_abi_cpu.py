@@ -147,3 +147,17 @@ def test_grouped_argument_validation():
     assert call(mats=ctypes.addressof(bad)) == bl.BL_ERR_INVALID_ARG  # N = 0
     bad[1] = bl.BlMatrix(FAKE, FAKE, 16, None, None)
     assert call(mats=ctypes.addressof(bad)) == bl.BL_ERR_INVALID_ARG  # no output
+
+
+def test_probe_argument_validation():
+    L = bl.lib()
+    assert L.bitlinear_probe_stream_words(1024) == 1
+    assert L.bitlinear_probe_stream_words(32768) == 1 and L.bitlinear_probe_stream_words(32769 * 1024) == 1025
+    assert L.bitlinear_probe_stream_words(1000) == -1 and L.bitlinear_probe_stream_words(0) == -1
+    assert L.bitlinear_probe_stream(None, 1024, FAKE, 1, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_probe_stream(FAKE, 1000, FAKE, 1, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_probe_stream(FAKE + 8, 1024, FAKE, 1, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_probe_stream(FAKE, 65536, FAKE, 1, None) == bl.BL_ERR_INVALID_ARG  # needs 2 words
+    assert L.bitlinear_probe_mfma(0, 1, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_probe_mfma(1, 0, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_probe_mfma(1, 1, None, None) == bl.BL_ERR_INVALID_ARG
