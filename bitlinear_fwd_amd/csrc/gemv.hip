@@ -6,32 +6,33 @@
 // load carries many of them.  aratech.ae BitNet b1.58 article, "BitLinear": activations
 // are int8 with a per-token absmax scale; y is the product rescaled by both scales.
 //
-// Decode is HBM-bound (0.25 byte of weights per multiply-add at M = 1), so both kernels
-// are built as a streaming read of the packed matrix:
-//   * a workgroup owns RB 16-row output blocks; its W waves split the K tiles of those
-//     blocks into contiguous runs; each wave streams whole 1 KiB tiles with one
-//     16-byte-per-lane non-temporal load per tile, through a ring of NB batches of U
-//     tiles (NB-1 batches stay in flight while one is computed);
-//   * every load in the steady-state loop is unconditional (indices past the wave's run
-//     are clamped to a valid tile and their codes zeroed) and each batch is fenced with
-//     a scheduling barrier, so the compiler emits exact vmcnt waits instead of draining
-//     the whole load queue;
-//   * each lane's 16 bytes are 64 consecutive codes of one row, decoded in registers
-//     (decode16) straight into the B operand of v_mfma_i32_16x16x64_i8; the A operand is
-//     the matching 16 int8 activations of token lane%16;
-//   * rows of A beyond M repeat row M-1; they only feed output rows that are not stored;
-//   * partial 16x16 int32 tiles of the waves are summed in LDS in wave order (exact) and
+// Decode is HBM-bound (0.25 byte of weights per multiply-add at M = 1), so every kernel
+// here is a streaming read of the packed matrix in which the arithmetic hides:
+//   * each lane loads 16 bytes of a 1 KiB tile (non-temporal): 64 consecutive codes of
+//     one row, decoded in registers (decode16) straight into the B operand of
+//     v_mfma_i32_16x16x64_i8; one wave-wide load is one whole tile;
+//   * the waves of a workgroup split the K tiles of its 16-row block(s) into contiguous
+//     runs; all loads are unconditional (indices past a run are clamped to a valid tile
+//     and its codes zeroed), so the compiler emits exact vmcnt waits;
+//   * rows of the A operand beyond M repeat a real token or carry other pieces; they only
+//     feed output rows that are never stored;
+//   * the waves' partial 16x16 int32 tiles are summed in LDS in wave order (exact) and
 //     rescaled by y = acc * gamma * a[m] / 127.
 //
-// Activations reach the A operand in one of two ways:
-//   k_gemv_lds  (M <= 4, small K): the workgroup stages the M rows once in LDS - copied
-//               from int8 xq, or (fused form) quantised in the kernel from bf16/fp32 x
-//               with the same arithmetic as the standalone activation quantiser - using
-//               an exact, compile-time number of 16-byte pieces per thread issued before
-//               the weight loads (vector-memory loads retire in order, so their wait
-//               does not wait for the weights);
-//   k_gemv_reg  (larger M*K): each wave loads the 16-byte fragments of a tile index with
-//               the weights of that batch and reuses them for its RB row blocks.
+// The kernels differ in where the activations (the A operand) come from:
+//   k_gemv_dpp   1..4 tokens: every load of a wave's run is issued at once and the
+//                activations stay in registers, put into place by DPP lane shifts; the
+//                fused form (bf16/fp32 x) quantises in the kernel; k_gemv_dpp_group runs
+//                several matrices of one input in one launch;
+//   k_gemv_dppm  9..16 tokens on short rows: the same register runs for a token group
+//                of 8 or 16, activation registers shared by 1 or 2 row blocks;
+//   k_gemv_reg   other 5..16-token shapes: activation fragments loaded per tile with
+//                the weights of a ring of batches, shared by 1, 2 or 4 row blocks;
+//   k_gemv_lds   the fused form where its register pieces would not fit (many row
+//                blocks, short rows): every workgroup quantises the rows into LDS with an
+//                exact, compile-time number of 16-byte pieces per thread issued before
+//                the weight loads (vector-memory loads retire in order, so their wait
+//                does not wait for the weights).
 #include "bl_internal.h"
 
 #include <algorithm>
@@ -74,13 +75,13 @@ __device__ __forceinline__ void gemv_epilogue(const v4i* red, int wave, int lane
 }
 
 // ---------------------------------------------------------------------------------------
-// k_gemv_lds: activations staged in LDS.  kSrc: 0 = int8 xq (K_pad columns), 1 = bf16 x,
-// 2 = fp32 x (K columns, quantised here).  S = 16-byte pieces per thread (exact: the
+// k_gemv_lds: the fused form with the activations quantised into LDS by every workgroup.
+// kSrc: 1 = bf16 x, 2 = fp32 x (K columns).  S = 16-byte pieces per thread (exact: the
 // launcher picks S = ceil(pieces / threads)).
 template <int W, int U, int NB, int S, int kSrc>
 __global__ __launch_bounds__(W * 64) void k_gemv_lds(const uint8_t* __restrict__ packed,
                                                      const float* __restrict__ gamma, const void* __restrict__ X,
-                                                     const float* __restrict__ absmax_in, int M, int N, int K,
+                                                     int M, int N, int K,
                                                      int K_pad, int chunks, int rblocks, float* __restrict__ Y,
                                                      int32_t* __restrict__ acc_out, int8_t* __restrict__ xq_out,
                                                      float* __restrict__ absmax_out) {
@@ -99,10 +100,11 @@ __global__ __launch_bounds__(W * 64) void k_gemv_lds(const uint8_t* __restrict__
   const int lds_stride = K_pad + 16;
   const uint4* wsrc = reinterpret_cast<const uint4*>(packed) + (size_t)rb0 * chunks * 64 + lane;
 
-  // activation pieces: int8 source -> 16 codes; bf16 -> 8 elements; fp32 -> 4 elements
-  constexpr int kElems = kSrc == 0 ? 16 : (kSrc == 1 ? 8 : 4);
-  constexpr int kElemBytes = kSrc == 0 ? 1 : (kSrc == 1 ? 2 : 4);
-  const int row_elems = kSrc == 0 ? K_pad : K;
+  // activation pieces: bf16 -> 8 elements, fp32 -> 4 elements per 16 bytes
+  static_assert(kSrc == 1 || kSrc == 2, "the LDS-staged kernel is the fused form only");
+  constexpr int kElems = kSrc == 1 ? 8 : 4;
+  constexpr int kElemBytes = kSrc == 1 ? 2 : 4;
+  const int row_elems = K;
   const int per_row = row_elems / kElems;
   const int pieces = M * per_row;
   uint4 st[S];
@@ -126,16 +128,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_lds(const uint8_t* __restrict__
 #pragma unroll
   for (int b = 0; b < NB; ++b) load(b, c0 + b * U);
 
-  if (kSrc == 0) {
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      const int idx = (int)threadIdx.x + j * W * 64;
-      if (idx < pieces) {
-        const int m = idx / per_row, p = idx - m * per_row;
-        *reinterpret_cast<uint4*>(act_lds + m * lds_stride + 16 * p) = st[j];
-      }
-    }
-  } else {
+  {
     // fused activation quantiser: per-row absmax, s = 127/a, xq = clamp(rint(x*s))
     float v[S][kElems];
     float pm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -260,8 +253,7 @@ __global__ __launch_bounds__(W * 64) void k_gemv_lds(const uint8_t* __restrict__
 
   red[wave * 64 + lane] = c;
   __syncthreads();
-  const float* am = kSrc == 0 ? absmax_in : row_amax;
-  gemv_epilogue<W, 1>(red, wave, lane, rb0, rblocks, M, N, gamma[0], am, Y, acc_out);
+  gemv_epilogue<W, 1>(red, wave, lane, rb0, rblocks, M, N, gamma[0], row_amax, Y, acc_out);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -715,7 +707,7 @@ template <int W, int U, int NB, int S, int kSrc>
 hipError_t launch_lds(const Args& a, hipStream_t s) {
   const size_t lds = (size_t)a.M * (a.K_pad + 16);
   hipLaunchKernelGGL((k_gemv_lds<W, U, NB, S, kSrc>), dim3(a.rblocks), dim3(W * 64), lds, s, a.packed, a.gamma, a.X,
-                     a.absmax, a.M, a.N, a.K, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc, a.xq_out, a.absmax_out);
+                     a.M, a.N, a.K, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc, a.xq_out, a.absmax_out);
   return hipGetLastError();
 }
 
