@@ -344,7 +344,8 @@ class PreparedCall:
     stream handle, converted to ctypes values up front.  Calling it re-issues the same
     launch for the cost of one foreign call, for launch loops where the per-call Python
     work of the functions above would take longer than the kernel itself.  The caller keeps
-    the tensors the pointers came from alive."""
+    the tensors the pointers came from alive.  The stream is the one current when the call
+    was prepared: to record the call into a HIP graph, prepare it inside the capture."""
 
     def __init__(self, fn: str, *args):
         self._name = fn

@@ -58,3 +58,80 @@ def test_graph_replays_match_eager():
         assert torch.isfinite(scratch)
         for d, ye in zip(mats, eager):
             check_equal(host(d["y"]).view(np.uint32), host(ye).view(np.uint32), f"replay {rep}")
+
+
+def test_grouped_call_replays_in_a_graph():
+    print("case: graph replay of a grouped call (gate + up) and the 9..16-token decode", flush=True)
+    k = 2560
+    mats = []
+    for i, n in enumerate((6912, 6912)):
+        w = synth.latent_weights(n, k, seed=9300 + i, device=DEV)
+        packed, gamma = bl.quantize_weights(w)
+        mats.append((packed, gamma, n))
+    x = synth.activations(1, k, seed=9400, dtype=torch.bfloat16, device=DEV)
+    x16 = synth.activations(16, k, seed=9401, dtype=torch.bfloat16, device=DEV)
+    xq = torch.empty((1, bl.k_pad(k)), dtype=torch.int8, device=DEV)
+    a = torch.empty(1, dtype=torch.float32, device=DEV)
+    xq16 = torch.empty((16, bl.k_pad(k)), dtype=torch.int8, device=DEV)
+    a16 = torch.empty(16, dtype=torch.float32, device=DEV)
+    ys = [torch.empty((1, n), dtype=torch.float32, device=DEV) for _, _, n in mats]
+    y16 = torch.empty((16, 6912), dtype=torch.float32, device=DEV)
+    # a pre-marshalled call holds the stream current when it was prepared, so a graph
+    # captures the binding's call (which takes the capture stream); eagerly both agree
+    bl.prepare_forward_grouped([(p, g, n, y) for (p, g, n), y in zip(mats, ys)], x, k, xq, a)()
+    torch.cuda.synchronize()
+    prepared = [t.clone() for t in ys]
+
+    def step():
+        outs, _, _ = bl.forward_grouped(mats, x, k, xq=xq, absmax=a)
+        for t, o in zip(ys, outs):
+            t.copy_(o)
+        bl.quantize_acts(x16, xq16, a16)
+        bl.forward(mats[0][0], mats[0][1], xq16, a16, 6912, k, y=y16)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in ys + [y16]]
+    for o, e in zip(prepared, eager[:2]):
+        check_equal(host(o).view(np.uint32), host(e).view(np.uint32), "grouped eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in ys + [y16]:
+            t.fill_(float("nan"))
+        scratch = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        for t, e in zip(ys + [y16], eager):
+            check_equal(host(t).view(np.uint32), host(e).view(np.uint32), f"grouped replay {rep}")
+
+
+def test_two_streams_run_concurrently():
+    # the library keeps no state between calls: two streams working at the same time on
+    # different matrices give the results each gives alone
+    print("case: two streams", flush=True)
+    probs = []
+    for i, (m, n, k) in enumerate(((1, 6912, 2560), (40, 1000, 2560))):
+        w = synth.latent_weights(n, k, seed=9500 + i, device=DEV)
+        packed, gamma = bl.quantize_weights(w)
+        x = synth.activations(m, k, seed=9550 + i, dtype=torch.bfloat16, device=DEV)
+        probs.append((packed, gamma, x, n, k))
+    alone = []
+    for packed, gamma, x, n, k in probs:
+        (y, _, _) = bl.forward_fused(packed, gamma, x, n, k)
+        torch.cuda.synchronize()
+        alone.append(y.clone())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    results = [[], []]
+    for _ in range(8):
+        for s, (packed, gamma, x, n, k), res in zip(streams, probs, results):
+            with torch.cuda.stream(s):
+                (y, _, _) = bl.forward_fused(packed, gamma, x, n, k)
+                res.append(y)
+    torch.cuda.synchronize()
+    for res, ref in zip(results, alone):
+        for y in res:
+            check_equal(host(y).view(np.uint32), host(ref).view(np.uint32), "two streams")
