@@ -21,6 +21,7 @@ are listed with the design notes.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from fractions import Fraction
@@ -70,6 +71,8 @@ def _load():
         lib.orc_bf16_to_f32.argtypes = [p, i64, p]
         lib.orc_quant_acts.restype = None
         lib.orc_quant_acts.argtypes = [p, i64, i64, p, p]
+        lib.orc_subln_quant_acts.restype = None
+        lib.orc_subln_quant_acts.argtypes = [p, i64, i64, p, ctypes.c_double, p, p, p]
         lib.orc_matmul.restype = ctypes.c_int
         lib.orc_matmul.argtypes = [p, p, i64, i64, i64, i64, p]
         lib.orc_rescale.restype = None
@@ -223,6 +226,29 @@ def quant_acts(x: np.ndarray):
     a = np.empty(m, dtype=np.float32)
     _load().orc_quant_acts(_ptr(x), m, k, _ptr(xq), _ptr(a))
     return xq, a
+
+
+def subln_quant_acts(x: np.ndarray, gain=None, eps: float = 1e-5):
+    """Sub-layer RMS normalisation, then per-token absmax int8 (orc_subln_quant_acts).
+
+    Returns (xq [M][K_pad] int8, scale [M] fp32, scale64 [M] fp64, h_absmax [M] fp32):
+    the codes, the dequantisation scale max|n| rounded to fp32 and in fp64, and the
+    absmax of h = fl32(x * gain) on which the codes were decided.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    m, k = x.shape
+    xq = np.empty((m, k_pad(k)), dtype=np.int8)
+    ha = np.empty(m, dtype=np.float32)
+    sc = np.empty(m, dtype=np.float64)
+    g = None
+    if gain is not None:
+        g = np.ascontiguousarray(gain, dtype=np.float32)
+        assert g.shape == (k,)
+    if not (eps >= 0.0 and math.isfinite(eps)):
+        raise ValueError("eps must be finite and >= 0")
+    _load().orc_subln_quant_acts(_ptr(x), m, k, None if g is None else _ptr(g), float(np.float32(eps)),
+                                 _ptr(xq), _ptr(ha), _ptr(sc))
+    return xq, sc.astype(np.float32), sc, ha
 
 
 def matmul(q: np.ndarray, xq: np.ndarray, k: int) -> np.ndarray:

@@ -173,6 +173,35 @@ void orc_quant_acts(const float* x, int64_t m_rows, int64_t k_cols, int8_t* xq, 
   }
 }
 
+/* [AT] "BitLinear: the building block": a sub-layer normalisation (a simplified
+ * LayerNorm) sits just before the activation quantiser.  Reading: RMS normalisation,
+ * no centring and no bias, with a per-feature gain g (NULL: all ones) and eps >= 0,
+ *     n[k] = x[k] * g[k] / sqrt(sum_k x[k]^2 / K + eps),
+ * then the per-token absmax quantiser on n.  The factor 1/sqrt(...) is one positive
+ * number per row, and absmax quantisation maps a row and any positive multiple of it to
+ * the same codes (the factor divides out of n[k] * 127 / max|n|).  So the codes are
+ * taken on h[k] = fl32(x[k] * g[k]) with exactly the arithmetic of orc_quant_acts, and
+ * the factor goes into the scale:
+ *     scale[m] = max_k |h[k]| / sqrt(sum_k x[k]^2 / K + eps)     (= max_k |n[k]|)
+ * in fp64 (each x^2 is exact in fp64; the sum is in index order).  h_absmax[m] is
+ * max_k |h[k]|; a row whose h is all zero gives zero codes and scale 0. */
+void orc_subln_quant_acts(const float* x, int64_t m_rows, int64_t k_cols, const float* gain, double eps,
+                          int8_t* xq, float* h_absmax, double* scale) {
+  const int64_t kp = orc_k_pad(k_cols);
+  float* h = (float*)malloc((size_t)(k_cols > 0 ? k_cols : 1) * sizeof(float));
+  for (int64_t m = 0; m < m_rows; ++m) {
+    const float* row = x + m * k_cols;
+    double ss = 0.0;
+    for (int64_t k = 0; k < k_cols; ++k) {
+      ss += (double)row[k] * (double)row[k];
+      h[k] = gain ? row[k] * gain[k] : row[k];
+    }
+    orc_quant_acts(h, 1, k_cols, xq + m * kp, &h_absmax[m]);
+    scale[m] = h_absmax[m] == 0.0f ? 0.0 : (double)h_absmax[m] / sqrt(ss / (double)k_cols + eps);
+  }
+  free(h);
+}
+
 /* [BH] section 1.1: each term is +x, -x or nothing; the sum is exact in integers.
  * q is [N][K] (ternary), xq is [M][ldx]; acc is [M][N].  Returns ORC_ERR_RANGE if
  * a sum does not fit int32. */

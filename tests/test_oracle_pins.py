@@ -257,6 +257,97 @@ def test_act_quant_exhaustive_bf16_rounding():
         assert np.all(code[tie] % 2 == 0)
 
 
+# ------------------------------------------------------------------ SubLN + activation quant
+# [AT] "BitLinear: the building block": a simplified LayerNorm right before the
+# activation quantiser; read as RMS normalisation n = x * g / sqrt(mean(x^2) + eps).
+def _subln(x, gain=None, eps=0.0):
+    xq, sc32, sc64, ha = oracle.subln_quant_acts(np.asarray(x, np.float32), gain, eps)
+    return xq, sc32, sc64, ha
+
+
+def test_subln_closed_forms():
+    k = 300
+    # (3, 4): mean square 12.5; codes round(127 * 3/4) = round(95.25) = 95 and 127
+    xq, _, sc, ha = _subln([[3.0, 4.0]])
+    assert xq[0, :2].tolist() == [95, 127] and ha[0] == 4.0
+    assert sc[0] == pytest.approx(4.0 / math.sqrt(12.5), rel=1e-15)
+    # the gain scales the features but not the mean square: h = (3, 8)
+    xq, _, sc, ha = _subln([[3.0, 4.0]], gain=[1.0, 2.0])
+    assert xq[0, :2].tolist() == [48, 127] and ha[0] == 8.0  # round(47.625)
+    assert sc[0] == pytest.approx(8.0 / math.sqrt(12.5), rel=1e-15)
+    # constant row c: every normalised entry is c / |c|, so the scale is 1 (exactly
+    # where c^2 sums without rounding in fp64)
+    for c in (0.75, -3.0e-3, 1.0e4):
+        xq, sc32, sc, _ = _subln([[c] * k])
+        assert np.all(xq[0, :k] == 127 * int(np.sign(c))) and np.all(xq[0, k:] == 0)
+        assert sc[0] == pytest.approx(1.0, rel=1e-13) and sc32[0] == 1.0
+        assert c != 0.75 or sc[0] == 1.0
+    # eps sits inside the square root, added to the mean square
+    _, _, sc, _ = _subln([[0.75] * k], eps=0.25)
+    assert sc[0] == pytest.approx(0.75 / math.sqrt(0.5625 + 0.25), rel=1e-15)
+    # one non-zero feature v: mean square v^2 / K, so the scale is sqrt(K) at any v
+    for kk, v in ((1000, -2.5), (777, 1.0e-20), (4096, 3.0e30)):
+        row = np.zeros((1, kk), np.float32)
+        row[0, 7] = v
+        xq, _, sc, _ = _subln(row)
+        assert xq[0, 7] == 127 * int(np.sign(v)) and np.count_nonzero(xq) == 1
+        assert sc[0] == pytest.approx(math.sqrt(kk), rel=1e-15)
+        _, _, sc, _ = _subln(row, gain=np.full(kk, 3.0, np.float32))  # h = fl32(3 v)
+        assert sc[0] == pytest.approx(3.0 * math.sqrt(kk), rel=2.0 ** -24)
+    # a zero row, or a zero gain, gives zero codes and a zero scale at any eps
+    for eps in (0.0, 1e-5):
+        xq, sc32, sc, _ = _subln(np.zeros((1, k), np.float32), eps=eps)
+        assert not xq.any() and sc[0] == 0.0 and sc32[0] == 0.0
+        xq, _, sc, _ = _subln(np.ones((1, k), np.float32), gain=np.zeros(k, np.float32), eps=eps)
+        assert not xq.any() and sc[0] == 0.0
+
+
+def test_subln_codes_reduce_to_the_plain_quantiser():
+    x = synth.activations(9, 700, seed=23, dtype=torch.float32, outlier_p=0.01, outlier_mult=20.0).numpy()
+    g = _rng(4).uniform(-2.0, 2.0, 700).astype(np.float32)
+    # no gain: the codes and the absmax they were decided on are the plain quantiser's
+    xq, _, _, ha = _subln(x, eps=1e-5)
+    xq0, a0 = oracle.quant_acts(x)
+    assert np.array_equal(xq, xq0) and np.array_equal(ha, a0)
+    # a gain: the plain quantiser applied to the fp32 products x * g
+    xq, _, _, ha = _subln(x, gain=g, eps=1e-5)
+    xq1, a1 = oracle.quant_acts(x * g)
+    assert np.array_equal(xq, xq1) and np.array_equal(ha, a1)
+
+
+def test_subln_positive_scale_invariance():
+    # with eps = 0 the normalisation removes any positive per-row factor: a power of two
+    # scales x, x^2 and the square root exactly, so codes and scale are unchanged
+    x = synth.activations(6, 513, seed=29, dtype=torch.float32).numpy()
+    g = _rng(5).uniform(0.5, 1.5, 513).astype(np.float32)
+    xq, sc32, sc, _ = _subln(x, gain=g)
+    for f in (2.0 ** 7, 2.0 ** -9):
+        xq2, sc32b, sc2, _ = _subln(x * np.float32(f), gain=g)
+        assert np.array_equal(xq2, xq) and np.array_equal(sc2, sc) and np.array_equal(sc32b, sc32)
+    xqn, _, scn, _ = _subln(-x, gain=g)
+    assert np.array_equal(xqn, -xq) and np.array_equal(scn, sc)
+
+
+def test_subln_matches_normalise_then_quantise():
+    # normalise first in fp64, then quantise the normalised row: the same codes except at
+    # near-ties (where fp32 rounding of x * g decides), and scale = max |n|
+    m, k, eps = 12, 1000, 1e-5
+    x = synth.activations(m, k, seed=31, dtype=torch.float32, outlier_p=0.005, outlier_mult=30.0).numpy()
+    g = _rng(6).uniform(-1.5, 1.5, k).astype(np.float32)
+    xq, _, sc, _ = _subln(x, gain=g, eps=eps)
+    xd = x.astype(np.float64)
+    eps32 = float(np.float32(eps))
+    n = xd * g.astype(np.float64) / np.sqrt(np.mean(xd * xd, axis=1, keepdims=True) + eps32)
+    amax = np.max(np.abs(n), axis=1)
+    assert np.allclose(sc, amax, rtol=1e-7, atol=0)
+    t = n * 127.0 / amax[:, None]
+    lit = np.rint(t)
+    near_tie = np.abs(np.abs(t - np.trunc(t)) - 0.5) < 1e-4
+    agree = lit == xq[:, :k]
+    assert np.all(agree | near_tie)
+    assert np.count_nonzero(~agree) <= np.count_nonzero(near_tie)
+
+
 # ------------------------------------------------------------------ P5/P6: contraction
 def test_matmul_special_cases():
     # [BH] 1.1: +1 adds the activation, -1 subtracts it, 0 skips it
