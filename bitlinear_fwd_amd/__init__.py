@@ -69,6 +69,15 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_probe_mfma.argtypes = [i64, i64, p, p]
         L.bitlinear_forward_grouped.restype = c_int
         L.bitlinear_forward_grouped.argtypes = [p, c_int, p, c_int, i64, i64, p, p, p]
+        f32 = ctypes.c_float
+        L.bitlinear_subln_quantize_acts.restype = c_int
+        L.bitlinear_subln_quantize_acts.argtypes = [p, c_int, i64, i64, p, f32, p, p, p]
+        L.bitlinear_forward_subln.restype = c_int
+        L.bitlinear_forward_subln.argtypes = [p, p, p, c_int, i64, i64, i64, p, f32, p, p, p, p, p]
+        L.bitlinear_forward_grouped_subln.restype = c_int
+        L.bitlinear_forward_grouped_subln.argtypes = [p, c_int, p, c_int, i64, i64, p, f32, p, p, p]
+        L.bitlinear_forward_subln_plan.restype = c_int
+        L.bitlinear_forward_subln_plan.argtypes = [i64, i64, i64, c_int, p]
         _lib = L
     return _lib
 
@@ -78,7 +87,8 @@ EXPORTED_SYMBOLS = (
     "bitlinear_packed_bytes", "bitlinear_wq_workspace_bytes", "bitlinear_quantize_weights",
     "bitlinear_quantize_acts", "bitlinear_forward", "bitlinear_forward_fused", "bitlinear_forward_plan",
     "bitlinear_forward_fused_plan", "bitlinear_forward_grouped", "bitlinear_probe_stream_words",
-    "bitlinear_probe_stream", "bitlinear_probe_mfma",
+    "bitlinear_probe_stream", "bitlinear_probe_mfma", "bitlinear_subln_quantize_acts", "bitlinear_forward_subln",
+    "bitlinear_forward_grouped_subln", "bitlinear_forward_subln_plan",
 )
 
 MAX_GROUP = 8
@@ -146,6 +156,15 @@ def forward_fused_plan(m: int, n: int, k: int, dtype: str = "bf16") -> dict:
     out = (ctypes.c_int32 * 6)()
     dt = BL_BF16 if dtype == "bf16" else BL_F32
     _check("bitlinear_forward_fused_plan", lib().bitlinear_forward_fused_plan(m, n, k, dt, out))
+    return _plan_dict(out)
+
+
+def forward_subln_plan(m: int, n: int, k: int, dtype: str = "bf16") -> dict:
+    """What bitlinear_forward_subln does for (M, N, K): kernel "fused" (one launch) or the
+    forward launch that follows the normalising quantiser."""
+    out = (ctypes.c_int32 * 6)()
+    dt = BL_BF16 if dtype == "bf16" else BL_F32
+    _check("bitlinear_forward_subln_plan", lib().bitlinear_forward_subln_plan(m, n, k, dt, out))
     return _plan_dict(out)
 
 
@@ -313,6 +332,101 @@ def forward_grouped(mats, x, k: int, xq=None, absmax=None, want_y: bool = True, 
     return outs, xq, absmax
 
 
+def _acts_dtype(x, k=None) -> int:
+    import torch
+
+    _require_cuda(x, "x")
+    if x.dim() != 2 or (k is not None and x.shape[1] != k):
+        raise ValueError("x must be 2-D [tokens, K]")
+    if x.dtype == torch.float32:
+        return BL_F32
+    if x.dtype == torch.bfloat16:
+        return BL_BF16
+    raise ValueError("x must be float32 or bfloat16")
+
+
+def _gain_ptr(gain, k: int):
+    import torch
+
+    if gain is None:
+        return None
+    _require_cuda(gain, "gain")
+    if gain.dtype != torch.float32 or gain.dim() != 1 or gain.shape[0] != k or not gain.is_contiguous():
+        raise ValueError("gain must be a contiguous float32 [K] tensor")
+    return gain.data_ptr()
+
+
+def subln_quantize_acts(x, gain=None, eps: float = 1e-5, xq=None, scale=None):
+    """Sub-layer RMS normalisation (per-feature gain, eps) fused with the per-token absmax
+    int8 quantiser.  Returns ``(xq int8 [M][K_pad], scale fp32 [M])``; scale is the
+    absmax of the normalised row and takes the place of absmax in ``forward``."""
+    import torch
+
+    dt = _acts_dtype(x)
+    m, k = x.shape
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((m, k_pad(k)), dtype=torch.int8, device=dev)
+    if scale is None:
+        scale = torch.empty(m, dtype=torch.float32, device=dev)
+    _check("bitlinear_subln_quantize_acts", lib().bitlinear_subln_quantize_acts(
+        x.data_ptr(), dt, m, k, _gain_ptr(gain, k), eps, xq.data_ptr(), scale.data_ptr(), _stream(dev)))
+    return xq, scale
+
+
+def forward_subln(packed, gamma, x, n: int, k: int, gain=None, eps: float = 1e-5, y=None, acc=None, xq=None,
+                  scale=None, want_y: bool = True, want_acc: bool = False):
+    """Sub-layer normalisation, quantisation and the packed-weight product in one call.
+    Returns (y and/or acc, xq, scale) as forward_fused."""
+    import torch
+
+    for t, name in ((packed, "packed"), (gamma, "gamma")):
+        _require_cuda(t, name)
+    dt = _acts_dtype(x, k)
+    m = x.shape[0]
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((m, k_pad(k)), dtype=torch.int8, device=dev)
+    if scale is None:
+        scale = torch.empty(m, dtype=torch.float32, device=dev)
+    if want_y and y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    if want_acc and acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    _check("bitlinear_forward_subln", lib().bitlinear_forward_subln(
+        packed.data_ptr(), gamma.data_ptr(), x.data_ptr(), dt, m, n, k, _gain_ptr(gain, k), eps,
+        y.data_ptr() if y is not None else None, acc.data_ptr() if acc is not None else None,
+        xq.data_ptr(), scale.data_ptr(), _stream(dev)))
+    out = (y, acc) if (want_y and want_acc) else (y if want_y else acc)
+    return out, xq, scale
+
+
+def forward_grouped_subln(mats, x, k: int, gain=None, eps: float = 1e-5, xq=None, scale=None,
+                          want_y: bool = True, want_acc: bool = False):
+    """forward_grouped behind the sub-layer normalisation: one normalising quantisation,
+    shared by every matrix.  Returns (outs, xq, scale)."""
+    import torch
+
+    dt = _acts_dtype(x, k)
+    m = x.shape[0]
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((m, k_pad(k)), dtype=torch.int8, device=dev)
+    if scale is None:
+        scale = torch.empty(m, dtype=torch.float32, device=dev)
+    full, outs = [], []
+    for packed, gamma, n in mats:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev) if want_y else None
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev) if want_acc else None
+        full.append((packed, gamma, n, y, acc))
+        outs.append((y, acc) if (want_y and want_acc) else (y if want_y else acc))
+    arr = _group_array(full)
+    _check("bitlinear_forward_grouped_subln", lib().bitlinear_forward_grouped_subln(
+        ctypes.addressof(arr), len(full), x.data_ptr(), dt, m, k, _gain_ptr(gain, k), eps, xq.data_ptr(),
+        scale.data_ptr(), _stream(dev)))
+    return outs, xq, scale
+
+
 def probe_stream(buf, out=None):
     """Read the uint8 device tensor ``buf`` with the decode access pattern (measurement
     probe); returns the per-32-KiB-block XOR checksums (uint32 device tensor)."""
@@ -383,6 +497,29 @@ def prepare_forward_grouped(mats, x, k: int, xq, absmax) -> PreparedCall:
     call = PreparedCall("bitlinear_forward_grouped", ctypes.addressof(arr), len(mats), x.data_ptr(), dt,
                         x.shape[0], k, xq.data_ptr(), absmax.data_ptr(), _stream(x.device))
     call._keep = arr  # the host descriptor array must outlive the call object
+    return call
+
+
+def prepare_forward_subln(packed, gamma, x, n: int, k: int, gain, eps: float, y, xq, scale) -> PreparedCall:
+    """bitlinear_forward_subln on these tensors (y fp32 output), marshalled once."""
+    for t, name in ((packed, "packed"), (gamma, "gamma"), (y, "y"), (xq, "xq"), (scale, "scale")):
+        _require_cuda(t, name)
+    dt = _acts_dtype(x, k)
+    return PreparedCall("bitlinear_forward_subln", packed.data_ptr(), gamma.data_ptr(), x.data_ptr(), dt,
+                        x.shape[0], n, k, _gain_ptr(gain, k), eps, y.data_ptr(), None, xq.data_ptr(),
+                        scale.data_ptr(), _stream(x.device))
+
+
+def prepare_forward_grouped_subln(mats, x, k: int, gain, eps: float, xq, scale) -> PreparedCall:
+    """bitlinear_forward_grouped_subln on these tensors: ``mats`` is a list of
+    (packed, gamma, n, y) with fp32 outputs y, marshalled once."""
+    for t, name in ((xq, "xq"), (scale, "scale")):
+        _require_cuda(t, name)
+    dt = _acts_dtype(x, k)
+    arr = _group_array([(pk, g, n, y, None) for pk, g, n, y in mats])
+    call = PreparedCall("bitlinear_forward_grouped_subln", ctypes.addressof(arr), len(mats), x.data_ptr(), dt,
+                        x.shape[0], k, _gain_ptr(gain, k), eps, xq.data_ptr(), scale.data_ptr(), _stream(x.device))
+    call._keep = arr
     return call
 
 

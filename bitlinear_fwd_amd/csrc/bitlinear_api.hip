@@ -16,6 +16,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
+// eps of the sub-layer normalisation: finite and >= 0 (NaN fails both comparisons)
+bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.4028234663852886e38f; }
+
+int grouped_impl(const bl_matrix* mats, int count, const void* X, int dt, int64_t M, int64_t K, const float* gain,
+                 float eps, int8_t* Xq, float* absmax, void* stream, bool norm);
+
 }  // namespace
 
 extern "C" {
@@ -62,6 +68,17 @@ int bitlinear_quantize_acts(const void* X, int dt, int64_t M, int64_t K, int8_t*
       bl::launch_act_quant(X, dt == BL_BF16 ? 1 : 0, M, K, Xq, absmax, static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_subln_quantize_acts(const void* X, int dt, int64_t M, int64_t K, const float* gain, float eps,
+                                  int8_t* Xq, float* scale, void* stream) {
+  if (!X || !Xq || !scale) return BL_ERR_INVALID_ARG;
+  if (M < 1 || K < 1 || M >= kMaxDim || K > kMaxK || !eps_ok(eps)) return BL_ERR_INVALID_ARG;
+  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
+  if (!aligned(X, dt == BL_F32 ? 4 : 2) || !aligned(Xq, 16) || !aligned(scale, 4) || !aligned(gain, 4))
+    return BL_ERR_INVALID_ARG;
+  return hip_status(bl::launch_subln_quant(X, dt == BL_BF16 ? 1 : 0, M, K, gain, eps, Xq, scale,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                       int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream) {
   if (!packed || !gamma || !Xq || !absmax || (!Y && !acc)) return BL_ERR_INVALID_ARG;
@@ -96,36 +113,38 @@ int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const voi
   return bitlinear_forward(packed, gamma, Xq, absmax, M, N, K, Y, acc, stream);
 }
 
+int bitlinear_forward_subln(const uint8_t* packed, const float* gamma, const void* X, int dt, int64_t M, int64_t N,
+                            int64_t K, const float* gain, float eps, float* Y, int32_t* acc, int8_t* Xq,
+                            float* scale, void* stream) {
+  if (!packed || !gamma || !X || !Xq || !scale || (!Y && !acc)) return BL_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK || !eps_ok(eps)) return BL_ERR_INVALID_ARG;
+  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
+  if (!aligned(packed, 16) || !aligned(Xq, 16) || !aligned(gamma, 4) || !aligned(scale, 4) || !aligned(gain, 4) ||
+      !aligned(X, dt == BL_F32 ? 4 : 2) || (Y && !aligned(Y, 4)) || (acc && !aligned(acc, 4)))
+    return BL_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bf16 = dt == BL_BF16 ? 1 : 0;
+  if (M <= kDecodeMaxM && aligned(X, 16) && aligned(gain, 16)) {
+    const bl::GemvPlan p = bl::plan_gemv(M, N, K, bf16 ? 3 : 4);
+    if (p.dpp && p.ok) {
+      const bl::NormArgs norm{gain, eps};
+      return hip_status(bl::launch_gemv_fused(packed, gamma, X, bf16, M, N, K, Y, acc, Xq, scale, s, &norm));
+    }
+  }
+  // general case: the normalising quantiser, then the forward, both on the stream
+  if (bl::launch_subln_quant(X, bf16, M, K, gain, eps, Xq, scale, s) != hipSuccess) return BL_ERR_HIP;
+  return bitlinear_forward(packed, gamma, Xq, scale, M, N, K, Y, acc, stream);
+}
+
 int bitlinear_forward_grouped(const bl_matrix* mats, int count, const void* X, int dt, int64_t M, int64_t K,
                               int8_t* Xq, float* absmax, void* stream) {
-  if (!mats || !X || !Xq || !absmax) return BL_ERR_INVALID_ARG;
-  if (count < 1 || count > bl::kMaxGroup) return BL_ERR_INVALID_ARG;
-  if (M < 1 || K < 1 || M >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
-  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
-  if (!aligned(Xq, 16) || !aligned(absmax, 4) || !aligned(X, dt == BL_F32 ? 4 : 2)) return BL_ERR_INVALID_ARG;
-  bl::GroupMat gm[bl::kMaxGroup];
-  for (int j = 0; j < count; ++j) {
-    const bl_matrix& m = mats[j];
-    if (!m.packed || !m.gamma || (!m.Y && !m.acc)) return BL_ERR_INVALID_ARG;
-    if (m.N < 1 || m.N >= kMaxDim) return BL_ERR_INVALID_ARG;
-    if (!aligned(m.packed, 16) || !aligned(m.gamma, 4) || (m.Y && !aligned(m.Y, 4)) || (m.acc && !aligned(m.acc, 4)))
-      return BL_ERR_INVALID_ARG;
-    gm[j] = bl::GroupMat{m.packed, m.gamma, m.N, m.Y, m.acc};
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (aligned(X, 16)) {
-    bool launched = false;
-    const hipError_t e = bl::launch_gemv_grouped(gm, count, X, dt == BL_BF16, M, K, Xq, absmax, s, &launched);
-    if (launched || e != hipSuccess) return hip_status(e);
-  }
-  // general case: one activation quantisation, then one forward per matrix
-  if (bl::launch_act_quant(X, dt == BL_BF16 ? 1 : 0, M, K, Xq, absmax, s) != hipSuccess) return BL_ERR_HIP;
-  for (int j = 0; j < count; ++j) {
-    const int st = bitlinear_forward(mats[j].packed, mats[j].gamma, Xq, absmax, M, mats[j].N, K, mats[j].Y,
-                                     mats[j].acc, stream);
-    if (st != BL_OK) return st;
-  }
-  return BL_OK;
+  return grouped_impl(mats, count, X, dt, M, K, nullptr, 0.0f, Xq, absmax, stream, false);
+}
+
+int bitlinear_forward_grouped_subln(const bl_matrix* mats, int count, const void* X, int dt, int64_t M, int64_t K,
+                                    const float* gain, float eps, int8_t* Xq, float* scale, void* stream) {
+  if (!eps_ok(eps) || !aligned(gain, 4)) return BL_ERR_INVALID_ARG;
+  return grouped_impl(mats, count, X, dt, M, K, gain, eps, Xq, scale, stream, true);
 }
 
 int64_t bitlinear_probe_stream_words(int64_t bytes) {
@@ -164,6 +183,24 @@ int bitlinear_forward_fused_plan(int64_t M, int64_t N, int64_t K, int dt, int32_
   return bitlinear_forward_plan(M, N, K, out);
 }
 
+int bitlinear_forward_subln_plan(int64_t M, int64_t N, int64_t K, int dt, int32_t out[6]) {
+  if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
+  if (M <= kDecodeMaxM) {
+    const bl::GemvPlan p = bl::plan_gemv(M, N, K, dt == BL_BF16 ? 3 : 4);
+    if (p.dpp && p.ok) {
+      out[0] = 3;
+      out[1] = (int32_t)p.groups;
+      out[2] = p.waves * 64;
+      out[3] = p.rb;
+      out[4] = 2;
+      out[5] = p.run;
+      return BL_OK;
+    }
+  }
+  return bitlinear_forward_plan(M, N, K, out);
+}
+
 int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]) {
   if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
   if (M <= kDecodeMaxM) {
@@ -187,3 +224,44 @@ int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]) {
 }
 
 }  // extern "C"
+
+namespace {
+
+int grouped_impl(const bl_matrix* mats, int count, const void* X, int dt, int64_t M, int64_t K, const float* gain,
+                 float eps, int8_t* Xq, float* absmax, void* stream, bool norm) {
+  if (!mats || !X || !Xq || !absmax) return BL_ERR_INVALID_ARG;
+  if (count < 1 || count > bl::kMaxGroup) return BL_ERR_INVALID_ARG;
+  if (M < 1 || K < 1 || M >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
+  if (!aligned(Xq, 16) || !aligned(absmax, 4) || !aligned(X, dt == BL_F32 ? 4 : 2)) return BL_ERR_INVALID_ARG;
+  bl::GroupMat gm[bl::kMaxGroup];
+  for (int j = 0; j < count; ++j) {
+    const bl_matrix& m = mats[j];
+    if (!m.packed || !m.gamma || (!m.Y && !m.acc)) return BL_ERR_INVALID_ARG;
+    if (m.N < 1 || m.N >= kMaxDim) return BL_ERR_INVALID_ARG;
+    if (!aligned(m.packed, 16) || !aligned(m.gamma, 4) || (m.Y && !aligned(m.Y, 4)) || (m.acc && !aligned(m.acc, 4)))
+      return BL_ERR_INVALID_ARG;
+    gm[j] = bl::GroupMat{m.packed, m.gamma, m.N, m.Y, m.acc};
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bl::NormArgs nargs{gain, eps};
+  if (aligned(X, 16) && aligned(gain, 16)) {
+    bool launched = false;
+    const hipError_t e =
+        bl::launch_gemv_grouped(gm, count, X, dt == BL_BF16, M, K, Xq, absmax, s, &launched, norm ? &nargs : nullptr);
+    if (launched || e != hipSuccess) return hip_status(e);
+  }
+  // general case: one activation quantisation, then one forward per matrix
+  const hipError_t eq = norm ? bl::launch_subln_quant(X, dt == BL_BF16 ? 1 : 0, M, K, gain, eps, Xq, absmax, s)
+                             : bl::launch_act_quant(X, dt == BL_BF16 ? 1 : 0, M, K, Xq, absmax, s);
+  if (eq != hipSuccess) return BL_ERR_HIP;
+  for (int j = 0; j < count; ++j) {
+    const int st = bitlinear_forward(mats[j].packed, mats[j].gamma, Xq, absmax, M, mats[j].N, K, mats[j].Y,
+                                     mats[j].acc, stream);
+    if (st != BL_OK) return st;
+  }
+  return BL_OK;
+}
+
+}  // namespace
+

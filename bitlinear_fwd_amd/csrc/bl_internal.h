@@ -86,7 +86,8 @@ struct GemvPlan {
   bool ok = true;       // the requested activation source is supported by this plan
   int64_t groups = 0;   // workgroups
 };
-// src: 0 = int8 activations (bitlinear_forward), 1 = bf16 x, 2 = fp32 x (fused form)
+// src: 0 = int8 activations (bitlinear_forward), 1 = bf16 x, 2 = fp32 x (fused form),
+// 3 / 4 = bf16 / fp32 x through the sub-layer normalisation (register form only)
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src);
 
 // Launch plan of the prefill kernel.
@@ -103,10 +104,22 @@ hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, uint8_t* pa
                                void* workspace, hipStream_t s);
 hipError_t launch_act_quant(const void* X, int bf16, int64_t M, int64_t K, int8_t* Xq, float* absmax,
                             hipStream_t s);
+// The quantiser behind the sub-layer RMS normalisation: codes of fl32(x * gain), scale
+// max|x * gain| / sqrt(mean(x^2) + eps) (gain null: all ones).
+hipError_t launch_subln_quant(const void* X, int bf16, int64_t M, int64_t K, const float* gain, float eps,
+                              int8_t* Xq, float* scale, hipStream_t s);
+// Sub-layer normalisation arguments of the fused decode forms.
+struct NormArgs {
+  const float* gain;  // fp32 [K], 16-byte aligned, or null
+  float eps;
+};
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
+// norm non-null: the normalising form, only where plan_gemv(M, N, K, 3 or 4) gives the
+// register form (hipErrorInvalidConfiguration otherwise, nothing enqueued).
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const void* X, int bf16, int64_t M, int64_t N,
-                             int64_t K, float* Y, int32_t* acc, int8_t* Xq_out, float* absmax_out, hipStream_t s);
+                             int64_t K, float* Y, int32_t* acc, int8_t* Xq_out, float* absmax_out, hipStream_t s,
+                             const NormArgs* norm = nullptr);
 // One matrix of a grouped call (matrices sharing one activation input).
 struct GroupMat {
   const uint8_t* packed;
@@ -118,7 +131,8 @@ struct GroupMat {
 // One fused launch for the whole group when the register form of the decode kernel
 // covers it (M <= 4): *launched tells whether it did (nothing is enqueued otherwise).
 hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, int bf16, int64_t M, int64_t K,
-                               int8_t* Xq_out, float* absmax_out, hipStream_t s, bool* launched);
+                               int8_t* Xq_out, float* absmax_out, hipStream_t s, bool* launched,
+                               const NormArgs* norm = nullptr);
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
 

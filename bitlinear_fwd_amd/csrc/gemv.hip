@@ -358,6 +358,11 @@ __global__ __launch_bounds__(W * 64) void k_gemv_reg(const uint8_t* __restrict__
 // every token, the per-token absmax is the maximum over them (wave reductions, then one
 // barrier across the waves); each lane then quantises its own pieces with the
 // arithmetic of the standalone quantiser, and workgroup 0 stores xq and absmax.
+// kSrc = 3 (bf16) / 4 (fp32) adds the sub-layer RMS normalisation in front of the
+// quantiser, as the standalone normalising quantiser does: the pieces become
+// h = fl32(x g) before the absmax, each lane also sums the squares of x over the pieces
+// it alone covers (fp64), and the scale stored and used in the rescale is
+// max|h| / sqrt(mean(x^2) + eps).
 // Matrices that share one activation input (bitlinear_forward_grouped); a single forward
 // is a group of one.  rb_end[j] = row blocks of matrices 0..j.
 struct MatGroup {
@@ -389,10 +394,15 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Activation sources of the decode kernels: 0 = int8 xq, 1 / 2 = bf16 / fp32 x, 3 / 4 =
+// bf16 / fp32 x through the sub-layer normalisation.
+constexpr bool src_bf16(int src) { return src == 1 || src == 3; }
+constexpr bool src_norm(int src) { return src >= 3; }
+
 template <int MM, int kSrc>
 struct DppShape {
-  static constexpr int UA = 16 / (4 * MM);                        // tiles per activation piece
-  static constexpr int kParts = kSrc == 0 ? 1 : (kSrc == 1 ? 2 : 4);  // 16-byte loads per piece
+  static constexpr int UA = 16 / (4 * MM);                                // tiles per activation piece
+  static constexpr int kParts = kSrc == 0 ? 1 : (src_bf16(kSrc) ? 2 : 4);  // 16-byte loads per piece
 };
 
 template <int T, int MM, int kSrc>
@@ -400,14 +410,17 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
                                               int N, float* __restrict__ Y, int32_t* __restrict__ acc_out, int rb0,
                                               const void* __restrict__ X, const float* __restrict__ absmax_in, int M,
                                               int K, int K_pad, int chunks, int8_t* __restrict__ xq_out,
-                                              float* __restrict__ absmax_out) {
+                                              float* __restrict__ absmax_out, const float* __restrict__ gain,
+                                              float eps) {
   static_assert(MM >= 1 && MM <= 4, "one to four tokens");
+  constexpr bool kNorm = src_norm(kSrc);
   constexpr int UA = DppShape<MM, kSrc>::UA;
   constexpr int NA = (T + UA - 1) / UA;    // activation pieces per lane
   constexpr int kParts = DppShape<MM, kSrc>::kParts;
   constexpr int kPartElems = 16 / kParts;  // elements per 16-byte load
   __shared__ v4i red[16 * 64];
   __shared__ float amax_w[16][4];
+  __shared__ double ss_w[kNorm ? 16 : 1][4];
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -426,7 +439,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
     if constexpr (kSrc == 0) {
       raw[j][0] = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(X) + (size_t)pm * K_pad + col);
     } else {
-      constexpr int kEB = kSrc == 1 ? 2 : 4;
+      constexpr int kEB = src_bf16(kSrc) ? 2 : 4;
       static_for<kParts>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
         const int e = col + kPartElems * h;
@@ -435,6 +448,21 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
       });
     }
   });
+  // normalising form: the gain of the piece's 16 columns (4 loads; null gain: all ones)
+  uint4 graw[kNorm ? NA : 1][4];
+  if constexpr (kNorm) {
+    if (gain) {
+      static_for<NA>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        const int col = min(c0 + j * UA + pu, chunks - 1) * kTileCols + 64 * g + 16 * pi;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int e = col + 4 * h;
+          graw[j][h] = *reinterpret_cast<const uint4*>(gain + (e + 4 <= K ? e : K - 4));
+        }
+      });
+    }
+  }
   // The fused form issues its weight loads only after the absmax barrier: loads issued
   // earlier by any wave of the compute unit delay the activation loads queued behind
   // them, and with them the barrier (measured: up to 5 us on 58.7 MB matrices).
@@ -448,24 +476,39 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
 
   uint4 act[NA];
   float am[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // fused form: absmax of tokens 0..MM-1
+  float asc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // and the scale of each token (= am unless kNorm)
   if constexpr (kSrc == 0) {
     static_for<NA>([&](auto jc) { act[decltype(jc)::value] = raw[decltype(jc)::value][0]; });
   } else {
     float v[NA][16];
     float lmax = 0.0f;
+    double lss = 0.0;  // kNorm: sum of x^2 over the pieces this lane alone covers
     static_for<NA>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const int col = min(c0 + j * UA + pu, chunks - 1) * kTileCols + 64 * g + 16 * pi;
+      // a piece is counted once: not a repeat (lanes past 4 UA pieces per token), inside
+      // this wave's run, and not a clamped tile past the matrix
+      const bool own = pq < 4 * UA && j * UA + pu < T && c0 + j * UA + pu < chunks;
       static_for<kParts>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
         const bool in = col + kPartElems * h + kPartElems <= K;
         const uint32_t d[4] = {raw[j][h].x, raw[j][h].y, raw[j][h].z, raw[j][h].w};
 #pragma unroll
         for (int e = 0; e < kPartElems; ++e) {
+          constexpr int kBf = src_bf16(kSrc);
           float f;
-          if constexpr (kSrc == 1) f = __uint_as_float(e & 1 ? (d[e >> 1] & 0xFFFF0000u) : (d[e >> 1] << 16));
+          if constexpr (kBf) f = __uint_as_float(e & 1 ? (d[e >> 1] & 0xFFFF0000u) : (d[e >> 1] << 16));
           else f = __uint_as_float(d[e]);
           f = in ? f : 0.0f;
+          if constexpr (kNorm) {
+            lss = own ? fma((double)f, (double)f, lss) : lss;
+            if (gain) {
+              const int q = kPartElems * h + e;  // column offset inside the piece
+              const uint4 gq = graw[j][q >> 2];
+              const uint32_t gb = (q & 3) == 0 ? gq.x : ((q & 3) == 1 ? gq.y : ((q & 3) == 2 ? gq.z : gq.w));
+              f = f * __uint_as_float(gb);
+            }
+          }
           v[j][kPartElems * h + e] = f;
           lmax = fmaxf(lmax, fabsf(f));
         }
@@ -477,6 +520,12 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
       if (lane == 0) amax_w[wave][m] = x;
+      if constexpr (kNorm) {
+        double y = pm == m ? lss : 0.0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) y += __shfl_xor(y, off, 64);
+        if (lane == 0) ss_w[wave][m] = y;
+      }
     }
     lds_barrier();
 #pragma unroll
@@ -484,6 +533,12 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
       float a = 0.0f;
       for (int w2 = 0; w2 < W; ++w2) a = fmaxf(a, amax_w[w2][m]);
       am[m] = a;
+      asc[m] = a;
+      if constexpr (kNorm) {
+        double ss = 0.0;
+        for (int w2 = 0; w2 < W; ++w2) ss += ss_w[w2][m];
+        asc[m] = a > 0.0f ? (float)((double)a / sqrt(ss / (double)K + (double)eps)) : 0.0f;
+      }
     }
     const float apm = pm == 0 ? am[0] : (pm == 1 ? am[1] : (pm == 2 ? am[2] : am[3]));
     const float sc = apm > 0.0f ? 127.0f / apm : 0.0f;
@@ -503,7 +558,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
         *reinterpret_cast<uint4*>(xq_out + (size_t)pm * K_pad + col) = act[j];
       }
     });
-    if (blockIdx.x == 0 && threadIdx.x < MM) absmax_out[threadIdx.x] = am[threadIdx.x];
+    if (blockIdx.x == 0 && threadIdx.x < MM) absmax_out[threadIdx.x] = asc[threadIdx.x];
   }
   static_for<T>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
@@ -556,7 +611,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * g + v;
         if (m < M) {
-          const float a = kSrc == 0 ? absmax_in[m] : (m == 0 ? am[0] : (m == 1 ? am[1] : (m == 2 ? am[2] : am[3])));
+          const float a = kSrc == 0 ? absmax_in[m] : (m == 0 ? asc[0] : (m == 1 ? asc[1] : (m == 2 ? asc[2] : asc[3])));
           if (acc_out) acc_out[(size_t)m * N + n] = sum[v];
           if (Y) Y[(size_t)m * N + n] = (float)sum[v] * gm * a * (1.0f / 127.0f);
         }
@@ -573,14 +628,27 @@ __global__ __launch_bounds__(1024) void k_gemv_dpp(const uint8_t* __restrict__ p
                                                   int32_t* __restrict__ acc_out, int8_t* __restrict__ xq_out,
                                                   float* __restrict__ absmax_out) {
   gemv_dpp_body<T, MM, kSrc>(packed, gamma, N, Y, acc_out, (int)blockIdx.x, X, absmax_in, M, K, K_pad, chunks,
-                             xq_out, absmax_out);
+                             xq_out, absmax_out, nullptr, 0.0f);
+}
+
+// The normalising form (kSrc 3 / 4) of the same kernel, with the gain and eps.
+template <int T, int MM, int kSrc>
+__global__ __launch_bounds__(1024) void k_gemv_dpp_norm(const uint8_t* __restrict__ packed,
+                                                       const float* __restrict__ gamma, const void* __restrict__ X,
+                                                       const float* __restrict__ gain, float eps, int M, int N, int K,
+                                                       int K_pad, int chunks, float* __restrict__ Y,
+                                                       int32_t* __restrict__ acc_out, int8_t* __restrict__ xq_out,
+                                                       float* __restrict__ absmax_out) {
+  gemv_dpp_body<T, MM, kSrc>(packed, gamma, N, Y, acc_out, (int)blockIdx.x, X, nullptr, M, K, K_pad, chunks, xq_out,
+                             absmax_out, gain, eps);
 }
 
 // Grouped form: workgroups take the row blocks of the group's matrices one after another.
 template <int T, int MM, int kSrc>
 __global__ __launch_bounds__(1024) void k_gemv_dpp_group(const MatGroup grp, const void* __restrict__ X, int M,
                                                         int K, int K_pad, int chunks, int8_t* __restrict__ xq_out,
-                                                        float* __restrict__ absmax_out) {
+                                                        float* __restrict__ absmax_out, const float* __restrict__ gain,
+                                                        float eps) {
   int mat = 0;  // uniform
 #pragma unroll
   for (int k = 0; k + 1 < kMaxGroup; ++k)
@@ -601,7 +669,7 @@ __global__ __launch_bounds__(1024) void k_gemv_dpp_group(const MatGroup grp, con
       rb_base = grp.rb_end[k - 1];
     }
   gemv_dpp_body<T, MM, kSrc>(packed, gamma, N, Y, acc_out, (int)blockIdx.x - rb_base, X, nullptr, M, K, K_pad,
-                             chunks, xq_out, absmax_out);
+                             chunks, xq_out, absmax_out, gain, eps);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -701,6 +769,8 @@ struct Args {
   int32_t* acc;
   int8_t* xq_out;
   float* absmax_out;
+  const float* gain = nullptr;  // normalising sources only
+  float eps = 0.0f;
 };
 
 template <int W, int U, int NB, int S, int kSrc>
@@ -752,10 +822,15 @@ hipError_t launch_reg_w(int W, const Args& a, hipStream_t s) {
 }
 
 // Fused forms hold the raw activation pieces in registers until the barrier: limit them
-// to 8 sixteen-byte loads per lane.
+// to 8 sixteen-byte loads per lane, or 12 with the 4 gain loads of each piece.
+constexpr bool dpp_fits_n(int T, int M, int src) {
+  if (src == 0) return true;
+  const int ua = 16 / (4 * M), parts = src_bf16(src) ? 2 : 4, na = (T + ua - 1) / ua;
+  return src_norm(src) ? na * (parts + 4) <= 12 : na * parts <= 8;
+}
 template <int T, int MM, int kSrc>
 constexpr bool dpp_fits() {
-  return kSrc == 0 || ((T + DppShape<MM, kSrc>::UA - 1) / DppShape<MM, kSrc>::UA) * DppShape<MM, kSrc>::kParts <= 8;
+  return dpp_fits_n(T, MM, kSrc);
 }
 
 
@@ -765,13 +840,18 @@ hipError_t launch_dpp(int W, const Args& a, hipStream_t s, const MatGroup* grp =
     if (grp) {
       if constexpr (kSrc != 0) {
         hipLaunchKernelGGL((k_gemv_dpp_group<T, MM, kSrc>), dim3(grp->rb_end[grp->count - 1]), dim3(W * 64), 0, s,
-                           *grp, a.X, a.M, a.K, a.K_pad, a.chunks, a.xq_out, a.absmax_out);
+                           *grp, a.X, a.M, a.K, a.K_pad, a.chunks, a.xq_out, a.absmax_out, a.gain, a.eps);
         return hipGetLastError();
       }
       return hipErrorInvalidConfiguration;  // groups are formed by the fused (x input) call only
     }
-    hipLaunchKernelGGL((k_gemv_dpp<T, MM, kSrc>), dim3(a.rblocks), dim3(W * 64), 0, s, a.packed, a.gamma, a.X,
-                       a.absmax, a.M, a.N, a.K, a.K_pad, a.chunks, a.Y, a.acc, a.xq_out, a.absmax_out);
+    if constexpr (src_norm(kSrc)) {
+      hipLaunchKernelGGL((k_gemv_dpp_norm<T, MM, kSrc>), dim3(a.rblocks), dim3(W * 64), 0, s, a.packed, a.gamma, a.X,
+                         a.gain, a.eps, a.M, a.N, a.K, a.K_pad, a.chunks, a.Y, a.acc, a.xq_out, a.absmax_out);
+    } else {
+      hipLaunchKernelGGL((k_gemv_dpp<T, MM, kSrc>), dim3(a.rblocks), dim3(W * 64), 0, s, a.packed, a.gamma, a.X,
+                         a.absmax, a.M, a.N, a.K, a.K_pad, a.chunks, a.Y, a.acc, a.xq_out, a.absmax_out);
+    }
     return hipGetLastError();
   } else {
     return hipErrorInvalidConfiguration;  // not planned (dpp_fused_ok)
@@ -822,12 +902,8 @@ hipError_t launch_dppm(int W, const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Host mirror of dpp_fits for the planner.
-bool dpp_fused_ok(int64_t T, int64_t M, int src) {
-  if (src == 0) return true;
-  const int64_t ua = 16 / (4 * M), parts = src == 1 ? 2 : 4;
-  return (T + ua - 1) / ua * parts <= 8;
-}
+// dpp_fits for the planner.
+bool dpp_fused_ok(int64_t T, int64_t M, int src) { return dpp_fits_n((int)T, (int)M, src); }
 
 // waves per workgroup: enough waves in flight without splitting K finer than ~2 tiles
 // per wave, and at most ~32 waves per compute unit overall
@@ -845,7 +921,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   const int64_t chunks = K_pad / kTileCols;
   const int64_t rblocks = n_pad(N) / kTileRows;
   // the fused forms read x in whole 16-byte pieces
-  const bool k_ok = src == 0 || (src == 1 && K % 8 == 0) || (src == 2 && K % 4 == 0);
+  const bool k_ok = src == 0 || (src_bf16(src) ? K % 8 == 0 : K % 4 == 0);
   if (M <= 4 && k_ok) {
     // about 32 waves per compute unit over the launch, at least two tiles per wave, then
     // the shortest supported run that covers the row block with at most 16 waves
@@ -855,8 +931,12 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
     // prefer at most 9 waves (measured: 2560 x 6912 at 9 waves 4.8 us, at 14 waves 5.3 us)
     // unless the longer runs that needs would not fit in registers
     const int64_t tries[2] = {src != 0 ? std::min<int64_t>(w, 9) : w, w};
-    for (const int64_t wt : tries) {
-      const int64_t t = dpp_run((chunks + wt - 1) / wt);
+    int64_t runs[3] = {dpp_run((chunks + tries[0] - 1) / tries[0]), dpp_run((chunks + tries[1] - 1) / tries[1]), 0};
+    // the normalising sources have no LDS form: else the longest run that fits in registers
+    if (src_norm(src))
+      for (int r : kDppRuns)
+        if (dpp_fused_ok(r, M, src) && (chunks + r - 1) / r <= 16) runs[2] = r;
+    for (const int64_t t : runs) {
       if (t > 0 && (chunks + t - 1) / t <= 16 && dpp_fused_ok(t, M, src)) {
         p.dpp = true;
         p.run = (int)t;
@@ -870,12 +950,12 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   // fused form for short rows when the register form does not fit: every workgroup
   // quantises all M*K activations into LDS
   const bool small = M <= 4 && M * (K_pad + 16) <= kMaxLdsActBytes;
-  if (src != 0 && small && k_ok && M * K <= kMaxFusedElems) {
+  if ((src == 1 || src == 2) && small && k_ok && M * K <= kMaxFusedElems) {
     p.lds_act = true;
     p.rb = 1;
     p.groups = rblocks;
     p.waves = pick_waves(chunks, rblocks);
-    const int64_t elems = src == 1 ? 8 : 4;
+    const int64_t elems = src_bf16(src) ? 8 : 4;
     const int64_t pieces = M * K / elems;
     // every piece must be covered by at most 4 loads per thread
     while (p.waves < 16 && pieces > 4 * 64 * p.waves) p.waves *= 2;
@@ -916,22 +996,31 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
 }
 
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const void* X, int bf16, int64_t M, int64_t N,
-                             int64_t K, float* Y, int32_t* acc, int8_t* Xq_out, float* absmax_out, hipStream_t s) {
-  const GemvPlan p = plan_gemv(M, N, K, bf16 ? 1 : 2);
+                             int64_t K, float* Y, int32_t* acc, int8_t* Xq_out, float* absmax_out, hipStream_t s,
+                             const NormArgs* norm) {
+  const int src = (bf16 ? 1 : 2) + (norm ? 2 : 0);
+  const GemvPlan p = plan_gemv(M, N, K, src);
   Args a{packed, gamma, X, nullptr, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
-         (int)(n_pad(N) / kTileRows), Y, acc, Xq_out, absmax_out};
+         (int)(n_pad(N) / kTileRows), Y, acc, Xq_out, absmax_out, norm ? norm->gain : nullptr,
+         norm ? norm->eps : 0.0f};
+  if (norm) {
+    if (!p.dpp || !p.ok) return hipErrorInvalidConfiguration;  // not planned: the caller checks the plan
+    return bf16 ? launch_dpp_run<3>(p.run, (int)M, p.waves, a, s) : launch_dpp_run<4>(p.run, (int)M, p.waves, a, s);
+  }
   if (p.dpp) return bf16 ? launch_dpp_run<1>(p.run, (int)M, p.waves, a, s) : launch_dpp_run<2>(p.run, (int)M, p.waves, a, s);
   if (bf16) return launch_lds_w<1>(p.waves, p.stage, a, s);
   return launch_lds_w<2>(p.waves, p.stage, a, s);
 }
 
 hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, int bf16, int64_t M, int64_t K,
-                               int8_t* Xq_out, float* absmax_out, hipStream_t s, bool* launched) {
+                               int8_t* Xq_out, float* absmax_out, hipStream_t s, bool* launched,
+                               const NormArgs* norm) {
   *launched = false;
   if (count < 1 || count > kMaxGroup || M > 4) return hipSuccess;
   int64_t rb_total = 0;
   for (int j = 0; j < count; ++j) rb_total += n_pad(mats[j].N) / kTileRows;
-  const GemvPlan p = plan_gemv(M, rb_total * kTileRows, K, bf16 ? 1 : 2);
+  const int src = (bf16 ? 1 : 2) + (norm ? 2 : 0);
+  const GemvPlan p = plan_gemv(M, rb_total * kTileRows, K, src);
   if (!(p.dpp && p.ok)) return hipSuccess;
   *launched = true;
   MatGroup g{};
@@ -947,9 +1036,13 @@ hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, i
     g.acc[j] = mats[j].acc;
   }
   Args a{nullptr, nullptr, X, nullptr, (int)M, 0, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols), 0,
-         nullptr, nullptr, Xq_out, absmax_out};
-  if (bf16) return launch_dpp_run<1>(p.run, (int)M, p.waves, a, s, &g);
-  return launch_dpp_run<2>(p.run, (int)M, p.waves, a, s, &g);
+         nullptr, nullptr, Xq_out, absmax_out, norm ? norm->gain : nullptr, norm ? norm->eps : 0.0f};
+  switch (src) {
+    case 1: return launch_dpp_run<1>(p.run, (int)M, p.waves, a, s, &g);
+    case 2: return launch_dpp_run<2>(p.run, (int)M, p.waves, a, s, &g);
+    case 3: return launch_dpp_run<3>(p.run, (int)M, p.waves, a, s, &g);
+    default: return launch_dpp_run<4>(p.run, (int)M, p.waves, a, s, &g);
+  }
 }
 
 }  // namespace bl

@@ -156,6 +156,53 @@ int bitlinear_forward_grouped(const bl_matrix* mats, int count, const void* X, i
                               int8_t* Xq, float* absmax, void* stream);
 
 /*
+ * Sub-layer normalisation in front of step 2.  The aratech.ae article ("BitLinear: the
+ * building block") puts a simplified LayerNorm (SubLN) right before the activation
+ * quantiser.  This library reads it as RMS normalisation with no centring and no bias:
+ *     n[m][k] = X[m][k] * gain[k] / sqrt(mean_k X[m][k]^2 + eps),
+ * and quantises n per token as step 2.  Absmax quantisation gives a row and any positive
+ * multiple of it the same codes, so the codes are those of h = fl32(X * gain) under
+ * step 2's arithmetic (bit for bit), and the scale written out is
+ *     scale[m] = max_k |h[m][k]| / sqrt(mean_k X[m][k]^2 + eps)   (= max_k |n[m][k]|),
+ * evaluated in fp64 from an fp64 sum of squares and rounded once to fp32; an all-zero h
+ * gives zero codes and scale 0.  scale takes the place of absmax in bitlinear_forward.
+ *   X      [M][K] fp32 (dt = BL_F32) or bf16 (dt = BL_BF16), row-major.
+ *   gain   fp32 [K] per-feature gain (device, 4-byte aligned), or NULL for all ones.
+ *   eps    finite, >= 0 (BL_ERR_INVALID_ARG otherwise).
+ *   Xq     out: int8 [M][K_pad], 16-byte aligned; scale out: fp32 [M].
+ */
+int bitlinear_subln_quantize_acts(const void* X, int dt, int64_t M, int64_t K, const float* gain, float eps,
+                                  int8_t* Xq, float* scale, void* stream);
+
+/*
+ * Sub-layer normalisation + steps 2, 3, 4: bitlinear_forward_fused with the normalising
+ * quantiser above in place of step 2 (Xq and scale out as bitlinear_subln_quantize_acts;
+ * the rest as bitlinear_forward_fused).  Results are identical to
+ * bitlinear_subln_quantize_acts followed by bitlinear_forward.  For M <= 4 with a
+ * 16-byte aligned X and gain, K a multiple of 8 (bf16) or 4 (fp32) and K within a size
+ * limit that depends on M and dt (bitlinear_forward_subln_plan tells), one kernel launch
+ * does all of it; otherwise the two kernels run back to back.
+ */
+int bitlinear_forward_subln(const uint8_t* packed, const float* gamma, const void* X, int dt, int64_t M, int64_t N,
+                            int64_t K, const float* gain, float eps, float* Y, int32_t* acc, int8_t* Xq,
+                            float* scale, void* stream);
+
+/*
+ * bitlinear_forward_grouped behind the sub-layer normalisation (gain, eps as above): one
+ * normalising quantisation shared by all matrices of the group, in one launch under the
+ * conditions of bitlinear_forward_subln (with N the sum of N_pad over the group).
+ */
+int bitlinear_forward_grouped_subln(const bl_matrix* mats, int count, const void* X, int dt, int64_t M, int64_t K,
+                                    const float* gain, float eps, int8_t* Xq, float* scale, void* stream);
+
+/*
+ * Host-only: what bitlinear_forward_subln does for (M, N, K, dt), in the format of
+ * bitlinear_forward_fused_plan (out[0] = 3: one fused launch with activations in
+ * registers; otherwise the plan of the forward that follows the normalising quantiser).
+ */
+int bitlinear_forward_subln_plan(int64_t M, int64_t N, int64_t K, int dt, int32_t out[6]);
+
+/*
  * Host-only description of the launch bitlinear_forward would make for (M, N, K); no
  * device work.  out[0] = kernel (1 = decode, 2 = prefill), out[1] = workgroups,
  * out[2] = threads per workgroup, out[3] = decode: 16-row output blocks per workgroup,

@@ -161,3 +161,52 @@ def test_probe_argument_validation():
     assert L.bitlinear_probe_mfma(0, 1, FAKE, None) == bl.BL_ERR_INVALID_ARG
     assert L.bitlinear_probe_mfma(1, 0, FAKE, None) == bl.BL_ERR_INVALID_ARG
     assert L.bitlinear_probe_mfma(1, 1, None, None) == bl.BL_ERR_INVALID_ARG
+
+
+def test_subln_argument_validation():
+    L = bl.lib()
+    nan, inf = float("nan"), float("inf")
+    q = L.bitlinear_subln_quantize_acts
+    assert q(None, bl.BL_F32, 1, 16, None, 1e-5, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert q(FAKE, bl.BL_F32, 1, 16, None, -1e-5, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert q(FAKE, bl.BL_F32, 1, 16, None, nan, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert q(FAKE, bl.BL_F32, 1, 16, None, inf, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert q(FAKE, bl.BL_F32, 1, 16, FAKE + 2, 1e-5, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG  # gain alignment
+    assert q(FAKE, bl.BL_F32, 0, 16, None, 1e-5, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert q(FAKE, 9, 1, 16, None, 1e-5, FAKE, FAKE, None) == bl.BL_ERR_UNSUPPORTED
+    assert q(FAKE, bl.BL_BF16, 1, 16, None, 1e-5, FAKE + 8, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    f = L.bitlinear_forward_subln
+    ok = dict(packed=FAKE, gamma=FAKE, x=FAKE, dt=bl.BL_BF16, M=1, N=16, K=256, gain=None, eps=1e-5, y=FAKE,
+              acc=None, xq=FAKE, sc=FAKE)
+
+    def call(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return f(d["packed"], d["gamma"], d["x"], d["dt"], d["M"], d["N"], d["K"], d["gain"], d["eps"], d["y"],
+                 d["acc"], d["xq"], d["sc"], None)
+
+    assert call(packed=None) == bl.BL_ERR_INVALID_ARG
+    assert call(sc=None) == bl.BL_ERR_INVALID_ARG
+    assert call(y=None, acc=None) == bl.BL_ERR_INVALID_ARG
+    assert call(eps=-1.0) == bl.BL_ERR_INVALID_ARG
+    assert call(gain=FAKE + 1) == bl.BL_ERR_INVALID_ARG
+    assert call(K=(1 << 24) + 1) == bl.BL_ERR_INVALID_ARG
+    assert call(dt=3) == bl.BL_ERR_UNSUPPORTED
+    one = (bl.BlMatrix * 2)(*[bl.BlMatrix(FAKE, FAKE, 16, FAKE, None) for _ in range(2)])
+    g = L.bitlinear_forward_grouped_subln
+    assert g(ctypes.addressof(one), 2, FAKE, bl.BL_BF16, 1, 256, None, nan, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert g(ctypes.addressof(one), 0, FAKE, bl.BL_BF16, 1, 256, None, 0.0, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert g(None, 2, FAKE, bl.BL_BF16, 1, 256, None, 0.0, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
+
+
+def test_subln_plan_host():
+    # one launch for the decode shapes of a 2B-class layer; beyond the register budget
+    # (fp32, long rows) the two-kernel path; prefill sizes use the prefill plan
+    assert bl.forward_subln_plan(1, 6912, 2560)["kernel"] == "fused"
+    assert bl.forward_subln_plan(1, 2560, 6912)["kernel"] == "fused"
+    assert bl.forward_subln_plan(4, 640, 2560)["kernel"] == "fused"
+    assert bl.forward_subln_plan(1, 700, 28672, "f32")["kernel"] == "decode"
+    assert bl.forward_subln_plan(8, 700, 2560)["kernel"] == "decode"
+    assert bl.forward_subln_plan(2048, 6912, 2560)["kernel"] == "prefill"
+    # the plain fused plans are unchanged by the normalising form
+    assert bl.forward_fused_plan(3, 65600, 768, "f32")["acts"] == "lds"
