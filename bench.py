@@ -26,7 +26,8 @@ packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
   legs         the other workloads: M = 16 full layer, M = 2048 prefill (int8 TOPS vs
                5.0 POPS dense int8 MFMA), 100B-class M = 1 and M = 8 sweeps, and the 2B
                decode workloads with the projections of one input (gate/up, Q/K/V) grouped
-               into one bitlinear_forward_grouped call ("1g", "2g");
+               into one bitlinear_forward_grouped call ("1g", "2g"), and the same
+               workloads behind the sub-layer RMS normalisation ("1s", "1gs", "2s");
   ceilings     measured on this GPU by the library's probes: HBM read rate with the decode
                access pattern at 58.7 MB and 4.4 MB per launch, and the int8 MFMA rate;
                roofline.frac_of_measured_ceiling sets the dominant kernel against the
@@ -55,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
-    ap.add_argument("--legs", default="1g,2,2g,3,4",
+    ap.add_argument("--legs", default="1g,1s,1gs,2,2g,2s,3,4",
                     help="other workloads timed into 'legs' ('' for none); a trailing g times the workload "
                          "with the projections of one input grouped into one call")
     ap.add_argument("--graph", action="store_true",
@@ -82,17 +83,24 @@ class Matrix:
         self.ops = 2 * m * n * k
 
 
+SUBLN_EPS = 1e-5
+
+
 class Workload:
-    def __init__(self, bl, synth, idx, m, dev):
+    def __init__(self, bl, synth, idx, m, dev, subln=False):
         import torch
 
         self.wl = synth.WORKLOADS[idx]
         self.m = m
         self.bl = bl
+        self.subln = subln  # sub-layer RMS normalisation (per-matrix gain) in front of the quantiser
         self.sweep = self.wl.layers > 1  # a step sweeps every layer instead of one set
         nsets = self.wl.layers if self.sweep else self.wl.rotate_sets
         self.sets = [[Matrix(bl, synth, self.wl, s, i, k, n, m, dev) for i, (_, k, n) in enumerate(self.wl.matrices)]
                      for s in range(nsets)]
+        for s, st in enumerate(self.sets):
+            for i, mat in enumerate(st):
+                mat.gain = synth.subln_gain(mat.k, synth.gain_seed(idx, s, i), device=dev) if subln else None
         torch.cuda.synchronize()
         self.bufs = {}
         for mat in self.sets[0]:
@@ -104,8 +112,8 @@ class Workload:
         # forward_fused for a few tokens (one kernel when the library fuses the shape, else
         # quantiser + forward); quantiser + forward otherwise
         self.use_fused = m <= 4
-        self.fused = {key: m <= 4 and bl.forward_fused_plan(m, key[1], key[0], self._dt())["kernel"] == "fused"
-                      for key in self.bufs}
+        plan = bl.forward_subln_plan if subln else bl.forward_fused_plan
+        self.fused = {key: m <= 4 and plan(m, key[1], key[0], self._dt())["kernel"] == "fused" for key in self.bufs}
         self.cursor = 0
         self.graphs = None
         self.calls = [self.prepared(group, False) for group in self.step_groups()]
@@ -123,10 +131,16 @@ class Workload:
         bl = self.bl
         xq, a, y = self.bufs[(mat.k, mat.n)]
         if self.fused[(mat.k, mat.n)] or (self.use_fused and not forward_only):
-            bl.forward_fused(mat.packed, mat.gamma, mat.x, mat.n, mat.k, y=y, xq=xq, absmax=a)
+            if self.subln:
+                bl.forward_subln(mat.packed, mat.gamma, mat.x, mat.n, mat.k, mat.gain, SUBLN_EPS, y=y, xq=xq, scale=a)
+            else:
+                bl.forward_fused(mat.packed, mat.gamma, mat.x, mat.n, mat.k, y=y, xq=xq, absmax=a)
         else:
             if not forward_only:
-                bl.quantize_acts(mat.x, xq, a)
+                if self.subln:
+                    bl.subln_quantize_acts(mat.x, mat.gain, SUBLN_EPS, xq, a)
+                else:
+                    bl.quantize_acts(mat.x, xq, a)
             bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
 
     def set_grouping(self, grouping):
@@ -149,22 +163,31 @@ class Workload:
             for idxs in self.grouping:
                 first = group[idxs[0]]
                 xq, a, _ = self.bufs[(first.k, first.n)]
-                if len(idxs) == 1:
+                mats = [(group[i].packed, group[i].gamma, group[i].n, self.group_y[si][i]) for i in idxs]
+                if self.subln:
+                    calls.append(bl.prepare_forward_grouped_subln(mats, first.x, first.k, first.gain, SUBLN_EPS,
+                                                                  xq, a))
+                elif len(idxs) == 1:
                     calls.append(bl.prepare_forward_fused(first.packed, first.gamma, first.x, first.n, first.k,
                                                           self.group_y[si][idxs[0]], xq, a))
                 else:
-                    calls.append(bl.prepare_forward_grouped(
-                        [(group[i].packed, group[i].gamma, group[i].n, self.group_y[si][i]) for i in idxs],
-                        first.x, first.k, xq, a))
+                    calls.append(bl.prepare_forward_grouped(mats, first.x, first.k, xq, a))
             return calls
         calls = []
         for mat in group:
             xq, a, y = self.bufs[(mat.k, mat.n)]
             if self.fused[(mat.k, mat.n)] or (self.use_fused and not forward_only):
-                calls.append(bl.prepare_forward_fused(mat.packed, mat.gamma, mat.x, mat.n, mat.k, y, xq, a))
+                if self.subln:
+                    calls.append(bl.prepare_forward_subln(mat.packed, mat.gamma, mat.x, mat.n, mat.k, mat.gain,
+                                                          SUBLN_EPS, y, xq, a))
+                else:
+                    calls.append(bl.prepare_forward_fused(mat.packed, mat.gamma, mat.x, mat.n, mat.k, y, xq, a))
             else:
                 if not forward_only:
-                    calls.append(bl.prepare_quantize_acts(mat.x, xq, a))
+                    if self.subln:
+                        calls.append(bl.prepare_subln_quantize_acts(mat.x, mat.gain, SUBLN_EPS, xq, a))
+                    else:
+                        calls.append(bl.prepare_quantize_acts(mat.x, xq, a))
                 calls.append(bl.prepare_forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y))
         return calls
 
@@ -311,6 +334,8 @@ def dominant_kernel(w: Workload) -> str:
     plan = w.bl.forward_plan(m, key[1], key[0])
     if plan["kernel"] == "prefill":
         return "k_gemm_mfma (prefill, %dx%d tiles)" % (plan["tile_m"], plan["tile_n"])
+    if w.fused[key] and w.subln:
+        return "k_gemv_dpp_norm (sub-layer normalisation + activation quantise + decode, one kernel)"
     if w.fused[key]:
         fplan = w.bl.forward_fused_plan(m, key[1], key[0], w._dt())
         if fplan["acts"] == "registers":
@@ -480,26 +505,34 @@ def main():
     roof["frac_of_measured_ceiling"] = round(roof["achieved"] / ceil, 4)
     legs = {}
     for tok in [t.strip() for t in args.legs.split(",") if t.strip()]:
-        grouped = tok.endswith("g")
-        idx = int(tok.rstrip("g"))
-        if idx == args.workload and not grouped:
+        flags = tok.lstrip("0123456789")
+        idx = int(tok[: len(tok) - len(flags)])
+        grouped, subln = "g" in flags, "s" in flags
+        if idx == args.workload and not flags:
             continue
         if grouped and idx not in GROUPINGS:
             continue
         for m in synth.WORKLOADS[idx].m_list:
-            w = Workload(bl, synth, idx, m, dev)
+            w = Workload(bl, synth, idx, m, dev, subln=subln)
             if grouped:
                 w.set_grouping(GROUPINGS[idx])
             if args.graph:
                 w.capture()
             steps = max(3, args.steps // (40 if w.sweep else 1))
             lms = time_steps(w, steps, max(1, args.warmup // (40 if w.sweep else 4)))
-            key = f"w{idx}{'g' if grouped else ''}_m{m}"
+            key = f"w{idx}{flags}_m{m}"
             if grouped:
                 legs[key] = leg_summary(w, lms, None, None, None)
                 legs[key]["grouping"] = [[w.wl.matrices[i][0] for i in g] for g in GROUPINGS[idx]]
-                legs[key]["note"] = ("projections of one input in one bitlinear_forward_grouped call (shared "
-                                     "activation quantisation); per-step bytes and ops as the ungrouped workload")
+                legs[key]["note"] = ("projections of one input in one grouped call (shared activation "
+                                     "quantisation); per-step bytes and ops as the ungrouped workload")
+                if subln:
+                    legs[key]["note"] += "; sub-layer RMS normalisation in front of the quantiser"
+            elif subln:
+                legs[key] = leg_summary(w, lms, None, None, None)
+                legs[key]["kernel"] = dominant_kernel(w)
+                legs[key]["note"] = ("sub-layer RMS normalisation (per-feature gain, eps 1e-5) in front of the "
+                                     "quantiser, in the same kernel where the plan fuses it")
             else:
                 l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
                 legs[key] = leg_summary(w, lms, l_ms, l_b, l_o)

@@ -523,6 +523,15 @@ def prepare_forward_grouped_subln(mats, x, k: int, gain, eps: float, xq, scale) 
     return call
 
 
+def prepare_subln_quantize_acts(x, gain, eps: float, xq, scale) -> PreparedCall:
+    """bitlinear_subln_quantize_acts on these tensors, marshalled once."""
+    for t, name in ((xq, "xq"), (scale, "scale")):
+        _require_cuda(t, name)
+    dt = _acts_dtype(x)
+    return PreparedCall("bitlinear_subln_quantize_acts", x.data_ptr(), dt, x.shape[0], x.shape[1],
+                        _gain_ptr(gain, x.shape[1]), eps, xq.data_ptr(), scale.data_ptr(), _stream(x.device))
+
+
 def prepare_quantize_acts(x, xq, absmax) -> PreparedCall:
     """bitlinear_quantize_acts on these tensors, marshalled once."""
     import torch

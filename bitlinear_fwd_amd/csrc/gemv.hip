@@ -429,6 +429,12 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   const uint4* wsrc = reinterpret_cast<const uint4*>(packed) + (size_t)rb0 * chunks * 64 + lane;
   const int pm = r % MM, pq = r / MM;
   const int pu = min(pq / 4, UA - 1), pi = pq % 4;
+  // Piece j of this lane is one the wave uses: not a repeat (lanes past 4 UA pieces per
+  // token), inside the wave's run, and not a clamped tile past the matrix.  Every
+  // (token, column) is the piece of exactly one such lane in the workgroup.  The fused
+  // forms load x (and the gain) for these pieces only; the others hold zeros, which
+  // change neither the absmax nor the sum of squares and never reach a computed tile.
+  auto own = [&](int j) { return pq < 4 * UA && j * UA + pu < T && c0 + j * UA + pu < chunks; };
 
   // every activation load first (their wait then does not wait for the weights), then
   // every weight load of the run
@@ -440,11 +446,13 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
       raw[j][0] = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(X) + (size_t)pm * K_pad + col);
     } else {
       constexpr int kEB = src_bf16(kSrc) ? 2 : 4;
+      const bool ld = own(j);
       static_for<kParts>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
         const int e = col + kPartElems * h;
         const int es = e + kPartElems <= K ? e : K - kPartElems;  // columns past K: any valid load, zeroed below
-        raw[j][h] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(X) + ((size_t)pm * K + es) * kEB);
+        raw[j][h] = make_uint4(0u, 0u, 0u, 0u);
+        if (ld) raw[j][h] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(X) + ((size_t)pm * K + es) * kEB);
       });
     }
   });
@@ -455,10 +463,12 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
       static_for<NA>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         const int col = min(c0 + j * UA + pu, chunks - 1) * kTileCols + 64 * g + 16 * pi;
+        const bool ld = own(j);
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           const int e = col + 4 * h;
-          graw[j][h] = *reinterpret_cast<const uint4*>(gain + (e + 4 <= K ? e : K - 4));
+          graw[j][h] = make_uint4(0u, 0u, 0u, 0u);
+          if (ld) graw[j][h] = *reinterpret_cast<const uint4*>(gain + (e + 4 <= K ? e : K - 4));
         }
       });
     }
@@ -476,19 +486,15 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
 
   uint4 act[NA];
   float am[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // fused form: absmax of tokens 0..MM-1
-  float asc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // and the scale of each token (= am unless kNorm)
+  double lss = 0.0;                         // kNorm: sum of x^2 over this lane's pieces
   if constexpr (kSrc == 0) {
     static_for<NA>([&](auto jc) { act[decltype(jc)::value] = raw[decltype(jc)::value][0]; });
   } else {
     float v[NA][16];
     float lmax = 0.0f;
-    double lss = 0.0;  // kNorm: sum of x^2 over the pieces this lane alone covers
     static_for<NA>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const int col = min(c0 + j * UA + pu, chunks - 1) * kTileCols + 64 * g + 16 * pi;
-      // a piece is counted once: not a repeat (lanes past 4 UA pieces per token), inside
-      // this wave's run, and not a clamped tile past the matrix
-      const bool own = pq < 4 * UA && j * UA + pu < T && c0 + j * UA + pu < chunks;
       static_for<kParts>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
         const bool in = col + kPartElems * h + kPartElems <= K;
@@ -501,7 +507,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
           else f = __uint_as_float(d[e]);
           f = in ? f : 0.0f;
           if constexpr (kNorm) {
-            lss = own ? fma((double)f, (double)f, lss) : lss;
+            lss = fma((double)f, (double)f, lss);  // zero for the pieces the lane does not own
             if (gain) {
               const int q = kPartElems * h + e;  // column offset inside the piece
               const uint4 gq = graw[j][q >> 2];
@@ -520,12 +526,6 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
       if (lane == 0) amax_w[wave][m] = x;
-      if constexpr (kNorm) {
-        double y = pm == m ? lss : 0.0;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) y += __shfl_xor(y, off, 64);
-        if (lane == 0) ss_w[wave][m] = y;
-      }
     }
     lds_barrier();
 #pragma unroll
@@ -533,12 +533,6 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
       float a = 0.0f;
       for (int w2 = 0; w2 < W; ++w2) a = fmaxf(a, amax_w[w2][m]);
       am[m] = a;
-      asc[m] = a;
-      if constexpr (kNorm) {
-        double ss = 0.0;
-        for (int w2 = 0; w2 < W; ++w2) ss += ss_w[w2][m];
-        asc[m] = a > 0.0f ? (float)((double)a / sqrt(ss / (double)K + (double)eps)) : 0.0f;
-      }
     }
     const float apm = pm == 0 ? am[0] : (pm == 1 ? am[1] : (pm == 2 ? am[2] : am[3]));
     const float sc = apm > 0.0f ? 127.0f / apm : 0.0f;
@@ -553,18 +547,28 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
         q[d] = word;
       }
       act[j] = make_uint4(q[0], q[1], q[2], q[3]);
-      if (blockIdx.x == 0) {
+      if (blockIdx.x == 0 && own(j)) {
         const int col = min(c0 + j * UA + pu, chunks - 1) * kTileCols + 64 * g + 16 * pi;
         *reinterpret_cast<uint4*>(xq_out + (size_t)pm * K_pad + col) = act[j];
       }
     });
-    if (blockIdx.x == 0 && threadIdx.x < MM) absmax_out[threadIdx.x] = asc[threadIdx.x];
   }
   static_for<T>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
     if constexpr (t >= kEarly) w[t] = load_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
   });
   __builtin_amdgcn_sched_barrier(0);
+  // kNorm: the per-token sums of squares are only needed by the rescale: they are reduced
+  // here, while the weight loads are in flight, and cross the waves with the partial tiles
+  if constexpr (kNorm) {
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      double y = pm == m ? lss : 0.0;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) y += __shfl_xor(y, off, 64);
+      if (lane == 0) ss_w[wave][m] = y;
+    }
+  }
 
   v4i c = {0, 0, 0, 0};
   static_for<NA>([&](auto jc) {
@@ -602,6 +606,17 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   __syncthreads();
   // sum the W partial tiles in wave order (exact) and store row block rb0
   if (wave == 0) {
+    float asc[4] = {am[0], am[1], am[2], am[3]};  // fused forms: the scale of each token
+    if constexpr (kNorm) {
+#pragma unroll
+      for (int m = 0; m < MM; ++m) {
+        double ss = 0.0;
+        for (int w2 = 0; w2 < W; ++w2) ss += ss_w[w2][m];
+        asc[m] = am[m] > 0.0f ? (float)((double)am[m] / sqrt(ss / (double)K + (double)eps)) : 0.0f;
+      }
+    }
+    if (kSrc != 0 && blockIdx.x == 0 && lane < MM)
+      absmax_out[lane] = lane == 0 ? asc[0] : (lane == 1 ? asc[1] : (lane == 2 ? asc[2] : asc[3]));
     v4i sum = red[lane];
     for (int w2 = 1; w2 < W; ++w2) sum += red[w2 * 64 + lane];
     const int n = rb0 * kTileRows + r;

@@ -9,7 +9,9 @@ Recipe (the workloads' shapes and distributions):
   * activations x[M][K], i.i.d. N(0, 1); an optional outlier mask draws each entry
     independently with probability p and multiplies it by a factor (x20 at p = 1 %,
     x30 at p = 0.5 %), before the cast to bf16 where the workload is bf16;
-  * seeds: 1000 * workload + 10 * layer + matrix index for weights, +500 for activations.
+  * sub-layer normalisation gains g[K], fp32, i.i.d. uniform on [0.5, 1.5);
+  * seeds: 1000 * workload + 10 * layer + matrix index for weights, +500 for activations,
+    +700 for gains.
 """
 from __future__ import annotations
 
@@ -45,12 +47,22 @@ def activations(m: int, k: int, seed: int, dtype=torch.bfloat16, device="cpu",
     return x.to(dtype)
 
 
+def subln_gain(k: int, seed: int, device="cpu") -> torch.Tensor:
+    """fp32 [k] ~ uniform[0.5, 1.5): a per-feature gain of the sub-layer normalisation."""
+    g = _gen(seed, device)
+    return torch.rand(k, generator=g, device=device, dtype=torch.float32).add_(0.5)
+
+
 def weight_seed(workload: int, layer: int, matrix: int) -> int:
     return 1000 * workload + 10 * layer + matrix
 
 
 def act_seed(workload: int, layer: int, matrix: int) -> int:
     return weight_seed(workload, layer, matrix) + 500
+
+
+def gain_seed(workload: int, layer: int, matrix: int) -> int:
+    return weight_seed(workload, layer, matrix) + 700
 
 
 @dataclass
