@@ -234,12 +234,12 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
-    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.3 KiB (x1.99980),
+    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.4 KiB (x1.99980),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4592518, "fetch_kib": 2230.03, "write_kib": 25.27, "sha": "accc5a11c597c96a"},
-    (2, 16): {"bytes_per_launch": 3159765, "fetch_kib": 1441.29, "write_kib": 203.43, "sha": "accc5a11c597c96a"},
-    (3, 2048): {"bytes_per_launch": 107258282, "fetch_kib": 33431.6, "write_kib": 37888.0, "sha": "3a955bb30b5ef120"},
-    (4, 1): {"bytes_per_launch": 59234959, "fetch_kib": 28881.25, "write_kib": 90.0, "sha": "accc5a11c597c96a"},
+    (1, 1): {"bytes_per_launch": 4595859, "fetch_kib": 2231.67, "write_kib": 25.27, "sha": "33dffa12a86c1e50"},
+    (2, 16): {"bytes_per_launch": 3158885, "fetch_kib": 1440.86, "write_kib": 203.43, "sha": "33dffa12a86c1e50"},
+    (3, 2048): {"bytes_per_launch": 107230687, "fetch_kib": 33418.15, "write_kib": 37888.00, "sha": "1bcc1b322725b312"},
+    (4, 1): {"bytes_per_launch": 59277405, "fetch_kib": 28902.00, "write_kib": 90.00, "sha": "33dffa12a86c1e50"},
 }
 
 
