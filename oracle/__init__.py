@@ -49,7 +49,7 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_SRC) > os.path.getmtime(_LIB_PATH):
             build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
         i64, p = ctypes.c_int64, ctypes.c_void_p
@@ -73,6 +73,8 @@ def _load():
         lib.orc_quant_acts.argtypes = [p, i64, i64, p, p]
         lib.orc_subln_quant_acts.restype = None
         lib.orc_subln_quant_acts.argtypes = [p, i64, i64, p, ctypes.c_double, p, p, p]
+        lib.orc_gated_relu2.restype = None
+        lib.orc_gated_relu2.argtypes = [p, p, i64, p]
         lib.orc_matmul.restype = ctypes.c_int
         lib.orc_matmul.argtypes = [p, p, i64, i64, i64, i64, p]
         lib.orc_rescale.restype = None
@@ -286,3 +288,21 @@ def forward(q: np.ndarray, gamma, xq: np.ndarray, absmax: np.ndarray, k: int):
     """(acc int32 [M][N], y float64 [M][N]) from ternary codes and quantised activations."""
     acc = matmul(q, xq, k)
     return acc, rescale(acc, gamma, absmax)
+
+
+def gated_relu2(y_gate: np.ndarray, y_up: np.ndarray) -> np.ndarray:
+    """Squared-ReLU gating of a gate / up pair: relu(y_gate)^2 * y_up in fp64."""
+    g = np.ascontiguousarray(y_gate, dtype=np.float64)
+    u = np.ascontiguousarray(y_up, dtype=np.float64)
+    assert g.shape == u.shape
+    h = np.empty(g.shape, dtype=np.float64)
+    _load().orc_gated_relu2(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
+def ffn_gate_up(q_gate: np.ndarray, gamma_gate, q_up: np.ndarray, gamma_up, xq: np.ndarray, absmax: np.ndarray,
+                k: int) -> np.ndarray:
+    """h [M][N] fp64 of the gate / up pair on quantised activations: two forwards, then gating."""
+    _, y_g = forward(q_gate, gamma_gate, xq, absmax, k)
+    _, y_u = forward(q_up, gamma_up, xq, absmax, k)
+    return gated_relu2(y_g, y_u)

@@ -225,3 +225,13 @@ void orc_rescale(const int32_t* acc, int64_t m_rows, int64_t n_rows, float gamma
     for (int64_t n = 0; n < n_rows; ++n)
       y[m * n_rows + n] = (double)acc[m * n_rows + n] * (double)gamma * (double)absmax[m] / 127.0;
 }
+
+/* [AT] "BitLinear: the building block": the feed-forward layers use the squared ReLU
+ * activation.  Reading for a gate / up pair of BitLinear projections of one input:
+ * h = relu(y_gate)^2 * y_up, elementwise, in fp64 on the fp64 outputs of orc_rescale. */
+void orc_gated_relu2(const double* y_gate, const double* y_up, int64_t count, double* h) {
+  for (int64_t i = 0; i < count; ++i) {
+    const double r = y_gate[i] > 0.0 ? y_gate[i] : 0.0;
+    h[i] = r * r * y_up[i];
+  }
+}

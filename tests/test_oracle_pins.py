@@ -348,6 +348,45 @@ def test_subln_matches_normalise_then_quantise():
     assert np.count_nonzero(~agree) <= np.count_nonzero(near_tie)
 
 
+# ------------------------------------------------------------------ squared-ReLU gating
+# [AT] "BitLinear: the building block": squared ReLU in the feed-forward layers; read for a
+# gate / up pair as h = relu(gate)^2 * up.
+def test_gated_relu2_closed_forms():
+    g = np.array([2.0, -1.0, 0.0, 0.5, -0.0, 3.0, 1e-3])
+    u = np.array([3.0, 5.0, 7.0, -4.0, 2.0, 0.0, 1e6])
+    h = oracle.gated_relu2(g, u)
+    assert h.tolist() == [12.0, 0.0, 0.0, -1.0, 0.0, 0.0, pytest.approx(1.0, rel=1e-12)]
+    assert not np.signbit(h[1])  # a negative gate: relu gives +0, times a positive up is +0
+
+
+def test_gated_relu2_properties():
+    rng = _rng(11)
+    g, u = rng.normal(size=(5, 300)), rng.normal(size=(5, 300))
+    h = oracle.gated_relu2(g, u)
+    assert np.all(h[g <= 0] == 0)
+    pos = g > 0
+    # homogeneous of degree 2 in the gate and 1 in up (powers of two keep it exact)
+    assert np.array_equal(oracle.gated_relu2(4.0 * g, u), 16.0 * h)
+    assert np.array_equal(oracle.gated_relu2(g, -2.0 * u), -2.0 * h)
+    # equals the square of the gate times up where the gate is positive
+    assert np.allclose(h[pos], g[pos] ** 2 * u[pos], rtol=1e-15, atol=0)
+
+
+def test_ffn_gate_up_matches_two_forwards():
+    rng = _rng(12)
+    k, n, m = 300, 40, 3
+    qg, qu = (rng.integers(-1, 2, (n, k)).astype(np.int8) for _ in range(2))
+    x = synth.activations(m, k, seed=41, dtype=torch.float32).numpy()
+    xq, a = oracle.quant_acts(x)
+    h = oracle.ffn_gate_up(qg, np.float32(0.02), qu, np.float32(0.03), xq, a, k)
+    # with the gate equal to up and all-(+1) codes, h = relu(s)^3 for s = sum(xq) * gamma * a / 127
+    ones = np.ones((1, k), np.int8)
+    s = xq[:, :k].astype(np.int64).sum(axis=1) * float(np.float32(0.5)) * a.astype(np.float64) / 127
+    h1 = oracle.ffn_gate_up(ones, np.float32(0.5), ones, np.float32(0.5), xq, a, k)[:, 0]
+    assert np.allclose(h1, np.maximum(s, 0) ** 3, rtol=1e-14, atol=0)
+    assert h.shape == (m, n) and np.all(np.isfinite(h))
+
+
 # ------------------------------------------------------------------ P5/P6: contraction
 def test_matmul_special_cases():
     # [BH] 1.1: +1 adds the activation, -1 subtracts it, 0 skips it
