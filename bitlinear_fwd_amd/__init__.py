@@ -76,6 +76,13 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward_subln.argtypes = [p, p, p, c_int, i64, i64, i64, p, f32, p, p, p, p, p]
         L.bitlinear_forward_grouped_subln.restype = c_int
         L.bitlinear_forward_grouped_subln.argtypes = [p, c_int, p, c_int, i64, i64, p, f32, p, p, p]
+        L.bitlinear_gated_relu2_workspace_bytes.restype = i64
+        L.bitlinear_gated_relu2_workspace_bytes.argtypes = [i64, i64]
+        L.bitlinear_forward_gated_relu2.restype = c_int
+        L.bitlinear_forward_gated_relu2.argtypes = [p, p, p, p, p, c_int, i64, i64, i64, c_int, p, f32, p, p, p, p,
+                                                    i64, p]
+        L.bitlinear_forward_gated_relu2_plan.restype = c_int
+        L.bitlinear_forward_gated_relu2_plan.argtypes = [i64, i64, i64, c_int, c_int, p]
         L.bitlinear_forward_subln_plan.restype = c_int
         L.bitlinear_forward_subln_plan.argtypes = [i64, i64, i64, c_int, p]
         _lib = L
@@ -88,7 +95,8 @@ EXPORTED_SYMBOLS = (
     "bitlinear_quantize_acts", "bitlinear_forward", "bitlinear_forward_fused", "bitlinear_forward_plan",
     "bitlinear_forward_fused_plan", "bitlinear_forward_grouped", "bitlinear_probe_stream_words",
     "bitlinear_probe_stream", "bitlinear_probe_mfma", "bitlinear_subln_quantize_acts", "bitlinear_forward_subln",
-    "bitlinear_forward_grouped_subln", "bitlinear_forward_subln_plan",
+    "bitlinear_forward_grouped_subln", "bitlinear_forward_subln_plan", "bitlinear_gated_relu2_workspace_bytes",
+    "bitlinear_forward_gated_relu2", "bitlinear_forward_gated_relu2_plan",
 )
 
 MAX_GROUP = 8
@@ -165,6 +173,16 @@ def forward_subln_plan(m: int, n: int, k: int, dtype: str = "bf16") -> dict:
     out = (ctypes.c_int32 * 6)()
     dt = BL_BF16 if dtype == "bf16" else BL_F32
     _check("bitlinear_forward_subln_plan", lib().bitlinear_forward_subln_plan(m, n, k, dt, out))
+    return _plan_dict(out)
+
+
+def forward_gated_relu2_plan(m: int, n: int, k: int, dtype: str = "bf16", subln: bool = False) -> dict:
+    """What bitlinear_forward_gated_relu2 does for (M, N, K): kernel "fused" (one launch)
+    or the plan of each of the two forwards."""
+    out = (ctypes.c_int32 * 6)()
+    dt = BL_BF16 if dtype == "bf16" else BL_F32
+    _check("bitlinear_forward_gated_relu2_plan",
+           lib().bitlinear_forward_gated_relu2_plan(m, n, k, dt, int(subln), out))
     return _plan_dict(out)
 
 
@@ -427,6 +445,37 @@ def forward_grouped_subln(mats, x, k: int, gain=None, eps: float = 1e-5, xq=None
     return outs, xq, scale
 
 
+def forward_gated_relu2(gate, up, x, n: int, k: int, subln: bool = False, gain=None, eps: float = 1e-5, h=None,
+                        xq=None, scale=None, workspace=None):
+    """Gate / up pair of one input with the squared-ReLU gating: ``gate`` and ``up`` are
+    (packed, gamma) of two N x K matrices.  Returns (h fp32 [M][N], xq, scale)."""
+    import torch
+
+    for t, name in ((gate[0], "gate packed"), (gate[1], "gate gamma"), (up[0], "up packed"), (up[1], "up gamma")):
+        _require_cuda(t, name)
+    dt = _acts_dtype(x, k)
+    m = x.shape[0]
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((m, k_pad(k)), dtype=torch.int8, device=dev)
+    if scale is None:
+        scale = torch.empty(m, dtype=torch.float32, device=dev)
+    if h is None:
+        h = torch.empty((m, n), dtype=torch.float32, device=dev)
+    fused = forward_gated_relu2_plan(m, n, k, "bf16" if dt == BL_BF16 else "f32", subln)["kernel"] == "fused"
+    fused = fused and x.data_ptr() % 16 == 0 and (not subln or gain is None or gain.data_ptr() % 16 == 0)
+    if workspace is None and not fused:
+        workspace = torch.empty(int(lib().bitlinear_gated_relu2_workspace_bytes(m, n)), dtype=torch.uint8,
+                                device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("bitlinear_forward_gated_relu2", lib().bitlinear_forward_gated_relu2(
+        gate[0].data_ptr(), gate[1].data_ptr(), up[0].data_ptr(), up[1].data_ptr(), x.data_ptr(), dt, m, n, k,
+        int(subln), _gain_ptr(gain, k) if subln else None, eps, h.data_ptr(), xq.data_ptr(), scale.data_ptr(),
+        ws_ptr, ws_len, _stream(dev)))
+    return h, xq, scale
+
+
 def probe_stream(buf, out=None):
     """Read the uint8 device tensor ``buf`` with the decode access pattern (measurement
     probe); returns the per-32-KiB-block XOR checksums (uint32 device tensor)."""
@@ -530,6 +579,20 @@ def prepare_subln_quantize_acts(x, gain, eps: float, xq, scale) -> PreparedCall:
     dt = _acts_dtype(x)
     return PreparedCall("bitlinear_subln_quantize_acts", x.data_ptr(), dt, x.shape[0], x.shape[1],
                         _gain_ptr(gain, x.shape[1]), eps, xq.data_ptr(), scale.data_ptr(), _stream(x.device))
+
+
+def prepare_forward_gated_relu2(gate, up, x, n: int, k: int, subln: bool, gain, eps: float, h, xq, scale,
+                                workspace=None) -> PreparedCall:
+    """bitlinear_forward_gated_relu2 on these tensors, marshalled once."""
+    for t, name in ((h, "h"), (xq, "xq"), (scale, "scale")):
+        _require_cuda(t, name)
+    dt = _acts_dtype(x, k)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return PreparedCall("bitlinear_forward_gated_relu2", gate[0].data_ptr(), gate[1].data_ptr(), up[0].data_ptr(),
+                        up[1].data_ptr(), x.data_ptr(), dt, x.shape[0], n, k, int(subln),
+                        _gain_ptr(gain, k) if subln else None, eps, h.data_ptr(), xq.data_ptr(), scale.data_ptr(),
+                        ws_ptr, ws_len, _stream(x.device))
 
 
 def prepare_quantize_acts(x, xq, absmax) -> PreparedCall:

@@ -136,6 +136,62 @@ int bitlinear_forward_subln(const uint8_t* packed, const float* gamma, const voi
   return bitlinear_forward(packed, gamma, Xq, scale, M, N, K, Y, acc, stream);
 }
 
+int64_t bitlinear_gated_relu2_workspace_bytes(int64_t M, int64_t N) {
+  if (M < 1 || N < 1 || M >= kMaxDim || N >= kMaxDim) return -1;
+  return M * N * (int64_t)sizeof(float);
+}
+
+int bitlinear_forward_gated_relu2(const uint8_t* gate_packed, const float* gate_gamma, const uint8_t* up_packed,
+                                  const float* up_gamma, const void* X, int dt, int64_t M, int64_t N, int64_t K,
+                                  int subln, const float* gain, float eps, float* H, int8_t* Xq, float* scale,
+                                  void* workspace, int64_t ws_bytes, void* stream) {
+  if (!gate_packed || !gate_gamma || !up_packed || !up_gamma || !X || !H || !Xq || !scale) return BL_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (subln != 0 && subln != 1) return BL_ERR_INVALID_ARG;
+  if (subln && (!eps_ok(eps) || !aligned(gain, 4))) return BL_ERR_INVALID_ARG;
+  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
+  if (!aligned(gate_packed, 16) || !aligned(up_packed, 16) || !aligned(gate_gamma, 4) || !aligned(up_gamma, 4) ||
+      !aligned(Xq, 16) || !aligned(scale, 4) || !aligned(H, 4) || !aligned(X, dt == BL_F32 ? 4 : 2))
+    return BL_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bf16 = dt == BL_BF16 ? 1 : 0;
+  const bl::NormArgs nargs{subln ? gain : nullptr, eps};
+  const int src = (bf16 ? 1 : 2) + (subln ? 2 : 0);
+  if (aligned(X, 16) && aligned(nargs.gain, 16) && bl::gated_fused_ok(M, N, K, src))
+    return hip_status(bl::launch_gemv_gated(gate_packed, gate_gamma, up_packed, up_gamma, X, bf16, M, N, K, H, Xq,
+                                            scale, s, subln ? &nargs : nullptr));
+  // general case: one quantisation, the two forwards (gate into H, up into the workspace),
+  // then the gating in place
+  if (!workspace || ws_bytes < M * N * (int64_t)sizeof(float) || !aligned(workspace, 4)) return BL_ERR_INVALID_ARG;
+  const hipError_t eq = subln ? bl::launch_subln_quant(X, bf16, M, K, gain, eps, Xq, scale, s)
+                              : bl::launch_act_quant(X, bf16, M, K, Xq, scale, s);
+  if (eq != hipSuccess) return BL_ERR_HIP;
+  float* yu = static_cast<float*>(workspace);
+  int st = bitlinear_forward(gate_packed, gate_gamma, Xq, scale, M, N, K, H, nullptr, stream);
+  if (st != BL_OK) return st;
+  st = bitlinear_forward(up_packed, up_gamma, Xq, scale, M, N, K, yu, nullptr, stream);
+  if (st != BL_OK) return st;
+  return hip_status(bl::launch_gated_relu2(H, yu, M * N, H, s));
+}
+
+int bitlinear_forward_gated_relu2_plan(int64_t M, int64_t N, int64_t K, int dt, int subln, int32_t out[6]) {
+  if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (subln != 0 && subln != 1) return BL_ERR_INVALID_ARG;
+  if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
+  const int src = (dt == BL_BF16 ? 1 : 2) + (subln ? 2 : 0);
+  if (bl::gated_fused_ok(M, N, K, src)) {
+    const bl::GemvPlan p = bl::plan_gemv(M, N, K, src);
+    out[0] = 3;
+    out[1] = (int32_t)p.groups;
+    out[2] = p.waves * 64;
+    out[3] = p.rb;
+    out[4] = 2;
+    out[5] = p.run;
+    return BL_OK;
+  }
+  return bitlinear_forward_plan(M, N, K, out);
+}
+
 int bitlinear_forward_grouped(const bl_matrix* mats, int count, const void* X, int dt, int64_t M, int64_t K,
                               int8_t* Xq, float* absmax, void* stream) {
   return grouped_impl(mats, count, X, dt, M, K, nullptr, 0.0f, Xq, absmax, stream, false);

@@ -133,6 +133,15 @@ struct GroupMat {
 hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, int bf16, int64_t M, int64_t K,
                                int8_t* Xq_out, float* absmax_out, hipStream_t s, bool* launched,
                                const NormArgs* norm = nullptr);
+// Gate / up pair with the squared-ReLU gating: one launch where gated_fused_ok (M <= 4,
+// register form of the fused decode kernel, runs of at most 8 tiles); otherwise
+// hipErrorInvalidConfiguration and nothing enqueued.
+bool gated_fused_ok(int64_t M, int64_t N, int64_t K, int src);
+hipError_t launch_gemv_gated(const uint8_t* packed_gate, const float* gamma_gate, const uint8_t* packed_up,
+                             const float* gamma_up, const void* X, int bf16, int64_t M, int64_t N, int64_t K, float* H,
+                             int8_t* Xq_out, float* absmax_out, hipStream_t s, const NormArgs* norm);
+// h = relu(y_gate)^2 * y_up elementwise (h may alias y_gate).
+hipError_t launch_gated_relu2(const float* y_gate, const float* y_up, int64_t count, float* h, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
 

@@ -375,6 +375,12 @@ struct MatGroup {
   int32_t* acc[kMaxGroup];
 };
 
+// Squared-ReLU gating of one output pair, in fp32: relu(g)^2 * u.
+__device__ __forceinline__ float gated_relu2(float g, float u) {
+  const float r = g > 0.0f ? g : 0.0f;
+  return r * r * u;
+}
+
 template <int s>
 __device__ __forceinline__ int row_shl(int v) {
   if constexpr (s == 0) return v;
@@ -405,20 +411,25 @@ struct DppShape {
   static constexpr int kParts = kSrc == 0 ? 1 : (src_bf16(kSrc) ? 2 : 4);  // 16-byte loads per piece
 };
 
-template <int T, int MM, int kSrc>
+// kPair: a gate / up pair of matrices with the same shape (packed, gamma = gate; packed2,
+// gamma2 = up).  The workgroup streams row block rb0 of both with one set of activation
+// registers and writes the squared-ReLU gating relu(y_gate)^2 * y_up to Y.
+template <int T, int MM, int kSrc, bool kPair = false>
 __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed, const float* __restrict__ gamma,
                                               int N, float* __restrict__ Y, int32_t* __restrict__ acc_out, int rb0,
                                               const void* __restrict__ X, const float* __restrict__ absmax_in, int M,
                                               int K, int K_pad, int chunks, int8_t* __restrict__ xq_out,
                                               float* __restrict__ absmax_out, const float* __restrict__ gain,
-                                              float eps) {
+                                              float eps, const uint8_t* __restrict__ packed2 = nullptr,
+                                              const float* __restrict__ gamma2 = nullptr) {
   static_assert(MM >= 1 && MM <= 4, "one to four tokens");
+  static_assert(!kPair || kSrc != 0, "the gated pair is formed by the fused (x input) calls only");
   constexpr bool kNorm = src_norm(kSrc);
   constexpr int UA = DppShape<MM, kSrc>::UA;
   constexpr int NA = (T + UA - 1) / UA;    // activation pieces per lane
   constexpr int kParts = DppShape<MM, kSrc>::kParts;
   constexpr int kPartElems = 16 / kParts;  // elements per 16-byte load
-  __shared__ v4i red[16 * 64];
+  __shared__ v4i red[(kPair ? 2 : 1) * 16 * 64];
   __shared__ float amax_w[16][4];
   __shared__ double ss_w[kNorm ? 16 : 1][4];
   const int W = blockDim.x >> 6;
@@ -427,6 +438,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   const int r = lane & 15, g = lane >> 4;
   const int c0 = wave * T;
   const uint4* wsrc = reinterpret_cast<const uint4*>(packed) + (size_t)rb0 * chunks * 64 + lane;
+  const uint4* wsrc2 = kPair ? reinterpret_cast<const uint4*>(packed2) + (size_t)rb0 * chunks * 64 + lane : nullptr;
   const int pm = r % MM, pq = r / MM;
   const int pu = min(pq / 4, UA - 1), pi = pq % 4;
   // Piece j of this lane is one the wave uses: not a repeat (lanes past 4 UA pieces per
@@ -478,6 +490,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   // them, and with them the barrier (measured: up to 5 us on 58.7 MB matrices).
   constexpr int kEarly = kSrc == 0 ? T : 0;
   uint4 w[T];
+  uint4 w2[kPair ? T : 1];
   static_for<kEarly>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
     w[t] = load_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
@@ -556,6 +569,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   static_for<T>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
     if constexpr (t >= kEarly) w[t] = load_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
+    if constexpr (kPair) w2[t] = load_nt(wsrc2 + (size_t)min(c0 + t, chunks - 1) * 64);
   });
   __builtin_amdgcn_sched_barrier(0);
   // kNorm: the per-token sums of squares are only needed by the rescale: they are reduced
@@ -571,6 +585,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   }
 
   v4i c = {0, 0, 0, 0};
+  v4i c2 = {0, 0, 0, 0};
   static_for<NA>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     static_for<UA>([&](auto uc) {
@@ -597,12 +612,17 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
             av.w = row_shl<sft>((int)act[j].w);
           }
           c = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, decode16(word), c, 0, 0, 0);
+          if constexpr (kPair) {
+            const uint32_t word2 = live ? word_of(w2[t], i) : 0u;
+            c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, decode16(word2), c2, 0, 0, 0);
+          }
         });
       }
     });
   });
 
   red[wave * 64 + lane] = c;
+  if constexpr (kPair) red[(16 + wave) * 64 + lane] = c2;
   __syncthreads();
   // sum the W partial tiles in wave order (exact) and store row block rb0
   if (wave == 0) {
@@ -619,16 +639,27 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
       absmax_out[lane] = lane == 0 ? asc[0] : (lane == 1 ? asc[1] : (lane == 2 ? asc[2] : asc[3]));
     v4i sum = red[lane];
     for (int w2 = 1; w2 < W; ++w2) sum += red[w2 * 64 + lane];
+    v4i sum2 = {0, 0, 0, 0};
+    if constexpr (kPair) {
+      sum2 = red[16 * 64 + lane];
+      for (int w2 = 1; w2 < W; ++w2) sum2 += red[(16 + w2) * 64 + lane];
+    }
     const int n = rb0 * kTileRows + r;
     if (n < N) {
       const float gm = gamma[0];
+      const float gm2 = kPair ? gamma2[0] : 0.0f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * g + v;
         if (m < M) {
           const float a = kSrc == 0 ? absmax_in[m] : (m == 0 ? asc[0] : (m == 1 ? asc[1] : (m == 2 ? asc[2] : asc[3])));
-          if (acc_out) acc_out[(size_t)m * N + n] = sum[v];
-          if (Y) Y[(size_t)m * N + n] = (float)sum[v] * gm * a * (1.0f / 127.0f);
+          const float y = (float)sum[v] * gm * a * (1.0f / 127.0f);
+          if constexpr (kPair) {
+            Y[(size_t)m * N + n] = gated_relu2(y, (float)sum2[v] * gm2 * a * (1.0f / 127.0f));
+          } else {
+            if (acc_out) acc_out[(size_t)m * N + n] = sum[v];
+            if (Y) Y[(size_t)m * N + n] = y;
+          }
         }
       }
     }
@@ -656,6 +687,27 @@ __global__ __launch_bounds__(1024) void k_gemv_dpp_norm(const uint8_t* __restric
                                                        float* __restrict__ absmax_out) {
   gemv_dpp_body<T, MM, kSrc>(packed, gamma, N, Y, acc_out, (int)blockIdx.x, X, nullptr, M, K, K_pad, chunks, xq_out,
                              absmax_out, gain, eps);
+}
+
+// The gate / up pair with the squared-ReLU gating (kSrc 1..4; gain null unless 3 / 4).
+template <int T, int MM, int kSrc>
+__global__ __launch_bounds__(1024) void k_gemv_dpp_pair(const uint8_t* __restrict__ packed,
+                                                       const float* __restrict__ gamma,
+                                                       const uint8_t* __restrict__ packed2,
+                                                       const float* __restrict__ gamma2, const void* __restrict__ X,
+                                                       const float* __restrict__ gain, float eps, int M, int N, int K,
+                                                       int K_pad, int chunks, float* __restrict__ H,
+                                                       int8_t* __restrict__ xq_out, float* __restrict__ absmax_out) {
+  gemv_dpp_body<T, MM, kSrc, true>(packed, gamma, N, H, nullptr, (int)blockIdx.x, X, nullptr, M, K, K_pad, chunks,
+                                   xq_out, absmax_out, gain, eps, packed2, gamma2);
+}
+
+// Squared-ReLU gating of separately computed outputs (the path for shapes the pair kernel
+// does not take): h = relu(y_gate)^2 * y_up; h may be y_gate itself.
+__global__ __launch_bounds__(256) void k_gated_relu2(const float* yg, const float* __restrict__ yu, int64_t count,
+                                                     float* h) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256)
+    h[i] = gated_relu2(yg[i], yu[i]);
 }
 
 // Grouped form: workgroups take the row blocks of the group's matrices one after another.
@@ -909,6 +961,45 @@ hipError_t launch_dpp_run(int T, int M, int W, const Args& a, hipStream_t s, con
   }
 }
 
+// The gated pair keeps two weight runs in registers: runs of at most 8 tiles.
+constexpr int kPairMaxRun = 8;
+
+template <int T, int MM, int kSrc>
+hipError_t launch_pair(int W, const Args& a, const uint8_t* packed2, const float* gamma2, hipStream_t s) {
+  if constexpr (dpp_fits<T, MM, kSrc>() && T <= kPairMaxRun) {
+    hipLaunchKernelGGL((k_gemv_dpp_pair<T, MM, kSrc>), dim3(a.rblocks), dim3(W * 64), 0, s, a.packed, a.gamma, packed2,
+                       gamma2, a.X, a.gain, a.eps, a.M, a.N, a.K, a.K_pad, a.chunks, a.Y, a.xq_out, a.absmax_out);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidConfiguration;  // not planned
+  }
+}
+
+template <int T, int kSrc>
+hipError_t launch_pair_m(int M, int W, const Args& a, const uint8_t* p2, const float* g2, hipStream_t s) {
+  switch (M) {
+    case 1: return launch_pair<T, 1, kSrc>(W, a, p2, g2, s);
+    case 2: return launch_pair<T, 2, kSrc>(W, a, p2, g2, s);
+    case 3: return launch_pair<T, 3, kSrc>(W, a, p2, g2, s);
+    default: return launch_pair<T, 4, kSrc>(W, a, p2, g2, s);
+  }
+}
+
+template <int kSrc>
+hipError_t launch_pair_run(int T, int M, int W, const Args& a, const uint8_t* p2, const float* g2, hipStream_t s) {
+  switch (T) {
+    case 1: return launch_pair_m<1, kSrc>(M, W, a, p2, g2, s);
+    case 2: return launch_pair_m<2, kSrc>(M, W, a, p2, g2, s);
+    case 3: return launch_pair_m<3, kSrc>(M, W, a, p2, g2, s);
+    case 4: return launch_pair_m<4, kSrc>(M, W, a, p2, g2, s);
+    case 5: return launch_pair_m<5, kSrc>(M, W, a, p2, g2, s);
+    case 6: return launch_pair_m<6, kSrc>(M, W, a, p2, g2, s);
+    case 7: return launch_pair_m<7, kSrc>(M, W, a, p2, g2, s);
+    case 8: return launch_pair_m<8, kSrc>(M, W, a, p2, g2, s);
+    default: return hipErrorInvalidConfiguration;
+  }
+}
+
 template <int T, int MM, int RB>
 hipError_t launch_dppm(int W, const Args& a, hipStream_t s) {
   const unsigned groups = (unsigned)((a.rblocks + RB - 1) / RB);
@@ -1058,6 +1149,35 @@ hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, i
     case 3: return launch_dpp_run<3>(p.run, (int)M, p.waves, a, s, &g);
     default: return launch_dpp_run<4>(p.run, (int)M, p.waves, a, s, &g);
   }
+}
+
+bool gated_fused_ok(int64_t M, int64_t N, int64_t K, int src) {
+  if (M > 4 || src == 0) return false;
+  const GemvPlan p = plan_gemv(M, N, K, src);
+  return p.dpp && p.ok && p.run <= kPairMaxRun;
+}
+
+hipError_t launch_gemv_gated(const uint8_t* packed_gate, const float* gamma_gate, const uint8_t* packed_up,
+                             const float* gamma_up, const void* X, int bf16, int64_t M, int64_t N, int64_t K, float* H,
+                             int8_t* Xq_out, float* absmax_out, hipStream_t s, const NormArgs* norm) {
+  const int src = (bf16 ? 1 : 2) + (norm ? 2 : 0);
+  if (!gated_fused_ok(M, N, K, src)) return hipErrorInvalidConfiguration;
+  const GemvPlan p = plan_gemv(M, N, K, src);
+  Args a{packed_gate, gamma_gate, X, nullptr, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
+         (int)(n_pad(N) / kTileRows), H, nullptr, Xq_out, absmax_out, norm ? norm->gain : nullptr,
+         norm ? norm->eps : 0.0f};
+  switch (src) {
+    case 1: return launch_pair_run<1>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+    case 2: return launch_pair_run<2>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+    case 3: return launch_pair_run<3>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+    default: return launch_pair_run<4>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+  }
+}
+
+hipError_t launch_gated_relu2(const float* y_gate, const float* y_up, int64_t count, float* h, hipStream_t s) {
+  const int64_t groups = std::min<int64_t>((count + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_gated_relu2, dim3((unsigned)groups), dim3(256), 0, s, y_gate, y_up, count, h);
+  return hipGetLastError();
 }
 
 }  // namespace bl

@@ -203,6 +203,35 @@ int bitlinear_forward_grouped_subln(const bl_matrix* mats, int count, const void
 int bitlinear_forward_subln_plan(int64_t M, int64_t N, int64_t K, int dt, int32_t out[6]);
 
 /*
+ * A gate / up pair of projections of one input with the squared-ReLU gating of the
+ * feed-forward layers (aratech.ae, "BitLinear: the building block": squared ReLU in the
+ * feed-forward layers), read for the pair as
+ *     H[m][n] = relu(y_gate[m][n])^2 * y_up[m][n]        (fp32, relu(v) = max(v, 0)),
+ * where y_gate and y_up are the outputs bitlinear_forward would give for the two
+ * matrices (both N x K) on the same quantised activations.
+ *   X, dt, Xq, scale  as bitlinear_forward_fused (subln = 0) or bitlinear_forward_subln
+ *                     (subln = 1, with gain and eps as there; ignored when subln = 0).
+ *   H                 out: fp32 [M][N].
+ *   workspace         device scratch of at least bitlinear_gated_relu2_workspace_bytes(M, N)
+ *                     bytes (4-byte aligned), used only when the pair does not run as one
+ *                     kernel (bitlinear_forward_gated_relu2_plan tells); may be NULL when it
+ *                     does.  A missing or short workspace then gives BL_ERR_INVALID_ARG.
+ * For M <= 4 with a 16-byte aligned X (and gain), under the size limits of
+ * bitlinear_forward_fused / bitlinear_forward_subln and runs of at most 8 tiles per wave,
+ * one kernel streams the same 16-row block of both matrices per workgroup with one set of
+ * activation registers and applies the gating in its epilogue.  Otherwise: the quantiser,
+ * the two forwards (gate into H, up into the workspace) and an elementwise gating kernel.
+ */
+int64_t bitlinear_gated_relu2_workspace_bytes(int64_t M, int64_t N);
+int bitlinear_forward_gated_relu2(const uint8_t* gate_packed, const float* gate_gamma, const uint8_t* up_packed,
+                                  const float* up_gamma, const void* X, int dt, int64_t M, int64_t N, int64_t K,
+                                  int subln, const float* gain, float eps, float* H, int8_t* Xq, float* scale,
+                                  void* workspace, int64_t ws_bytes, void* stream);
+/* Host-only: out[0] = 3 when the pair runs as one kernel (format of
+ * bitlinear_forward_fused_plan), otherwise the plan of each forward. */
+int bitlinear_forward_gated_relu2_plan(int64_t M, int64_t N, int64_t K, int dt, int subln, int32_t out[6]);
+
+/*
  * Host-only description of the launch bitlinear_forward would make for (M, N, K); no
  * device work.  out[0] = kernel (1 = decode, 2 = prefill), out[1] = workgroups,
  * out[2] = threads per workgroup, out[3] = decode: 16-row output blocks per workgroup,

@@ -210,3 +210,31 @@ def test_subln_plan_host():
     assert bl.forward_subln_plan(2048, 6912, 2560)["kernel"] == "prefill"
     # the plain fused plans are unchanged by the normalising form
     assert bl.forward_fused_plan(3, 65600, 768, "f32")["acts"] == "lds"
+
+
+def test_gated_relu2_argument_validation():
+    L = bl.lib()
+    f = L.bitlinear_forward_gated_relu2
+    ok = dict(gp=FAKE, gg=FAKE, up=FAKE, ug=FAKE, x=FAKE, dt=bl.BL_BF16, M=1, N=16, K=256, subln=0, gain=None,
+              eps=0.0, h=FAKE, xq=FAKE, sc=FAKE, ws=None, wsb=0)
+
+    def call(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return f(d["gp"], d["gg"], d["up"], d["ug"], d["x"], d["dt"], d["M"], d["N"], d["K"], d["subln"], d["gain"],
+                 d["eps"], d["h"], d["xq"], d["sc"], d["ws"], d["wsb"], None)
+
+    assert call(gp=None) == bl.BL_ERR_INVALID_ARG
+    assert call(ug=None) == bl.BL_ERR_INVALID_ARG
+    assert call(h=None) == bl.BL_ERR_INVALID_ARG
+    assert call(up=FAKE + 4) == bl.BL_ERR_INVALID_ARG
+    assert call(subln=2) == bl.BL_ERR_INVALID_ARG
+    assert call(subln=1, eps=-1.0) == bl.BL_ERR_INVALID_ARG
+    assert call(dt=5) == bl.BL_ERR_UNSUPPORTED
+    # off the one-kernel path (M = 8) the workspace is required
+    assert call(M=8) == bl.BL_ERR_INVALID_ARG
+    assert call(M=8, ws=FAKE, wsb=8 * 16 * 4 - 1) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_gated_relu2_workspace_bytes(8, 16) == 512
+    assert L.bitlinear_gated_relu2_workspace_bytes(0, 16) == -1
+    assert bl.forward_gated_relu2_plan(1, 6912, 2560)["kernel"] == "fused"
+    assert bl.forward_gated_relu2_plan(8, 6912, 2560)["kernel"] == "decode"
