@@ -27,7 +27,8 @@ packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
                5.0 POPS dense int8 MFMA), 100B-class M = 1 and M = 8 sweeps, and the 2B
                decode workloads with the projections of one input (gate/up, Q/K/V) grouped
                into one bitlinear_forward_grouped call ("1g", "2g"), and the same
-               workloads behind the sub-layer RMS normalisation ("1s", "1gs", "2s");
+               workloads behind the sub-layer RMS normalisation ("1s", "1gs", "2s"), and the
+               gate/up pair with the squared-ReLU gating epilogue in one launch ("1f", "1fs");
   ceilings     measured on this GPU by the library's probes: HBM read rate with the decode
                access pattern at 58.7 MB and 4.4 MB per launch, and the int8 MFMA rate;
                roofline.frac_of_measured_ceiling sets the dominant kernel against the
@@ -56,7 +57,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
-    ap.add_argument("--legs", default="1g,1s,1gs,2,2g,2s,3,4",
+    ap.add_argument("--legs", default="1g,1s,1gs,1f,1fs,2,2g,2s,3,4",
                     help="other workloads timed into 'legs' ('' for none); a trailing g times the workload "
                          "with the projections of one input grouped into one call")
     ap.add_argument("--graph", action="store_true",
@@ -143,6 +144,15 @@ class Workload:
                     bl.quantize_acts(mat.x, xq, a)
             bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
 
+    def set_gated_pair(self):
+        """Gate and up (matrices 0 and 1, one input) as one gated squared-ReLU call, then the
+        down projection: two launches per step, with the same weight bytes as the three."""
+        import torch
+
+        self.gated = True
+        self.gated_h = [torch.empty((self.m, st[0].n), dtype=torch.float32, device=st[0].x.device) for st in self.sets]
+        self.calls = [self.prepared(group, False) for group in self.step_groups()]
+
     def set_grouping(self, grouping):
         """Projections of one input launched as one grouped call: ``grouping`` lists the
         matrix indices of each group (a group's matrices take the first one's input).
@@ -157,6 +167,19 @@ class Workload:
     def prepared(self, group, forward_only):
         """The step's launches as pre-marshalled C-ABI calls (one foreign call each)."""
         bl = self.bl
+        if getattr(self, "gated", False) and not forward_only:
+            si = next(i for i, st in enumerate(self.sets) if st[0] is group[0])
+            gate, up, down = group
+            xq, a, _ = self.bufs[(gate.k, gate.n)]
+            calls = [bl.prepare_forward_gated_relu2((gate.packed, gate.gamma), (up.packed, up.gamma), gate.x, gate.n,
+                                                    gate.k, self.subln, gate.gain, SUBLN_EPS, self.gated_h[si], xq, a)]
+            xq, a, y = self.bufs[(down.k, down.n)]
+            if self.subln:
+                calls.append(bl.prepare_forward_subln(down.packed, down.gamma, down.x, down.n, down.k, down.gain,
+                                                      SUBLN_EPS, y, xq, a))
+            else:
+                calls.append(bl.prepare_forward_fused(down.packed, down.gamma, down.x, down.n, down.k, y, xq, a))
+            return calls
         if getattr(self, "grouping", None) and not forward_only:
             si = next(i for i, st in enumerate(self.sets) if st[0] is group[0])
             calls = []
@@ -507,21 +530,29 @@ def main():
     for tok in [t.strip() for t in args.legs.split(",") if t.strip()]:
         flags = tok.lstrip("0123456789")
         idx = int(tok[: len(tok) - len(flags)])
-        grouped, subln = "g" in flags, "s" in flags
+        grouped, subln, gated = "g" in flags, "s" in flags, "f" in flags
         if idx == args.workload and not flags:
             continue
-        if grouped and idx not in GROUPINGS:
+        if (grouped and idx not in GROUPINGS) or (gated and idx != 1):
             continue
         for m in synth.WORKLOADS[idx].m_list:
             w = Workload(bl, synth, idx, m, dev, subln=subln)
             if grouped:
                 w.set_grouping(GROUPINGS[idx])
+            if gated:
+                w.set_gated_pair()
             if args.graph:
                 w.capture()
             steps = max(3, args.steps // (40 if w.sweep else 1))
             lms = time_steps(w, steps, max(1, args.warmup // (40 if w.sweep else 4)))
             key = f"w{idx}{flags}_m{m}"
-            if grouped:
+            if gated:
+                legs[key] = leg_summary(w, lms, None, None, None)
+                legs[key]["note"] = ("gate and up in one bitlinear_forward_gated_relu2 launch (squared-ReLU gating "
+                                     "epilogue), then down; per-step bytes as the three matrices")
+                if subln:
+                    legs[key]["note"] += "; sub-layer RMS normalisation in front of both quantisers"
+            elif grouped:
                 legs[key] = leg_summary(w, lms, None, None, None)
                 legs[key]["grouping"] = [[w.wl.matrices[i][0] for i in g] for g in GROUPINGS[idx]]
                 legs[key]["note"] = ("projections of one input in one grouped call (shared activation "
