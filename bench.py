@@ -29,6 +29,8 @@ packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
                into one bitlinear_forward_grouped call ("1g", "2g"), and the same
                workloads behind the sub-layer RMS normalisation ("1s", "1gs", "2s"), and the
                gate/up pair with the squared-ReLU gating epilogue in one launch ("1f", "1fs");
+               the two-kernel int8 path ("1i") and the table-lookup decode ("1l") for
+               comparison with the matrix-core decode;
   ceilings     measured on this GPU by the library's probes: HBM read rate with the decode
                access pattern at 58.7 MB and 4.4 MB per launch, and the int8 MFMA rate;
                roofline.frac_of_measured_ceiling sets the dominant kernel against the
@@ -57,7 +59,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
-    ap.add_argument("--legs", default="1g,1s,1gs,1f,1fs,2,2g,2s,3,4",
+    ap.add_argument("--legs", default="1g,1s,1gs,1f,1fs,1i,1l,2,2g,2s,3,4",
                     help="other workloads timed into 'legs' ('' for none); a trailing g times the workload "
                          "with the projections of one input grouped into one call")
     ap.add_argument("--graph", action="store_true",
@@ -88,13 +90,16 @@ SUBLN_EPS = 1e-5
 
 
 class Workload:
-    def __init__(self, bl, synth, idx, m, dev, subln=False):
+    def __init__(self, bl, synth, idx, m, dev, subln=False, path="fused"):
         import torch
 
         self.wl = synth.WORKLOADS[idx]
         self.m = m
         self.bl = bl
         self.subln = subln  # sub-layer RMS normalisation (per-matrix gain) in front of the quantiser
+        # "fused": one call per matrix where the library fuses it; "int8": the quantiser, then
+        # bitlinear_forward; "lut": the quantiser, then the table-lookup forward
+        self.path = path
         self.sweep = self.wl.layers > 1  # a step sweeps every layer instead of one set
         nsets = self.wl.layers if self.sweep else self.wl.rotate_sets
         self.sets = [[Matrix(bl, synth, self.wl, s, i, k, n, m, dev) for i, (_, k, n) in enumerate(self.wl.matrices)]
@@ -112,9 +117,10 @@ class Workload:
                                   torch.empty((m, mat.n), dtype=torch.float32, device=dev))
         # forward_fused for a few tokens (one kernel when the library fuses the shape, else
         # quantiser + forward); quantiser + forward otherwise
-        self.use_fused = m <= 4
+        self.use_fused = m <= 4 and path == "fused"
         plan = bl.forward_subln_plan if subln else bl.forward_fused_plan
-        self.fused = {key: m <= 4 and plan(m, key[1], key[0], self._dt())["kernel"] == "fused" for key in self.bufs}
+        self.fused = {key: self.use_fused and plan(m, key[1], key[0], self._dt())["kernel"] == "fused"
+                      for key in self.bufs}
         self.cursor = 0
         self.graphs = None
         self.calls = [self.prepared(group, False) for group in self.step_groups()]
@@ -142,7 +148,10 @@ class Workload:
                     bl.subln_quantize_acts(mat.x, mat.gain, SUBLN_EPS, xq, a)
                 else:
                     bl.quantize_acts(mat.x, xq, a)
-            bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
+            if self.path == "lut":
+                bl.forward_lut(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
+            else:
+                bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
 
     def set_gated_pair(self):
         """Gate and up (matrices 0 and 1, one input) as one gated squared-ReLU call, then the
@@ -211,7 +220,10 @@ class Workload:
                         calls.append(bl.prepare_subln_quantize_acts(mat.x, mat.gain, SUBLN_EPS, xq, a))
                     else:
                         calls.append(bl.prepare_quantize_acts(mat.x, xq, a))
-                calls.append(bl.prepare_forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y))
+                if self.path == "lut":
+                    calls.append(bl.prepare_forward_lut(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y))
+                else:
+                    calls.append(bl.prepare_forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y))
         return calls
 
     def capture(self):
@@ -531,12 +543,15 @@ def main():
         flags = tok.lstrip("0123456789")
         idx = int(tok[: len(tok) - len(flags)])
         grouped, subln, gated = "g" in flags, "s" in flags, "f" in flags
+        path = "lut" if "l" in flags else ("int8" if "i" in flags else "fused")
         if idx == args.workload and not flags:
             continue
         if (grouped and idx not in GROUPINGS) or (gated and idx != 1):
             continue
         for m in synth.WORKLOADS[idx].m_list:
-            w = Workload(bl, synth, idx, m, dev, subln=subln)
+            if path == "lut" and any(bl.forward_lut_plan(m, n, k) is None for _, k, n in synth.WORKLOADS[idx].matrices):
+                continue
+            w = Workload(bl, synth, idx, m, dev, subln=subln, path=path)
             if grouped:
                 w.set_grouping(GROUPINGS[idx])
             if gated:
@@ -559,6 +574,15 @@ def main():
                                      "quantisation); per-step bytes and ops as the ungrouped workload")
                 if subln:
                     legs[key]["note"] += "; sub-layer RMS normalisation in front of the quantiser"
+            elif path != "fused":
+                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
+                legs[key] = leg_summary(w, lms, l_ms, l_b, l_o)
+                legs[key]["kernel"] = ("k_gemv_lut (table-lookup decode)" if path == "lut"
+                                       else dominant_kernel(w))
+                legs[key]["note"] = ("activation quantiser, then the " +
+                                     ("table-lookup forward (bitlinear_forward_lut)" if path == "lut"
+                                      else "int8 forward (bitlinear_forward)") +
+                                     "; forward_launch_* time the forward launches alone")
             elif subln:
                 legs[key] = leg_summary(w, lms, None, None, None)
                 legs[key]["kernel"] = dominant_kernel(w)

@@ -83,6 +83,10 @@ def lib() -> ctypes.CDLL:
                                                     i64, p]
         L.bitlinear_forward_gated_relu2_plan.restype = c_int
         L.bitlinear_forward_gated_relu2_plan.argtypes = [i64, i64, i64, c_int, c_int, p]
+        L.bitlinear_forward_lut.restype = c_int
+        L.bitlinear_forward_lut.argtypes = [p, p, p, p, i64, i64, i64, p, p, p]
+        L.bitlinear_forward_lut_plan.restype = c_int
+        L.bitlinear_forward_lut_plan.argtypes = [i64, i64, i64, p]
         L.bitlinear_forward_subln_plan.restype = c_int
         L.bitlinear_forward_subln_plan.argtypes = [i64, i64, i64, c_int, p]
         _lib = L
@@ -96,7 +100,8 @@ EXPORTED_SYMBOLS = (
     "bitlinear_forward_fused_plan", "bitlinear_forward_grouped", "bitlinear_probe_stream_words",
     "bitlinear_probe_stream", "bitlinear_probe_mfma", "bitlinear_subln_quantize_acts", "bitlinear_forward_subln",
     "bitlinear_forward_grouped_subln", "bitlinear_forward_subln_plan", "bitlinear_gated_relu2_workspace_bytes",
-    "bitlinear_forward_gated_relu2", "bitlinear_forward_gated_relu2_plan",
+    "bitlinear_forward_gated_relu2", "bitlinear_forward_gated_relu2_plan", "bitlinear_forward_lut",
+    "bitlinear_forward_lut_plan",
 )
 
 MAX_GROUP = 8
@@ -138,6 +143,9 @@ def wq_workspace_bytes(n: int, k: int) -> int:
 
 
 def _plan_dict(out) -> dict:
+    if out[0] == 4:
+        return {"kernel": "lut", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
+                "tiles_per_wave": out[4], "lds_bytes": out[5]}
     if out[0] == 3:
         return {"kernel": "fused", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
                 "acts": "registers" if out[4] == 2 else "lds", "lds_acts": out[4] == 1,
@@ -267,6 +275,37 @@ def forward(packed, gamma, xq, absmax, n: int, k: int, y=None, acc=None, want_y:
         packed.data_ptr(), gamma.data_ptr(), xq.data_ptr(), absmax.data_ptr(), m, n, k,
         y.data_ptr() if y is not None else None, acc.data_ptr() if acc is not None else None,
         _stream(dev)))
+    if want_y and want_acc:
+        return y, acc
+    return y if want_y else acc
+
+
+def forward_lut_plan(m: int, n: int, k: int):
+    """The launch bitlinear_forward_lut makes for (M, N, K), or None where it does not apply."""
+    out = (ctypes.c_int32 * 6)()
+    st = lib().bitlinear_forward_lut_plan(m, n, k, out)
+    if st == BL_ERR_UNSUPPORTED:
+        return None
+    _check("bitlinear_forward_lut_plan", st)
+    return _plan_dict(out)
+
+
+def forward_lut(packed, gamma, xq, absmax, n: int, k: int, y=None, acc=None, want_y: bool = True,
+                want_acc: bool = False):
+    """bitlinear_forward computed by table lookups (comparison variant, M <= 4)."""
+    import torch
+
+    for t, name in ((packed, "packed"), (gamma, "gamma"), (xq, "xq"), (absmax, "absmax")):
+        _require_cuda(t, name)
+    m = xq.shape[0]
+    dev = xq.device
+    if want_y and y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    if want_acc and acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    _check("bitlinear_forward_lut", lib().bitlinear_forward_lut(
+        packed.data_ptr(), gamma.data_ptr(), xq.data_ptr(), absmax.data_ptr(), m, n, k,
+        y.data_ptr() if y is not None else None, acc.data_ptr() if acc is not None else None, _stream(dev)))
     if want_y and want_acc:
         return y, acc
     return y if want_y else acc
@@ -593,6 +632,14 @@ def prepare_forward_gated_relu2(gate, up, x, n: int, k: int, subln: bool, gain, 
                         up[1].data_ptr(), x.data_ptr(), dt, x.shape[0], n, k, int(subln),
                         _gain_ptr(gain, k) if subln else None, eps, h.data_ptr(), xq.data_ptr(), scale.data_ptr(),
                         ws_ptr, ws_len, _stream(x.device))
+
+
+def prepare_forward_lut(packed, gamma, xq, absmax, n: int, k: int, y) -> PreparedCall:
+    """bitlinear_forward_lut on these tensors (y fp32 output), marshalled once."""
+    for t, name in ((packed, "packed"), (gamma, "gamma"), (xq, "xq"), (absmax, "absmax"), (y, "y")):
+        _require_cuda(t, name)
+    return PreparedCall("bitlinear_forward_lut", packed.data_ptr(), gamma.data_ptr(), xq.data_ptr(), absmax.data_ptr(),
+                        xq.shape[0], n, k, y.data_ptr(), None, _stream(xq.device))
 
 
 def prepare_quantize_acts(x, xq, absmax) -> PreparedCall:

@@ -3,6 +3,7 @@
 #include "../../include/bitlinear.h"
 
 #include "bl_internal.h"
+#include "gemv_lut.h"
 
 namespace {
 
@@ -134,6 +135,30 @@ int bitlinear_forward_subln(const uint8_t* packed, const float* gamma, const voi
   // general case: the normalising quantiser, then the forward, both on the stream
   if (bl::launch_subln_quant(X, bf16, M, K, gain, eps, Xq, scale, s) != hipSuccess) return BL_ERR_HIP;
   return bitlinear_forward(packed, gamma, Xq, scale, M, N, K, Y, acc, stream);
+}
+
+int bitlinear_forward_lut(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
+                          int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream) {
+  if (!packed || !gamma || !Xq || !absmax || (!Y && !acc)) return BL_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (!aligned(packed, 16) || !aligned(Xq, 16) || !aligned(gamma, 4) || !aligned(absmax, 4) ||
+      (Y && !aligned(Y, 4)) || (acc && !aligned(acc, 4)))
+    return BL_ERR_INVALID_ARG;
+  if (!bl::plan_gemv_lut(M, N, K).ok) return BL_ERR_UNSUPPORTED;
+  return hip_status(bl::launch_gemv_lut(packed, gamma, Xq, absmax, M, N, K, Y, acc, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward_lut_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]) {
+  if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  const bl::LutPlan p = bl::plan_gemv_lut(M, N, K);
+  if (!p.ok) return BL_ERR_UNSUPPORTED;
+  out[0] = 4;
+  out[1] = (int32_t)p.groups;
+  out[2] = p.waves * 64;
+  out[3] = 1;
+  out[4] = p.run;
+  out[5] = (int32_t)p.lds_bytes;
+  return BL_OK;
 }
 
 int64_t bitlinear_gated_relu2_workspace_bytes(int64_t M, int64_t N) {

@@ -232,6 +232,23 @@ int bitlinear_forward_gated_relu2(const uint8_t* gate_packed, const float* gate_
 int bitlinear_forward_gated_relu2_plan(int64_t M, int64_t N, int64_t K, int dt, int subln, int32_t out[6]);
 
 /*
+ * Steps 3 + 4 by table lookups: the lookup-table technique of the CPU kernels the
+ * bhfrc.com write-up (section 4) and the aratech.ae article describe, built on gfx950 LDS
+ * for comparison with bitlinear_forward.  Same arguments, layouts and results (acc
+ * bit-exact, y as bitlinear_forward).  For each pair of activations that share a nibble
+ * of the packed layout (columns c and c + 4), a 16-entry int16 table holds the pair's
+ * contribution for every nibble value; each packed byte is then two lookups and two adds.
+ * Supported for M <= 4 and K with M * roundup(K, 256) within the table budget
+ * (bitlinear_forward_lut_plan); otherwise BL_ERR_UNSUPPORTED and nothing is enqueued.
+ */
+int bitlinear_forward_lut(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
+                          int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream);
+/* Host-only: out[0] = 4, out[1] = workgroups, out[2] = threads, out[3] = 1, out[4] = K
+ * tiles per wave, out[5] = LDS bytes of tables.  BL_ERR_UNSUPPORTED where the shape does
+ * not fit, BL_ERR_INVALID_ARG for invalid sizes. */
+int bitlinear_forward_lut_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]);
+
+/*
  * Host-only description of the launch bitlinear_forward would make for (M, N, K); no
  * device work.  out[0] = kernel (1 = decode, 2 = prefill), out[1] = workgroups,
  * out[2] = threads per workgroup, out[3] = decode: 16-row output blocks per workgroup,

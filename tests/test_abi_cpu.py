@@ -238,3 +238,13 @@ def test_gated_relu2_argument_validation():
     assert L.bitlinear_gated_relu2_workspace_bytes(0, 16) == -1
     assert bl.forward_gated_relu2_plan(1, 6912, 2560)["kernel"] == "fused"
     assert bl.forward_gated_relu2_plan(8, 6912, 2560)["kernel"] == "decode"
+
+
+def test_lut_plan_and_validation():
+    L = bl.lib()
+    assert bl.forward_lut_plan(1, 6912, 2560)["kernel"] == "lut"
+    assert bl.forward_lut_plan(5, 64, 256) is None
+    assert bl.forward_lut_plan(1, 64, 28672) is None
+    assert L.bitlinear_forward_lut(None, FAKE, FAKE, FAKE, 1, 16, 256, FAKE, None, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_forward_lut(FAKE, FAKE, FAKE, FAKE, 1, 16, 256, None, None, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_forward_lut(FAKE, FAKE, FAKE, FAKE, 5, 16, 256, FAKE, None, None) == bl.BL_ERR_UNSUPPORTED
