@@ -75,6 +75,16 @@ def _load():
         lib.orc_subln_quant_acts.argtypes = [p, i64, i64, p, ctypes.c_double, p, p, p]
         lib.orc_gated_relu2.restype = None
         lib.orc_gated_relu2.argtypes = [p, p, i64, p]
+        lib.orc_kb_pad.restype = i64
+        lib.orc_kb_pad.argtypes = [i64]
+        lib.orc_packed_bytes_binary.restype = i64
+        lib.orc_packed_bytes_binary.argtypes = [i64, i64]
+        lib.orc_binarise.restype = None
+        lib.orc_binarise.argtypes = [p, i64, p]
+        lib.orc_pack_binary.restype = ctypes.c_int
+        lib.orc_pack_binary.argtypes = [p, i64, i64, p]
+        lib.orc_unpack_binary.restype = None
+        lib.orc_unpack_binary.argtypes = [p, i64, i64, p]
         lib.orc_matmul.restype = ctypes.c_int
         lib.orc_matmul.argtypes = [p, p, i64, i64, i64, i64, p]
         lib.orc_rescale.restype = None
@@ -306,3 +316,44 @@ def ffn_gate_up(q_gate: np.ndarray, gamma_gate, q_up: np.ndarray, gamma_up, xq: 
     _, y_g = forward(q_gate, gamma_gate, xq, absmax, k)
     _, y_u = forward(q_up, gamma_up, xq, absmax, k)
     return gated_relu2(y_g, y_u)
+
+
+# ----------------------------------------------------------------------------- binary variant
+def kb_pad(k: int) -> int:
+    return int(_load().orc_kb_pad(k))
+
+
+def packed_bytes_binary(n: int, k: int) -> int:
+    return int(_load().orc_packed_bytes_binary(n, k))
+
+
+def binarise(w: np.ndarray) -> np.ndarray:
+    """sign(W) in {-1, +1} with +1 for W >= 0 (lpnh.cn section 2.1)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    q = np.empty(w.shape, dtype=np.int8)
+    _load().orc_binarise(_ptr(w), w.size, _ptr(q))
+    return q
+
+
+def pack_binary(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    n, k = q.shape
+    out = np.empty(packed_bytes_binary(n, k), dtype=np.uint8)
+    if _load().orc_pack_binary(_ptr(q), n, k, _ptr(out)) != 0:
+        raise ValueError("binary codes must be -1 or +1")
+    return out
+
+
+def unpack_binary(packed: np.ndarray, n: int, k: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    assert packed.size == packed_bytes_binary(n, k)
+    out = np.empty((n, k), dtype=np.int8)
+    _load().orc_unpack_binary(_ptr(packed), n, k, _ptr(out))
+    return out
+
+
+def quantize_weights_binary(w: np.ndarray):
+    """(beta, q [N][K] in {-1, +1}, packed) for latent weights W[N][K]; beta = mean |W|."""
+    beta = gamma_absmean(w)
+    q = binarise(w)
+    return beta, q, pack_binary(q)

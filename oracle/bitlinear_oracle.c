@@ -235,3 +235,64 @@ void orc_gated_relu2(const double* y_gate, const double* y_up, int64_t count, do
     h[i] = r * r * y_up[i];
   }
 }
+
+/* ---- 1-bit sign-binary variant (contrast point) -------------------------------------
+ * lpnh.cn news 2861808, section 2.1: binary weights sign(W) with a scaling factor that
+ * compensates the lost magnitude.  Readings: q = +1 for W >= 0 (also -0.0), -1 for
+ * W < 0 (a 1-bit code has no zero); the scale beta is the same exact mean |W| as gamma.
+ *
+ * Packed layout of the binary variant (a choice): N_pad = roundup(N, 16), KB_pad =
+ * roundup(K, 512); 1024-byte tiles, tile (nb, c) at (nb * (KB_pad / 512) + c) * 1024,
+ * rows 16 nb .. 16 nb + 15, columns 512 c .. 512 c + 511.  Inside a tile, row r and column
+ * offset kk: s = kk / 256, g = (kk % 256) / 64, i = (kk % 64) / 16, e = kk % 16; the
+ * 32-bit little-endian word at byte 16 * (16 g + r) + 4 * (2 s + i / 2) holds the bit at
+ * position 8 * (e % 4) + 4 * (i % 2) + e / 4; bit 1 = +1, bit 0 = -1.  Bits outside N x K
+ * are 0. */
+int64_t orc_kb_pad(int64_t k) { return (k + 511) / 512 * 512; }
+int64_t orc_packed_bytes_binary(int64_t n, int64_t k) { return orc_n_pad(n) * orc_kb_pad(k) / 8; }
+
+void orc_binarise(const float* w, int64_t count, int8_t* q) {
+  for (int64_t i = 0; i < count; ++i) q[i] = w[i] < 0.0f ? -1 : 1;
+}
+
+static void orc_bin_position(int64_t n, int64_t k, int64_t kbp, int64_t* off, int* bit) {
+  const int64_t nb = n / 16, r = n % 16, c = k / 512, kk = k % 512;
+  const int64_t s = kk / 256, g = (kk % 256) / 64, i = (kk % 64) / 16, e = kk % 16;
+  *off = (nb * (kbp / 512) + c) * 1024 + 16 * (16 * g + r) + 4 * (2 * s + i / 2);
+  *bit = (int)(8 * (e % 4) + 4 * (i % 2) + e / 4);
+}
+
+int orc_pack_binary(const int8_t* q, int64_t n_rows, int64_t k_cols, uint8_t* packed) {
+  const int64_t kbp = orc_kb_pad(k_cols);
+  memset(packed, 0, (size_t)orc_packed_bytes_binary(n_rows, k_cols));
+  for (int64_t n = 0; n < n_rows; ++n) {
+    for (int64_t k = 0; k < k_cols; ++k) {
+      const int8_t v = q[n * k_cols + k];
+      if (v != 1 && v != -1) return ORC_ERR_RANGE;
+      if (v == 1) {
+        int64_t off;
+        int bit;
+        orc_bin_position(n, k, kbp, &off, &bit);
+        uint32_t word;
+        memcpy(&word, packed + off, 4);
+        word |= 1u << bit;
+        memcpy(packed + off, &word, 4);
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+void orc_unpack_binary(const uint8_t* packed, int64_t n_rows, int64_t k_cols, int8_t* q) {
+  const int64_t kbp = orc_kb_pad(k_cols);
+  for (int64_t n = 0; n < n_rows; ++n) {
+    for (int64_t k = 0; k < k_cols; ++k) {
+      int64_t off;
+      int bit;
+      orc_bin_position(n, k, kbp, &off, &bit);
+      uint32_t word;
+      memcpy(&word, packed + off, 4);
+      q[n * k_cols + k] = ((word >> bit) & 1u) ? 1 : -1;
+    }
+  }
+}

@@ -387,6 +387,51 @@ def test_ffn_gate_up_matches_two_forwards():
     assert h.shape == (m, n) and np.all(np.isfinite(h))
 
 
+# ------------------------------------------------------------------ 1-bit binary variant
+# lpnh.cn section 2.1: binary weights sign(W) with a magnitude-compensating scale.
+# Hand-derived bit positions of the binary layout (1024-byte tiles of 16 rows x 512
+# columns; 16-byte slot 16 g + r; word 2 s + i / 2; bit 8 (e % 4) + 4 (i % 2) + e / 4).
+def test_binary_pack_hand_derived_positions():
+    n, k = 17, 1100
+    assert oracle.kb_pad(k) == 1536 and oracle.packed_bytes_binary(n, k) == 32 * 1536 // 8
+    expect = {
+        (0, 0): (0, 0), (0, 1): (1, 0), (0, 4): (0, 1), (0, 15): (3, 3), (0, 16): (0, 4), (0, 17): (1, 4),
+        (0, 32): (4, 0), (0, 63): (7, 7), (0, 64): (256, 0), (0, 256): (8, 0), (0, 300): (12, 3),
+        (0, 512): (1024, 0), (1, 0): (16, 0), (16, 0): (3072, 0),
+    }
+    for (r, c), (byte, bit) in expect.items():
+        q = -np.ones((n, k), np.int8)
+        q[r, c] = 1
+        packed = oracle.pack_binary(q)
+        nz = np.nonzero(packed)[0]
+        assert nz.tolist() == [byte] and packed[byte] == 1 << bit, ((r, c), nz, packed[nz])
+        assert np.array_equal(oracle.unpack_binary(packed, n, k), q)
+
+
+def test_binary_roundtrip_sizes_and_sign():
+    w = np.array([[0.5, -0.5, 0.0, -0.0, 1e-30, -1e-30, 3.0, -7.0]], np.float32)
+    assert oracle.binarise(w).tolist() == [[1, -1, 1, 1, 1, -1, 1, -1]]
+    assert oracle.packed_bytes_binary(28672, 8192) == 28672 * 8192 // 8  # half the ternary bytes
+    assert oracle.packed_bytes_binary(2560, 6912) * 2 > oracle.packed_bytes(2560, 6912)  # K pads to 512
+    rng = _rng(13)
+    q = np.where(rng.random((33, 777)) < 0.5, 1, -1).astype(np.int8)
+    packed = oracle.pack_binary(q)
+    assert np.array_equal(oracle.unpack_binary(packed, 33, 777), q)
+    # bits outside the matrix are 0
+    full = np.unpackbits(packed).sum()
+    assert full == np.count_nonzero(q == 1)
+    with pytest.raises(ValueError):
+        oracle.pack_binary(np.zeros((1, 4), np.int8))
+    # beta is the exact mean |W| (pinned above for gamma); the forward is the integer one
+    wl = synth.latent_weights(40, 300, seed=5).numpy()
+    beta, qb, _ = oracle.quantize_weights_binary(wl)
+    assert beta == oracle.gamma_absmean(wl) and set(np.unique(qb)) <= {-1, 1}
+    x = synth.activations(2, 300, seed=6, dtype=torch.float32).numpy()
+    xq, a = oracle.quant_acts(x)
+    acc, _ = oracle.forward(np.ones((1, 300), np.int8), beta, xq, a, 300)
+    assert acc[:, 0].tolist() == xq[:, :300].astype(np.int64).sum(axis=1).tolist()
+
+
 # ------------------------------------------------------------------ P5/P6: contraction
 def test_matmul_special_cases():
     # [BH] 1.1: +1 adds the activation, -1 subtracts it, 0 skips it
