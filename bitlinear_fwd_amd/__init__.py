@@ -83,6 +83,17 @@ def lib() -> ctypes.CDLL:
                                                     i64, p]
         L.bitlinear_forward_gated_relu2_plan.restype = c_int
         L.bitlinear_forward_gated_relu2_plan.argtypes = [i64, i64, i64, c_int, c_int, p]
+        for name in ("bitlinear_kb_pad",):
+            getattr(L, name).restype = i64
+            getattr(L, name).argtypes = [i64]
+        L.bitlinear_packed_bytes_binary.restype = i64
+        L.bitlinear_packed_bytes_binary.argtypes = [i64, i64]
+        L.bitlinear_quantize_weights_binary.restype = c_int
+        L.bitlinear_quantize_weights_binary.argtypes = [p, i64, i64, p, p, p, i64, p]
+        L.bitlinear_forward_binary.restype = c_int
+        L.bitlinear_forward_binary.argtypes = [p, p, p, p, i64, i64, i64, p, p, p]
+        L.bitlinear_forward_binary_plan.restype = c_int
+        L.bitlinear_forward_binary_plan.argtypes = [i64, i64, i64, p]
         L.bitlinear_forward_lut.restype = c_int
         L.bitlinear_forward_lut.argtypes = [p, p, p, p, i64, i64, i64, p, p, p]
         L.bitlinear_forward_lut_plan.restype = c_int
@@ -101,7 +112,8 @@ EXPORTED_SYMBOLS = (
     "bitlinear_probe_stream", "bitlinear_probe_mfma", "bitlinear_subln_quantize_acts", "bitlinear_forward_subln",
     "bitlinear_forward_grouped_subln", "bitlinear_forward_subln_plan", "bitlinear_gated_relu2_workspace_bytes",
     "bitlinear_forward_gated_relu2", "bitlinear_forward_gated_relu2_plan", "bitlinear_forward_lut",
-    "bitlinear_forward_lut_plan",
+    "bitlinear_forward_lut_plan", "bitlinear_kb_pad", "bitlinear_packed_bytes_binary",
+    "bitlinear_quantize_weights_binary", "bitlinear_forward_binary", "bitlinear_forward_binary_plan",
 )
 
 MAX_GROUP = 8
@@ -143,6 +155,9 @@ def wq_workspace_bytes(n: int, k: int) -> int:
 
 
 def _plan_dict(out) -> dict:
+    if out[0] == 5:
+        return {"kernel": "binary", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
+                "tiles_per_wave": out[4]}
     if out[0] == 4:
         return {"kernel": "lut", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
                 "tiles_per_wave": out[4], "lds_bytes": out[5]}
@@ -275,6 +290,66 @@ def forward(packed, gamma, xq, absmax, n: int, k: int, y=None, acc=None, want_y:
         packed.data_ptr(), gamma.data_ptr(), xq.data_ptr(), absmax.data_ptr(), m, n, k,
         y.data_ptr() if y is not None else None, acc.data_ptr() if acc is not None else None,
         _stream(dev)))
+    if want_y and want_acc:
+        return y, acc
+    return y if want_y else acc
+
+
+def kb_pad(k: int) -> int:
+    return int(lib().bitlinear_kb_pad(k))
+
+
+def packed_bytes_binary(n: int, k: int) -> int:
+    return int(lib().bitlinear_packed_bytes_binary(n, k))
+
+
+def quantize_weights_binary(W, packed=None, beta=None, workspace=None):
+    """1-bit sign-binary weights: (packed binary buffer, beta = exact mean |W|) on the GPU."""
+    import torch
+
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float32 tensor")
+    W = W.contiguous()
+    n, k = W.shape
+    dev = W.device
+    if packed is None:
+        packed = torch.empty(packed_bytes_binary(n, k), dtype=torch.uint8, device=dev)
+    if beta is None:
+        beta = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(wq_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+    _check("bitlinear_quantize_weights_binary", lib().bitlinear_quantize_weights_binary(
+        W.data_ptr(), n, k, packed.data_ptr(), beta.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(dev)))
+    return packed, beta
+
+
+def forward_binary_plan(m: int, n: int, k: int):
+    """The launch bitlinear_forward_binary makes for (M, N, K), or None where it does not apply."""
+    out = (ctypes.c_int32 * 6)()
+    st = lib().bitlinear_forward_binary_plan(m, n, k, out)
+    if st == BL_ERR_UNSUPPORTED:
+        return None
+    _check("bitlinear_forward_binary_plan", st)
+    return _plan_dict(out)
+
+
+def forward_binary(packed, beta, xq, absmax, n: int, k: int, y=None, acc=None, want_y: bool = True,
+                   want_acc: bool = False):
+    """bitlinear_forward with 1-bit sign-binary weights (M <= 4)."""
+    import torch
+
+    for t, name in ((packed, "packed"), (beta, "beta"), (xq, "xq"), (absmax, "absmax")):
+        _require_cuda(t, name)
+    m = xq.shape[0]
+    dev = xq.device
+    if want_y and y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    if want_acc and acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    _check("bitlinear_forward_binary", lib().bitlinear_forward_binary(
+        packed.data_ptr(), beta.data_ptr(), xq.data_ptr(), absmax.data_ptr(), m, n, k,
+        y.data_ptr() if y is not None else None, acc.data_ptr() if acc is not None else None, _stream(dev)))
     if want_y and want_acc:
         return y, acc
     return y if want_y else acc
@@ -640,6 +715,14 @@ def prepare_forward_lut(packed, gamma, xq, absmax, n: int, k: int, y) -> Prepare
         _require_cuda(t, name)
     return PreparedCall("bitlinear_forward_lut", packed.data_ptr(), gamma.data_ptr(), xq.data_ptr(), absmax.data_ptr(),
                         xq.shape[0], n, k, y.data_ptr(), None, _stream(xq.device))
+
+
+def prepare_forward_binary(packed, beta, xq, absmax, n: int, k: int, y) -> PreparedCall:
+    """bitlinear_forward_binary on these tensors (y fp32 output), marshalled once."""
+    for t, name in ((packed, "packed"), (beta, "beta"), (xq, "xq"), (absmax, "absmax"), (y, "y")):
+        _require_cuda(t, name)
+    return PreparedCall("bitlinear_forward_binary", packed.data_ptr(), beta.data_ptr(), xq.data_ptr(),
+                        absmax.data_ptr(), xq.shape[0], n, k, y.data_ptr(), None, _stream(xq.device))
 
 
 def prepare_quantize_acts(x, xq, absmax) -> PreparedCall:

@@ -12,8 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbitlinear.so")
-SOURCES = ["bitlinear_api.hip", "weight_quant.hip", "act_quant.hip", "gemv.hip", "gemv_lut.hip", "gemm.hip",
-           "probes.hip"]
+SOURCES = ["bitlinear_api.hip", "weight_quant.hip", "act_quant.hip", "gemv.hip", "gemv_lut.hip", "gemv_bin.hip",
+           "gemm.hip", "probes.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

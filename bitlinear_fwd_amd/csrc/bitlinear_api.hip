@@ -4,6 +4,7 @@
 
 #include "bl_internal.h"
 #include "gemv_lut.h"
+#include "binary.h"
 
 namespace {
 
@@ -135,6 +136,46 @@ int bitlinear_forward_subln(const uint8_t* packed, const float* gamma, const voi
   // general case: the normalising quantiser, then the forward, both on the stream
   if (bl::launch_subln_quant(X, bf16, M, K, gain, eps, Xq, scale, s) != hipSuccess) return BL_ERR_HIP;
   return bitlinear_forward(packed, gamma, Xq, scale, M, N, K, Y, acc, stream);
+}
+
+int64_t bitlinear_kb_pad(int64_t K) { return K < 1 ? -1 : bl::kb_pad(K); }
+int64_t bitlinear_packed_bytes_binary(int64_t N, int64_t K) {
+  return (N < 1 || K < 1) ? -1 : bl::packed_bytes_binary(N, K);
+}
+
+int bitlinear_quantize_weights_binary(const float* W, int64_t N, int64_t K, uint8_t* packed, float* beta,
+                                      void* workspace, int64_t ws_bytes, void* stream) {
+  if (!W || !packed || !beta || !workspace) return BL_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim) return BL_ERR_INVALID_ARG;
+  if (N > kMaxCount / K) return BL_ERR_UNSUPPORTED;
+  if (ws_bytes < bl::kWqWorkspaceBytes) return BL_ERR_INVALID_ARG;
+  if (!aligned(W, 4) || !aligned(packed, 16) || !aligned(beta, 4) || !aligned(workspace, 8)) return BL_ERR_INVALID_ARG;
+  return hip_status(
+      bl::launch_weight_quant_binary(W, N, K, packed, beta, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward_binary(const uint8_t* packed, const float* beta, const int8_t* Xq, const float* absmax,
+                             int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream) {
+  if (!packed || !beta || !Xq || !absmax || (!Y && !acc)) return BL_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  if (!aligned(packed, 16) || !aligned(Xq, 16) || !aligned(beta, 4) || !aligned(absmax, 4) ||
+      (Y && !aligned(Y, 4)) || (acc && !aligned(acc, 4)))
+    return BL_ERR_INVALID_ARG;
+  if (!bl::plan_gemv_bin(M, N, K).ok) return BL_ERR_UNSUPPORTED;
+  return hip_status(bl::launch_gemv_bin(packed, beta, Xq, absmax, M, N, K, Y, acc, static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_forward_binary_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]) {
+  if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
+  const bl::BinPlan p = bl::plan_gemv_bin(M, N, K);
+  if (!p.ok) return BL_ERR_UNSUPPORTED;
+  out[0] = 5;
+  out[1] = (int32_t)p.groups;
+  out[2] = p.waves * 64;
+  out[3] = 1;
+  out[4] = p.run;
+  out[5] = 0;
+  return BL_OK;
 }
 
 int bitlinear_forward_lut(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,

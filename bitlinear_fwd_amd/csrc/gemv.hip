@@ -34,6 +34,7 @@
 //                the weight loads (vector-memory loads retire in order, so their wait
 //                does not wait for the weights).
 #include "bl_internal.h"
+#include "decode_common.h"
 
 #include <algorithm>
 
@@ -42,14 +43,6 @@ namespace {
 
 constexpr int kMaxLdsActBytes = 48 * 1024;
 constexpr int64_t kMaxFusedElems = 8192;  // M*K limit of the one-kernel quantise + decode
-
-__device__ __forceinline__ uint32_t word_of(const uint4& w, int i) {
-  return i == 0 ? w.x : (i == 1 ? w.y : (i == 2 ? w.z : w.w));
-}
-
-__device__ __forceinline__ uint4 load_nt(const uint4* p) {
-  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p)));
-}
 
 // Sum the W waves' partial tiles (red[w][j][lane]) and write y / acc for row block j.
 template <int W, int RB>
@@ -379,19 +372,6 @@ struct MatGroup {
 __device__ __forceinline__ float gated_relu2(float g, float u) {
   const float r = g > 0.0f ? g : 0.0f;
   return r * r * u;
-}
-
-template <int s>
-__device__ __forceinline__ int row_shl(int v) {
-  if constexpr (s == 0) return v;
-  else return __builtin_amdgcn_mov_dpp(v, 0x100 + s, 0xF, 0xF, true);
-}
-
-// One token: the A operand of step (u, i) only needs piece 4 u + i in lane 0 of each row,
-// and a 64-bit DPP row_newbcast copies that lane to the whole row in two moves.
-template <int n>
-__device__ __forceinline__ uint64_t row_bcast64(uint64_t v) {
-  return (uint64_t)__builtin_amdgcn_update_dpp((long)0, (long)v, 0x150 + n, 0xF, 0xF, false);
 }
 
 // Work-group barrier that only orders LDS: unlike __syncthreads() it carries no release

@@ -16,6 +16,7 @@
 // column group g; the partial sums are reduced over g by shuffles and over the waves in
 // LDS, then rescaled as in the other decode kernels.
 #include "gemv_lut.h"
+#include "decode_common.h"
 
 namespace bl {
 namespace {
@@ -26,15 +27,6 @@ constexpr int kPairBytes = 32;  // 16 int16 entries
 // in four different 16-bank ranges instead of on the same banks.
 constexpr int kBlockBytes = 8 * kPairBytes + 16;
 constexpr int kTileTableBytes = 16 * kBlockBytes;  // 16 blocks per 256-column tile
-
-__device__ __forceinline__ uint4 load_weights_nt(const uint4* p) {
-  const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
-  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
-}
-
-__device__ __forceinline__ uint32_t word_at(const uint4& w, int i) {
-  return i == 0 ? w.x : (i == 1 ? w.y : (i == 2 ? w.z : w.w));
-}
 
 __device__ __forceinline__ int sbyte(uint32_t word, int b) { return (int)(int8_t)(word >> (8 * b)); }
 
@@ -84,7 +76,7 @@ __global__ __launch_bounds__(1024) void k_gemv_lut(const uint8_t* __restrict__ p
   uint4 w[T];
   static_for<T>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
-    w[t] = load_weights_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
+    w[t] = load_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
   });
 
   // tables: block (m, t, q) = (m T + t) 16 + q holds the pairs (h, b), h = 0, 1 and b = 0..3,
@@ -123,7 +115,7 @@ __global__ __launch_bounds__(1024) void k_gemv_lut(const uint8_t* __restrict__ p
     const bool live = c0 + t < chunks;  // tiles past the matrix contribute nothing
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t word = live ? word_at(w[t], i) : 0u;  // nibble 0 looks up entry 0 = 0
+      const uint32_t word = live ? word_of(w[t], i) : 0u;  // nibble 0 looks up entry 0 = 0
       const uint8_t* base = tab + (size_t)(t * 16 + 4 * g + i) * kBlockBytes;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {

@@ -12,6 +12,7 @@
 // so the bins are identical for any schedule.  One thread then forms the exact 320-bit
 // sum and divides it by N*K with round-to-nearest-even into fp32.
 #include "bl_internal.h"
+#include "binary.h"
 
 namespace bl {
 namespace {
@@ -183,7 +184,60 @@ __global__ __launch_bounds__(256) void k_ternarise_pack(const float* __restrict_
   reinterpret_cast<uint4*>(packed + tile * kTileBytes)[slot] = make_uint4(word[0], word[1], word[2], word[3]);
 }
 
+// 1-bit binary variant: one thread per 16-byte slot (g, r) of a 1024-byte binary tile
+// (layout in binary.h): word j covers column group g of the 256-column half s = j / 2,
+// steps i = 2 (j % 2) and 2 (j % 2) + 1; column e of step i sits at bit
+// 8 (e % 4) + 4 (i % 2) + e / 4.
+__global__ __launch_bounds__(256) void k_binarise_pack(const float* __restrict__ W, int64_t N, int64_t K,
+                                                       int64_t n_tiles, int64_t chunks_b,
+                                                       uint8_t* __restrict__ packed) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tile = t >> 6;
+  if (tile >= n_tiles) return;
+  const int slot = (int)(t & 63);
+  const int64_t nb = tile / chunks_b, c = tile - nb * chunks_b;
+  const int64_t n = nb * kTileRows + (slot & 15);
+  const int g = slot >> 4;
+  uint32_t word[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int s = j >> 1;
+    uint32_t x = 0;
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * (j & 1) + ii;
+      const int64_t k0 = c * kBinTileCols + 256 * s + 64 * g + 16 * i;
+      for (int e = 0; e < 16; ++e) {
+        const int64_t k = k0 + e;
+        const bool plus = n < N && k < K && !(W[n * K + k] < 0.0f);
+        x |= (uint32_t)plus << (8 * (e & 3) + 4 * ii + (e >> 2));
+      }
+    }
+    word[j] = x;
+  }
+  reinterpret_cast<uint4*>(packed + tile * kTileBytes)[slot] = make_uint4(word[0], word[1], word[2], word[3]);
+}
+
 }  // namespace
+
+hipError_t launch_weight_quant_binary(const float* W, int64_t N, int64_t K, uint8_t* packed, float* beta,
+                                      void* workspace, hipStream_t s) {
+  unsigned long long* bins = static_cast<unsigned long long*>(workspace);
+  float* inv = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWqBins * 8);
+  const int64_t count = N * K;
+  const int vec4_all = ((reinterpret_cast<uintptr_t>(W) & 15u) == 0) ? 1 : 0;
+  hipLaunchKernelGGL(k_wq_clear, dim3(1), dim3(64), 0, s, bins);
+  int64_t blocks = (count / 4 + kBinThreads - 1) / kBinThreads;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_wq_bins, dim3((unsigned)blocks), dim3(kBinThreads), 0, s, W, count, vec4_all, bins);
+  hipLaunchKernelGGL(k_wq_finalize, dim3(1), dim3(64), 0, s, bins, (uint64_t)count, beta, inv);
+  const int64_t chunks_b = kb_pad(K) / kBinTileCols;
+  const int64_t n_tiles = n_pad(N) / kTileRows * chunks_b;
+  const int64_t threads = n_tiles * 64;
+  hipLaunchKernelGGL(k_binarise_pack, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, W, N, K, n_tiles,
+                     chunks_b, packed);
+  return hipGetLastError();
+}
 
 hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
                                void* workspace, hipStream_t s) {

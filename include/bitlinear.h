@@ -249,6 +249,36 @@ int bitlinear_forward_lut(const uint8_t* packed, const float* gamma, const int8_
 int bitlinear_forward_lut_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]);
 
 /*
+ * 1-bit sign-binary weights, the contrast point to the ternary path (lpnh.cn news
+ * 2861808, section 2.1: binary weights sign(W) with a scaling factor that compensates the
+ * lost magnitude).  Readings: q = +1 for W >= 0 (including -0.0), -1 for W < 0; the scale
+ * beta is the exact mean |W| (as gamma); activations, contraction and rescale are steps
+ * 2-4 with beta in place of gamma.  One bit per weight: half the packed bytes.
+ *
+ * Binary layout.  N_pad = roundup(N, 16), KB_pad = roundup(K, 512); N_pad * KB_pad / 8
+ * bytes of 1024-byte tiles, tile (nb, c) at (nb * (KB_pad / 512) + c) * 1024 covering rows
+ * 16 nb .. 16 nb + 15 and columns 512 c .. 512 c + 511.  Row r, column offset kk: with
+ * s = kk / 256, g = (kk % 256) / 64, i = (kk % 64) / 16, e = kk % 16, the little-endian
+ * 32-bit word at byte 16 * (16 g + r) + 4 * (2 s + i / 2) holds the weight at bit
+ * 8 * (e % 4) + 4 * (i % 2) + e / 4: 1 = +1, 0 = -1.  Bits outside N x K are 0.
+ *
+ * bitlinear_quantize_weights_binary: arguments as bitlinear_quantize_weights (packed:
+ *   bitlinear_packed_bytes_binary(N, K) bytes, 16-byte aligned; beta: device fp32).
+ * bitlinear_forward_binary: arguments as bitlinear_forward with the binary buffer and
+ *   beta; M = 1..4 and K within the plan (bitlinear_forward_binary_plan), otherwise
+ *   BL_ERR_UNSUPPORTED and nothing is enqueued.
+ */
+int64_t bitlinear_kb_pad(int64_t K);                          /* roundup(K, 512)            */
+int64_t bitlinear_packed_bytes_binary(int64_t N, int64_t K);  /* N_pad * KB_pad / 8         */
+int bitlinear_quantize_weights_binary(const float* W, int64_t N, int64_t K, uint8_t* packed, float* beta,
+                                      void* workspace, int64_t ws_bytes, void* stream);
+int bitlinear_forward_binary(const uint8_t* packed, const float* beta, const int8_t* Xq, const float* absmax,
+                             int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream);
+/* Host-only: out[0] = 5, out[1] = workgroups, out[2] = threads, out[3] = 1, out[4] = binary
+ * tiles per wave, out[5] = 0; BL_ERR_UNSUPPORTED where the shape does not fit. */
+int bitlinear_forward_binary_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]);
+
+/*
  * Host-only description of the launch bitlinear_forward would make for (M, N, K); no
  * device work.  out[0] = kernel (1 = decode, 2 = prefill), out[1] = workgroups,
  * out[2] = threads per workgroup, out[3] = decode: 16-row output blocks per workgroup,

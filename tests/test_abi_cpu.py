@@ -248,3 +248,20 @@ def test_lut_plan_and_validation():
     assert L.bitlinear_forward_lut(None, FAKE, FAKE, FAKE, 1, 16, 256, FAKE, None, None) == bl.BL_ERR_INVALID_ARG
     assert L.bitlinear_forward_lut(FAKE, FAKE, FAKE, FAKE, 1, 16, 256, None, None, None) == bl.BL_ERR_INVALID_ARG
     assert L.bitlinear_forward_lut(FAKE, FAKE, FAKE, FAKE, 5, 16, 256, FAKE, None, None) == bl.BL_ERR_UNSUPPORTED
+
+
+def test_binary_sizes_plan_and_validation():
+    L = bl.lib()
+    assert bl.kb_pad(6912) == 7168 and bl.kb_pad(512) == 512 and L.bitlinear_kb_pad(0) == -1
+    assert bl.packed_bytes_binary(28672, 8192) == 28672 * 8192 // 8
+    assert bl.packed_bytes_binary(17, 300) == 32 * 512 // 8
+    assert bl.forward_binary_plan(1, 6912, 2560)["kernel"] == "binary"
+    assert bl.forward_binary_plan(5, 64, 512) is None
+    ws = bl.wq_workspace_bytes(16, 512)
+    q = L.bitlinear_quantize_weights_binary
+    assert q(None, 16, 512, FAKE, FAKE, FAKE, ws, None) == bl.BL_ERR_INVALID_ARG
+    assert q(FAKE, 16, 512, FAKE + 8, FAKE, FAKE, ws, None) == bl.BL_ERR_INVALID_ARG
+    assert q(FAKE, 16, 512, FAKE, FAKE, FAKE, ws - 1, None) == bl.BL_ERR_INVALID_ARG
+    f = L.bitlinear_forward_binary
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 16, 512, None, None, None) == bl.BL_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 5, 16, 512, FAKE, None, None) == bl.BL_ERR_UNSUPPORTED
