@@ -29,8 +29,8 @@ packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
                into one bitlinear_forward_grouped call ("1g", "2g"), and the same
                workloads behind the sub-layer RMS normalisation ("1s", "1gs", "2s"), and the
                gate/up pair with the squared-ReLU gating epilogue in one launch ("1f", "1fs");
-               the two-kernel int8 path ("1i") and the table-lookup decode ("1l") for
-               comparison with the matrix-core decode;
+               the two-kernel int8 path ("1i"), the table-lookup decode ("1l") and the 1-bit
+               sign-binary variant ("1b", "4b") for comparison with the ternary decode;
   ceilings     measured on this GPU by the library's probes: HBM read rate with the decode
                access pattern at 58.7 MB and 4.4 MB per launch, and the int8 MFMA rate;
                roofline.frac_of_measured_ceiling sets the dominant kernel against the
@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
-    ap.add_argument("--legs", default="1g,1s,1gs,1f,1fs,1i,1l,2,2g,2s,3,4",
+    ap.add_argument("--legs", default="1g,1s,1gs,1f,1fs,1i,1l,1b,2,2g,2s,3,4,4b",
                     help="other workloads timed into 'legs' ('' for none); a trailing g times the workload "
                          "with the projections of one input grouped into one call")
     ap.add_argument("--graph", action="store_true",
@@ -75,14 +75,14 @@ def parse():
 class Matrix:
     """One quantised weight matrix with its pre-drawn activations."""
 
-    def __init__(self, bl, synth, wl, layer, midx, k, n, m, dev):
+    def __init__(self, bl, synth, wl, layer, midx, k, n, m, dev, binary=False):
         w = synth.latent_weights(n, k, seed=synth.weight_seed(wl.index, layer, midx), device=dev)
-        self.packed, self.gamma = bl.quantize_weights(w)
+        self.packed, self.gamma = bl.quantize_weights_binary(w) if binary else bl.quantize_weights(w)
         del w
         self.x = synth.activations(m, k, seed=synth.act_seed(wl.index, layer, midx), dtype=wl.act_dtype,
                                    device=dev, outlier_p=wl.outlier_p, outlier_mult=wl.outlier_mult)
         self.n, self.k, self.m = n, k, m
-        self.bytes = bl.packed_bytes(n, k)
+        self.bytes = bl.packed_bytes_binary(n, k) if binary else bl.packed_bytes(n, k)
         self.ops = 2 * m * n * k
 
 
@@ -98,12 +98,13 @@ class Workload:
         self.bl = bl
         self.subln = subln  # sub-layer RMS normalisation (per-matrix gain) in front of the quantiser
         # "fused": one call per matrix where the library fuses it; "int8": the quantiser, then
-        # bitlinear_forward; "lut": the quantiser, then the table-lookup forward
+        # bitlinear_forward; "lut": the quantiser, then the table-lookup forward; "binary":
+        # 1-bit sign-binary weights, the quantiser, then bitlinear_forward_binary
         self.path = path
         self.sweep = self.wl.layers > 1  # a step sweeps every layer instead of one set
         nsets = self.wl.layers if self.sweep else self.wl.rotate_sets
-        self.sets = [[Matrix(bl, synth, self.wl, s, i, k, n, m, dev) for i, (_, k, n) in enumerate(self.wl.matrices)]
-                     for s in range(nsets)]
+        self.sets = [[Matrix(bl, synth, self.wl, s, i, k, n, m, dev, binary=path == "binary")
+                      for i, (_, k, n) in enumerate(self.wl.matrices)] for s in range(nsets)]
         for s, st in enumerate(self.sets):
             for i, mat in enumerate(st):
                 mat.gain = synth.subln_gain(mat.k, synth.gain_seed(idx, s, i), device=dev) if subln else None
@@ -150,6 +151,8 @@ class Workload:
                     bl.quantize_acts(mat.x, xq, a)
             if self.path == "lut":
                 bl.forward_lut(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
+            elif self.path == "binary":
+                bl.forward_binary(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
             else:
                 bl.forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y=y)
 
@@ -222,6 +225,8 @@ class Workload:
                         calls.append(bl.prepare_quantize_acts(mat.x, xq, a))
                 if self.path == "lut":
                     calls.append(bl.prepare_forward_lut(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y))
+                elif self.path == "binary":
+                    calls.append(bl.prepare_forward_binary(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y))
                 else:
                     calls.append(bl.prepare_forward(mat.packed, mat.gamma, xq, a, mat.n, mat.k, y))
         return calls
@@ -264,17 +269,18 @@ class Workload:
 # same process (--copy-calibration).  A figure holds only for the kernel source it was taken
 # on: the sha256 of the kernel's source files is stored with it, and a mismatch reports null.
 KERNEL_SOURCES = {
-    "decode": ("bitlinear_fwd_amd/csrc/gemv.hip", "bitlinear_fwd_amd/csrc/bl_internal.h"),
+    "decode": ("bitlinear_fwd_amd/csrc/gemv.hip", "bitlinear_fwd_amd/csrc/decode_common.h",
+               "bitlinear_fwd_amd/csrc/bl_internal.h"),
     "prefill": ("bitlinear_fwd_amd/csrc/gemm.hip", "bitlinear_fwd_amd/csrc/bl_internal.h"),
 }
 TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
-    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.4 KiB (x1.99980),
+    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.3 KiB (x1.99980),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4595859, "fetch_kib": 2231.67, "write_kib": 25.27, "sha": "33dffa12a86c1e50"},
-    (2, 16): {"bytes_per_launch": 3158885, "fetch_kib": 1440.86, "write_kib": 203.43, "sha": "33dffa12a86c1e50"},
-    (3, 2048): {"bytes_per_launch": 107230687, "fetch_kib": 33418.15, "write_kib": 37888.00, "sha": "1bcc1b322725b312"},
-    (4, 1): {"bytes_per_launch": 59277405, "fetch_kib": 28902.00, "write_kib": 90.00, "sha": "33dffa12a86c1e50"},
+    (1, 1): {"bytes_per_launch": 4596272, "fetch_kib": 2231.87, "write_kib": 25.27, "sha": "74d285a470665523"},
+    (2, 16): {"bytes_per_launch": 3159765, "fetch_kib": 1441.29, "write_kib": 203.43, "sha": "74d285a470665523"},
+    (3, 2048): {"bytes_per_launch": 107178725, "fetch_kib": 33392.75, "write_kib": 37888.00, "sha": "c04444811925d07f"},
+    (4, 1): {"bytes_per_launch": 59272331, "fetch_kib": 28899.50, "write_kib": 90.00, "sha": "74d285a470665523"},
 }
 
 
@@ -543,13 +549,14 @@ def main():
         flags = tok.lstrip("0123456789")
         idx = int(tok[: len(tok) - len(flags)])
         grouped, subln, gated = "g" in flags, "s" in flags, "f" in flags
-        path = "lut" if "l" in flags else ("int8" if "i" in flags else "fused")
+        path = "lut" if "l" in flags else ("int8" if "i" in flags else ("binary" if "b" in flags else "fused"))
         if idx == args.workload and not flags:
             continue
         if (grouped and idx not in GROUPINGS) or (gated and idx != 1):
             continue
         for m in synth.WORKLOADS[idx].m_list:
-            if path == "lut" and any(bl.forward_lut_plan(m, n, k) is None for _, k, n in synth.WORKLOADS[idx].matrices):
+            plan_of = {"lut": bl.forward_lut_plan, "binary": bl.forward_binary_plan}.get(path)
+            if plan_of and any(plan_of(m, n, k) is None for _, k, n in synth.WORKLOADS[idx].matrices):
                 continue
             w = Workload(bl, synth, idx, m, dev, subln=subln, path=path)
             if grouped:
@@ -577,11 +584,13 @@ def main():
             elif path != "fused":
                 l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
                 legs[key] = leg_summary(w, lms, l_ms, l_b, l_o)
-                legs[key]["kernel"] = ("k_gemv_lut (table-lookup decode)" if path == "lut"
-                                       else dominant_kernel(w))
+                legs[key]["kernel"] = {"lut": "k_gemv_lut (table-lookup decode)",
+                                       "binary": "k_gemv_bin (1-bit sign-binary decode)"}.get(path) or dominant_kernel(w)
                 legs[key]["note"] = ("activation quantiser, then the " +
-                                     ("table-lookup forward (bitlinear_forward_lut)" if path == "lut"
-                                      else "int8 forward (bitlinear_forward)") +
+                                     {"lut": "table-lookup forward (bitlinear_forward_lut)",
+                                      "binary": "1-bit sign-binary forward (bitlinear_forward_binary; "
+                                                "packed_GBps counts the 1-bit bytes)"}.get(
+                                         path, "int8 forward (bitlinear_forward)") +
                                      "; forward_launch_* time the forward launches alone")
             elif subln:
                 legs[key] = leg_summary(w, lms, None, None, None)
