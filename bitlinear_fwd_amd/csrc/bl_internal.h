@@ -82,6 +82,8 @@ struct GemvPlan {
   bool dpp = false;     // activations held in registers, shifted into place by DPP (M <= 4,
                         // or 9..16 tokens on rows of at most 4096 elements)
   int run = 0;          // dpp: K tiles per wave (all loads of a wave issued at once)
+  bool early = false;   // fused dpp with at most one workgroup per compute unit: weight
+                        // loads issued before the activation barrier
   int stage = 0;        // LDS staging: 16-byte activation pieces per thread
   bool ok = true;       // the requested activation source is supported by this plan
   int64_t groups = 0;   // workgroups

@@ -381,9 +381,12 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Activation sources of the decode kernels: 0 = int8 xq, 1 / 2 = bf16 / fp32 x, 3 / 4 =
-// bf16 / fp32 x through the sub-layer normalisation.
-constexpr bool src_bf16(int src) { return src == 1 || src == 3; }
-constexpr bool src_norm(int src) { return src >= 3; }
+// bf16 / fp32 x through the sub-layer normalisation.  kSrcEarly added to 1 / 2 selects the
+// fused form that issues its weight loads before the activation barrier.
+constexpr int kSrcEarly = 8;
+constexpr bool src_bf16(int src) { return (src & 7) == 1 || (src & 7) == 3; }
+constexpr bool src_norm(int src) { return (src & 7) >= 3; }
+constexpr bool src_early(int src) { return (src & kSrcEarly) != 0; }
 
 template <int MM, int kSrc>
 struct DppShape {
@@ -467,8 +470,12 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   }
   // The fused form issues its weight loads only after the absmax barrier: loads issued
   // earlier by any wave of the compute unit delay the activation loads queued behind
-  // them, and with them the barrier (measured: up to 5 us on 58.7 MB matrices).
-  constexpr int kEarly = kSrc == 0 ? T : 0;
+  // them, and with them the barrier (measured: up to 5 us on 58.7 MB matrices).  With one
+  // workgroup per compute unit (kSrcEarly, chosen by the planner) nothing else queues on
+  // the unit: after a barrier that only orders the issue (every wave's activation loads
+  // go first) the weights are issued before the activation barrier and stream during it.
+  constexpr int kEarly = (kSrc == 0 || src_early(kSrc)) ? T : 0;
+  if constexpr (src_early(kSrc)) asm volatile("s_barrier" ::: "memory");
   uint4 w[T];
   uint4 w2[kPair ? T : 1];
   static_for<kEarly>([&](auto tc) {
@@ -1029,6 +1036,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
         p.waves = (int)((chunks + t - 1) / t);
         p.groups = rblocks;
         p.ok = true;
+        // measured on 2B-class shapes: 160 workgroups 4.82 -> 4.38 us; 432 workgroups
+        // 4.60 -> 4.91 us (two per unit queue behind each other's weights)
+        p.early = (src == 1 || src == 2) && rblocks <= 256;
         return p;
       }
     }
@@ -1093,6 +1103,9 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const vo
     if (!p.dpp || !p.ok) return hipErrorInvalidConfiguration;  // not planned: the caller checks the plan
     return bf16 ? launch_dpp_run<3>(p.run, (int)M, p.waves, a, s) : launch_dpp_run<4>(p.run, (int)M, p.waves, a, s);
   }
+  if (p.dpp && p.early)
+    return bf16 ? launch_dpp_run<1 + kSrcEarly>(p.run, (int)M, p.waves, a, s)
+                : launch_dpp_run<2 + kSrcEarly>(p.run, (int)M, p.waves, a, s);
   if (p.dpp) return bf16 ? launch_dpp_run<1>(p.run, (int)M, p.waves, a, s) : launch_dpp_run<2>(p.run, (int)M, p.waves, a, s);
   if (bf16) return launch_lds_w<1>(p.waves, p.stage, a, s);
   return launch_lds_w<2>(p.waves, p.stage, a, s);
