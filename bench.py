@@ -277,10 +277,10 @@ TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
     # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.3 KiB (x1.99980),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4596272, "fetch_kib": 2231.87, "write_kib": 25.27, "sha": "74d285a470665523"},
-    (2, 16): {"bytes_per_launch": 3159765, "fetch_kib": 1441.29, "write_kib": 203.43, "sha": "74d285a470665523"},
-    (3, 2048): {"bytes_per_launch": 107178725, "fetch_kib": 33392.75, "write_kib": 37888.00, "sha": "c04444811925d07f"},
-    (4, 1): {"bytes_per_launch": 59272331, "fetch_kib": 28899.50, "write_kib": 90.00, "sha": "74d285a470665523"},
+    (1, 1): {"bytes_per_launch": 4595590, "fetch_kib": 2231.53, "write_kib": 25.27, "sha": "e57aa3164cde6246"},
+    (2, 16): {"bytes_per_launch": 3159911, "fetch_kib": 1441.36, "write_kib": 203.43, "sha": "e57aa3164cde6246"},
+    (3, 2048): {"bytes_per_launch": 107265654, "fetch_kib": 33435.20, "write_kib": 37888.00, "sha": "0d6bafb972a121db"},
+    (4, 1): {"bytes_per_launch": 59277962, "fetch_kib": 28902.25, "write_kib": 90.00, "sha": "e57aa3164cde6246"},
 }
 
 
