@@ -18,6 +18,8 @@
 #include "gemv_lut.h"
 #include "decode_common.h"
 
+#include <atomic>
+
 namespace bl {
 namespace {
 
@@ -156,12 +158,20 @@ hipError_t launch_lut(const LutPlan& p, const uint8_t* packed, const float* gamm
                       const float* absmax, int M, int N, int K_pad, int chunks, float* Y, int32_t* acc,
                       hipStream_t s) {
   auto kern = k_gemv_lut<T, MM>;
-  static bool raised = false;  // per instantiation: allow dynamic LDS beyond 64 KiB once
-  if (p.lds_bytes > 64 * 1024 && !raised) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLutBytes);
+  // per instantiation and device: allow dynamic LDS beyond 64 KiB (set once; a repeated
+  // set from a concurrent first call is harmless)
+  static std::atomic<uint64_t> raised{0};
+  if (p.lds_bytes > 64 * 1024) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    raised = true;
+    const uint64_t bit = uint64_t(1) << (dev & 63);
+    if (!(raised.load(std::memory_order_relaxed) & bit)) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kMaxLutBytes);
+      if (e != hipSuccess) return e;
+      raised.fetch_or(bit, std::memory_order_relaxed);
+    }
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)p.groups), dim3(p.waves * 64), (unsigned)p.lds_bytes, s, packed, gamma, Xq,
                      absmax, M, N, K_pad, chunks, Y, acc);
