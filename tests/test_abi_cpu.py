@@ -265,3 +265,38 @@ def test_binary_sizes_plan_and_validation():
     f = L.bitlinear_forward_binary
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 16, 512, None, None, None) == bl.BL_ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, FAKE, 5, 16, 512, FAKE, None, None) == bl.BL_ERR_UNSUPPORTED
+
+
+def test_launch_plans_cover_every_tile():
+    # host-only sweep of every planner: a plan's waves x tiles per wave must cover all K
+    # tiles, and its workgroups all row blocks, or outputs would silently go missing
+    shapes_k = [1, 8, 255, 256, 257, 1000, 2560, 4096, 6912, 8192, 12000, 28672, 40000]
+    shapes_n = [1, 16, 17, 640, 2560, 6912, 28672]
+    for m in (1, 2, 3, 4, 5, 8, 16):
+        for k in shapes_k:
+            chunks = bl.k_pad(k) // 256
+            chunks_b = bl.kb_pad(k) // 512
+            for n in shapes_n:
+                rblocks = bl.n_pad(n) // 16
+                plans = [("forward", bl.forward_plan(m, n, k))]
+                for dt in ("bf16", "f32"):
+                    plans.append(("fused", bl.forward_fused_plan(m, n, k, dt)))
+                    plans.append(("subln", bl.forward_subln_plan(m, n, k, dt)))
+                    plans.append(("gated", bl.forward_gated_relu2_plan(m, n, k, dt, True)))
+                for name, p in plans:
+                    assert p["workgroups"] >= 1 and p["threads"] % 64 == 0 and 64 <= p["threads"] <= 1024, (name, p)
+                    if p["kernel"] in ("fused", "decode") and p.get("acts") == "registers":
+                        waves = p["threads"] // 64
+                        assert waves * p["tiles_per_wave"] >= chunks, (name, m, n, k, p)
+                        assert waves <= 16 and (waves - 1) * p["tiles_per_wave"] < chunks, (name, m, n, k, p)
+                        assert p["workgroups"] * p["row_blocks"] >= rblocks, (name, m, n, k, p)
+                lut = bl.forward_lut_plan(m, n, k)
+                if lut is not None:
+                    waves = lut["threads"] // 64
+                    assert m <= 4 and waves * lut["tiles_per_wave"] >= chunks and lut["workgroups"] == rblocks
+                    assert lut["lds_bytes"] == waves * lut["tiles_per_wave"] * m * 4352 <= 148 * 1024
+                binp = bl.forward_binary_plan(m, n, k)
+                if binp is not None:
+                    waves = binp["threads"] // 64
+                    assert m <= 4 and waves <= 16 and waves * binp["tiles_per_wave"] >= chunks_b
+                    assert binp["workgroups"] == rblocks

@@ -135,3 +135,59 @@ def test_two_streams_run_concurrently():
     for res, ref in zip(results, alone):
         for y in res:
             check_equal(host(y).view(np.uint32), host(ref).view(np.uint32), "two streams")
+
+
+def test_newer_entry_points_replay_in_a_graph():
+    # the sub-layer normalisation (fused and two-kernel), the gated pair (fused and general
+    # path with its workspace), the table-lookup and the binary decode, captured together
+    print("case: graph replay of subln, gated pair, lut and binary calls", flush=True)
+    k, n = 2560, 6912
+    w = synth.latent_weights(n, k, seed=9500, device=DEV)
+    packed, gamma = bl.quantize_weights(w)
+    packed_b, beta = bl.quantize_weights_binary(w)
+    w2 = synth.latent_weights(n, k, seed=9501, device=DEV)
+    packed2, gamma2 = bl.quantize_weights(w2)
+    del w, w2
+    gain = synth.subln_gain(k, 9502, device=DEV)
+    x1 = synth.activations(1, k, seed=9503, dtype=torch.bfloat16, device=DEV)
+    x8 = synth.activations(8, k, seed=9504, dtype=torch.bfloat16, device=DEV)
+    bufs = {}
+
+    def buf(name, shape, dtype=torch.float32):
+        if name not in bufs:
+            bufs[name] = torch.empty(shape, dtype=dtype, device=DEV)
+        return bufs[name]
+
+    ws = torch.empty(bl.lib().bitlinear_gated_relu2_workspace_bytes(8, n), dtype=torch.uint8, device=DEV)
+    outs = ["y_subln1", "y_subln8", "h1", "h8", "y_lut", "y_bin"]
+
+    def step():
+        xq1, a1 = buf("xq1", (1, bl.k_pad(k)), torch.int8), buf("a1", (1,))
+        xq8, a8 = buf("xq8", (8, bl.k_pad(k)), torch.int8), buf("a8", (8,))
+        bl.forward_subln(packed, gamma, x1, n, k, gain, 1e-5, y=buf("y_subln1", (1, n)), xq=xq1, scale=a1)
+        bl.subln_quantize_acts(x8, gain, 1e-5, xq8, a8)
+        bl.forward(packed, gamma, xq8, a8, n, k, y=buf("y_subln8", (8, n)))
+        bl.forward_gated_relu2((packed, gamma), (packed2, gamma2), x1, n, k, subln=True, gain=gain, h=buf("h1", (1, n)),
+                               xq=xq1, scale=a1)
+        bl.forward_gated_relu2((packed, gamma), (packed2, gamma2), x8, n, k, h=buf("h8", (8, n)), xq=xq8, scale=a8,
+                               workspace=ws)
+        bl.quantize_acts(x1, xq1, a1)
+        bl.forward_lut(packed, gamma, xq1, a1, n, k, y=buf("y_lut", (1, n)))
+        bl.forward_binary(packed_b, beta, xq1, a1, n, k, y=buf("y_bin", (1, n)))
+
+    step()
+    torch.cuda.synchronize()
+    eager = {o: bufs[o].clone() for o in outs}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for o in outs:
+            bufs[o].fill_(float("nan"))
+        scratch = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(scratch)
+        for o in outs:
+            check_equal(host(bufs[o]).view(np.uint32), host(eager[o]).view(np.uint32), f"{o} replay {rep}")
