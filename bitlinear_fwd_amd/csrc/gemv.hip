@@ -989,6 +989,7 @@ hipError_t launch_pair_run(int T, int M, int W, const Args& a, const uint8_t* p2
 
 template <int T, int MM, int RB>
 hipError_t launch_dppm(int W, const Args& a, hipStream_t s) {
+  if (W * RB > 16 || (int64_t)W * T < a.chunks) return hipErrorInvalidConfiguration;  // LDS partials, coverage
   const unsigned groups = (unsigned)((a.rblocks + RB - 1) / RB);
   hipLaunchKernelGGL((k_gemv_dppm<T, MM, RB>), dim3(groups), dim3(W * 64), 0, s, a.packed, a.gamma,
                      static_cast<const int8_t*>(a.X), a.absmax, a.M, a.N, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc);
@@ -1062,9 +1063,10 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   p.lds_act = false;
   p.rb = 1;
   p.ok = src == 0;  // the register paths read int8 activations only
-  if (M > 8 && chunks <= 16) {
-    // 9..16 tokens on short rows: two-tile register runs, activation registers shared by
-    // two row blocks once there are enough blocks to fill the chip
+  if (M > 4 && chunks <= 16) {
+    // 5..16 tokens on short rows: two-tile register runs (a token group of 8 or 16),
+    // activation registers shared by two row blocks once there are enough blocks to fill
+    // the chip (measured at M = 8, 2560 -> 6912: 5.49 us per-tile loads, 4.40 us here)
     p.dpp = true;
     p.run = 2;
     p.rb = rblocks >= 384 ? 2 : 1;
@@ -1084,7 +1086,8 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
   const GemvPlan p = plan_gemv(M, N, K, 0);
   Args a{packed, gamma, Xq, absmax, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
          (int)(n_pad(N) / kTileRows), Y, acc, nullptr, nullptr};
-  if (p.dpp && M > 4) return p.rb == 2 ? launch_dppm<2, 16, 2>(p.waves, a, s) : launch_dppm<2, 16, 1>(p.waves, a, s);
+  if (p.dpp && M > 8) return p.rb == 2 ? launch_dppm<2, 16, 2>(p.waves, a, s) : launch_dppm<2, 16, 1>(p.waves, a, s);
+  if (p.dpp && M > 4) return p.rb == 2 ? launch_dppm<2, 8, 2>(p.waves, a, s) : launch_dppm<2, 8, 1>(p.waves, a, s);
   if (p.dpp) return launch_dpp_run<0>(p.run, (int)M, p.waves, a, s);
   if (p.rb == 4) return launch_reg_w<4, 1, 2>(p.waves, a, s);
   if (p.rb == 2) return launch_reg_w<2, 1, 2>(p.waves, a, s);

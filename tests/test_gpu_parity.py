@@ -193,13 +193,15 @@ def test_forward_decode(m, n, k):
     (3, 1000, 2560, "registers", 1, 2),
     # K beyond 16 waves x 16 tiles: activations loaded with each tile
     (4, 40, 70000, "per-tile loads", 1, 0),
-    # M = 5..16: activations loaded with each tile, 1/2/4 row blocks per workgroup
-    (5, 8200, 300, "per-tile loads", 2, 0), (8, 2560, 6912, "per-tile loads", 1, 0),
-    (7, 9000, 4100, "per-tile loads", 2, 0), (16, 4200, 9000, "per-tile loads", 1, 0),
-    (6, 20000, 1000, "per-tile loads", 4, 0),
-    # M = 9..16 on rows up to 4096: two-tile register runs, 1 or 2 row blocks per workgroup
+    # M = 5..16 on rows over 4096: activations loaded with each tile, 1/2/4 row blocks
+    (8, 2560, 6912, "per-tile loads", 1, 0), (7, 9000, 4100, "per-tile loads", 2, 0),
+    (16, 4200, 9000, "per-tile loads", 1, 0), (6, 20000, 5000, "per-tile loads", 4, 0),
+    # M = 5..16 on rows up to 4096: two-tile register runs (token group of 8 for M <= 8,
+    # 16 above), 1 or 2 row blocks per workgroup
     (16, 16400, 256, "registers", 2, 2), (12, 16400, 1000, "registers", 2, 2), (9, 300, 512, "registers", 1, 2),
-    (13, 7000, 4096, "registers", 2, 2), (16, 100, 3000, "registers", 1, 2), (11, 6150, 2560, "registers", 2, 2)])
+    (13, 7000, 4096, "registers", 2, 2), (16, 100, 3000, "registers", 1, 2), (11, 6150, 2560, "registers", 2, 2),
+    (5, 8200, 300, "registers", 2, 2), (6, 20000, 1000, "registers", 2, 2), (8, 6912, 2560, "registers", 2, 2),
+    (7, 100, 700, "registers", 1, 2), (8, 33, 4096, "registers", 1, 2)])
 def test_forward_decode_variants(m, n, k, acts, rb, run):
     # every decode-kernel variant against the oracle, including ragged N and K
     plan = bl.forward_plan(m, n, k)
