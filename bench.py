@@ -262,6 +262,15 @@ class Workload:
     def ops_per_step(self):
         return sum(mat.ops for mat in self.step_groups()[0])
 
+    def allin_bytes_per_step(self):
+        """Algorithmic bytes of the whole step: packed weights, the activation input (x in
+        its dtype) and the fp32 outputs of every matrix."""
+        xb = 2 if self._dt() == "bf16" else 4
+        return sum(mat.bytes + mat.m * mat.k * xb + mat.m * mat.n * 4 for mat in self.step_groups()[0])
+
+    def matrices_per_step(self):
+        return len(self.step_groups()[0])
+
 
 # HBM traffic per launch of the dominant kernel, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, averaged over the step's launches), each
@@ -474,12 +483,14 @@ def cpu_baseline(w: Workload, budget_s: float):
     return done_bytes, done_ops, t_used, mats
 
 
-def leg_summary(w: Workload, ms: float, launch_ms, launch_bytes, launch_ops):
+def leg_summary(w: Workload, ms: float, launch_ms, launch_bytes, launch_ops, ceilings=None):
     gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9
     tops = w.ops_per_step() / (ms * 1e-3) / 1e12
     out = {
         "workload": w.wl.name, "M": w.m, "ms_per_step": round(ms, 5),
+        "us_per_matrix": round(ms * 1e3 / w.matrices_per_step(), 3),
         "packed_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "allin_GBps": round(w.allin_bytes_per_step() / (ms * 1e-3) / 1e9, 1),
         "int8_TOPS": round(tops, 2), "mfma_frac": round(tops / I8_PEAK_TOPS, 4),
         "tokens_per_s_eq": round(w.m / (ms * 1e-3), 1),  # every matrix of the step applied once per token
     }
@@ -487,6 +498,13 @@ def leg_summary(w: Workload, ms: float, launch_ms, launch_bytes, launch_ops):
         out["forward_launch_us"] = round(launch_ms * 1e3, 3)
         out["forward_launch_GBps"] = round(launch_bytes / (launch_ms * 1e-3) / 1e9, 1)
         out["forward_launch_TOPS"] = round(launch_ops / (launch_ms * 1e-3) / 1e12, 2)
+        if ceilings:
+            if w.m > 16:
+                out["forward_frac_of_measured_mfma"] = round(out["forward_launch_TOPS"] / ceilings["mfma_int8_TOPS"], 4)
+            else:
+                big = launch_bytes >= 20e6
+                c = ceilings["stream_58.7MB_GBps"] if big else ceilings["stream_4.4MB_GBps"]
+                out["forward_frac_of_measured_stream"] = round(out["forward_launch_GBps"] / c, 4)
     return out
 
 
@@ -544,6 +562,9 @@ def main():
         ceil = ceilings["mfma_int8_TOPS"]
     roof["measured_ceiling"] = ceil
     roof["frac_of_measured_ceiling"] = round(roof["achieved"] / ceil, 4)
+    if decode:
+        roof["note"] = ("algorithmic bytes are the 2-bit packed weights; the information bound of ternary "
+                        "codes, log2(3) bits per weight, is 79 % of them")
     legs = {}
     for tok in [t.strip() for t in args.legs.split(",") if t.strip()]:
         flags = tok.lstrip("0123456789")
@@ -583,7 +604,7 @@ def main():
                     legs[key]["note"] += "; sub-layer RMS normalisation in front of the quantiser"
             elif path != "fused":
                 l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
-                legs[key] = leg_summary(w, lms, l_ms, l_b, l_o)
+                legs[key] = leg_summary(w, lms, l_ms, l_b, l_o, ceilings)
                 legs[key]["kernel"] = {"lut": "k_gemv_lut (table-lookup decode)",
                                        "binary": "k_gemv_bin (1-bit sign-binary decode)"}.get(path) or dominant_kernel(w)
                 legs[key]["note"] = ("activation quantiser, then the " +
@@ -599,7 +620,7 @@ def main():
                                      "quantiser, in the same kernel where the plan fuses it")
             else:
                 l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
-                legs[key] = leg_summary(w, lms, l_ms, l_b, l_o)
+                legs[key] = leg_summary(w, lms, l_ms, l_b, l_o, ceilings)
                 legs[key]["kernel"] = dominant_kernel(w)
                 legs[key]["traffic_bytes_per_launch"] = measured_traffic(dominant_kernel(w), idx, m)
             del w
@@ -623,6 +644,11 @@ def main():
                    "matrices": [list(x) for x in head.wl.matrices],
                    "distinct_weight_sets": len(head.sets),
                    "packed_bytes_per_step": head.bytes_per_step(),
+                   "allin_GBps": round(head.allin_bytes_per_step() / (ms * 1e-3) / 1e9, 1),
+                   "us_per_matrix": round(ms * 1e3 / len(mats), 3),
+                   "tokens_per_s_eq": round(m_head / (ms * 1e-3), 1),
+                   "seeds": "torch.Generator per tensor: 1000*workload + 10*set + matrix for weights, "
+                            "+500 for activations, +700 for sub-layer gains",
                    "launch": "hip graph replay" if args.graph else "pre-marshalled eager C-ABI calls",
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None},
         "roofline": roof,

@@ -52,7 +52,7 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_quantize_weights.restype = c_int
         L.bitlinear_quantize_weights.argtypes = [p, i64, i64, p, p, p, i64, p]
         L.bitlinear_quantize_acts.restype = c_int
-        L.bitlinear_quantize_acts.argtypes = [p, c_int, i64, i64, p, p, p]
+        L.bitlinear_quantize_acts.argtypes = [p, c_int, i64, i64, p, p, p, p]
         L.bitlinear_forward_fused.restype = c_int
         L.bitlinear_forward_fused.argtypes = [p, p, p, c_int, i64, i64, i64, p, p, p, p, p]
         L.bitlinear_forward_plan.restype = c_int
@@ -245,10 +245,11 @@ def quantize_weights(W, packed=None, gamma=None, workspace=None):
     return packed, gamma
 
 
-def quantize_acts(x, xq=None, absmax=None):
+def quantize_acts(x, xq=None, absmax=None, rowsum=None, want_rowsum: bool = False):
     """Per-token absmax int8 quantisation of x[M][K] (fp32 or bf16) on the GPU.
 
-    Returns ``(xq int8 [M][K_pad], absmax fp32 [M])``."""
+    Returns ``(xq int8 [M][K_pad], absmax fp32 [M])``, plus the exact int32 row sums of
+    the codes when ``want_rowsum`` is set or ``rowsum`` is given."""
     import torch
 
     _require_cuda(x, "x")
@@ -266,9 +267,12 @@ def quantize_acts(x, xq=None, absmax=None):
         xq = torch.empty((m, k_pad(k)), dtype=torch.int8, device=dev)
     if absmax is None:
         absmax = torch.empty(m, dtype=torch.float32, device=dev)
+    if want_rowsum and rowsum is None:
+        rowsum = torch.empty(m, dtype=torch.int32, device=dev)
     _check("bitlinear_quantize_acts", lib().bitlinear_quantize_acts(
-        x.data_ptr(), dt, m, k, xq.data_ptr(), absmax.data_ptr(), _stream(dev)))
-    return xq, absmax
+        x.data_ptr(), dt, m, k, xq.data_ptr(), absmax.data_ptr(), rowsum.data_ptr() if rowsum is not None else None,
+        _stream(dev)))
+    return (xq, absmax, rowsum) if rowsum is not None else (xq, absmax)
 
 
 def forward(packed, gamma, xq, absmax, n: int, k: int, y=None, acc=None, want_y: bool = True,
@@ -733,7 +737,7 @@ def prepare_quantize_acts(x, xq, absmax) -> PreparedCall:
         _require_cuda(t, name)
     dt = BL_BF16 if x.dtype == torch.bfloat16 else BL_F32
     return PreparedCall("bitlinear_quantize_acts", x.data_ptr(), dt, x.shape[0], x.shape[1], xq.data_ptr(),
-                        absmax.data_ptr(), _stream(x.device))
+                        absmax.data_ptr(), None, _stream(x.device))
 
 
 def prepare_forward(packed, gamma, xq, absmax, n: int, k: int, y) -> PreparedCall:

@@ -18,6 +18,9 @@
 // above, and the factor only enters the scale written out: a = max|h| / sqrt(mean(x^2)
 // + eps) = max|n|.  The sum of squares is accumulated in fp64 (each square is exact),
 // so its summation order moves a by far less than one fp32 ulp.
+//
+// Optionally the row sum of the codes, sum_k xq[m][k], is written as an exact int32
+// (|sum| <= 127 K): v_dot4 of each group's codes with ones, then an integer reduction.
 #include "bl_internal.h"
 
 namespace bl {
@@ -104,15 +107,37 @@ __device__ __forceinline__ uint2 quant_group(const float (&v)[8], float s) {
   return make_uint2(lo, hi);
 }
 
+// Sum of the eight int8 codes of a group (exact).
+__device__ __forceinline__ int group_sum(uint2 q) {
+  return __builtin_amdgcn_sdot4((int)q.y, 0x01010101, __builtin_amdgcn_sdot4((int)q.x, 0x01010101, 0, false), false);
+}
+
+// Row sum of the codes over the workgroup: shuffles, then the waves' partials in order.
+template <int kTh>
+__device__ __forceinline__ void block_rowsum(int v, int* red_i, int32_t* out) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((threadIdx.x & 63) == 0) red_i[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < kTh / 64; ++w) t += red_i[w];
+    *out = t;
+  }
+}
+
 // Vector path: 8 elements per 16-byte load (bf16) or 4 per 16-byte load (fp32, two
 // loads per group of 8).  Requires K % 8 == 0, a 16-byte aligned X (and gain); each
 // group of 8 elements produces one 8-byte store of codes.
 template <bool kBf16, int kTh, bool kNorm>
 __global__ __launch_bounds__(kTh) void k_act_quant_vec(const void* __restrict__ X, int64_t K, int64_t K_pad,
                                                        const float* __restrict__ gain, float eps,
-                                                       int8_t* __restrict__ Xq, float* __restrict__ absmax) {
+                                                       int8_t* __restrict__ Xq, float* __restrict__ absmax,
+                                                       int32_t* __restrict__ rowsum) {
   __shared__ float red[kTh / 64];
   __shared__ double red_ss[kNorm ? kTh / 64 : 1];
+  __shared__ int red_i[kTh / 64];
   const int64_t m = blockIdx.x;
   const int64_t groups = K / 8;
   float v[kMaxVecPerThread][8];
@@ -139,29 +164,39 @@ __global__ __launch_bounds__(kTh) void k_act_quant_vec(const void* __restrict__ 
   const float s = a > 0.0f ? 127.0f / a : 0.0f;
   if (threadIdx.x == 0) absmax[m] = kNorm ? norm_scale(a, ss, K, eps) : a;
   uint2* out = reinterpret_cast<uint2*>(Xq + m * K_pad);
+  int rs = 0;
 #pragma unroll
   for (int j = 0; j < kMaxVecPerThread; ++j) {
     const int64_t gi = threadIdx.x + (int64_t)j * kTh;
-    if (gi < groups) out[gi] = quant_group(v[j], s);
+    if (gi < groups) {
+      const uint2 q = quant_group(v[j], s);
+      out[gi] = q;
+      rs += group_sum(q);
+    }
   }
   for (int64_t gi = threadIdx.x + (int64_t)kMaxVecPerThread * kTh; gi < groups; gi += kTh) {
     float t[8];
     double unused = 0.0;
     load_group<kBf16>(X, m, K, gi, t);
     norm_group<kNorm>(gain, 8 * gi, t, unused);
-    out[gi] = quant_group(t, s);
+    const uint2 q = quant_group(t, s);
+    out[gi] = q;
+    rs += group_sum(q);
   }
   // zero padding columns K .. K_pad-1 (K is a multiple of 8 here, K_pad of 256)
   for (int64_t gi = groups + threadIdx.x; gi < K_pad / 8; gi += kTh) out[gi] = make_uint2(0u, 0u);
+  if (rowsum) block_rowsum<kTh>(rs, red_i, rowsum + m);
 }
 
 // Scalar path for any K and alignment.
 template <bool kBf16, bool kNorm>
 __global__ __launch_bounds__(kThreads) void k_act_quant_scalar(const void* __restrict__ X, int64_t K, int64_t K_pad,
                                                                const float* __restrict__ gain, float eps,
-                                                               int8_t* __restrict__ Xq, float* __restrict__ absmax) {
+                                                               int8_t* __restrict__ Xq, float* __restrict__ absmax,
+                                                               int32_t* __restrict__ rowsum) {
   __shared__ float red[kThreads / 64];
   __shared__ double red_ss[kNorm ? kThreads / 64 : 1];
+  __shared__ int red_i[kThreads / 64];
   const int64_t m = blockIdx.x;
   auto load = [&](int64_t k) -> float {
     return kBf16 ? bf16_to_f32(static_cast<const uint16_t*>(X)[m * K + k]) : static_cast<const float*>(X)[m * K + k];
@@ -178,13 +213,18 @@ __global__ __launch_bounds__(kThreads) void k_act_quant_scalar(const void* __res
   const float s = a > 0.0f ? 127.0f / a : 0.0f;
   if (threadIdx.x == 0) absmax[m] = kNorm ? norm_scale(a, ss, K, eps) : a;
   int8_t* out = Xq + m * K_pad;
-  for (int64_t k = threadIdx.x; k < K_pad; k += kThreads)
-    out[k] = k < K ? quant_code(h_of(load(k), k), s) : (int8_t)0;
+  int rs = 0;
+  for (int64_t k = threadIdx.x; k < K_pad; k += kThreads) {
+    const int8_t q = k < K ? quant_code(h_of(load(k), k), s) : (int8_t)0;
+    out[k] = q;
+    rs += q;
+  }
+  if (rowsum) block_rowsum<kThreads>(rs, red_i, rowsum + m);
 }
 
 template <bool kNorm>
 void launch_rows(const void* X, int bf16, int64_t M, int64_t K, const float* gain, float eps, int8_t* Xq,
-                 float* absmax, hipStream_t s) {
+                 float* absmax, int32_t* rowsum, hipStream_t s) {
   const int64_t K_pad = k_pad(K);
   const bool vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15u) == 0) &&
                    ((reinterpret_cast<uintptr_t>(gain) & 15u) == 0);
@@ -194,29 +234,29 @@ void launch_rows(const void* X, int bf16, int64_t M, int64_t K, const float* gai
     const bool wide = K / 8 > (int64_t)kMaxVecPerThread * kThreads;
     const dim3 wblock(wide ? 1024 : kThreads);
     if (wide) {
-      if (bf16) hipLaunchKernelGGL((k_act_quant_vec<true, 1024, kNorm>), grid, wblock, 0, s, X, K, K_pad, gain, eps, Xq, absmax);
-      else hipLaunchKernelGGL((k_act_quant_vec<false, 1024, kNorm>), grid, wblock, 0, s, X, K, K_pad, gain, eps, Xq, absmax);
+      if (bf16) hipLaunchKernelGGL((k_act_quant_vec<true, 1024, kNorm>), grid, wblock, 0, s, X, K, K_pad, gain, eps, Xq, absmax, rowsum);
+      else hipLaunchKernelGGL((k_act_quant_vec<false, 1024, kNorm>), grid, wblock, 0, s, X, K, K_pad, gain, eps, Xq, absmax, rowsum);
     } else {
-      if (bf16) hipLaunchKernelGGL((k_act_quant_vec<true, kThreads, kNorm>), grid, block, 0, s, X, K, K_pad, gain, eps, Xq, absmax);
-      else hipLaunchKernelGGL((k_act_quant_vec<false, kThreads, kNorm>), grid, block, 0, s, X, K, K_pad, gain, eps, Xq, absmax);
+      if (bf16) hipLaunchKernelGGL((k_act_quant_vec<true, kThreads, kNorm>), grid, block, 0, s, X, K, K_pad, gain, eps, Xq, absmax, rowsum);
+      else hipLaunchKernelGGL((k_act_quant_vec<false, kThreads, kNorm>), grid, block, 0, s, X, K, K_pad, gain, eps, Xq, absmax, rowsum);
     }
   } else {
-    if (bf16) hipLaunchKernelGGL((k_act_quant_scalar<true, kNorm>), grid, block, 0, s, X, K, K_pad, gain, eps, Xq, absmax);
-    else hipLaunchKernelGGL((k_act_quant_scalar<false, kNorm>), grid, block, 0, s, X, K, K_pad, gain, eps, Xq, absmax);
+    if (bf16) hipLaunchKernelGGL((k_act_quant_scalar<true, kNorm>), grid, block, 0, s, X, K, K_pad, gain, eps, Xq, absmax, rowsum);
+    else hipLaunchKernelGGL((k_act_quant_scalar<false, kNorm>), grid, block, 0, s, X, K, K_pad, gain, eps, Xq, absmax, rowsum);
   }
 }
 
 }  // namespace
 
 hipError_t launch_act_quant(const void* X, int bf16, int64_t M, int64_t K, int8_t* Xq, float* absmax,
-                            hipStream_t s) {
-  launch_rows<false>(X, bf16, M, K, nullptr, 0.0f, Xq, absmax, s);
+                            hipStream_t s, int32_t* rowsum) {
+  launch_rows<false>(X, bf16, M, K, nullptr, 0.0f, Xq, absmax, rowsum, s);
   return hipGetLastError();
 }
 
 hipError_t launch_subln_quant(const void* X, int bf16, int64_t M, int64_t K, const float* gain, float eps,
                               int8_t* Xq, float* scale, hipStream_t s) {
-  launch_rows<true>(X, bf16, M, K, gain, eps, Xq, scale, s);
+  launch_rows<true>(X, bf16, M, K, gain, eps, Xq, scale, nullptr, s);
   return hipGetLastError();
 }
 

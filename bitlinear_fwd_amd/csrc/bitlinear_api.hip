@@ -61,13 +61,14 @@ int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* pa
 }
 
 int bitlinear_quantize_acts(const void* X, int dt, int64_t M, int64_t K, int8_t* Xq, float* absmax,
-                            void* stream) {
+                            int32_t* rowsum, void* stream) {
   if (!X || !Xq || !absmax) return BL_ERR_INVALID_ARG;
   if (M < 1 || K < 1 || M >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
   if (dt != BL_F32 && dt != BL_BF16) return BL_ERR_UNSUPPORTED;
-  if (!aligned(X, dt == BL_F32 ? 4 : 2) || !aligned(Xq, 16) || !aligned(absmax, 4)) return BL_ERR_INVALID_ARG;
+  if (!aligned(X, dt == BL_F32 ? 4 : 2) || !aligned(Xq, 16) || !aligned(absmax, 4) || !aligned(rowsum, 4))
+    return BL_ERR_INVALID_ARG;
   return hip_status(
-      bl::launch_act_quant(X, dt == BL_BF16 ? 1 : 0, M, K, Xq, absmax, static_cast<hipStream_t>(stream)));
+      bl::launch_act_quant(X, dt == BL_BF16 ? 1 : 0, M, K, Xq, absmax, static_cast<hipStream_t>(stream), rowsum));
 }
 
 int bitlinear_subln_quantize_acts(const void* X, int dt, int64_t M, int64_t K, const float* gain, float eps,

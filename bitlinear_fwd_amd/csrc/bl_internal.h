@@ -104,8 +104,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 // C ABI before these are called.
 hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
                                void* workspace, hipStream_t s);
+// rowsum (nullable): int32 [M], the exact sum of each row's codes.
 hipError_t launch_act_quant(const void* X, int bf16, int64_t M, int64_t K, int8_t* Xq, float* absmax,
-                            hipStream_t s);
+                            hipStream_t s, int32_t* rowsum = nullptr);
 // The quantiser behind the sub-layer RMS normalisation: codes of fl32(x * gain), scale
 // max|x * gain| / sqrt(mean(x^2) + eps) (gain null: all ones).
 hipError_t launch_subln_quant(const void* X, int bf16, int64_t M, int64_t K, const float* gain, float eps,

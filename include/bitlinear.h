@@ -96,9 +96,10 @@ int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* pa
  *   X       [M][K] fp32 (dt = BL_F32) or bf16 (dt = BL_BF16), row-major, element-aligned.
  *   Xq      out: int8 [M][K_pad], 16-byte aligned; columns K..K_pad-1 are set to 0.
  *   absmax  out: fp32 [M], a[m] = max_k |X[m][k]|.
+ *   rowsum  out (nullable): int32 [M], sum_k Xq[m][k], exact (|sum| <= 127 K).
  */
 int bitlinear_quantize_acts(const void* X, int dt, int64_t M, int64_t K, int8_t* Xq, float* absmax,
-                            void* stream);
+                            int32_t* rowsum, void* stream);
 
 /*
  * Steps 3 + 4 - packed-ternary x int8 contraction with exact int32 accumulation

@@ -95,11 +95,12 @@ def test_quantize_argument_validation():
     assert L.bitlinear_quantize_weights(FAKE, 0, 256, FAKE, FAKE, FAKE, ws, None) == bl.BL_ERR_INVALID_ARG
     assert L.bitlinear_quantize_weights(FAKE, 16, 256, FAKE + 4, FAKE, FAKE, ws, None) == bl.BL_ERR_INVALID_ARG
     assert L.bitlinear_quantize_weights(FAKE, 1 << 21, 1 << 20, FAKE, FAKE, FAKE, ws, None) == bl.BL_ERR_UNSUPPORTED
-    assert L.bitlinear_quantize_acts(FAKE, 5, 1, 16, FAKE, FAKE, None) == bl.BL_ERR_UNSUPPORTED
-    assert L.bitlinear_quantize_acts(None, bl.BL_F32, 1, 16, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
-    assert L.bitlinear_quantize_acts(FAKE, bl.BL_F32, 0, 16, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
-    assert L.bitlinear_quantize_acts(FAKE + 2, bl.BL_F32, 1, 16, FAKE, FAKE, None) == bl.BL_ERR_INVALID_ARG
-    assert L.bitlinear_quantize_acts(FAKE, bl.BL_BF16, 1, 16, FAKE + 8, FAKE, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_acts(FAKE, 5, 1, 16, FAKE, FAKE, None, None) == bl.BL_ERR_UNSUPPORTED
+    assert L.bitlinear_quantize_acts(None, bl.BL_F32, 1, 16, FAKE, FAKE, None, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_acts(FAKE, bl.BL_F32, 0, 16, FAKE, FAKE, None, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_acts(FAKE + 2, bl.BL_F32, 1, 16, FAKE, FAKE, None, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_acts(FAKE, bl.BL_BF16, 1, 16, FAKE + 8, FAKE, None, None) == bl.BL_ERR_INVALID_ARG
+    assert L.bitlinear_quantize_acts(FAKE, bl.BL_BF16, 1, 16, FAKE, FAKE, FAKE + 2, None) == bl.BL_ERR_INVALID_ARG
 
 
 def test_binding_rejects_cpu_tensors():

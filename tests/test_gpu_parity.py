@@ -91,11 +91,13 @@ def test_weight_quant_deterministic():
 
 # ------------------------------------------------------------------ activation quantiser
 def _aq_check(x_dev: torch.Tensor, tag: str):
-    xq, a = bl.quantize_acts(x_dev)
+    xq, a, rs = bl.quantize_acts(x_dev, want_rowsum=True)
     torch.cuda.synchronize()
     xq_ref, a_ref = oracle.quant_acts(acts_host_f32(x_dev))
     check_equal(host(a).view(np.uint32), a_ref.view(np.uint32), f"absmax {tag}")
     check_equal(host(xq), xq_ref, f"xq {tag}")
+    # the optional row sums: exact sums of the oracle's codes
+    check_equal(host(rs), xq_ref.astype(np.int64).sum(axis=1).astype(np.int32), f"rowsum {tag}")
     return xq, a, xq_ref, a_ref
 
 
