@@ -284,12 +284,12 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
-    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.3 KiB (x1.99980),
+    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.2 KiB (x1.99980),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4595590, "fetch_kib": 2231.53, "write_kib": 25.27, "sha": "e57aa3164cde6246"},
-    (2, 16): {"bytes_per_launch": 3159911, "fetch_kib": 1441.36, "write_kib": 203.43, "sha": "e57aa3164cde6246"},
-    (3, 2048): {"bytes_per_launch": 107265654, "fetch_kib": 33435.20, "write_kib": 37888.00, "sha": "0d6bafb972a121db"},
-    (4, 1): {"bytes_per_launch": 59277962, "fetch_kib": 28902.25, "write_kib": 90.00, "sha": "e57aa3164cde6246"},
+    (1, 1): {"bytes_per_launch": 4592478, "fetch_kib": 2230.01, "write_kib": 25.28, "sha": "61e496dcdd1ac5d2"},
+    (2, 16): {"bytes_per_launch": 3160074, "fetch_kib": 1441.44, "write_kib": 203.43, "sha": "61e496dcdd1ac5d2"},
+    (3, 2048): {"bytes_per_launch": 107301005, "fetch_kib": 33452.47, "write_kib": 37888.00, "sha": "10f7ae3fb6364136"},
+    (4, 1): {"bytes_per_launch": 59279705, "fetch_kib": 28902.76, "write_kib": 90.03, "sha": "61e496dcdd1ac5d2"},
 }
 
 
@@ -627,10 +627,10 @@ def main():
             torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:
-        b, o, t, mats = cpu_baseline(head, args.cpu_seconds)
+        b, o, t, n_cpu = cpu_baseline(head, args.cpu_seconds)
         cpu = {"value": round(b / t / 1e9, 4) if decode else round(o / t / 1e12, 6),
                "unit": "GB/s" if decode else "TOPS", "cores": 1, "kind": "oracle",
-               "sample": f"{mats} matrices of the same workload (act quant + unpack + int matmul + rescale), "
+               "sample": f"{n_cpu} matrices of the same workload (act quant + unpack + int matmul + rescale), "
                          f"{t:.1f} s, single-threaded scalar C"}
     out = {
         "metric": "BitLinear decode packed-weight GB/s (% HBM peak); prefill int8 TOPS (% MFMA)",
@@ -645,7 +645,7 @@ def main():
                    "distinct_weight_sets": len(head.sets),
                    "packed_bytes_per_step": head.bytes_per_step(),
                    "allin_GBps": round(head.allin_bytes_per_step() / (ms * 1e-3) / 1e9, 1),
-                   "us_per_matrix": round(ms * 1e3 / len(mats), 3),
+                   "us_per_matrix": round(ms * 1e3 / head.matrices_per_step(), 3),
                    "tokens_per_s_eq": round(m_head / (ms * 1e-3), 1),
                    "seeds": "torch.Generator per tensor: 1000*workload + 10*set + matrix for weights, "
                             "+500 for activations, +700 for sub-layer gains",
