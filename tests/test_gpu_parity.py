@@ -261,6 +261,30 @@ def test_forward_extreme_accumulators():
         check_y(host(y), np.broadcast_to(exp.astype(np.float64), (m, 32)), "extreme y")
 
 
+@pytest.mark.parametrize("m", [1, 3, 17])
+def test_forward_at_the_largest_k(m):
+    # K = 2^24, the library's limit: |acc| <= 127 K = 2^31 - 2^24 still fits int32.  Closed
+    # form on extreme rows (all +1 / all -1 against +127), and random codes against the
+    # oracle on the decode (M <= 16) and prefill (M = 17) kernels
+    k, n = 1 << 24, 18
+    _announce("forward at K = 2^24", m)
+    rng = np.random.default_rng(m)
+    q = rng.integers(-1, 2, (n, k)).astype(np.int8)
+    q[0] = 1
+    q[1] = -1
+    xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
+    xq[0] = 127
+    a = rng.uniform(0.5, 2.0, m).astype(np.float32)
+    d = lambda arr: torch.from_numpy(np.ascontiguousarray(arr)).to(DEV)
+    y, acc = bl.forward(d(oracle.pack(q)), d(np.array([0.01], np.float32)), d(xq), d(a), n, k,
+                        want_y=True, want_acc=True)
+    torch.cuda.synchronize()
+    acc_ref, y_ref = oracle.forward(q, np.float32(0.01), xq, a, k)
+    assert acc_ref[0, 0] == 127 * k and acc_ref[0, 1] == -127 * k
+    check_equal(host(acc), acc_ref, f"acc K=2^24 m={m}")
+    check_y(host(y), y_ref, f"y K=2^24 m={m}")
+
+
 def test_forward_only_acc_or_only_y():
     m, n, k = 3, 40, 512
     rng = np.random.default_rng(1)
