@@ -393,7 +393,7 @@ def dominant_kernel(w: Workload) -> str:
         return "k_gemv_lds (fused activation quantise + decode, activations in LDS)"
     if plan["acts"] == "registers":
         if m > 4:
-            return "k_gemv_dppm (decode, 9..16 tokens, activation registers shared by row blocks)"
+            return "k_gemv_dppm (decode, 5..16 tokens, activation registers shared by row blocks)"
         return "k_gemv_dpp (decode, activations broadcast across lanes)"
     return "k_gemv_lds (decode, activations in LDS)" if plan["lds_acts"] else "k_gemv_reg (decode)"
 

@@ -109,9 +109,10 @@ int bitlinear_quantize_acts(const void* X, int dt, int64_t M, int64_t K, int8_t*
  *   Xq      int8 [M][K_pad] and absmax fp32 [M] from bitlinear_quantize_acts.
  *   Y       out (nullable): fp32 [M][N], y = acc * gamma * absmax[m] / 127.
  *   acc     out (nullable): int32 [M][N], the exact accumulators.
- * At least one of Y and acc must be non-null.  M = 1..16 runs the decode kernel
+ * At least one of Y and acc must be non-null.  M = 1..16 runs the decode kernels
  * (HBM-streaming, MFMA on in-register decoded weights); larger M runs the prefill GEMM
- * (weights decoded into LDS, int8 MFMA).  |acc| <= 127*K must fit int32: K <= 2^24.
+ * (activations staged in LDS, weights decoded in registers, int8 MFMA).  |acc| <= 127*K
+ * must fit int32: K <= 2^24.
  */
 int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                       int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream);
