@@ -286,10 +286,10 @@ TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
     # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.2 KiB (x1.99980),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4592478, "fetch_kib": 2230.01, "write_kib": 25.28, "sha": "61e496dcdd1ac5d2"},
-    (2, 16): {"bytes_per_launch": 3160074, "fetch_kib": 1441.44, "write_kib": 203.43, "sha": "61e496dcdd1ac5d2"},
-    (3, 2048): {"bytes_per_launch": 107301005, "fetch_kib": 33452.47, "write_kib": 37888.00, "sha": "10f7ae3fb6364136"},
-    (4, 1): {"bytes_per_launch": 59279705, "fetch_kib": 28902.76, "write_kib": 90.03, "sha": "61e496dcdd1ac5d2"},
+    (1, 1): {"bytes_per_launch": 4591117, "fetch_kib": 2229.34, "write_kib": 25.28, "sha": "0b3a71925d61a11e"},
+    (2, 16): {"bytes_per_launch": 3161248, "fetch_kib": 1442.01, "write_kib": 203.43, "sha": "0b3a71925d61a11e"},
+    (3, 2048): {"bytes_per_launch": 107175702, "fetch_kib": 33391.30, "write_kib": 37888.00, "sha": "259a3897057444e6"},
+    (4, 1): {"bytes_per_launch": 59256152, "fetch_kib": 28891.26, "write_kib": 90.03, "sha": "0b3a71925d61a11e"},
 }
 
 

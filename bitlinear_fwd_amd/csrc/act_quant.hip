@@ -98,13 +98,7 @@ __device__ __forceinline__ void load_group(const void* X, int64_t m, int64_t K, 
 }
 
 __device__ __forceinline__ uint2 quant_group(const float (&v)[8], float s) {
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    lo |= (uint32_t)(uint8_t)quant_code(v[e], s) << (8 * e);
-    hi |= (uint32_t)(uint8_t)quant_code(v[4 + e], s) << (8 * e);
-  }
-  return make_uint2(lo, hi);
+  return make_uint2(quant_code4(v[0], v[1], v[2], v[3], s), quant_code4(v[4], v[5], v[6], v[7], s));
 }
 
 // Sum of the eight int8 codes of a group (exact).

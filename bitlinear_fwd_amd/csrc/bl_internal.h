@@ -74,16 +74,32 @@ __device__ __forceinline__ int8_t quant_code(float x, float s) {
   return (int8_t)(int)r;
 }
 
+// quant_code of four values, packed little-endian into one word.  For |r| < 2^22, adding
+// 1.5 * 2^23 to r = fl32(x * s) rounds r to an integer (half to even, as rintf) held in the
+// low mantissa bits, so the low byte of the sum is the two's-complement code; |r| <= 127
+// whenever s = fl32(127 / a) is finite and |x| <= a, so no clamp is needed.  Two permutes
+// and an OR gather the four low bytes.  Multiply and add stay separate roundings.
+__device__ __forceinline__ uint32_t quant_code4(float a, float b, float c, float d, float s) {
+  const float k = 12582912.0f;
+  const uint32_t ta = __float_as_uint(__fadd_rn(__fmul_rn(a, s), k));
+  const uint32_t tb = __float_as_uint(__fadd_rn(__fmul_rn(b, s), k));
+  const uint32_t tc = __float_as_uint(__fadd_rn(__fmul_rn(c, s), k));
+  const uint32_t td = __float_as_uint(__fadd_rn(__fmul_rn(d, s), k));
+  return __builtin_amdgcn_perm(tb, ta, 0x0c0c0400u) | __builtin_amdgcn_perm(td, tc, 0x04000c0cu);
+}
+
 // Launch plan of the decode kernel for one shape (exposed for tests and the benchmark).
 struct GemvPlan {
   int waves = 1;        // waves per workgroup; they split the K tiles into contiguous runs
   int rb = 1;           // 16-row output blocks per workgroup
   bool lds_act = false; // activations staged in LDS (fused quantise + decode)
   bool dpp = false;     // activations held in registers, shifted into place by DPP (M <= 4,
-                        // or 9..16 tokens on rows of at most 4096 elements)
+                        // or 5..16 tokens on rows of at most 4096 elements)
   int run = 0;          // dpp: K tiles per wave (all loads of a wave issued at once)
   bool early = false;   // fused dpp with at most one workgroup per compute unit: weight
                         // loads issued before the activation barrier
+  bool mid = false;     // fused dpp, up to two workgroups per unit and short runs: weight
+                        // loads issued once the activation pieces have landed
   int stage = 0;        // LDS staging: 16-byte activation pieces per thread
   bool ok = true;       // the requested activation source is supported by this plan
   int64_t groups = 0;   // workgroups

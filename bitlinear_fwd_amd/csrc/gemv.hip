@@ -183,12 +183,8 @@ __global__ __launch_bounds__(W * 64) void k_gemv_lds(const uint8_t* __restrict__
         const float s = m == 0 ? scale[0] : (m == 1 ? scale[1] : (m == 2 ? scale[2] : scale[3]));
         uint32_t packed_q[kElems / 4];
 #pragma unroll
-        for (int e4 = 0; e4 < kElems / 4; ++e4) {
-          uint32_t q = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) q |= (uint32_t)(uint8_t)quant_code(v[j][4 * e4 + e], s) << (8 * e);
-          packed_q[e4] = q;
-        }
+        for (int e4 = 0; e4 < kElems / 4; ++e4)
+          packed_q[e4] = quant_code4(v[j][4 * e4], v[j][4 * e4 + 1], v[j][4 * e4 + 2], v[j][4 * e4 + 3], s);
         uint8_t* dst = act_lds + m * lds_stride + kElems * p;
         if (kSrc == 1) *reinterpret_cast<uint2*>(dst) = make_uint2(packed_q[0], packed_q[1]);
         else *reinterpret_cast<uint32_t*>(dst) = packed_q[0];
@@ -382,11 +378,14 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Activation sources of the decode kernels: 0 = int8 xq, 1 / 2 = bf16 / fp32 x, 3 / 4 =
 // bf16 / fp32 x through the sub-layer normalisation.  kSrcEarly added to 1 / 2 selects the
-// fused form that issues its weight loads before the activation barrier.
+// fused form that issues its weight loads before the activation barrier; kSrcMid added to
+// 1..4 the form that issues them as soon as its own activation pieces have landed.
 constexpr int kSrcEarly = 8;
+constexpr int kSrcMid = 32;
 constexpr bool src_bf16(int src) { return (src & 7) == 1 || (src & 7) == 3; }
 constexpr bool src_norm(int src) { return (src & 7) >= 3; }
 constexpr bool src_early(int src) { return (src & kSrcEarly) != 0; }
+constexpr bool src_mid(int src) { return (src & kSrcMid) != 0; }
 
 template <int MM, int kSrc>
 struct DppShape {
@@ -445,9 +444,11 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
       static_for<kParts>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
         const int e = col + kPartElems * h;
-        const int es = e + kPartElems <= K ? e : K - kPartElems;  // columns past K: any valid load, zeroed below
+        // K is a multiple of the 16-byte load: a load is wholly inside the row or past
+        // it, and pieces past it stay zero
         raw[j][h] = make_uint4(0u, 0u, 0u, 0u);
-        if (ld) raw[j][h] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(X) + ((size_t)pm * K + es) * kEB);
+        if (ld && e + kPartElems <= K)
+          raw[j][h] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(X) + ((size_t)pm * K + e) * kEB);
       });
     }
   });
@@ -474,13 +475,18 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   // workgroup per compute unit (kSrcEarly, chosen by the planner) nothing else queues on
   // the unit: after a barrier that only orders the issue (every wave's activation loads
   // go first) the weights are issued before the activation barrier and stream during it.
-  constexpr int kEarly = (kSrc == 0 || src_early(kSrc)) ? T : 0;
+  // With up to two workgroups per unit and short runs (kSrcMid) each wave waits for its
+  // own activation pieces and then issues its weights, which stream during the
+  // conversion, the absmax barrier and the quantisation.
+  constexpr int kEarly = (kSrc == 0 || src_early(kSrc) || src_mid(kSrc)) ? T : 0;
   if constexpr (src_early(kSrc)) asm volatile("s_barrier" ::: "memory");
+  if constexpr (src_mid(kSrc)) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters at their maxima
   uint4 w[T];
   uint4 w2[kPair ? T : 1];
   static_for<kEarly>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
     w[t] = load_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
+    if constexpr (kPair && src_mid(kSrc)) w2[t] = load_nt(wsrc2 + (size_t)min(c0 + t, chunks - 1) * 64);
   });
   __builtin_amdgcn_sched_barrier(0);
 
@@ -494,10 +500,8 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
     float lmax = 0.0f;
     static_for<NA>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      const int col = min(c0 + j * UA + pu, chunks - 1) * kTileCols + 64 * g + 16 * pi;
       static_for<kParts>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
-        const bool in = col + kPartElems * h + kPartElems <= K;
         const uint32_t d[4] = {raw[j][h].x, raw[j][h].y, raw[j][h].z, raw[j][h].w};
 #pragma unroll
         for (int e = 0; e < kPartElems; ++e) {
@@ -505,7 +509,6 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
           float f;
           if constexpr (kBf) f = __uint_as_float(e & 1 ? (d[e >> 1] & 0xFFFF0000u) : (d[e >> 1] << 16));
           else f = __uint_as_float(d[e]);
-          f = in ? f : 0.0f;
           if constexpr (kNorm) {
             lss = fma((double)f, (double)f, lss);  // zero for the pieces the lane does not own
             if (gain) {
@@ -540,12 +543,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
       constexpr int j = decltype(jc)::value;
       uint32_t q[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) word |= (uint32_t)(uint8_t)quant_code(v[j][4 * d + e], sc) << (8 * e);
-        q[d] = word;
-      }
+      for (int d = 0; d < 4; ++d) q[d] = quant_code4(v[j][4 * d], v[j][4 * d + 1], v[j][4 * d + 2], v[j][4 * d + 3], sc);
       act[j] = make_uint4(q[0], q[1], q[2], q[3]);
       if (blockIdx.x == 0 && own(j)) {
         const int col = min(c0 + j * UA + pu, chunks - 1) * kTileCols + 64 * g + 16 * pi;
@@ -556,7 +554,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   static_for<T>([&](auto tc) {
     constexpr int t = decltype(tc)::value;
     if constexpr (t >= kEarly) w[t] = load_nt(wsrc + (size_t)min(c0 + t, chunks - 1) * 64);
-    if constexpr (kPair) w2[t] = load_nt(wsrc2 + (size_t)min(c0 + t, chunks - 1) * 64);
+    if constexpr (kPair && !src_mid(kSrc)) w2[t] = load_nt(wsrc2 + (size_t)min(c0 + t, chunks - 1) * 64);
   });
   __builtin_amdgcn_sched_barrier(0);
   // kNorm: the per-token sums of squares are only needed by the rescale: they are reduced
@@ -948,6 +946,18 @@ hipError_t launch_dpp_run(int T, int M, int W, const Args& a, hipStream_t s, con
   }
 }
 
+// Runs of at most four tiles (the forms the planner only picks for short runs).
+template <int kSrc>
+hipError_t launch_dpp_run4(int T, int M, int W, const Args& a, hipStream_t s) {
+  switch (T) {
+    case 1: return launch_dpp_m<1, kSrc>(M, W, a, s, nullptr);
+    case 2: return launch_dpp_m<2, kSrc>(M, W, a, s, nullptr);
+    case 3: return launch_dpp_m<3, kSrc>(M, W, a, s, nullptr);
+    case 4: return launch_dpp_m<4, kSrc>(M, W, a, s, nullptr);
+    default: return hipErrorInvalidConfiguration;
+  }
+}
+
 // The gated pair keeps two weight runs in registers: runs of at most 8 tiles.
 constexpr int kPairMaxRun = 8;
 
@@ -1040,6 +1050,12 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
         // measured on 2B-class shapes: 160 workgroups 4.82 -> 4.38 us; 432 workgroups
         // 4.60 -> 4.91 us (two per unit queue behind each other's weights)
         p.early = (src == 1 || src == 2) && rblocks <= 256;
+        // measured (bf16 x, M = 1): 2560 x 6912 (432 workgroups, 2-tile runs) 4.63 -> 4.20
+        // us, 4096 x 8192 5.30 -> 4.90 us, 8192 x 8192 (4-tile runs) 6.55 -> 6.22 us; with
+        // more workgroups per unit or longer runs the activation loads of later
+        // workgroups queue behind the weights (8192 x 16384 9.25 -> 9.38 us, 16384 x 8192
+        // 9.16 -> 9.92 us, 28672 x 8192 14.1 -> 22.3 us)
+        p.mid = src != 0 && rblocks > 256 && rblocks <= 512 && t <= 4;
         return p;
       }
     }
@@ -1104,8 +1120,14 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const vo
          norm ? norm->eps : 0.0f};
   if (norm) {
     if (!p.dpp || !p.ok) return hipErrorInvalidConfiguration;  // not planned: the caller checks the plan
+    if (p.mid)
+      return bf16 ? launch_dpp_run4<3 + kSrcMid>(p.run, (int)M, p.waves, a, s)
+                  : launch_dpp_run4<4 + kSrcMid>(p.run, (int)M, p.waves, a, s);
     return bf16 ? launch_dpp_run<3>(p.run, (int)M, p.waves, a, s) : launch_dpp_run<4>(p.run, (int)M, p.waves, a, s);
   }
+  if (p.dpp && p.mid)
+    return bf16 ? launch_dpp_run4<1 + kSrcMid>(p.run, (int)M, p.waves, a, s)
+                : launch_dpp_run4<2 + kSrcMid>(p.run, (int)M, p.waves, a, s);
   if (p.dpp && p.early)
     return bf16 ? launch_dpp_run<1 + kSrcEarly>(p.run, (int)M, p.waves, a, s)
                 : launch_dpp_run<2 + kSrcEarly>(p.run, (int)M, p.waves, a, s);
@@ -1162,6 +1184,16 @@ hipError_t launch_gemv_gated(const uint8_t* packed_gate, const float* gamma_gate
   Args a{packed_gate, gamma_gate, X, nullptr, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
          (int)(n_pad(N) / kTileRows), H, nullptr, Xq_out, absmax_out, norm ? norm->gain : nullptr,
          norm ? norm->eps : 0.0f};
+  // the pair streams two runs per wave: with the mid ordering measured 5.66 -> 5.04 us
+  // (2560 x 6912, M = 1), 6.15 -> 5.30 us (M = 2), 6.28 -> 5.93 us (normalised)
+  if (p.mid) {
+    switch (src) {
+      case 1: return launch_pair_run<1 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+      case 2: return launch_pair_run<2 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+      case 3: return launch_pair_run<3 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+      default: return launch_pair_run<4 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+    }
+  }
   switch (src) {
     case 1: return launch_pair_run<1>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
     case 2: return launch_pair_run<2>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);

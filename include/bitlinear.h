@@ -43,7 +43,9 @@
  *   - Arguments are validated on the host before anything is enqueued; errors are
  *     returned synchronously as a negative bl_status and nothing is launched.  A failed
  *     launch returns BL_ERR_HIP.  Device data (NaN/Inf) is never inspected: inputs must
- *     be finite.
+ *     be finite.  An activation row that is not all zero needs a finite fp32 scale
+ *     127 / a: a row whose largest magnitude a is below 127 / FLT_MAX (about 3.7e-37)
+ *     gets unspecified codes.
  *   - Work enqueued on one stream may run concurrently with work on another; buffers
  *     shared between streams are the caller's responsibility.
  */
