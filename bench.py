@@ -284,12 +284,12 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
-    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.2 KiB (x1.99980),
+    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.5 KiB (x1.99979),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4591117, "fetch_kib": 2229.34, "write_kib": 25.28, "sha": "0b3a71925d61a11e"},
-    (2, 16): {"bytes_per_launch": 3161248, "fetch_kib": 1442.01, "write_kib": 203.43, "sha": "0b3a71925d61a11e"},
-    (3, 2048): {"bytes_per_launch": 107175702, "fetch_kib": 33391.30, "write_kib": 37888.00, "sha": "259a3897057444e6"},
-    (4, 1): {"bytes_per_launch": 59256152, "fetch_kib": 28891.26, "write_kib": 90.03, "sha": "0b3a71925d61a11e"},
+    (1, 1): {"bytes_per_launch": 4586672, "fetch_kib": 2227.17, "write_kib": 25.28, "sha": "54dbe9cec317eae4"},
+    (2, 16): {"bytes_per_launch": 3152326, "fetch_kib": 1437.65, "write_kib": 203.43, "sha": "54dbe9cec317eae4"},
+    (3, 2048): {"bytes_per_launch": 107502591, "fetch_kib": 33550.92, "write_kib": 37888.00, "sha": "259a3897057444e6"},
+    (4, 1): {"bytes_per_launch": 59263829, "fetch_kib": 28895.01, "write_kib": 90.03, "sha": "54dbe9cec317eae4"},
 }
 
 

@@ -30,21 +30,29 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile each source to an object, then link the shared library atomically."""
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile the sources to objects (in parallel, at most `jobs` at once; 0 = one per
+    CPU up to 8), then link the shared library atomically."""
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            sys.stderr.write(res.stdout + res.stderr)
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    objs, procs, pending = [], [], list(SOURCES)
+    while pending or procs:
+        while pending and len(procs) < jobs:
+            src = pending.pop(0)
+            obj = os.path.join(objdir, src.replace(".hip", ".o"))
+            cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            objs.append(obj)
+        src, proc = procs.pop(0)
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            for _, other in procs:
+                other.wait()
             raise RuntimeError(f"hipcc failed on {src}")
-        objs.append(obj)
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

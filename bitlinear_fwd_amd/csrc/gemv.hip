@@ -948,12 +948,12 @@ hipError_t launch_dpp_run(int T, int M, int W, const Args& a, hipStream_t s, con
 
 // Runs of at most four tiles (the forms the planner only picks for short runs).
 template <int kSrc>
-hipError_t launch_dpp_run4(int T, int M, int W, const Args& a, hipStream_t s) {
+hipError_t launch_dpp_run4(int T, int M, int W, const Args& a, hipStream_t s, const MatGroup* grp = nullptr) {
   switch (T) {
-    case 1: return launch_dpp_m<1, kSrc>(M, W, a, s, nullptr);
-    case 2: return launch_dpp_m<2, kSrc>(M, W, a, s, nullptr);
-    case 3: return launch_dpp_m<3, kSrc>(M, W, a, s, nullptr);
-    case 4: return launch_dpp_m<4, kSrc>(M, W, a, s, nullptr);
+    case 1: return launch_dpp_m<1, kSrc>(M, W, a, s, grp);
+    case 2: return launch_dpp_m<2, kSrc>(M, W, a, s, grp);
+    case 3: return launch_dpp_m<3, kSrc>(M, W, a, s, grp);
+    case 4: return launch_dpp_m<4, kSrc>(M, W, a, s, grp);
     default: return hipErrorInvalidConfiguration;
   }
 }
@@ -993,6 +993,17 @@ hipError_t launch_pair_run(int T, int M, int W, const Args& a, const uint8_t* p2
     case 6: return launch_pair_m<6, kSrc>(M, W, a, p2, g2, s);
     case 7: return launch_pair_m<7, kSrc>(M, W, a, p2, g2, s);
     case 8: return launch_pair_m<8, kSrc>(M, W, a, p2, g2, s);
+    default: return hipErrorInvalidConfiguration;
+  }
+}
+
+template <int kSrc>
+hipError_t launch_pair_run4(int T, int M, int W, const Args& a, const uint8_t* p2, const float* g2, hipStream_t s) {
+  switch (T) {
+    case 1: return launch_pair_m<1, kSrc>(M, W, a, p2, g2, s);
+    case 2: return launch_pair_m<2, kSrc>(M, W, a, p2, g2, s);
+    case 3: return launch_pair_m<3, kSrc>(M, W, a, p2, g2, s);
+    case 4: return launch_pair_m<4, kSrc>(M, W, a, p2, g2, s);
     default: return hipErrorInvalidConfiguration;
   }
 }
@@ -1049,13 +1060,14 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
         p.ok = true;
         // measured on 2B-class shapes: 160 workgroups 4.82 -> 4.38 us; 432 workgroups
         // 4.60 -> 4.91 us (two per unit queue behind each other's weights)
-        p.early = (src == 1 || src == 2) && rblocks <= 256;
+        // (normalising sources: 6912 x 2560 5.46 -> 5.29 us, 2560 x 2560 4.61 -> 4.51 us)
+        p.early = src != 0 && rblocks <= 256;
         // measured (bf16 x, M = 1): 2560 x 6912 (432 workgroups, 2-tile runs) 4.63 -> 4.20
         // us, 4096 x 8192 5.30 -> 4.90 us, 8192 x 8192 (4-tile runs) 6.55 -> 6.22 us; with
         // more workgroups per unit or longer runs the activation loads of later
         // workgroups queue behind the weights (8192 x 16384 9.25 -> 9.38 us, 16384 x 8192
         // 9.16 -> 9.92 us, 28672 x 8192 14.1 -> 22.3 us)
-        p.mid = src != 0 && rblocks > 256 && rblocks <= 512 && t <= 4;
+        p.mid = src != 0 && !p.early && rblocks <= 512 && t <= 4;
         return p;
       }
     }
@@ -1120,6 +1132,9 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const vo
          norm ? norm->eps : 0.0f};
   if (norm) {
     if (!p.dpp || !p.ok) return hipErrorInvalidConfiguration;  // not planned: the caller checks the plan
+    if (p.early)
+      return bf16 ? launch_dpp_run<3 + kSrcEarly>(p.run, (int)M, p.waves, a, s)
+                  : launch_dpp_run<4 + kSrcEarly>(p.run, (int)M, p.waves, a, s);
     if (p.mid)
       return bf16 ? launch_dpp_run4<3 + kSrcMid>(p.run, (int)M, p.waves, a, s)
                   : launch_dpp_run4<4 + kSrcMid>(p.run, (int)M, p.waves, a, s);
@@ -1161,6 +1176,23 @@ hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, i
   }
   Args a{nullptr, nullptr, X, nullptr, (int)M, 0, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols), 0,
          nullptr, nullptr, Xq_out, absmax_out, norm ? norm->gain : nullptr, norm ? norm->eps : 0.0f};
+  // the weight-issue order the planner picks for the group's total row blocks
+  if (p.early) {
+    switch (src) {
+      case 1: return launch_dpp_run<1 + kSrcEarly>(p.run, (int)M, p.waves, a, s, &g);
+      case 2: return launch_dpp_run<2 + kSrcEarly>(p.run, (int)M, p.waves, a, s, &g);
+      case 3: return launch_dpp_run<3 + kSrcEarly>(p.run, (int)M, p.waves, a, s, &g);
+      default: return launch_dpp_run<4 + kSrcEarly>(p.run, (int)M, p.waves, a, s, &g);
+    }
+  }
+  if (p.mid) {
+    switch (src) {
+      case 1: return launch_dpp_run4<1 + kSrcMid>(p.run, (int)M, p.waves, a, s, &g);
+      case 2: return launch_dpp_run4<2 + kSrcMid>(p.run, (int)M, p.waves, a, s, &g);
+      case 3: return launch_dpp_run4<3 + kSrcMid>(p.run, (int)M, p.waves, a, s, &g);
+      default: return launch_dpp_run4<4 + kSrcMid>(p.run, (int)M, p.waves, a, s, &g);
+    }
+  }
   switch (src) {
     case 1: return launch_dpp_run<1>(p.run, (int)M, p.waves, a, s, &g);
     case 2: return launch_dpp_run<2>(p.run, (int)M, p.waves, a, s, &g);
@@ -1186,12 +1218,12 @@ hipError_t launch_gemv_gated(const uint8_t* packed_gate, const float* gamma_gate
          norm ? norm->eps : 0.0f};
   // the pair streams two runs per wave: with the mid ordering measured 5.66 -> 5.04 us
   // (2560 x 6912, M = 1), 6.15 -> 5.30 us (M = 2), 6.28 -> 5.93 us (normalised)
-  if (p.mid) {
+  if (p.mid && p.run <= 4) {
     switch (src) {
-      case 1: return launch_pair_run<1 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
-      case 2: return launch_pair_run<2 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
-      case 3: return launch_pair_run<3 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
-      default: return launch_pair_run<4 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+      case 1: return launch_pair_run4<1 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+      case 2: return launch_pair_run4<2 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+      case 3: return launch_pair_run4<3 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
+      default: return launch_pair_run4<4 + kSrcMid>(p.run, (int)M, p.waves, a, packed_up, gamma_up, s);
     }
   }
   switch (src) {

@@ -150,6 +150,68 @@ def test_act_quant_every_bf16_value():
         _aq_check(x.contiguous(), tag)
 
 
+def _tie_rows(k):
+    """Three activation rows whose products x * fl32(127 / a) land exactly on halves: row 0
+    has max 127 (scale 1.0) and holds +-(n + 0.5) for n = 0..126; row 1 has max 63.5
+    (scale 2.0) and holds +-(n / 2 + 0.25); row 2 is row 0 negated.  Every value is exact
+    in bf16.  The expected
+    codes are the round-half-to-even neighbours, written out here from the definition."""
+    halves = np.arange(127, dtype=np.float64) + 0.5
+    r0 = np.concatenate([[127.0], halves, -halves])
+    r1 = np.concatenate([[63.5], halves / 2, -halves / 2])
+    x = np.zeros((3, k), dtype=np.float32)
+    x[0, : r0.size] = r0
+    x[1, : r1.size] = r1
+    x[2, : r0.size] = -r0
+    even = lambda v: np.where(np.floor(v) % 2 == 0, np.floor(v), np.floor(v) + 1)  # v = n + 0.5 >= 0
+    c = np.concatenate([[127], even(halves), -even(halves)]).astype(np.int8)
+    want = np.zeros((3, k), dtype=np.int8)
+    want[0, : c.size] = c
+    want[1, : c.size] = c  # 2 * (n / 2 + 0.25) = n + 0.5: the same codes
+    want[2, : c.size] = -c
+    return x, want
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_act_quant_rounding_ties(dtype):
+    # the quantisers round half to even: a product exactly on a half goes to the even code
+    k = 256
+    x_np, want = _tie_rows(k)
+    x = torch.from_numpy(x_np).to(DEV).to(dtype)
+    assert np.array_equal(acts_host_f32(x), x_np)  # exact in bf16
+    _announce("act_quant ties", dtype)
+    xq, a, xq_ref, _ = _aq_check(x, f"ties {dtype}")
+    check_equal(xq_ref[:, :k], want, "oracle tie codes")
+    check_equal(host(xq)[:, :k], want, "tie codes")
+    # the fused forms quantise in the forward kernel: registers (one and 432 row blocks,
+    # the second issuing its weights as soon as the activations land) and the LDS form
+    for n, kk in ((512, k), (6912, k), (65600, 768)):
+        xx = torch.zeros((3, kk), dtype=dtype, device=DEV)
+        xx[:, :k] = x
+        ww = np.zeros((3, kk), dtype=np.int8)
+        ww[:, :k] = want
+        q = np.random.default_rng(n).integers(-1, 2, (n, kk)).astype(np.int8)
+        packed = torch.from_numpy(oracle.pack(q)).to(DEV)
+        plan = bl.forward_fused_plan(3, n, kk, "bf16" if dtype == torch.bfloat16 else "f32")
+        _announce("forward fused ties", n, kk, dtype, plan)
+        assert plan["kernel"] == "fused"
+        (y, acc), xq2, a2 = bl.forward_fused(packed, torch.tensor([0.02], device=DEV), xx, n, kk, want_y=True,
+                                             want_acc=True)
+        torch.cuda.synchronize()
+        check_equal(host(xq2)[:, :kk], ww, f"fused tie codes n={n}")
+        acc_ref, y_ref = oracle.forward(q, np.float32(0.02), host(xq2), host(a2), kk)
+        check_equal(host(acc), acc_ref, f"fused tie acc n={n}")
+        check_y(host(y), y_ref, f"fused tie y n={n}")
+    # the sub-layer normalisation with no gain decides the codes on x itself: the same ties
+    _announce("subln ties", dtype)
+    xq3, _ = bl.subln_quantize_acts(x, None, 1e-5)
+    (y3, acc3), xq4, _ = bl.forward_subln(packed, torch.tensor([0.02], device=DEV), xx, n, kk, None, 1e-5,
+                                          want_y=True, want_acc=True)
+    torch.cuda.synchronize()
+    check_equal(host(xq3)[:, :k], want, "subln tie codes")
+    check_equal(host(xq4)[:, :kk], ww, "fused subln tie codes")
+
+
 def test_act_quant_deterministic():
     x = synth.activations(64, 6912, seed=8, dtype=torch.bfloat16, device=DEV, outlier_p=0.005, outlier_mult=30.0)
     a1 = bl.quantize_acts(x)
