@@ -424,6 +424,21 @@ def test_forward_fused_single_kernel(m, n, k, dtype):
     _fused_check(m, n, k, dtype, seed=m * 31 + n + k)
 
 
+@pytest.mark.parametrize("m,n,k,dtype", [(5, 512, 256, torch.bfloat16), (8, 700, 2560, torch.bfloat16),
+                                         (9, 130, 4096, torch.bfloat16), (16, 6912, 2560, torch.bfloat16),
+                                         (12, 640, 2560, torch.bfloat16), (16, 33, 8, torch.bfloat16),
+                                         (7, 100, 1000, torch.bfloat16), (15, 1000, 3000, torch.bfloat16),
+                                         (16, 8208, 2560, torch.bfloat16), (8, 700, 2560, torch.float32),
+                                         (16, 2560, 6912, torch.bfloat16)])
+def test_forward_fused_5_to_16_tokens(m, n, k, dtype):
+    # 5..16 tokens: the quantiser and the forward as two launches inside the one call
+    # (ragged K and N, 8- and 16-token register forms, per-tile loads for long rows)
+    plan = bl.forward_fused_plan(m, n, k, "bf16" if dtype == torch.bfloat16 else "f32")
+    _announce("forward fused 5..16", m, n, k, dtype, plan)
+    assert plan["kernel"] != "fused"
+    _fused_check(m, n, k, dtype, seed=m * 41 + n + k)
+
+
 @pytest.mark.parametrize("m,n,k,dtype", [(3, 65600, 768, torch.float32), (4, 70000, 1024, torch.float32)])
 def test_forward_fused_lds_form(m, n, k, dtype):
     # many row blocks leave one wave per block; where its pieces would not fit in
