@@ -30,7 +30,10 @@ packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
                workloads behind the sub-layer RMS normalisation ("1s", "1gs", "2s"), and the
                gate/up pair with the squared-ReLU gating epilogue in one launch ("1f", "1fs");
                the two-kernel int8 path ("1i"), the table-lookup decode ("1l") and the 1-bit
-               sign-binary variant ("1b", "4b") for comparison with the ternary decode;
+               sign-binary variant ("1b", "4b") for comparison with the ternary decode, and
+               one GPU's share of the 100B-class matrices split over 8 GPUs ("5": the up
+               projection's 3584 output rows, the down projection's 3584 input columns);
+  gpu_state    rocm-smi clock and power readings before and after the timed region;
   ceilings     measured on this GPU by the library's probes: HBM read rate with the decode
                access pattern at 58.7 MB and 4.4 MB per launch, and the int8 MFMA rate;
                roofline.frac_of_measured_ceiling sets the dominant kernel against the
@@ -58,8 +61,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
-    ap.add_argument("--legs", default="1g,1s,1gs,1f,1fs,1i,1l,1b,2,2g,2s,3,4,4b",
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4, 5])
+    ap.add_argument("--legs", default="1g,1s,1gs,1f,1fs,1i,1l,1b,2,2g,2s,3,4,4b,5",
                     help="other workloads timed into 'legs' ('' for none); a trailing g times the workload "
                          "with the projections of one input grouped into one call")
     ap.add_argument("--graph", action="store_true",
@@ -398,6 +401,22 @@ def dominant_kernel(w: Workload) -> str:
     return "k_gemv_lds (decode, activations in LDS)" if plan["lds_acts"] else "k_gemv_reg (decode)"
 
 
+def gpu_state():
+    """Clock and power readings of the first GPU from rocm-smi (a child process), as the
+    tool prints them; None where it is missing or fails.  Context for the timings: the
+    clocks vary with load and temperature."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                             timeout=20)
+        card = next(iter(json.loads(out.stdout).values()))
+        keep = ("sclk", "mclk", "fclk", "socclk", "power")
+        return {k: v for k, v in card.items() if any(t in k.lower() for t in keep)}
+    except Exception:
+        return None
+
+
 def time_steps(w: Workload, steps: int, warmup: int):
     import torch
 
@@ -527,7 +546,9 @@ def main():
         head.capture()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+    state_before = gpu_state()
     ms = time_steps(head, args.steps, args.warmup)
+    state_after = gpu_state()
     decode = m_head <= 16
     mats = head.step_groups()[0]
     if all(head.fused.values()):
@@ -654,6 +675,7 @@ def main():
         "roofline": roof,
         "ceilings": ceilings,
         "cpu_baseline": cpu,
+        "gpu_state": {"before_timed_region": state_before, "after_timed_region": state_after},
         "legs": legs,
     }
     print(json.dumps(out), flush=True)

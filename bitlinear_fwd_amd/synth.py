@@ -98,4 +98,8 @@ WORKLOADS = {
                 (2048,), (("up", 2560, 6912), ("down", 6912, 2560)), torch.bfloat16, 0.005, 30.0),
     4: Workload(4, "100B-class decode M=1 and M=8: 8192->28672 and 28672->8192 over 80 layers",
                 (1, 8), (("up", 8192, 28672), ("down", 28672, 8192)), torch.bfloat16, layers=80),
+    # one GPU's share of workload 4 split over 8 GPUs: the up projection sharded by output
+    # rows (28672 / 8), the down projection by input columns (28672 / 8, partial sums)
+    5: Workload(5, "100B-class one-of-8 shard, M=1 and M=8: 8192->3584 and 3584->8192 over 80 layers",
+                (1, 8), (("up_shard", 8192, 3584), ("down_shard", 3584, 8192)), torch.bfloat16, layers=80),
 }

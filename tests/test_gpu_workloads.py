@@ -117,3 +117,14 @@ def test_workload4_fused_m1(midx):
     _, k, n = synth.WORKLOADS[4].matrices[midx]
     assert bl.forward_fused_plan(1, n, k, "bf16")["kernel"] == "fused"
     _run_fused(4, 0, midx, k, n, 1)
+
+
+@pytest.mark.parametrize("m", [1, 8])
+@pytest.mark.parametrize("midx", [0, 1])
+def test_workload5_one_of_8_shard(midx, m):
+    # one GPU's shard of the 100B-class matrices: 3584 output rows of the up projection,
+    # 3584 input columns of the down projection (whose partial sums an all-reduce would add)
+    _, k, n = synth.WORKLOADS[5].matrices[midx]
+    _run(5, 0, midx, k, n, m)
+    if m == 1:
+        _run_fused(5, 0, midx, k, n, 1)
