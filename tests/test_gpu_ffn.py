@@ -63,6 +63,9 @@ def _ffn_check(m, n, k, dtype, subln, seed, unaligned=False):
     (4, 130, 2048, torch.bfloat16, True),
     (1, 33, 8, torch.bfloat16, False),
     (1, 28672, 8192, torch.bfloat16, False),  # 100B-class up projection
+    # 257..512 row blocks, short runs: both weight runs issued as soon as the activations land
+    (2, 6912, 2560, torch.bfloat16, False), (3, 6912, 2560, torch.float32, True),
+    (4, 8192, 2048, torch.bfloat16, True), (2, 8192, 4096, torch.float32, False),
 ])
 def test_gated_pair_one_kernel(m, n, k, dtype, subln):
     plan = bl.forward_gated_relu2_plan(m, n, k, "bf16" if dtype == torch.bfloat16 else "f32", subln)

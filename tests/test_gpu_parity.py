@@ -414,7 +414,11 @@ def _fused_check(m, n, k, dtype, seed, unaligned=False):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("m,n,k", [(1, 512, 256), (1, 700, 2560), (2, 130, 4096), (3, 48, 1000), (4, 520, 2048),
                                    (1, 33, 8), (1, 16400, 512), (1, 64, 6912), (2, 130, 6912), (1, 40, 30000),
-                                   (2, 100, 12000), (4, 24, 4096)])
+                                   (2, 100, 12000), (4, 24, 4096),
+                                   # 257..512 row blocks, runs of at most 4 tiles: weights issued
+                                   # once the activations land; 513 blocks: after the barrier
+                                   (2, 6912, 2560), (4, 8192, 4096), (3, 4100, 1000), (1, 8192, 8192),
+                                   (1, 8208, 2560)])
 def test_forward_fused_single_kernel(m, n, k, dtype):
     # shapes one fused kernel takes: activation pieces held in registers, per-token absmax
     # across the workgroup's waves, ragged K, one to four tokens
@@ -492,6 +496,8 @@ def _grouped_check(m, ns, k, dtype, seed):
     (8, [300, 100], 2560, torch.bfloat16),             # more tokens: quantiser once, then forwards
     (40, [130, 64], 1000, torch.float32),              # prefill sizes
     (1, [100, 200], 300, torch.bfloat16),              # K not a multiple of 8: quantiser path
+    (2, [2560, 2560], 2560, torch.bfloat16),           # 320 row blocks: weights issued as activations land
+    (1, [4096, 2048], 4096, torch.float32),            # 384 row blocks
 ])
 def test_forward_grouped(m, ns, k, dtype):
     _announce("forward grouped", m, ns, k, dtype)

@@ -139,6 +139,8 @@ def _subln_fwd_check(m, n, k, dtype, gain, eps, seed):
     (2, 130, 4096, torch.bfloat16), (3, 48, 1000, torch.float32), (4, 520, 2048, torch.bfloat16),
     (1, 33, 8, torch.bfloat16), (2, 100, 1000, torch.float32), (4, 24, 1024, torch.float32),
     (3, 300, 2304, torch.bfloat16),
+    # 257..512 row blocks with short runs: weights issued as soon as the activations land
+    (2, 6912, 2560, torch.bfloat16), (4, 8192, 2048, torch.float32), (3, 4100, 1000, torch.bfloat16),
 ])
 @pytest.mark.parametrize("gain", ["signed", "none"])
 def test_forward_subln_single_kernel(m, n, k, dtype, gain):
@@ -167,6 +169,8 @@ def test_forward_subln_two_kernels(m, n, k, dtype, gain):
     (1, [6912, 6912], 2560, torch.bfloat16),           # gate + up
     (3, [17, 300, 1000], 1000, torch.float32),
     (8, [300, 100], 2560, torch.bfloat16),             # more tokens: two-kernel path
+    (2, [2560, 2560], 2560, torch.bfloat16),           # 320 row blocks: weights issued as activations land
+    (1, [6912], 2560, torch.bfloat16),                 # a group of one, 432 row blocks
 ])
 def test_forward_grouped_subln(m, ns, k, dtype):
     _announce("forward grouped subln", m, ns, k, dtype)
