@@ -279,7 +279,8 @@ class Workload:
 # (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, averaged over the step's launches), each
 # scaled by what the same counter reads for a device-to-device copy of known size run in the
 # same process (--copy-calibration).  A figure holds only for the kernel source it was taken
-# on: the sha256 of the kernel's source files is stored with it, and a mismatch reports null.
+# on: a hash of the kernel sources' code (comments and whitespace left out) is stored with
+# it, and a mismatch reports null.
 KERNEL_SOURCES = {
     "decode": ("bitlinear_fwd_amd/csrc/gemv.hip", "bitlinear_fwd_amd/csrc/decode_common.h",
                "bitlinear_fwd_amd/csrc/bl_internal.h"),
@@ -289,20 +290,26 @@ TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
     # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.5 KiB (x1.99979),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4586672, "fetch_kib": 2227.17, "write_kib": 25.28, "sha": "54dbe9cec317eae4"},
-    (2, 16): {"bytes_per_launch": 3152326, "fetch_kib": 1437.65, "write_kib": 203.43, "sha": "54dbe9cec317eae4"},
-    (3, 2048): {"bytes_per_launch": 107502591, "fetch_kib": 33550.92, "write_kib": 37888.00, "sha": "259a3897057444e6"},
-    (4, 1): {"bytes_per_launch": 59263829, "fetch_kib": 28895.01, "write_kib": 90.03, "sha": "54dbe9cec317eae4"},
+    (1, 1): {"bytes_per_launch": 4586672, "fetch_kib": 2227.17, "write_kib": 25.28, "sha": "f4ca3e501c7b0086"},
+    (2, 16): {"bytes_per_launch": 3152326, "fetch_kib": 1437.65, "write_kib": 203.43, "sha": "f4ca3e501c7b0086"},
+    (3, 2048): {"bytes_per_launch": 107502591, "fetch_kib": 33550.92, "write_kib": 37888.00, "sha": "0a096d97497bd600"},
+    (4, 1): {"bytes_per_launch": 59263829, "fetch_kib": 28895.01, "write_kib": 90.03, "sha": "f4ca3e501c7b0086"},
 }
 
 
 def source_sha(kind: str) -> str:
+    """Hash of the kernel sources' code: comments and whitespace are left out, so a change
+    of wording keeps the measured figures while any change of code drops them."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,8 +24,8 @@
 //                activations stay in registers, put into place by DPP lane shifts; the
 //                fused form (bf16/fp32 x) quantises in the kernel; k_gemv_dpp_group runs
 //                several matrices of one input in one launch;
-//   k_gemv_dppm  9..16 tokens on short rows: the same register runs for a token group
-//                of 8 or 16, activation registers shared by 1 or 2 row blocks;
+//   k_gemv_dppm  5..16 tokens on rows of at most 4096: the same register runs for a
+//                token group of 8 or 16, activation registers shared by 1 or 2 row blocks;
 //   k_gemv_reg   other 5..16-token shapes: activation fragments loaded per tile with
 //                the weights of a ring of batches, shared by 1, 2 or 4 row blocks;
 //   k_gemv_lds   the fused form where its register pieces would not fit (many row
@@ -346,7 +346,9 @@ __global__ __launch_bounds__(W * 64) void k_gemv_reg(const uint8_t* __restrict__
 // read from x itself, and since the pieces of a workgroup's waves cover every column of
 // every token, the per-token absmax is the maximum over them (wave reductions, then one
 // barrier across the waves); each lane then quantises its own pieces with the
-// arithmetic of the standalone quantiser, and workgroup 0 stores xq and absmax.
+// arithmetic of the standalone quantiser, and workgroup 0 stores xq and absmax.  Where the
+// weight loads go relative to that phase (after the barrier, before it, or as soon as the
+// wave's own pieces land) is a planner choice: kSrcEarly / kSrcMid below.
 // kSrc = 3 (bf16) / 4 (fp32) adds the sub-layer RMS normalisation in front of the
 // quantiser, as the standalone normalising quantiser does: the pieces become
 // h = fl32(x g) before the absmax, each lane also sums the squares of x over the pieces
