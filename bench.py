@@ -34,6 +34,8 @@ packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
                one GPU's share of the 100B-class matrices split over 8 GPUs ("5": the up
                projection's 3584 output rows, the down projection's 3584 input columns);
   gpu_state    rocm-smi clock and power readings before and after the timed region;
+  quantisers   the weight quantiser (2560 -> 6912 fp32 latents) and the activation quantiser
+               (bf16, decode and prefill sizes) timed alone, in bytes moved per second;
   ceilings     measured on this GPU by the library's probes: HBM read rate with the decode
                access pattern at 58.7 MB and 4.4 MB per launch, and the int8 MFMA rate;
                roofline.frac_of_measured_ceiling sets the dominant kernel against the
@@ -338,6 +340,51 @@ def copy_calibration(mib: int):
     del src, dst
 
 
+def measure_quantisers(bl, synth, dev, reps: int = 20):
+    """The two quantiser steps timed on their own (HIP events around back-to-back calls on
+    pre-allocated buffers), as bytes moved per second: the weight quantiser (a-1 + a-2:
+    the fp32 latents read, the packed codes written) on a 2B-class 2560 -> 6912 matrix, and
+    the activation quantiser (a-3: x read, int8 codes and scales written) at decode and
+    prefill sizes."""
+    import torch
+
+    out = {}
+    n, k = 6912, 2560
+    w = synth.latent_weights(n, k, seed=7, device=dev)
+    packed = torch.empty(bl.packed_bytes(n, k), dtype=torch.uint8, device=dev)
+    gamma = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(bl.wq_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+    call = lambda: bl.quantize_weights(w, packed, gamma, ws)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    moved = 4 * n * k + bl.packed_bytes(n, k)
+    out["weight_quant_2560x6912"] = {"us": round(us, 2), "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
+    del w, packed, ws
+    for m, kk in ((1, 2560), (16, 2560), (2048, 2560), (2048, 6912)):
+        x = synth.activations(m, kk, seed=8, dtype=torch.bfloat16, device=dev)
+        xq = torch.empty((m, bl.k_pad(kk)), dtype=torch.int8, device=dev)
+        a = torch.empty(m, dtype=torch.float32, device=dev)
+        pc = bl.prepare_quantize_acts(x, xq, a)
+        pc()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            pc()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        moved = 2 * m * kk + m * bl.k_pad(kk) + 4 * m
+        out[f"act_quant_M{m}_K{kk}_bf16"] = {"us": round(us, 2), "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
+    return out
+
+
 def measure_ceilings(bl, dev):
     """Measured ceilings on this GPU (library probes, back-to-back launches timed with HIP
     events): HBM read rate for the decode access pattern at the two matrix sizes (the
@@ -628,6 +675,7 @@ def main():
                 "launch_us": round(launch_ms * 1e3, 3), "launch_timing": launch_timing,
                 "algorithmic_ops_per_launch": int(launch_ops)}
     ceilings = measure_ceilings(bl, dev)
+    quantisers = measure_quantisers(bl, synth, dev)
     if decode:
         ceil = ceilings["stream_4.4MB_GBps"] if head.bytes_per_step() / len(mats) < 20e6 else ceilings["stream_58.7MB_GBps"]
     else:
@@ -731,6 +779,7 @@ def main():
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None},
         "roofline": roof,
         "ceilings": ceilings,
+        "quantisers": quantisers,
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_mt if cpu else None,
         "gpu_state": {"before_timed_region": state_before, "after_timed_region": state_after},

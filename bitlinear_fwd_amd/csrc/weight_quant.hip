@@ -23,22 +23,26 @@ __global__ __launch_bounds__(64) void k_wq_clear(unsigned long long* bins) {
   for (int i = threadIdx.x; i < kWqBins; i += 64) bins[i] = 0ull;
 }
 
-__device__ __forceinline__ void bin_add(unsigned long long* h, float v) {
+constexpr int kBinCopies = 16;  // LDS copies of the bins: lane l adds into copy l % 16
+
+// hc = this lane's copy: bin b of copy c sits at hc[b * kBinCopies]
+__device__ __forceinline__ void bin_add(unsigned long long* hc, float v) {
   const uint32_t bits = __float_as_uint(v) & 0x7FFFFFFFu;
   const uint32_t e = bits >> 23;
   const uint32_t sig = (bits & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-  atomicAdd(&h[e ? e : 1u], (unsigned long long)sig);  // subnormals share the scale of e = 1
+  atomicAdd(&hc[(e ? e : 1u) * kBinCopies], (unsigned long long)sig);  // subnormals share the scale of e = 1
 }
 
-// Per-wave LDS histograms (one uint64 bin per exponent field), merged into the global
-// bins with one atomic per non-empty bin per workgroup.
+// LDS histograms (one uint64 bin per exponent field) in 16 interleaved copies, so that
+// the lanes of a wave, whose weights mostly share a few exponents, contend four at a
+// time rather than all 64 (the 16 copies of a bin span all 32 banks); merged into the
+// global bins with one atomic per non-empty bin per workgroup.
 __global__ __launch_bounds__(kBinThreads) void k_wq_bins(const float* __restrict__ W, int64_t count,
                                                          int vec4, unsigned long long* __restrict__ bins) {
-  __shared__ unsigned long long h[kBinThreads / 64][kWqBins];
-  const int wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < (kBinThreads / 64) * kWqBins; i += kBinThreads) (&h[0][0])[i] = 0ull;
+  __shared__ unsigned long long h[kWqBins * kBinCopies];
+  for (int i = threadIdx.x; i < kWqBins * kBinCopies; i += kBinThreads) h[i] = 0ull;
   __syncthreads();
-  unsigned long long* hw = h[wave];
+  unsigned long long* hw = h + (threadIdx.x % kBinCopies);
   const int64_t stride = (int64_t)gridDim.x * kBinThreads;
   int64_t start = (int64_t)blockIdx.x * kBinThreads + threadIdx.x;
   int64_t tail_from = 0;
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(kBinThreads) void k_wq_bins(const float* __restrict
   __syncthreads();
   for (int b = threadIdx.x; b < kWqBins; b += kBinThreads) {
     unsigned long long t = 0;
-    for (int w = 0; w < kBinThreads / 64; ++w) t += h[w][b];
+    for (int c = 0; c < kBinCopies; ++c) t += h[b * kBinCopies + c];
     if (t) atomicAdd(&bins[b], t);
   }
 }
@@ -227,7 +231,7 @@ hipError_t launch_weight_quant_binary(const float* W, int64_t N, int64_t K, uint
   const int vec4_all = ((reinterpret_cast<uintptr_t>(W) & 15u) == 0) ? 1 : 0;
   hipLaunchKernelGGL(k_wq_clear, dim3(1), dim3(64), 0, s, bins);
   int64_t blocks = (count / 4 + kBinThreads - 1) / kBinThreads;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_wq_bins, dim3((unsigned)blocks), dim3(kBinThreads), 0, s, W, count, vec4_all, bins);
   hipLaunchKernelGGL(k_wq_finalize, dim3(1), dim3(64), 0, s, bins, (uint64_t)count, beta, inv);
@@ -247,7 +251,7 @@ hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, uint8_t* pa
   const int vec4_all = ((reinterpret_cast<uintptr_t>(W) & 15u) == 0) ? 1 : 0;
   hipLaunchKernelGGL(k_wq_clear, dim3(1), dim3(64), 0, s, bins);
   int64_t blocks = (count / 4 + kBinThreads - 1) / kBinThreads;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_wq_bins, dim3((unsigned)blocks), dim3(kBinThreads), 0, s, W, count, vec4_all, bins);
   hipLaunchKernelGGL(k_wq_finalize, dim3(1), dim3(64), 0, s, bins, (uint64_t)count, gamma, inv);
