@@ -70,60 +70,95 @@ __global__ __launch_bounds__(kBinThreads) void k_wq_bins(const float* __restrict
 // ---- exact finalisation (one thread) -------------------------------------------------
 constexpr int kLimbs = 11;  // 352 bits: bins (< 2^63) shifted by up to 253 bits
 
-__device__ void limbs_add_u64(uint32_t* x, int idx, uint64_t v) {
-  while (v && idx < kLimbs) {
-    const uint64_t s = (uint64_t)x[idx] + (v & 0xFFFFFFFFull);
-    x[idx] = (uint32_t)s;
-    v = (v >> 32) + (s >> 32);
-    ++idx;
-  }
+// Limb w of x, for a w known only at run time: a select chain, so x stays in registers.
+__device__ __forceinline__ uint32_t limbs_get(const uint32_t (&x)[kLimbs], int w) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) v = i == w ? x[i] : v;
+  return v;
 }
-
-__device__ __forceinline__ uint32_t limbs_bit(const uint32_t* x, int i) { return (x[i >> 5] >> (i & 31)) & 1u; }
 
 __global__ __launch_bounds__(64) void k_wq_finalize(const unsigned long long* __restrict__ bins, uint64_t count,
                                                     float* __restrict__ gamma_out, float* __restrict__ inv_out) {
   if (threadIdx.x != 0) return;
-  // S = sum_e bins[e] * 2^(e-1), the exact sum of |W| in units of 2^-149
-  uint32_t s[kLimbs];
-  for (int i = 0; i < kLimbs; ++i) s[i] = 0u;
+  // S = sum_e bins[e] * 2^(e-1), the exact sum of |W| in units of 2^-149.  Every bin is
+  // split into 32-bit pieces added to 64-bit per-limb accumulators (254 bins: no
+  // overflow), and the carries are propagated once at the end; the loop is unrolled so
+  // that every limb index is a constant and the limbs stay in registers.
+  uint64_t acc[kLimbs];
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) acc[i] = 0ull;
+#pragma unroll
   for (int e = 1; e < 255; ++e) {
     const uint64_t v = bins[e];
-    if (!v) continue;
     const int sh = e - 1, word = sh >> 5, bit = sh & 31;
-    limbs_add_u64(s, word, (v & 0xFFFFFFFFull) << bit);
-    limbs_add_u64(s, word + 1, (v >> 32) << bit);
+    const uint64_t lo = v << bit;
+    const uint64_t hi = bit ? v >> (64 - bit) : 0ull;
+    acc[word] += lo & 0xFFFFFFFFull;
+    if (word + 1 < kLimbs) acc[word + 1] += lo >> 32;
+    if (word + 2 < kLimbs) acc[word + 2] += hi;
+  }
+  uint32_t s[kLimbs];
+  uint64_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) {
+    const uint64_t t = acc[i] + carry;
+    s[i] = (uint32_t)t;
+    carry = t >> 32;
   }
   float g;
   if (bins[255] != 0ull) {
     g = __builtin_nanf("");  // a non-finite weight: no meaningful scale
   } else {
-    // Q = floor(S / count), R = S mod count, by restoring binary long division
+    // Q = floor(S / count), R = S mod count
     uint32_t q[kLimbs];
-    for (int i = 0; i < kLimbs; ++i) q[i] = 0u;
     uint64_t r = 0;
-    int top = -1;
-    for (int i = kLimbs * 32 - 1; i >= 0; --i) {
-      r = (r << 1) | limbs_bit(s, i);
-      if (r >= count) {
-        r -= count;
-        q[i >> 5] |= 1u << (i & 31);
-        if (top < 0) top = i;
+    if (count < (1ull << 32)) {
+      // one limb at a time: r < count < 2^32, so (r << 32) | limb fits 64 bits
+#pragma unroll
+      for (int i = kLimbs - 1; i >= 0; --i) {
+        const uint64_t cur = (r << 32) | s[i];
+        q[i] = (uint32_t)(cur / count);
+        r = cur - (uint64_t)q[i] * count;
+      }
+    } else {
+      // restoring binary long division (r < count < 2^63)
+#pragma unroll
+      for (int i = 0; i < kLimbs; ++i) q[i] = 0u;
+      for (int i = kLimbs * 32 - 1; i >= 0; --i) {
+        r = (r << 1) | ((limbs_get(s, i >> 5) >> (i & 31)) & 1u);
+        if (r >= count) {
+          r -= count;
+#pragma unroll
+          for (int w = 0; w < kLimbs; ++w) q[w] |= w == (i >> 5) ? 1u << (i & 31) : 0u;
+        }
       }
     }
+    // bit length of Q
+    int len = 0;
+#pragma unroll
+    for (int i = 0; i < kLimbs; ++i) len = q[i] ? 32 * i + 32 - __builtin_clz(q[i]) : len;
     // the mean is (Q + R/count) * 2^-149; keep 24 significant bits, round half to even
-    const int len = top + 1;  // bit length of Q
     const int shift = len > 24 ? len - 24 : 0;
-    uint32_t m = 0;
-    for (int i = 23; i >= 0; --i) m = (m << 1) | (i + shift < kLimbs * 32 ? limbs_bit(q, i + shift) : 0u);
+    // m = bits [shift, shift + 24) of Q: a 64-bit window of limbs shift/32 and shift/32 + 1
+    const int w0 = shift >> 5, b0 = shift & 31;
+    const uint64_t win = (uint64_t)limbs_get(q, w0) | ((uint64_t)limbs_get(q, w0 + 1) << 32);
+    uint32_t m = (uint32_t)(win >> b0) & 0xFFFFFFu;
     bool up;
     if (shift == 0) {
-      const uint64_t twice = r << 1;  // r < count < 2^40
+      const uint64_t twice = r << 1;  // r < count < 2^63
       up = twice > count || (twice == count && (m & 1u));
     } else {
-      const uint32_t half = limbs_bit(q, shift - 1);
+      const int hb = shift - 1;  // the first bit below the kept ones
+      const uint32_t half = (limbs_get(q, hb >> 5) >> (hb & 31)) & 1u;
+      // sticky: any bit of Q below bit hb, or a nonzero remainder
       bool sticky = r != 0;
-      for (int i = 0; i < shift - 1 && !sticky; ++i) sticky = limbs_bit(q, i) != 0;
+#pragma unroll
+      for (int i = 0; i < kLimbs; ++i) {
+        const int lo_bit = 32 * i;
+        const uint32_t mask = hb <= lo_bit ? 0u : (hb >= lo_bit + 32 ? 0xFFFFFFFFu : (1u << (hb - lo_bit)) - 1u);
+        sticky = sticky || (q[i] & mask) != 0u;
+      }
       up = half && (sticky || (m & 1u));
     }
     m += up ? 1u : 0u;
