@@ -73,6 +73,25 @@ def test_weight_quant_special_tensors():
         _wq_check(torch.from_numpy(w).to(DEV), name)
 
 
+def test_weight_quant_gamma_at_two_to_the_32_elements():
+    # N * K = 2^32 elements (256 x 2^24), beyond the one-limb-at-a-time division: ones with
+    # the first j entries set to 2 have the exact mean 1 + j * 2^-32.  One fp32 ulp at 1 is
+    # 2^-23 = 2^9 * 2^-32, so j = 256 is exactly half an ulp (ties to the even 1.0), j = 257
+    # is just above it (1 + 2^-23), and j = 768 is one and a half ulps (ties to the even
+    # 1 + 2^-22).  The codes are not checked: gamma is the point.
+    n, k = 256, 1 << 24
+    w = torch.ones((n, k), dtype=torch.float32, device=DEV)
+    for j, want in ((256, 0x3F800000), (257, 0x3F800001), (768, 0x3F800002)):
+        _announce("weight_quant 2^32 elements", j)
+        w.view(-1)[:j] = 2.0
+        _, gamma = bl.quantize_weights(w)
+        torch.cuda.synchronize()
+        assert gamma_bits(host(gamma)) == want, (j, hex(gamma_bits(host(gamma))))
+        w.view(-1)[:j] = 1.0
+    del w
+    torch.cuda.empty_cache()
+
+
 def test_weight_quant_unaligned_source():
     _announce("weight_quant unaligned")
     base = synth.latent_weights(1, 33 * 256 + 1, seed=3, device=DEV).reshape(-1)
