@@ -18,9 +18,10 @@
 //     layout, and 2-bit codes are 4x fewer bytes through the cache than int8;
 //   * one 16-byte word of a slot feeds one MFMA step and serves WM / 16 MFMAs, which
 //     keeps the decode VALU below the matrix-core time;
-//   * shapes: 64 x 256 output tiles (waves 1 x 4 of 64 x 64, three-slot ring) when there
-//     are enough of them to give every compute unit two; else 64 x 128 tiles (waves
-//     2 x 2 of 32 x 64, fewer registers, A reads issued a half-stage at a time);
+//   * shapes: 64 x 256 or 64 x 192 output tiles (waves 1 x 4 of 64 x 64 or 64 x 48,
+//     three-slot ring), whichever leaves the lighter last round of tiles; 64 x 128 tiles
+//     (waves 2 x 2 of 32 x 64, A reads issued a half-stage at a time) where 64 x 256 would
+//     not give every compute unit one (plan_gemm);
 //   * tile order is XCD-aware: consecutive workgroup ids go to different XCDs, so each
 //     XCD gets a contiguous run of output tiles (sharing activation rows in its L2).
 #include "bl_internal.h"
@@ -294,13 +295,28 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   (void)K;
   GemmPlan p;
   p.threads = 256;
-  // 64 x 256 tiles (four waves side by side, 64 x 64 each, three-slot ring: 24 KiB of
-  // LDS, 152 VGPRs, three workgroups per CU) when they give at least two per CU;
-  // otherwise 64 x 128 tiles of four 32 x 64 waves (124 VGPRs, four per CU) so that
-  // short-N shapes still fill the chip.
-  const int64_t wide = ((M + 63) / 64) * ((N + 255) / 256);
+  // Three tile shapes of 64 rows, four waves each:
+  //   64 x 256: waves of 64 x 64 side by side (three-slot ring, 24 KiB of LDS, 152
+  //             registers, three workgroups per CU): the most work per operand byte;
+  //   64 x 192: waves of 64 x 48 (118 registers, four per CU): the same structure, for
+  //             column counts that 256 would leave a ragged last round on;
+  //   64 x 128: 2 x 2 waves of 32 x 64 (124 registers, four per CU), when 64 x 256 tiles
+  //             would not even give every CU one, so that short shapes fill the chip.
+  // Between the first two, the cost of the last round decides: rounds of 256 tiles times
+  // the tile width, the 48-column waves counted at 0.976 of the 64-column rate (measured
+  // 8192^3: 486 vs 474 us).  Measured at M = 2048: 2560 columns 49.1 us (64 x 128) ->
+  // 43.9 us (64 x 192), 6912 columns 46.8 us (64 x 256) -> 45.9 us (64 x 192); 8192^3,
+  // 4096 x 2560 x 6912 and 2048 x 28672 x 8192 stay on 64 x 256.
+  const int64_t tm = (M + 63) / 64;
+  const int64_t t256 = tm * ((N + 255) / 256), t192 = tm * ((N + 191) / 192);
   p.bm = 64;
-  p.bn = wide >= 512 ? 256 : 128;
+  if (t256 < 256) {
+    p.bn = 128;
+  } else {
+    const double c256 = (double)((t256 + 255) / 256) * 256.0;
+    const double c192 = (double)((t192 + 255) / 256) * 192.0 / 0.976;
+    p.bn = c192 < c256 ? 192 : 256;
+  }
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   p.groups = 8 * ((tiles + 7) / 8);
   return p;
@@ -310,6 +326,7 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s) {
   const GemmPlan p = plan_gemm(M, N, K);
   if (p.bn == 256) return launch<1, 4, 64, 64, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
+  if (p.bn == 192) return launch<1, 4, 64, 48, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
   return launch<2, 2, 32, 64, 3, 1>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
 }
 

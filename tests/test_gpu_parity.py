@@ -301,10 +301,12 @@ def test_forward_prefill(m, n, k):
     _fwd_check(m, n, k, seed=m * 1000 + n + k)
 
 
-@pytest.mark.parametrize("m,n,k,tile_n", [(2048, 4100, 1000, 256), (1000, 3000, 777, 128), (333, 24000, 2600, 256)])
+@pytest.mark.parametrize("m,n,k,tile_n", [(2048, 4100, 1000, 192), (1000, 3000, 777, 128), (333, 24000, 2600, 192),
+                                          (4000, 8190, 1000, 256), (3000, 9000, 700, 192), (2048, 2560, 6912, 192)])
 def test_forward_prefill_tile_shapes(m, n, k, tile_n):
-    # both prefill tile shapes (64 x 256 when there are enough tiles, else 64 x 128) with
-    # ragged M, N and K; the oracle checks a sample of token rows covering tile edges
+    # the three prefill tile shapes (64 x 256 or 64 x 192 by the last round's load, 64 x
+    # 128 for short shapes) with ragged M, N and K; the oracle checks a sample of token
+    # rows covering tile edges
     plan = bl.forward_plan(m, n, k)
     _announce("forward prefill tiles", m, n, k, plan)
     assert plan["kernel"] == "prefill" and plan["tile_m"] == 64 and plan["tile_n"] == tile_n
