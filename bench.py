@@ -290,12 +290,12 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
-    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.5 KiB (x1.99979),
+    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.2 KiB (x1.99980),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4586672, "fetch_kib": 2227.17, "write_kib": 25.28, "sha": "f4ca3e501c7b0086"},
-    (2, 16): {"bytes_per_launch": 3152326, "fetch_kib": 1437.65, "write_kib": 203.43, "sha": "f4ca3e501c7b0086"},
-    (3, 2048): {"bytes_per_launch": 107502591, "fetch_kib": 33550.92, "write_kib": 37888.00, "sha": "0a096d97497bd600"},
-    (4, 1): {"bytes_per_launch": 59263829, "fetch_kib": 28895.01, "write_kib": 90.03, "sha": "f4ca3e501c7b0086"},
+    (1, 1): {"bytes_per_launch": 4586678, "fetch_kib": 2227.17, "write_kib": 25.28, "sha": "f7b3ff610e0d8111"},
+    (2, 16): {"bytes_per_launch": 3152324, "fetch_kib": 1437.65, "write_kib": 203.43, "sha": "f7b3ff610e0d8111"},
+    (3, 2048): {"bytes_per_launch": 97854081, "fetch_kib": 28839.16, "write_kib": 37888.19, "sha": "c189f7b120dfe497"},
+    (4, 1): {"bytes_per_launch": 59263829, "fetch_kib": 28895.01, "write_kib": 90.03, "sha": "f7b3ff610e0d8111"},
 }
 
 

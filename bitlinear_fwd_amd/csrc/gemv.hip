@@ -1108,6 +1108,11 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   else if (M > 4 && rblocks >= 2 * 256) p.rb = 2;
   p.groups = (rblocks + p.rb - 1) / p.rb;
   p.waves = pick_waves(chunks, p.groups);
+  // 5..16 tokens on long rows: runs of at least 8 tiles per wave while the launch keeps
+  // 1024 or more waves (measured at M = 8: 8192 x 28672 14.8 -> 13.1 us with 4 waves,
+  // 28672 x 8192 15.4 -> 14.9 us with 8; 6912 x 2560 keeps 8, 8192 x 8192 6.6 us either way)
+  if (M > 4)
+    while (p.waves > 1 && chunks < 8 * p.waves && p.groups * (p.waves / 2) >= 1024) p.waves /= 2;
   return p;
 }
 
