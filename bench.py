@@ -440,7 +440,8 @@ def dominant_kernel(w: Workload) -> str:
     key = max(w.bufs, key=lambda kn: kn[0] * kn[1])
     plan = w.bl.forward_plan(m, key[1], key[0])
     if plan["kernel"] == "prefill":
-        return "k_gemm_mfma (prefill, %dx%d tiles)" % (plan["tile_m"], plan["tile_n"])
+        groups = ", two K groups per tile" if plan["k_groups"] == 2 else ""
+        return "k_gemm_mfma (prefill, %dx%d tiles%s)" % (plan["tile_m"], plan["tile_n"], groups)
     if w.fused[key] and w.subln:
         return "k_gemv_dpp_norm (sub-layer normalisation + activation quantise + decode, one kernel)"
     if w.fused[key]:
@@ -459,11 +460,16 @@ def gpu_state():
     """Clock and power readings of the first GPU from rocm-smi (a child process), as the
     tool prints them; None where it is missing or fails.  Context for the timings: the
     clocks vary with load and temperature."""
+    import shutil
     import subprocess
 
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
-                             timeout=20)
+        # The tool is a Python script: run it with this interpreter rather than through its
+        # `env` line, so no process in the chain replaces itself (a profiler's preloaded
+        # library has already opened the GPU in every child).
+        smi = os.path.realpath(shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi")
+        out = subprocess.run([sys.executable, smi, "--showclocks", "--showpower", "--json"], capture_output=True,
+                             text=True, timeout=20)
         card = next(iter(json.loads(out.stdout).values()))
         keep = ("sclk", "mclk", "fclk", "socclk", "power")
         return {k: v for k, v in card.items() if any(t in k.lower() for t in keep)}
@@ -510,8 +516,9 @@ def time_forward_only(w: Workload, reps: int):
     else:
         keep = [w.prepared(group, True) for group in groups]
         runs = [(lambda calls=calls: [c() for c in calls]) for calls in keep]
-    for r in runs:  # warm
-        r()
+    for _ in range(3):  # warm: caches, and the clock out of its idle state
+        for r in runs:
+            r()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -656,7 +663,7 @@ def main():
         launch_bytes, launch_ops = head.bytes_per_step() / len(mats), head.ops_per_step() / len(mats)
         launch_timing = "timed region / launches (the step is only this kernel)"
     else:
-        launch_ms, launch_bytes, launch_ops = time_forward_only(head, 3 if head.sweep else 4 * len(head.sets))
+        launch_ms, launch_bytes, launch_ops = time_forward_only(head, 3 if head.sweep else 40 * len(head.sets))
         launch_timing = "graph replays of the forward launches alone"
     value = head.bytes_per_step() / (ms * 1e-3) / 1e9 if decode else head.ops_per_step() / (ms * 1e-3) / 1e12
     kernel = dominant_kernel(head)
@@ -723,7 +730,7 @@ def main():
                 if subln:
                     legs[key]["note"] += "; sub-layer RMS normalisation in front of the quantiser"
             elif path != "fused":
-                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
+                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 40 * len(w.sets))
                 legs[key] = leg_summary(w, lms, l_ms, l_b, l_o, ceilings)
                 legs[key]["kernel"] = {"lut": "k_gemv_lut (table-lookup decode)",
                                        "binary": "k_gemv_bin (1-bit sign-binary decode)"}.get(path) or dominant_kernel(w)
@@ -739,7 +746,7 @@ def main():
                 legs[key]["note"] = ("sub-layer RMS normalisation (per-feature gain, eps 1e-5) in front of the "
                                      "quantiser, in the same kernel where the plan fuses it")
             else:
-                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 4 * len(w.sets))
+                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 40 * len(w.sets))
                 legs[key] = leg_summary(w, lms, l_ms, l_b, l_o, ceilings)
                 legs[key]["kernel"] = dominant_kernel(w)
                 legs[key]["traffic_bytes_per_launch"] = measured_traffic(dominant_kernel(w), idx, m)

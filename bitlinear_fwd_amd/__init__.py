@@ -171,7 +171,7 @@ def _plan_dict(out) -> dict:
                 "acts": acts, "lds_acts": out[4] == 1, "lds_bytes": out[5] if out[4] == 1 else 0,
                 "tiles_per_wave": out[5] if out[4] == 2 else 0}
     return {"kernel": "prefill", "workgroups": out[1], "threads": out[2], "tile_m": out[3], "tile_n": out[4],
-            "lds_bytes": out[5]}
+            "k_groups": out[5]}
 
 
 def forward_plan(m: int, n: int, k: int) -> dict:

@@ -341,7 +341,7 @@ int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]) {
     out[2] = p.threads;
     out[3] = p.bm;
     out[4] = p.bn;
-    out[5] = 0;
+    out[5] = p.ks;
   }
   return BL_OK;
 }

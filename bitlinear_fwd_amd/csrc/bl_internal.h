@@ -111,6 +111,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src);
 // Launch plan of the prefill kernel.
 struct GemmPlan {
   int bm = 128, bn = 128;  // output tile
+  int ks = 1;              // K groups of four waves per tile (1 or 2)
   int threads = 256;
   int64_t groups = 0;
 };

@@ -70,13 +70,14 @@ constexpr int loads_between(int a, int b) {
   return n;
 }
 
-template <int GM, int GN, int WM, int WN, int D, int kPipe = 0>
-__global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ packed, const float* __restrict__ gamma,
+template <int GM, int GN, int WM, int WN, int D, int kPipe = 0, int KS = 1>
+__global__ __launch_bounds__(256 * KS) void k_gemm_mfma(const uint8_t* __restrict__ packed, const float* __restrict__ gamma,
                                                    const int8_t* __restrict__ Xq, const float* __restrict__ absmax,
                                                    int M, int N, int n_blocks, int K_pad, int chunks, int tiles_m,
                                                    int tiles_n, float* __restrict__ Y, int32_t* __restrict__ acc_out) {
   static_assert(GM * GN == 4, "four waves");
   static_assert(D >= 2, "at least two ring slots");
+  static_assert(KS == 1 || KS == 2, "one or two K groups");
   constexpr int BM = GM * WM, BN = GN * WN;
   constexpr int MB = WM / 16, NB = WN / 16;
   constexpr int kHalf = kTileCols / 2;        // bytes per activation row in a half-stage
@@ -84,14 +85,16 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
   constexpr int P = D - 1;                    // prefetch distance in half-stages
   constexpr int CB = (P + 1) / 2 + 1;         // weight register ring (chunks live at once)
   constexpr int kBody = std::lcm(D, 2 * CB);  // half-stages per trip: both ring indices static
+  constexpr int kSlab = BM * kHalf;           // one K group's slab of a ring slot
+  static_assert(KS == 1 || (MB % 2 == 0 && 4 * NB * 64 * 16 <= KS * kSlab), "K-group exchange fits a ring slot");
   // one LDS object per ring slot: distinct objects let the compiler see that the direct
   // loads into one slot do not alias reads of another (otherwise it waits for all of them)
-  __shared__ __attribute__((aligned(1024))) uint8_t As0[BM * kHalf];
-  __shared__ __attribute__((aligned(1024))) uint8_t As1[BM * kHalf];
-  __shared__ __attribute__((aligned(1024))) uint8_t As2[D > 2 ? BM * kHalf : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t As3[D > 3 ? BM * kHalf : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t As4[D > 4 ? BM * kHalf : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t As5[D > 5 ? BM * kHalf : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[KS * kSlab];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[KS * kSlab];
+  __shared__ __attribute__((aligned(1024))) uint8_t As2[D > 2 ? KS * kSlab : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t As3[D > 3 ? KS * kSlab : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t As4[D > 4 ? KS * kSlab : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t As5[D > 5 ? KS * kSlab : 16];
   static_assert(D <= 6, "ring of at most 6 slots");
   auto slab = [&](auto sc) -> uint8_t* {
     constexpr int sl = decltype(sc)::value;
@@ -103,7 +106,10 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
     else return As5;
   };
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = KS == 1 ? wave_all : wave_all & 3;  // wave within its K group
+  const int kg = KS == 1 ? 0 : wave_all >> 2;            // K group
+  const int kgoff = kg * kSlab;                          // the group's half of each ring slot
   const int r = lane & 15, g = lane >> 4;
   const int wm = wave / GN, wn = wave % GN;
 
@@ -117,7 +123,17 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
   const int t = xcd < full ? xcd * per_xcd + slot : full * per_xcd + (xcd - full) * (per_xcd - 1) + slot;
   if (slot >= (xcd < full ? per_xcd : per_xcd - 1)) return;
   const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
-  const int hstages = 2 * chunks;
+  // K group kg takes chunks [c_lo, c_hi).  Both groups run the same number of half-stages
+  // (they share the barriers); where the chunks do not split evenly the second group skips
+  // the compute of its last ones and its loads repeat a valid chunk.
+  const int cg = (chunks + KS - 1) / KS;
+  const int c_lo = kg * cg, c_hi = min(chunks, c_lo + cg);
+  const int hstages = 2 * cg;                                       // loop length, both groups
+  const int hs_mine = KS == 1 ? hstages : 2 * max(c_hi - c_lo, 0);  // half-stages this group computes
+  auto chunk_of = [&](int h) {
+    if constexpr (KS == 1) return min(h, hstages - 1) >> 1;
+    else return min(c_lo + (min(h, hstages - 1) >> 1), chunks - 1);
+  };
 
   // this lane's source for each direct load: row 8 (4 j + wave) + lane / 8, LDS slot
   // lane % 8 holding local piece lp = slot ^ swizzle, global piece 4 (lp >> 1) + 2h + (lp & 1)
@@ -147,7 +163,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
 
   // compute half-stage in ring slot s (steps 2h, 2h+1 of its chunk) with weights cb
   auto compute = [&](auto sc, int half, const uint4 (&wcur)[NB]) {
-    const uint8_t* slabp = slab(sc);
+    const uint8_t* slabp = slab(sc) + kgoff;
     if constexpr (kPipe == 1) {
       // both steps' A fragments are read up front; step 1's weights are decoded while
       // step 0's MFMAs run (interleaving requested from the scheduler)
@@ -211,8 +227,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
   // Prologue: half-stages 0 .. P-1.
   static_for<P>([&](auto hc) {
     constexpr int hs = decltype(hc)::value;
-    const int c = min(hs, hstages - 1) >> 1;
-    uint8_t* dst = slab(std::integral_constant<int, hs>{});
+    const int c = chunk_of(hs);
+    uint8_t* dst = slab(std::integral_constant<int, hs>{}) + kgoff;
 #pragma unroll
     for (int j = 0; j < kDma; ++j)
       load_g2lds16(asrc[j] + (size_t)c * kTileCols + 32 * (min(hs, hstages - 1) & 1), &dst[8 * (4 * j + wave) * kHalf]);
@@ -234,8 +250,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
       const int nh = hs + P;  // half-stage to issue
       {
         const int hc = min(nh, hstages - 1);
-        const int c = hc >> 1;
-        uint8_t* dst = slab(std::integral_constant<int, (k + P) % D>{});
+        const int c = chunk_of(nh);
+        uint8_t* dst = slab(std::integral_constant<int, (k + P) % D>{}) + kgoff;
 #pragma unroll
         for (int j = 0; j < kDma; ++j)
           load_g2lds16(asrc[j] + (size_t)c * kTileCols + 32 * (hc & 1), &dst[8 * (4 * j + wave) * kHalf]);
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (hs < hstages) compute(std::integral_constant<int, k % D>{}, k & 1, bw[(k / 2) % CB]);
+      if (hs < hs_mine) compute(std::integral_constant<int, k % D>{}, k & 1, bw[(k / 2) % CB]);
       // half-stage hs + 1 has landed: loads issued after it are those of hs + 2 .. hs + P
       wait_vmcnt<loads_between<kDma, NB>(k + 1, k + P)>();
       ring_barrier();
@@ -254,8 +270,13 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
   } while (base < hstages);
 
   const float gm = gamma[0];
+  // store row block mi of the wave's tile, adding `other` (the other K group's partial of
+  // the same row block, lane-major per column block)
+  auto store_block = [&](auto mc, const v4i* other) {
+    constexpr int mi = decltype(mc)::value;
+    v4i part[NB];
 #pragma unroll
-  for (int mi = 0; mi < MB; ++mi) {
+    for (int j = 0; j < NB; ++j) part[j] = other[j * 64];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = m0 + wm * WM + 16 * mi + 4 * g + v;
@@ -265,16 +286,59 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint8_t* __restrict__ p
       for (int j = 0; j < NB; ++j) {
         const int n = n0 + wn * WN + 16 * j + r;
         if (n < N) {
-          const int32_t a = acc[mi][j][v];
+          const int32_t a = acc[mi][j][v] + part[j][v];
           if (acc_out) acc_out[(size_t)m * N + n] = a;
           if (Y) Y[(size_t)m * N + n] = (float)a * sc;
         }
       }
     }
+  };
+  if constexpr (KS == 1) {
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * WM + 16 * mi + 4 * g + v;
+        if (m >= M) continue;
+        const float sc = gm * absmax[m] * (1.0f / 127.0f);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int n = n0 + wn * WN + 16 * j + r;
+          if (n < N) {
+            const int32_t a = acc[mi][j][v];
+            if (acc_out) acc_out[(size_t)m * N + n] = a;
+            if (Y) Y[(size_t)m * N + n] = (float)a * sc;
+          }
+        }
+      }
+    }
+  } else {
+    // Group 0 stores row blocks mi < MB/2 and group 1 the rest, each adding the other
+    // group's partial (int32, exact), which comes through LDS one row block per pass.
+    // The accumulators are only read (no VALU writes to them), which keeps the register
+    // count at the one-group kernel's.
+    wait_vmcnt<0>();  // ring refills past the last chunk have landed before the slots are reused
+    ring_barrier();
+    v4i* out = reinterpret_cast<v4i*>(kg == 0 ? As0 : As1) + wave * NB * 64 + lane;
+    const v4i* in = reinterpret_cast<const v4i*>(kg == 0 ? As1 : As0) + wave * NB * 64 + lane;
+    static_for<MB / 2>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      if (kg == 0) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) out[j * 64] = acc[MB / 2 + p][j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) out[j * 64] = acc[p][j];
+      }
+      ring_barrier();
+      if (kg == 0) store_block(std::integral_constant<int, p>{}, in);
+      else store_block(std::integral_constant<int, MB / 2 + p>{}, in);
+      ring_barrier();
+    });
   }
 }
 
-template <int GM, int GN, int WM, int WN, int D, int kPipe = 0>
+template <int GM, int GN, int WM, int WN, int D, int kPipe = 0, int KS = 1>
 hipError_t launch(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax, int64_t M,
                   int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s) {
   const int64_t K_pad = k_pad(K);
@@ -284,7 +348,7 @@ hipError_t launch(const uint8_t* packed, const float* gamma, const int8_t* Xq, c
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   const int tiles = tiles_m * tiles_n;
   const int grid = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL((k_gemm_mfma<GM, GN, WM, WN, D, kPipe>), dim3(grid), dim3(256), 0, s, packed, gamma, Xq, absmax, (int)M,
+  hipLaunchKernelGGL((k_gemm_mfma<GM, GN, WM, WN, D, kPipe, KS>), dim3(grid), dim3(256 * KS), 0, s, packed, gamma, Xq, absmax, (int)M,
                      (int)N, n_blocks, (int)K_pad, chunks, tiles_m, tiles_n, Y, acc);
   return hipGetLastError();
 }
@@ -294,29 +358,45 @@ hipError_t launch(const uint8_t* packed, const float* gamma, const int8_t* Xq, c
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   (void)K;
   GemmPlan p;
-  p.threads = 256;
-  // Three tile shapes of 64 rows, four waves each:
+  // Tile shapes of 64 rows; each K group is four waves:
   //   64 x 256: waves of 64 x 64 side by side (three-slot ring, 24 KiB of LDS, 152
   //             registers, three workgroups per CU): the most work per operand byte;
   //   64 x 192: waves of 64 x 48 (118 registers, four per CU): the same structure, for
   //             column counts that 256 would leave a ragged last round on;
-  //   64 x 128: 2 x 2 waves of 32 x 64 (124 registers, four per CU), when 64 x 256 tiles
-  //             would not even give every CU one, so that short shapes fill the chip.
-  // Between the first two, the cost of the last round decides: rounds of 256 tiles times
-  // the tile width, the 48-column waves counted at 0.976 of the 64-column rate (measured
-  // 8192^3: 486 vs 474 us).  Measured at M = 2048: 2560 columns 49.1 us (64 x 128) ->
-  // 43.9 us (64 x 192), 6912 columns 46.8 us (64 x 256) -> 45.9 us (64 x 192); 8192^3,
-  // 4096 x 2560 x 6912 and 2048 x 28672 x 8192 stay on 64 x 256.
+  //   64 x 128: 2 x 2 waves of 32 x 64 (124 registers, four per CU), for the few short
+  //             shapes that neither of the rules below covers.
+  // Where the tiles do not fill the chip, two K groups of four waves share each tile (eight
+  // waves, each group half the chunks, partials summed through LDS): twice the waves per
+  // tile at the same operand bytes per tile.  64 x 256 tiles when that gives 193..256 of
+  // them (one eight-wave workgroup per CU), else 64 x 192 tiles when there are at most 256
+  // (two per CU fit).  Measured: 1024 x 2560 x 6912 35.7 -> 27.4 us, 1024 x 2560 x 2560 18.1
+  // -> 14.1 us, 512 x 8192 x 8192 43.2 -> 37.4 us, 512 x 6912 x 2560 19.2 -> 17.2 us,
+  // 1536 x 2560 x 2560 18.4 -> 17.2 us; the one shape measured slower, 512 x 2560 x 6912, by
+  // 3 % (25.2 -> 25.9 us).  With more tiles the split costs more than it gives (2048 x 6912
+  // x 2560: 45.2 -> 48.7 us).
+  // Otherwise, between 64 x 256 and 64 x 192, the cost of the last round decides: rounds of
+  // 256 tiles times the tile width, the 48-column waves counted at 0.976 of the 64-column
+  // rate (measured 8192^3: 486 vs 474 us).  Measured at M = 2048: 2560 columns 49.1 us
+  // (64 x 128) -> 43.9 us (64 x 192), 6912 columns 46.8 us (64 x 256) -> 45.9 us (64 x 192);
+  // 8192^3, 4096 x 2560 x 6912 and 2048 x 28672 x 8192 stay on 64 x 256.
   const int64_t tm = (M + 63) / 64;
   const int64_t t256 = tm * ((N + 255) / 256), t192 = tm * ((N + 191) / 192);
   p.bm = 64;
-  if (t256 < 256) {
+  p.ks = 1;
+  if (t256 > 192 && t256 <= 256) {
+    p.bn = 256;
+    p.ks = 2;
+  } else if (t192 <= 256) {
+    p.bn = 192;
+    p.ks = 2;
+  } else if (t256 < 256) {
     p.bn = 128;
   } else {
     const double c256 = (double)((t256 + 255) / 256) * 256.0;
     const double c192 = (double)((t192 + 255) / 256) * 192.0 / 0.976;
     p.bn = c192 < c256 ? 192 : 256;
   }
+  p.threads = 256 * p.ks;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   p.groups = 8 * ((tiles + 7) / 8);
   return p;
@@ -325,6 +405,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s) {
   const GemmPlan p = plan_gemm(M, N, K);
+  if (p.ks == 2) {
+    if (p.bn == 256) return launch<1, 4, 64, 64, 3, 0, 2>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
+    return launch<1, 4, 64, 48, 3, 0, 2>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
+  }
   if (p.bn == 256) return launch<1, 4, 64, 64, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
   if (p.bn == 192) return launch<1, 4, 64, 48, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
   return launch<2, 2, 32, 64, 3, 1>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);

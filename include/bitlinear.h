@@ -289,8 +289,9 @@ int bitlinear_forward_binary_plan(int64_t M, int64_t N, int64_t K, int32_t out[6
  * prefill: output tile rows, out[4] = decode: where the activations live (0 = loaded with
  * each weight tile, 1 = staged in LDS, 2 = held in registers and broadcast across lanes),
  * prefill: output tile columns, out[5] = decode: dynamic LDS bytes (out[4] = 1) or K
- * tiles per wave (out[4] = 2), else 0.  Returns BL_OK or BL_ERR_INVALID_ARG (same size
- * rules as bitlinear_forward, null out).
+ * tiles per wave (out[4] = 2), else 0; prefill: groups of four waves that split each
+ * tile's K range (1 or 2).  Returns BL_OK or BL_ERR_INVALID_ARG (same size rules as
+ * bitlinear_forward, null out).
  */
 int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]);
 

@@ -301,15 +301,20 @@ def test_forward_prefill(m, n, k):
     _fwd_check(m, n, k, seed=m * 1000 + n + k)
 
 
-@pytest.mark.parametrize("m,n,k,tile_n", [(2048, 4100, 1000, 192), (1000, 3000, 777, 128), (333, 24000, 2600, 192),
-                                          (4000, 8190, 1000, 256), (3000, 9000, 700, 192), (2048, 2560, 6912, 192)])
-def test_forward_prefill_tile_shapes(m, n, k, tile_n):
-    # the three prefill tile shapes (64 x 256 or 64 x 192 by the last round's load, 64 x
-    # 128 for short shapes) with ragged M, N and K; the oracle checks a sample of token
-    # rows covering tile edges
+@pytest.mark.parametrize("m,n,k,tile_n,k_groups", [
+    (2048, 4100, 1000, 192, 1), (333, 24000, 2600, 192, 1), (4000, 8190, 1000, 256, 1), (3000, 9000, 700, 192, 1),
+    (2048, 2560, 6912, 192, 1), (1500, 2000, 777, 128, 1),
+    # two K groups per tile where the tiles do not fill the chip; odd chunk counts (K = 1100:
+    # 5 chunks, 6912: 27) leave the second group one chunk short
+    (1000, 3000, 777, 192, 2), (700, 2600, 1100, 192, 2), (500, 7000, 1100, 256, 2), (450, 8000, 6912, 256, 2)])
+def test_forward_prefill_tile_shapes(m, n, k, tile_n, k_groups):
+    # the prefill tile shapes (64 x 256 or 64 x 192 by the last round's load, 64 x 128 for
+    # a few short shapes, one or two K groups per tile) with ragged M, N and K; the oracle
+    # checks a sample of token rows covering tile edges
     plan = bl.forward_plan(m, n, k)
     _announce("forward prefill tiles", m, n, k, plan)
     assert plan["kernel"] == "prefill" and plan["tile_m"] == 64 and plan["tile_n"] == tile_n
+    assert plan["k_groups"] == k_groups and plan["threads"] == 256 * k_groups
     rng = np.random.default_rng(m + n + k)
     q = rng.integers(-1, 2, (n, k)).astype(np.int8)
     x = synth.activations(m, k, seed=m + k, dtype=torch.float32, outlier_p=0.01, outlier_mult=20.0).numpy()
