@@ -12,9 +12,11 @@ constexpr int kVersion = 10000;  // 1.0.0
 constexpr int64_t kMaxCount = int64_t(1) << 40;  // exactness bound of the gamma bins
 constexpr int64_t kMaxK = int64_t(1) << 24;      // |acc| <= 127 K < 2^31, and exact in fp32 for K < 2^17
 constexpr int64_t kMaxDim = int64_t(1) << 31;
-constexpr int kDecodeMaxM = 16;                  // tokens handled by the decode kernel
+constexpr int kDecodeMaxM = 16;                  // tokens always handled by the decode kernels
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+// decode kernels for up to 16 tokens, and for 17..64 where token groups beat the prefill kernel
+bool use_decode(int64_t M, int64_t N, int64_t K) { return M <= kDecodeMaxM || bl::token_groups_win(M, N, K); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
@@ -90,7 +92,7 @@ int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* X
       (Y && !aligned(Y, 4)) || (acc && !aligned(acc, 4)))
     return BL_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (M <= kDecodeMaxM) return hip_status(bl::launch_gemv(packed, gamma, Xq, absmax, M, N, K, Y, acc, s));
+  if (use_decode(M, N, K)) return hip_status(bl::launch_gemv(packed, gamma, Xq, absmax, M, N, K, Y, acc, s));
   if (bl::plan_gemm(M, N, K).groups > (int64_t(1) << 30)) return BL_ERR_UNSUPPORTED;  // grid size
   return hip_status(bl::launch_gemm(packed, gamma, Xq, absmax, M, N, K, Y, acc, s));
 }
@@ -326,7 +328,7 @@ int bitlinear_forward_subln_plan(int64_t M, int64_t N, int64_t K, int dt, int32_
 
 int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]) {
   if (!out || M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BL_ERR_INVALID_ARG;
-  if (M <= kDecodeMaxM) {
+  if (use_decode(M, N, K)) {
     const bl::GemvPlan p = bl::plan_gemv(M, N, K, 0);
     out[0] = 1;
     out[1] = (int32_t)p.groups;

@@ -101,12 +101,16 @@ struct GemvPlan {
   bool mid = false;     // fused dpp, up to two workgroups per unit and short runs: weight
                         // loads issued once the activation pieces have landed
   int stage = 0;        // LDS staging: 16-byte activation pieces per thread
+  int tg = 1;           // token groups of 16 (17..64 tokens: 2..4)
   bool ok = true;       // the requested activation source is supported by this plan
   int64_t groups = 0;   // workgroups
 };
 // src: 0 = int8 activations (bitlinear_forward), 1 = bf16 x, 2 = fp32 x (fused form),
 // 3 / 4 = bf16 / fp32 x through the sub-layer normalisation (register form only)
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src);
+// 17..64 tokens: true where the decode kernel with token groups of 16 is the faster path
+// (else the prefill kernel takes them)
+bool token_groups_win(int64_t M, int64_t N, int64_t K);
 
 // Launch plan of the prefill kernel.
 struct GemmPlan {

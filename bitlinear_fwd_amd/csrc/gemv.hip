@@ -44,21 +44,23 @@ namespace {
 constexpr int kMaxLdsActBytes = 48 * 1024;
 constexpr int64_t kMaxFusedElems = 8192;  // M*K limit of the one-kernel quantise + decode
 
-// Sum the W waves' partial tiles (red[w][j][lane]) and write y / acc for row block j.
-template <int W, int RB>
+// Sum the W waves' partial tiles (red[w][t][j][lane]) and write y / acc for token group t
+// (tokens 16 t .. 16 t + 15) of row block j.
+template <int W, int RB, int TG = 1>
 __device__ __forceinline__ void gemv_epilogue(const v4i* red, int wave, int lane, int rb0, int rblocks, int M, int N,
                                               float gm, const float* absmax, float* Y, int32_t* acc_out) {
   const int r = lane & 15, g = lane >> 4;
-  for (int j = wave; j < RB; j += W) {
+  for (int jj = wave; jj < RB * TG; jj += W) {
+    const int t = TG == 1 ? 0 : jj / RB, j = TG == 1 ? jj : jj % RB;
     if (rb0 + j >= rblocks) continue;
-    v4i s = red[j * 64 + lane];
-    for (int w = 1; w < W; ++w) s += red[(w * RB + j) * 64 + lane];
-    // lane holds D[4g + v][r]: token m = 4g + v, output n = 16*(rb0 + j) + r
+    v4i s = red[jj * 64 + lane];
+    for (int w = 1; w < W; ++w) s += red[(w * RB * TG + jj) * 64 + lane];
+    // lane holds D[4g + v][r]: token m = 16t + 4g + v, output n = 16*(rb0 + j) + r
     const int n = (rb0 + j) * kTileRows + r;
     if (n >= N) continue;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int m = 4 * g + v;
+      const int m = 16 * t + 4 * g + v;
       if (m < M) {
         if (acc_out) acc_out[(size_t)m * N + n] = s[v];
         if (Y) Y[(size_t)m * N + n] = (float)s[v] * gm * absmax[m] * (1.0f / 127.0f);
@@ -247,14 +249,15 @@ __global__ __launch_bounds__(W * 64) void k_gemv_lds(const uint8_t* __restrict__
 
 // ---------------------------------------------------------------------------------------
 // k_gemv_reg: activation fragments in registers, loaded per tile index with the weights
-// of that batch and shared by the RB row blocks of the workgroup.
-template <int W, int RB, int U, int NB>
+// of that batch and shared by the RB row blocks of the workgroup.  TG token groups of 16
+// (up to 64 tokens): each decoded weight fragment feeds TG matrix-core steps.
+template <int W, int RB, int U, int NB, int TG = 1>
 __global__ __launch_bounds__(W * 64) void k_gemv_reg(const uint8_t* __restrict__ packed,
                                                      const float* __restrict__ gamma, const int8_t* __restrict__ Xq,
                                                      const float* __restrict__ absmax, int M, int N, int K_pad,
                                                      int chunks, int rblocks, float* __restrict__ Y,
                                                      int32_t* __restrict__ acc_out) {
-  __shared__ v4i red[W * RB * 64];
+  __shared__ v4i red[W * RB * TG * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
@@ -262,41 +265,63 @@ __global__ __launch_bounds__(W * 64) void k_gemv_reg(const uint8_t* __restrict__
   const int tpw = (chunks + W - 1) / W;
   const int c0 = wave * tpw;
   const int c1 = min(chunks, c0 + tpw);
-  const int row = min(r, M - 1);
   const uint4* wsrc[RB];
 #pragma unroll
   for (int j = 0; j < RB; ++j)
     wsrc[j] = reinterpret_cast<const uint4*>(packed) + (size_t)min(rb0 + j, rblocks - 1) * chunks * 64 + lane;
-  const int8_t* xrow = Xq + (size_t)row * K_pad + 64 * g;
+  // token group tg reads token rows 16 tg + r (rows past M repeat row M-1: never stored)
+  const int8_t* xrow[TG];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) xrow[tg] = Xq + (size_t)min(16 * tg + r, M - 1) * K_pad + 64 * g;
   uint4 w[NB][U][RB];
-  uint4 a[NB][U][4];
+  uint4 a[NB][U][TG][4];
   auto load = [&](int b, int cb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = min(cb + u, c1 - 1);
 #pragma unroll
       for (int j = 0; j < RB; ++j) w[b][u][j] = load_nt(wsrc[j] + (size_t)t * 64);
-      const uint4* p = reinterpret_cast<const uint4*>(xrow + (size_t)t * kTileCols);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[b][u][i] = p[i];
+      for (int tg = 0; tg < TG; ++tg) {
+        const uint4* p = reinterpret_cast<const uint4*>(xrow[tg] + (size_t)t * kTileCols);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[b][u][tg][i] = p[i];
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  v4i c[RB];
+  v4i c[TG][RB];
 #pragma unroll
-  for (int j = 0; j < RB; ++j) c[j] = (v4i){0, 0, 0, 0};
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int j = 0; j < RB; ++j) c[tg][j] = (v4i){0, 0, 0, 0};
   auto compute = [&](int b, int cb, bool tail) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool live = !tail || cb + u < c1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const v4i av = as_v4i(a[b][u][i]);
+        if constexpr (TG == 1) {
+          const v4i av = as_v4i(a[b][u][0][i]);
 #pragma unroll
-        for (int j = 0; j < RB; ++j) {
-          uint32_t word = word_of(w[b][u][j], i);
-          if (tail) word = live ? word : 0u;
-          c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, decode16(word), c[j], 0, 0, 0);
+          for (int j = 0; j < RB; ++j) {
+            uint32_t word = word_of(w[b][u][j], i);
+            if (tail) word = live ? word : 0u;
+            c[0][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, decode16(word), c[0][j], 0, 0, 0);
+          }
+        } else {
+          v4i wd[RB];
+#pragma unroll
+          for (int j = 0; j < RB; ++j) {
+            uint32_t word = word_of(w[b][u][j], i);
+            if (tail) word = live ? word : 0u;
+            wd[j] = decode16(word);
+          }
+#pragma unroll
+          for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+            for (int j = 0; j < RB; ++j)
+              c[tg][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(a[b][u][tg][i]), wd[j], c[tg][j], 0, 0, 0);
         }
       }
     }
@@ -324,9 +349,11 @@ __global__ __launch_bounds__(W * 64) void k_gemv_reg(const uint8_t* __restrict__
   }
   // a missing row block (past rblocks) re-read a valid block's codes: never stored
 #pragma unroll
-  for (int j = 0; j < RB; ++j) red[(wave * RB + j) * 64 + lane] = c[j];
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int j = 0; j < RB; ++j) red[((wave * TG + tg) * RB + j) * 64 + lane] = c[tg][j];
   __syncthreads();
-  gemv_epilogue<W, RB>(red, wave, lane, rb0, rblocks, M, N, gamma[0], absmax, Y, acc_out);
+  gemv_epilogue<W, RB, TG>(red, wave, lane, rb0, rblocks, M, N, gamma[0], absmax, Y, acc_out);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -856,10 +883,10 @@ hipError_t launch_lds_w(int W, int S, const Args& a, hipStream_t s) {
   }
 }
 
-template <int W, int RB, int U, int NB>
+template <int W, int RB, int U, int NB, int TG = 1>
 hipError_t launch_reg(const Args& a, hipStream_t s) {
   const unsigned groups = (unsigned)((a.rblocks + RB - 1) / RB);
-  hipLaunchKernelGGL((k_gemv_reg<W, RB, U, NB>), dim3(groups), dim3(W * 64), 0, s, a.packed, a.gamma,
+  hipLaunchKernelGGL((k_gemv_reg<W, RB, U, NB, TG>), dim3(groups), dim3(W * 64), 0, s, a.packed, a.gamma,
                      static_cast<const int8_t*>(a.X), a.absmax, a.M, a.N, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc);
   return hipGetLastError();
 }
@@ -872,6 +899,18 @@ hipError_t launch_reg_w(int W, const Args& a, hipStream_t s) {
     case 4: return launch_reg<4, RB, U, NB>(a, s);
     case 2: return launch_reg<2, RB, U, NB>(a, s);
     default: return launch_reg<1, RB, U, NB>(a, s);
+  }
+}
+
+// 17..64 tokens: token groups of 16, one row block per workgroup, at most 8 waves (the
+// partial-tile buffer is W * TG KiB of LDS)
+template <int TG>
+hipError_t launch_reg_tg_w(int W, const Args& a, hipStream_t s) {
+  switch (W) {
+    case 8: return launch_reg<8, 1, 1, 2, TG>(a, s);
+    case 4: return launch_reg<4, 1, 1, 2, TG>(a, s);
+    case 2: return launch_reg<2, 1, 1, 2, TG>(a, s);
+    default: return launch_reg<1, 1, 1, 2, TG>(a, s);
   }
 }
 
@@ -1032,6 +1071,21 @@ int pick_waves(int64_t chunks, int64_t groups) {
 
 }  // namespace
 
+bool token_groups_win(int64_t M, int64_t N, int64_t K) {
+  // 17..64 tokens.  The token-group decode kernel re-reads every token row once per row
+  // block from L2 (about 8 TB/s measured); the prefill kernel has one 64-row tile per 192
+  // columns and is bound by the latency of its K loop (about 1.35 us per pair of 256-column
+  // chunks with two K groups).  Fitted to 17..64 tokens on 2560 -> 2560 / 6912, 6912 ->
+  // 2560, 8192 -> 28672 and 28672 -> 8192: decode 4.2-15 us where the prefill kernel took
+  // 11-24 us on the 2B-class shapes; 8192 -> 28672 stays on the prefill kernel (27 us
+  // against 36-116 us), 28672 -> 8192 up to 32 tokens (39-69 us against 77 us).
+  if (M <= 16 || M > 64) return false;
+  const int64_t K_pad = k_pad(K), chunks = K_pad / kTileCols, rblocks = n_pad(N) / kTileRows;
+  const double reread_s = (double)rblocks * (double)M * (double)K_pad / 8e12;
+  const double kloop_s = 1.35e-6 * (double)((chunks + 1) / 2);
+  return reread_s < kloop_s;
+}
+
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   GemvPlan p;
   const int64_t K_pad = k_pad(K);
@@ -1093,6 +1147,16 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   p.lds_act = false;
   p.rb = 1;
   p.ok = src == 0;  // the register paths read int8 activations only
+  if (M > 16) {
+    // 17..64 tokens: token groups of 16 through k_gemv_reg, one row block per workgroup
+    // (N / 16 workgroups where the prefill kernel would have N / 192 tiles), at most 8
+    // waves, and the same wave rule as below
+    p.tg = (int)((M + 15) / 16);
+    p.groups = rblocks;
+    p.waves = std::min(pick_waves(chunks, rblocks), 8);
+    while (p.waves > 1 && chunks < 8 * p.waves && p.groups * (p.waves / 2) >= 1024) p.waves /= 2;
+    return p;
+  }
   if (M > 4 && chunks <= 16) {
     // 5..16 tokens on short rows: two-tile register runs (a token group of 8 or 16),
     // activation registers shared by two row blocks once there are enough blocks to fill
@@ -1121,6 +1185,12 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
   const GemvPlan p = plan_gemv(M, N, K, 0);
   Args a{packed, gamma, Xq, absmax, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
          (int)(n_pad(N) / kTileRows), Y, acc, nullptr, nullptr};
+  switch (p.tg) {
+    case 2: return launch_reg_tg_w<2>(p.waves, a, s);
+    case 3: return launch_reg_tg_w<3>(p.waves, a, s);
+    case 4: return launch_reg_tg_w<4>(p.waves, a, s);
+    default: break;
+  }
   if (p.dpp && M > 8) return p.rb == 2 ? launch_dppm<2, 16, 2>(p.waves, a, s) : launch_dppm<2, 16, 1>(p.waves, a, s);
   if (p.dpp && M > 4) return p.rb == 2 ? launch_dppm<2, 8, 2>(p.waves, a, s) : launch_dppm<2, 8, 1>(p.waves, a, s);
   if (p.dpp) return launch_dpp_run<0>(p.run, (int)M, p.waves, a, s);

@@ -112,7 +112,10 @@ int bitlinear_quantize_acts(const void* X, int dt, int64_t M, int64_t K, int8_t*
  *   Y       out (nullable): fp32 [M][N], y = acc * gamma * absmax[m] / 127.
  *   acc     out (nullable): int32 [M][N], the exact accumulators.
  * At least one of Y and acc must be non-null.  M = 1..16 runs the decode kernels
- * (HBM-streaming, MFMA on in-register decoded weights); larger M runs the prefill GEMM
+ * (HBM-streaming, MFMA on in-register decoded weights), and so does M = 17..64 in token
+ * groups of 16 sharing each decoded weight fragment where that is estimated faster (every
+ * row block re-reads the token rows: short rows and few row blocks); other M runs the
+ * prefill GEMM
  * (activations staged in LDS, weights decoded in registers, int8 MFMA).  |acc| <= 127*K
  * must fit int32: K <= 2^24.
  */

@@ -268,12 +268,24 @@ def test_binary_sizes_plan_and_validation():
     assert f(FAKE, FAKE, FAKE, FAKE, 5, 16, 512, FAKE, None, None) == bl.BL_ERR_UNSUPPORTED
 
 
+def test_token_group_routing():
+    # 17..64 tokens go to the decode kernel with token groups where its L2 re-reads of the
+    # token rows cost less than the prefill kernel's K loop; 65 and more always prefill
+    decode = [(17, 2560, 2560), (64, 2560, 2560), (48, 6912, 2560), (64, 2560, 6912), (17, 8192, 28672),
+              (32, 8192, 28672), (40, 72, 700)]
+    prefill = [(17, 28672, 8192), (64, 28672, 8192), (48, 8192, 28672), (17, 28672, 4096), (65, 64, 256)]
+    for m, n, k in decode:
+        assert bl.forward_plan(m, n, k)["kernel"] == "decode", (m, n, k)
+    for m, n, k in prefill:
+        assert bl.forward_plan(m, n, k)["kernel"] == "prefill", (m, n, k)
+
+
 def test_launch_plans_cover_every_tile():
     # host-only sweep of every planner: a plan's waves x tiles per wave must cover all K
     # tiles, and its workgroups all row blocks, or outputs would silently go missing
     shapes_k = [1, 8, 255, 256, 257, 1000, 2560, 4096, 6912, 8192, 12000, 28672, 40000]
     shapes_n = [1, 16, 17, 640, 2560, 6912, 28672]
-    for m in (1, 2, 3, 4, 5, 8, 16):
+    for m in (1, 2, 3, 4, 5, 8, 16, 17, 32, 33, 48, 64):
         for k in shapes_k:
             chunks = bl.k_pad(k) // 256
             chunks_b = bl.kb_pad(k) // 512
@@ -291,6 +303,11 @@ def test_launch_plans_cover_every_tile():
                         assert waves * p["tiles_per_wave"] >= chunks, (name, m, n, k, p)
                         assert waves <= 16 and (waves - 1) * p["tiles_per_wave"] < chunks, (name, m, n, k, p)
                         assert p["workgroups"] * p["row_blocks"] >= rblocks, (name, m, n, k, p)
+                    if p["kernel"] == "decode" and p["acts"] == "per-tile loads":
+                        # waves split the K tiles into contiguous runs; workgroups own row blocks
+                        assert p["threads"] // 64 <= (8 if m > 16 else 16), (name, m, n, k, p)
+                        assert p["workgroups"] * p["row_blocks"] >= rblocks, (name, m, n, k, p)
+                    assert p["kernel"] != "prefill" if m <= 16 else True, (name, m, n, k, p)
                 lut = bl.forward_lut_plan(m, n, k)
                 if lut is not None:
                     waves = lut["threads"] // 64

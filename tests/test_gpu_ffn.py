@@ -77,7 +77,8 @@ def test_gated_pair_one_kernel(m, n, k, dtype, subln):
 @pytest.mark.parametrize("m,n,k,dtype,subln,unaligned", [
     (8, 300, 2560, torch.bfloat16, False, False),   # more tokens: quantiser, two forwards, gating
     (16, 512, 2560, torch.bfloat16, True, False),
-    (40, 130, 1000, torch.float32, False, False),   # prefill sizes
+    (40, 130, 1000, torch.float32, False, False),   # 17..64 tokens: token groups
+    (100, 130, 1000, torch.bfloat16, True, False),  # prefill sizes
     (1, 64, 300, torch.bfloat16, False, False),     # K not a multiple of 8
     (2, 64, 1024, torch.bfloat16, True, True),      # unaligned x
 ])

@@ -294,7 +294,28 @@ def test_forward_decode_variants(m, n, k, acts, rb, run):
     _fwd_check(m, n, k, seed=m * 7 + n * 3 + k)
 
 
-@pytest.mark.parametrize("m", [17, 31, 64, 100, 128, 129, 257])
+@pytest.mark.parametrize("m", [17, 24, 32, 33, 48, 49, 64])
+@pytest.mark.parametrize("n,k", [(16, 256), (17, 300), (130, 1000), (2560, 2560), (300, 6912), (1, 1)])
+def test_forward_token_groups(m, n, k):
+    # 17..64 tokens: the decode kernel with 2..4 token groups of 16 (the last one ragged)
+    # sharing each decoded weight fragment, 1..8 waves, against the oracle on every output
+    plan = bl.forward_plan(m, n, k)
+    _announce("forward token groups", m, n, k, plan)
+    assert plan["kernel"] == "decode" and plan["acts"] == "per-tile loads" and plan["threads"] <= 512
+    _fwd_check(m, n, k, seed=m * 1000 + n + k)
+
+
+@pytest.mark.parametrize("m,n,k", [(24, 20000, 2048), (64, 9000, 4096)])
+def test_forward_prefill_few_tokens(m, n, k):
+    # 17..64 tokens where the token rows would be re-read by too many row blocks: the
+    # prefill kernel (one 64-row tile high, two K groups), against the oracle on every output
+    plan = bl.forward_plan(m, n, k)
+    _announce("forward prefill few tokens", m, n, k, plan)
+    assert plan["kernel"] == "prefill" and plan["k_groups"] == 2
+    _fwd_check(m, n, k, seed=m * 1000 + n + k)
+
+
+@pytest.mark.parametrize("m", [65, 100, 128, 129, 257])
 @pytest.mark.parametrize("n,k", [(16, 256), (17, 300), (130, 1000), (300, 2304), (1, 1), (129, 513)])
 def test_forward_prefill(m, n, k):
     _announce("forward prefill", m, n, k)
@@ -334,7 +355,7 @@ def test_forward_extreme_accumulators():
     # all +1 / all -1 rows against all +127 activations: |acc| = 127 K, the int32 range
     # the path guarantees for the largest K of the workloads
     k = 28672
-    for m in (1, 16, 40):
+    for m in (1, 16, 40, 80):
         _announce("forward extreme", m)
         q = np.ones((32, k), np.int8)
         q[1::2] = -1
@@ -353,7 +374,8 @@ def test_forward_extreme_accumulators():
 def test_forward_at_the_largest_k(m):
     # K = 2^24, the library's limit: |acc| <= 127 K = 2^31 - 2^24 still fits int32.  Closed
     # form on extreme rows (all +1 / all -1 against +127), and random codes against the
-    # oracle on the decode (M <= 16) and prefill (M = 17) kernels
+    # oracle on the decode kernels (M = 1, 3; M = 17 in two token groups).  The prefill kernel
+    # meets the same per-element bound at K = 28672 in test_forward_extreme_accumulators.
     k, n = 1 << 24, 18
     _announce("forward at K = 2^24", m)
     rng = np.random.default_rng(m)
@@ -481,7 +503,8 @@ def test_forward_fused_lds_form(m, n, k, dtype):
 
 @pytest.mark.parametrize("m,n,k,dtype,unaligned", [(5, 64, 512, torch.bfloat16, False), (1, 64, 300, torch.bfloat16, False),
                                                    (2, 64, 1002, torch.float32, False), (3, 40, 512, torch.bfloat16, True),
-                                                   (40, 72, 700, torch.float32, False), (3, 40, 12000, torch.float32, False),
+                                                   (40, 72, 700, torch.float32, False), (100, 72, 700, torch.bfloat16, False),
+                                                   (3, 40, 12000, torch.float32, False),
                                                    (4, 30, 20000, torch.bfloat16, False)])
 def test_forward_fused_fallback(m, n, k, dtype, unaligned):
     # shapes outside the one-kernel path: the quantiser kernel then the forward kernel
@@ -520,7 +543,8 @@ def _grouped_check(m, ns, k, dtype, seed):
     (4, [700, 900], 4096, torch.float32),
     (1, [512], 256, torch.float32),                    # a group of one
     (8, [300, 100], 2560, torch.bfloat16),             # more tokens: quantiser once, then forwards
-    (40, [130, 64], 1000, torch.float32),              # prefill sizes
+    (40, [130, 64], 1000, torch.float32),              # 17..64 tokens: token groups
+    (100, [130, 64], 1000, torch.bfloat16),            # prefill sizes
     (1, [100, 200], 300, torch.bfloat16),              # K not a multiple of 8: quantiser path
     (2, [2560, 2560], 2560, torch.bfloat16),           # 320 row blocks: weights issued as activations land
     (1, [4096, 2048], 4096, torch.float32),            # 384 row blocks

@@ -154,7 +154,7 @@ def test_forward_subln_single_kernel(m, n, k, dtype, gain):
     (5, 64, 512, torch.bfloat16, "signed"), (16, 300, 2560, torch.bfloat16, "pos"),
     (1, 64, 300, torch.bfloat16, "signed"), (4, 30, 20000, torch.bfloat16, "pos"),
     (3, 40, 12000, torch.float32, "none"), (2, 64, 1000, torch.bfloat16, "unaligned"),
-    (40, 72, 700, torch.float32, "signed"),
+    (40, 72, 700, torch.float32, "signed"), (100, 72, 700, torch.bfloat16, "pos"),
 ])
 def test_forward_subln_two_kernels(m, n, k, dtype, gain):
     # outside the one-kernel path: the normalising quantiser, then the forward kernel
