@@ -663,7 +663,7 @@ def main():
         launch_bytes, launch_ops = head.bytes_per_step() / len(mats), head.ops_per_step() / len(mats)
         launch_timing = "timed region / launches (the step is only this kernel)"
     else:
-        launch_ms, launch_bytes, launch_ops = time_forward_only(head, 3 if head.sweep else 40 * len(head.sets))
+        launch_ms, launch_bytes, launch_ops = time_forward_only(head, 3 if head.sweep else max(40, 4 * len(head.sets)))
         launch_timing = "graph replays of the forward launches alone"
     value = head.bytes_per_step() / (ms * 1e-3) / 1e9 if decode else head.ops_per_step() / (ms * 1e-3) / 1e12
     kernel = dominant_kernel(head)
@@ -730,7 +730,7 @@ def main():
                 if subln:
                     legs[key]["note"] += "; sub-layer RMS normalisation in front of the quantiser"
             elif path != "fused":
-                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 40 * len(w.sets))
+                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else max(40, 4 * len(w.sets)))
                 legs[key] = leg_summary(w, lms, l_ms, l_b, l_o, ceilings)
                 legs[key]["kernel"] = {"lut": "k_gemv_lut (table-lookup decode)",
                                        "binary": "k_gemv_bin (1-bit sign-binary decode)"}.get(path) or dominant_kernel(w)
@@ -746,7 +746,7 @@ def main():
                 legs[key]["note"] = ("sub-layer RMS normalisation (per-feature gain, eps 1e-5) in front of the "
                                      "quantiser, in the same kernel where the plan fuses it")
             else:
-                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else 40 * len(w.sets))
+                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else max(40, 4 * len(w.sets)))
                 legs[key] = leg_summary(w, lms, l_ms, l_b, l_o, ceilings)
                 legs[key]["kernel"] = dominant_kernel(w)
                 legs[key]["traffic_bytes_per_launch"] = measured_traffic(dominant_kernel(w), idx, m)
