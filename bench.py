@@ -292,10 +292,10 @@ TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
     # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.2 KiB (x1.99980),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4586678, "fetch_kib": 2227.17, "write_kib": 25.28, "sha": "f7b3ff610e0d8111"},
-    (2, 16): {"bytes_per_launch": 3152324, "fetch_kib": 1437.65, "write_kib": 203.43, "sha": "f7b3ff610e0d8111"},
-    (3, 2048): {"bytes_per_launch": 97854081, "fetch_kib": 28839.16, "write_kib": 37888.19, "sha": "c189f7b120dfe497"},
-    (4, 1): {"bytes_per_launch": 59263829, "fetch_kib": 28895.01, "write_kib": 90.03, "sha": "f7b3ff610e0d8111"},
+    (1, 1): {"bytes_per_launch": 4591119, "fetch_kib": 2229.34, "write_kib": 25.28, "sha": "7934f31bef25a4c5"},
+    (2, 16): {"bytes_per_launch": 3158902, "fetch_kib": 1440.86, "write_kib": 203.43, "sha": "7934f31bef25a4c5"},
+    (3, 2048): {"bytes_per_launch": 97657963, "fetch_kib": 28743.36, "write_kib": 37888.20, "sha": "eb34b544b8f58144"},
+    (4, 1): {"bytes_per_launch": 59256152, "fetch_kib": 28891.26, "write_kib": 90.03, "sha": "7934f31bef25a4c5"},
 }
 
 
