@@ -902,16 +902,23 @@ hipError_t launch_reg_w(int W, const Args& a, hipStream_t s) {
   }
 }
 
-// 17..64 tokens: token groups of 16, one row block per workgroup, at most 8 waves (the
-// partial-tile buffer is W * TG KiB of LDS)
+// 17..64 tokens: token groups of 16 and RB row blocks per workgroup; the planner keeps
+// W * RB * TG <= 32 (the partial-tile buffer is W * RB * TG KiB of LDS)
+template <int TG, int RB>
+hipError_t launch_reg_tg_rb(int W, const Args& a, hipStream_t s) {
+  if constexpr (8 * RB * TG <= 32)
+    if (W == 8) return launch_reg<8, RB, 1, 2, TG>(a, s);
+  if constexpr (4 * RB * TG <= 32)
+    if (W == 4) return launch_reg<4, RB, 1, 2, TG>(a, s);
+  if (W == 2) return launch_reg<2, RB, 1, 2, TG>(a, s);
+  if (W == 1) return launch_reg<1, RB, 1, 2, TG>(a, s);
+  return hipErrorInvalidConfiguration;  // not planned
+}
 template <int TG>
-hipError_t launch_reg_tg_w(int W, const Args& a, hipStream_t s) {
-  switch (W) {
-    case 8: return launch_reg<8, 1, 1, 2, TG>(a, s);
-    case 4: return launch_reg<4, 1, 1, 2, TG>(a, s);
-    case 2: return launch_reg<2, 1, 1, 2, TG>(a, s);
-    default: return launch_reg<1, 1, 1, 2, TG>(a, s);
-  }
+hipError_t launch_reg_tg_w(int W, int RB, const Args& a, hipStream_t s) {
+  if (RB == 4) return launch_reg_tg_rb<TG, 4>(W, a, s);
+  if (RB == 2) return launch_reg_tg_rb<TG, 2>(W, a, s);
+  return launch_reg_tg_rb<TG, 1>(W, a, s);
 }
 
 // Fused forms hold the raw activation pieces in registers until the barrier: limit them
@@ -1071,17 +1078,22 @@ int pick_waves(int64_t chunks, int64_t groups) {
 
 }  // namespace
 
+// row blocks per workgroup of the token-group decode
+static int token_group_rb(int64_t rblocks) { return rblocks >= 1024 ? 4 : (rblocks >= 384 ? 2 : 1); }
+
 bool token_groups_win(int64_t M, int64_t N, int64_t K) {
-  // 17..64 tokens.  The token-group decode kernel re-reads every token row once per row
-  // block from L2 (about 8 TB/s measured); the prefill kernel has one 64-row tile per 192
-  // columns and is bound by the latency of its K loop (about 1.35 us per pair of 256-column
-  // chunks with two K groups).  Fitted to 17..64 tokens on 2560 -> 2560 / 6912, 6912 ->
-  // 2560, 8192 -> 28672 and 28672 -> 8192: decode 4.2-15 us where the prefill kernel took
-  // 11-24 us on the 2B-class shapes; 8192 -> 28672 stays on the prefill kernel (27 us
-  // against 36-116 us), 28672 -> 8192 up to 32 tokens (39-69 us against 77 us).
+  // 17..64 tokens.  The token-group decode kernel re-reads every token row once per
+  // workgroup from L2 (about 8 TB/s measured); the prefill kernel has one 64-row tile per
+  // 192 columns and is bound by the latency of its K loop (about 1.35 us per pair of
+  // 256-column chunks with two K groups).  Fitted to 17..64 tokens on 2560 -> 2560 / 6912,
+  // 6912 -> 2560, 8192 -> 28672 and 28672 -> 8192; the rule picks the faster path at all
+  // 20 measured points (decode 4.3-15 us where the prefill kernel took 11-24 us on the
+  // 2B-class shapes; 8192 -> 28672: 18-24 us against 27 us up to 32 tokens, then the
+  // prefill kernel; 28672 -> 8192: 22-73 us against 39-79 us).
   if (M <= 16 || M > 64) return false;
   const int64_t K_pad = k_pad(K), chunks = K_pad / kTileCols, rblocks = n_pad(N) / kTileRows;
-  const double reread_s = (double)rblocks * (double)M * (double)K_pad / 8e12;
+  const int64_t groups = (rblocks + token_group_rb(rblocks) - 1) / token_group_rb(rblocks);
+  const double reread_s = (double)groups * (double)M * (double)K_pad / 8e12;
   const double kloop_s = 1.35e-6 * (double)((chunks + 1) / 2);
   return reread_s < kloop_s;
 }
@@ -1148,12 +1160,18 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
   p.rb = 1;
   p.ok = src == 0;  // the register paths read int8 activations only
   if (M > 16) {
-    // 17..64 tokens: token groups of 16 through k_gemv_reg, one row block per workgroup
-    // (N / 16 workgroups where the prefill kernel would have N / 192 tiles), at most 8
-    // waves, and the same wave rule as below
+    // 17..64 tokens: token groups of 16 through k_gemv_reg (N / (16 RB) workgroups where
+    // the prefill kernel would have N / 192 tiles).  RB row blocks share each workgroup's
+    // activation registers, which divides the L2 re-reads of the token rows by RB, as long
+    // as about one workgroup per CU remains (measured, 17..64 tokens: 432 and 512 row
+    // blocks fastest with 2, 1792 with 4, 160 with 1).  At most 32 / (RB TG) waves, and the
+    // same wave rule as below.
     p.tg = (int)((M + 15) / 16);
-    p.groups = rblocks;
-    p.waves = std::min(pick_waves(chunks, rblocks), 8);
+    p.rb = token_group_rb(rblocks);
+    p.groups = (rblocks + p.rb - 1) / p.rb;
+    int cap = 8;
+    while (cap * p.rb * p.tg > 32) cap /= 2;
+    p.waves = std::min(pick_waves(chunks, p.groups), cap);
     while (p.waves > 1 && chunks < 8 * p.waves && p.groups * (p.waves / 2) >= 1024) p.waves /= 2;
     return p;
   }
@@ -1186,9 +1204,9 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
   Args a{packed, gamma, Xq, absmax, (int)M, (int)N, (int)K, (int)k_pad(K), (int)(k_pad(K) / kTileCols),
          (int)(n_pad(N) / kTileRows), Y, acc, nullptr, nullptr};
   switch (p.tg) {
-    case 2: return launch_reg_tg_w<2>(p.waves, a, s);
-    case 3: return launch_reg_tg_w<3>(p.waves, a, s);
-    case 4: return launch_reg_tg_w<4>(p.waves, a, s);
+    case 2: return launch_reg_tg_w<2>(p.waves, p.rb, a, s);
+    case 3: return launch_reg_tg_w<3>(p.waves, p.rb, a, s);
+    case 4: return launch_reg_tg_w<4>(p.waves, p.rb, a, s);
     default: break;
   }
   if (p.dpp && M > 8) return p.rb == 2 ? launch_dppm<2, 16, 2>(p.waves, a, s) : launch_dppm<2, 16, 1>(p.waves, a, s);

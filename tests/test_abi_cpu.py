@@ -271,11 +271,15 @@ def test_binary_sizes_plan_and_validation():
 def test_token_group_routing():
     # 17..64 tokens go to the decode kernel with token groups where its L2 re-reads of the
     # token rows cost less than the prefill kernel's K loop; 65 and more always prefill
-    decode = [(17, 2560, 2560), (64, 2560, 2560), (48, 6912, 2560), (64, 2560, 6912), (17, 8192, 28672),
-              (32, 8192, 28672), (40, 72, 700)]
-    prefill = [(17, 28672, 8192), (64, 28672, 8192), (48, 8192, 28672), (17, 28672, 4096), (65, 64, 256)]
-    for m, n, k in decode:
-        assert bl.forward_plan(m, n, k)["kernel"] == "decode", (m, n, k)
+    # (m, n, k, row blocks per workgroup)
+    decode = [(17, 2560, 2560, 1), (64, 2560, 2560, 1), (48, 6912, 2560, 2), (64, 2560, 6912, 1),
+              (17, 8192, 28672, 2), (48, 8192, 28672, 2), (17, 28672, 8192, 4), (32, 28672, 8192, 4),
+              (17, 28672, 4096, 4), (40, 72, 700, 1)]
+    prefill = [(48, 28672, 8192), (64, 28672, 8192), (48, 30000, 512), (64, 24000, 1024), (65, 64, 256)]
+    for m, n, k, rb in decode:
+        p = bl.forward_plan(m, n, k)
+        assert p["kernel"] == "decode" and p["row_blocks"] == rb, (m, n, k, p)
+        assert (p["threads"] // 64) * rb * ((m + 15) // 16) <= 32, (m, n, k, p)
     for m, n, k in prefill:
         assert bl.forward_plan(m, n, k)["kernel"] == "prefill", (m, n, k)
 

@@ -295,17 +295,30 @@ def test_forward_decode_variants(m, n, k, acts, rb, run):
 
 
 @pytest.mark.parametrize("m", [17, 24, 32, 33, 48, 49, 64])
-@pytest.mark.parametrize("n,k", [(16, 256), (17, 300), (130, 1000), (2560, 2560), (300, 6912), (1, 1)])
+@pytest.mark.parametrize("n,k", [(16, 256), (17, 300), (130, 1000), (2560, 2560), (300, 6912), (1, 1), (6190, 700),
+                                 (17000, 300)])
 def test_forward_token_groups(m, n, k):
     # 17..64 tokens: the decode kernel with 2..4 token groups of 16 (the last one ragged)
-    # sharing each decoded weight fragment, 1..8 waves, against the oracle on every output
+    # sharing each decoded weight fragment, 1..8 waves, 1, 2 (6190 columns: 387 row blocks,
+    # the last workgroup one short) or 4 row blocks per workgroup (17000: 1063 row blocks),
+    # against the oracle on every output
     plan = bl.forward_plan(m, n, k)
     _announce("forward token groups", m, n, k, plan)
     assert plan["kernel"] == "decode" and plan["acts"] == "per-tile loads" and plan["threads"] <= 512
     _fwd_check(m, n, k, seed=m * 1000 + n + k)
 
 
-@pytest.mark.parametrize("m,n,k", [(24, 20000, 2048), (64, 9000, 4096)])
+@pytest.mark.parametrize("m,n,k,waves,rb", [(64, 6190, 4096, 4, 2), (17, 17000, 2048, 4, 4), (40, 17000, 2048, 2, 4),
+                                            (33, 2560, 6912, 8, 1)])
+def test_forward_token_groups_waves(m, n, k, waves, rb):
+    # token groups with several waves per workgroup splitting K, and shared row blocks
+    plan = bl.forward_plan(m, n, k)
+    _announce("forward token groups waves", m, n, k, plan)
+    assert plan["kernel"] == "decode" and plan["threads"] == 64 * waves and plan["row_blocks"] == rb
+    _fwd_check(m, n, k, seed=m * 1000 + n + k)
+
+
+@pytest.mark.parametrize("m,n,k", [(48, 30000, 512), (64, 24000, 1024)])
 def test_forward_prefill_few_tokens(m, n, k):
     # 17..64 tokens where the token rows would be re-read by too many row blocks: the
     # prefill kernel (one 64-row tile high, two K groups), against the oracle on every output
