@@ -293,9 +293,9 @@ TRAFFIC = {
     # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.2 KiB (x1.99980),
     # WRITE_SIZE 262144.0 KiB (x1.0).
     (1, 1): {"bytes_per_launch": 4591120, "fetch_kib": 2229.34, "write_kib": 25.28, "sha": "61f7a96371860d6d"},
-    (2, 16): {"bytes_per_launch": 3160073, "fetch_kib": 1441.44, "write_kib": 203.43, "sha": "61f7a96371860d6d"},
-    (3, 2048): {"bytes_per_launch": 97727500, "fetch_kib": 28777.35, "write_kib": 37888.20, "sha": "eb34b544b8f58144"},
-    (4, 1): {"bytes_per_launch": 59258200, "fetch_kib": 28892.26, "write_kib": 90.03, "sha": "61f7a96371860d6d"},
+    (2, 16): {"bytes_per_launch": 3160072, "fetch_kib": 1441.44, "write_kib": 203.43, "sha": "61f7a96371860d6d"},
+    (3, 2048): {"bytes_per_launch": 93566491, "fetch_kib": 26745.46, "write_kib": 37888.07, "sha": "c5f333cc6f911977"},
+    (4, 1): {"bytes_per_launch": 59258204, "fetch_kib": 28892.26, "write_kib": 90.03, "sha": "61f7a96371860d6d"},
 }
 
 
