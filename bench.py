@@ -290,12 +290,12 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
-    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.2 KiB (x1.99980),
+    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.3 KiB (x1.99980),
     # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4591120, "fetch_kib": 2229.34, "write_kib": 25.28, "sha": "61f7a96371860d6d"},
-    (2, 16): {"bytes_per_launch": 3160072, "fetch_kib": 1441.44, "write_kib": 203.43, "sha": "61f7a96371860d6d"},
-    (3, 2048): {"bytes_per_launch": 93566491, "fetch_kib": 26745.46, "write_kib": 37888.07, "sha": "c5f333cc6f911977"},
-    (4, 1): {"bytes_per_launch": 59258204, "fetch_kib": 28892.26, "write_kib": 90.03, "sha": "61f7a96371860d6d"},
+    (1, 1): {"bytes_per_launch": 4591108, "fetch_kib": 2229.34, "write_kib": 25.28, "sha": "61f7a96371860d6d"},
+    (2, 16): {"bytes_per_launch": 3160075, "fetch_kib": 1441.44, "write_kib": 203.43, "sha": "61f7a96371860d6d"},
+    (3, 2048): {"bytes_per_launch": 94794700, "fetch_kib": 27345.22, "write_kib": 37888.06, "sha": "85d7b679bf307030"},
+    (4, 1): {"bytes_per_launch": 59258200, "fetch_kib": 28892.26, "write_kib": 90.03, "sha": "61f7a96371860d6d"},
 }
 
 

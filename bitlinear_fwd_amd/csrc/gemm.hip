@@ -19,9 +19,8 @@
 //   * one 16-byte word of a slot feeds one MFMA step and serves WM / 16 MFMAs, which
 //     keeps the decode VALU below the matrix-core time;
 //   * shapes: 64 x 256 or 64 x 192 output tiles (waves 1 x 4 of 64 x 64 or 64 x 48,
-//     three-slot ring), whichever leaves the lighter last round of tiles; 64 x 128 tiles
-//     (waves 2 x 2 of 32 x 64, A reads issued a half-stage at a time) where 64 x 256 would
-//     not give every compute unit one (plan_gemm);
+//     three-slot ring), whichever leaves the lighter last round of tiles, and two K groups
+//     of four waves per tile where there are few tiles (plan_gemm);
 //   * the loop body is unrolled over lcm(D, 2 CB) half-stages so that every ring index is
 //     static; half-stages past the end of K are skipped whole (measured: 2048 x 6912 x 2560
 //     48.9 -> 46.9 us, 4096 x 6912 x 2560 87.6 -> 82.3 us, 48 x 30000 x 512 9.4 -> 7.6 us);
@@ -73,7 +72,7 @@ constexpr int loads_between(int a, int b) {
   return n;
 }
 
-template <int GM, int GN, int WM, int WN, int D, int kPipe = 0, int KS = 1>
+template <int GM, int GN, int WM, int WN, int D, int KS = 1>
 __global__ __launch_bounds__(256 * KS) void k_gemm_mfma(const uint8_t* __restrict__ packed, const float* __restrict__ gamma,
                                                    const int8_t* __restrict__ Xq, const float* __restrict__ absmax,
                                                    int M, int N, int n_blocks, int K_pad, int chunks, int tiles_m,
@@ -167,43 +166,6 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_mfma(const uint8_t* __restric
   // compute half-stage in ring slot s (steps 2h, 2h+1 of its chunk) with weights cb
   auto compute = [&](auto sc, int half, const uint4 (&wcur)[NB]) {
     const uint8_t* slabp = slab(sc) + kgoff;
-    if constexpr (kPipe == 1) {
-      // both steps' A fragments are read up front; step 1's weights are decoded while
-      // step 0's MFMAs run (interleaving requested from the scheduler)
-      v4i af[2][MB];
-#pragma unroll
-      for (int ip = 0; ip < 2; ++ip)
-#pragma unroll
-        for (int mi = 0; mi < MB; ++mi) {
-          const int row = wm * WM + 16 * mi + r;
-          af[ip][mi] = *reinterpret_cast<const v4i*>(&slabp[row * kHalf + 16 * a_slot(row, 2 * g + ip)]);
-        }
-      v4i bf[2][NB];
-#pragma unroll
-      for (int ip = 0; ip < 2; ++ip) {
-        const int i = 2 * half + ip;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const uint32_t word = i == 0 ? wcur[j].x : (i == 1 ? wcur[j].y : (i == 2 ? wcur[j].z : wcur[j].w));
-          bf[ip][j] = decode16(word);
-        }
-      }
-#pragma unroll
-      for (int ip = 0; ip < 2; ++ip)
-#pragma unroll
-        for (int mi = 0; mi < MB; ++mi)
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            acc[mi][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[ip][mi], bf[ip][j], acc[mi][j], 0, 0, 0);
-      // schedule: the A reads first, step 0's decode, then MFMAs interleaved with the rest
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * MB, 0);   // DS reads
-      __builtin_amdgcn_sched_group_barrier(0x2, 9 * NB, 0);     // VALU: step 0 decode
-      static_for<MB * NB>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);        // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x2, 3, 0);        // ~3 VALU of step 1's decode
-      });
-      return;
-    }
 #pragma unroll
     for (int ip = 0; ip < 2; ++ip) {
       const int i = 2 * half + ip;
@@ -345,7 +307,7 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_mfma(const uint8_t* __restric
   }
 }
 
-template <int GM, int GN, int WM, int WN, int D, int kPipe = 0, int KS = 1>
+template <int GM, int GN, int WM, int WN, int D, int KS = 1>
 hipError_t launch(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax, int64_t M,
                   int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s) {
   const int64_t K_pad = k_pad(K);
@@ -355,7 +317,7 @@ hipError_t launch(const uint8_t* packed, const float* gamma, const int8_t* Xq, c
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   const int tiles = tiles_m * tiles_n;
   const int grid = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL((k_gemm_mfma<GM, GN, WM, WN, D, kPipe, KS>), dim3(grid), dim3(256 * KS), 0, s, packed, gamma, Xq, absmax, (int)M,
+  hipLaunchKernelGGL((k_gemm_mfma<GM, GN, WM, WN, D, KS>), dim3(grid), dim3(256 * KS), 0, s, packed, gamma, Xq, absmax, (int)M,
                      (int)N, n_blocks, (int)K_pad, chunks, tiles_m, tiles_n, Y, acc);
   return hipGetLastError();
 }
@@ -369,23 +331,23 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   //   64 x 256: waves of 64 x 64 side by side (three-slot ring, 24 KiB of LDS, 152
   //             registers, three workgroups per CU): the most work per operand byte;
   //   64 x 192: waves of 64 x 48 (118 registers, four per CU): the same structure, for
-  //             column counts that 256 would leave a ragged last round on;
-  //   64 x 128: 2 x 2 waves of 32 x 64 (124 registers, four per CU), for the few short
-  //             shapes that neither of the rules below covers.
+  //             column counts that 256 would leave a ragged last round on.
   // Where the tiles do not fill the chip, two K groups of four waves share each tile (eight
   // waves, each group half the chunks, partials summed through LDS): twice the waves per
   // tile at the same operand bytes per tile.  64 x 256 tiles when that gives 193..256 of
-  // them (one eight-wave workgroup per CU), else 64 x 192 tiles when there are at most 256
-  // (two per CU fit).  Measured: 1024 x 2560 x 6912 35.7 -> 27.4 us, 1024 x 2560 x 2560 18.1
-  // -> 14.1 us, 512 x 8192 x 8192 43.2 -> 37.4 us, 512 x 6912 x 2560 19.2 -> 17.2 us,
-  // 1536 x 2560 x 2560 18.4 -> 17.2 us; the one shape measured slower, 512 x 2560 x 6912, by
-  // 3 % (25.2 -> 25.9 us).  With more tiles the split costs more than it gives (2048 x 6912
-  // x 2560: 45.2 -> 48.7 us).
+  // them (one eight-wave workgroup per CU), else 64 x 192 tiles when there are at most 512
+  // (two per CU fit).  Measured against the one-group tiles: 1024 x 2560 x 6912 35.7 -> 27.4
+  // us, 1024 x 2560 x 2560 18.1 -> 14.1 us, 512 x 8192 x 8192 43.2 -> 37.4 us, 512 x 6912 x
+  // 2560 19.2 -> 17.2 us, 1536 x 2560 x 2560 18.4 -> 17.2 us, and with 448 tiles (2048 x 2560)
+  // 47.8 -> 42.3 us at K = 6912, 52.0 -> 46.6 us at K = 8192, 30.4 -> 27.6 us at K = 4096,
+  // 22.5 -> 20.4 us at K = 2560; the one shape measured slower, 512 x 2560 x 6912, by 3 %
+  // (25.2 -> 25.9 us).  With more tiles the split costs more than it gives (2048 x 6912 x
+  // 2560: 45.2 -> 47.8 us; 4096 x 2560 x 6912: 72.5 -> 78.2 us).
   // Otherwise, between 64 x 256 and 64 x 192, the cost of the last round decides: rounds of
   // 256 tiles times the tile width, the 48-column waves counted at 0.976 of the 64-column
-  // rate (measured 8192^3: 486 vs 474 us).  Measured at M = 2048: 2560 columns 49.1 us
-  // (64 x 128) -> 43.9 us (64 x 192), 6912 columns 46.8 us (64 x 256) -> 45.9 us (64 x 192);
-  // 8192^3, 4096 x 2560 x 6912 and 2048 x 28672 x 8192 stay on 64 x 256.
+  // rate (measured 8192^3: 486 vs 474 us).  Measured at M = 2048 x 6912 columns: 46.8 us
+  // (64 x 256) -> 45.9 us (64 x 192); 8192^3, 4096 x 2560 x 6912 and 2048 x 28672 x 8192
+  // stay on 64 x 256.
   const int64_t tm = (M + 63) / 64;
   const int64_t t256 = tm * ((N + 255) / 256), t192 = tm * ((N + 191) / 192);
   p.bm = 64;
@@ -393,11 +355,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   if (t256 > 192 && t256 <= 256) {
     p.bn = 256;
     p.ks = 2;
-  } else if (t192 <= 256) {
+  } else if (t192 <= 512) {
     p.bn = 192;
     p.ks = 2;
-  } else if (t256 < 256) {
-    p.bn = 128;
   } else {
     const double c256 = (double)((t256 + 255) / 256) * 256.0;
     const double c192 = (double)((t192 + 255) / 256) * 192.0 / 0.976;
@@ -413,12 +373,11 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s) {
   const GemmPlan p = plan_gemm(M, N, K);
   if (p.ks == 2) {
-    if (p.bn == 256) return launch<1, 4, 64, 64, 3, 0, 2>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
-    return launch<1, 4, 64, 48, 3, 0, 2>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
+    if (p.bn == 256) return launch<1, 4, 64, 64, 3, 2>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
+    return launch<1, 4, 64, 48, 3, 2>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
   }
   if (p.bn == 256) return launch<1, 4, 64, 64, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
-  if (p.bn == 192) return launch<1, 4, 64, 48, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
-  return launch<2, 2, 32, 64, 3, 1>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
+  return launch<1, 4, 64, 48, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
 }
 
 }  // namespace bl

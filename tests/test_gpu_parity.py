@@ -337,14 +337,14 @@ def test_forward_prefill(m, n, k):
 
 @pytest.mark.parametrize("m,n,k,tile_n,k_groups", [
     (2048, 4100, 1000, 192, 1), (333, 24000, 2600, 192, 1), (4000, 8190, 1000, 256, 1), (3000, 9000, 700, 192, 1),
-    (2048, 2560, 6912, 192, 1), (1500, 2000, 777, 128, 1),
+    (4096, 2560, 6912, 256, 1), (2048, 2560, 6912, 192, 2), (1500, 2000, 777, 192, 2),
     # two K groups per tile where the tiles do not fill the chip; odd chunk counts (K = 1100:
     # 5 chunks, 6912: 27) leave the second group one chunk short
     (1000, 3000, 777, 192, 2), (700, 2600, 1100, 192, 2), (500, 7000, 1100, 256, 2), (450, 8000, 6912, 256, 2)])
 def test_forward_prefill_tile_shapes(m, n, k, tile_n, k_groups):
-    # the prefill tile shapes (64 x 256 or 64 x 192 by the last round's load, 64 x 128 for
-    # a few short shapes, one or two K groups per tile) with ragged M, N and K; the oracle
-    # checks a sample of token rows covering tile edges
+    # the prefill tile shapes (64 x 256 or 64 x 192 by the last round's load, one or two K
+    # groups per tile) with ragged M, N and K; the oracle checks a sample of token rows
+    # covering tile edges
     plan = bl.forward_plan(m, n, k)
     _announce("forward prefill tiles", m, n, k, plan)
     assert plan["kernel"] == "prefill" and plan["tile_m"] == 64 and plan["tile_n"] == tile_n
