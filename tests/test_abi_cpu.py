@@ -284,6 +284,24 @@ def test_token_group_routing():
         assert bl.forward_plan(m, n, k)["kernel"] == "prefill", (m, n, k)
 
 
+def test_prefill_plans():
+    # host-only sweep of the prefill planner: a supported tile shape, 256 threads per K group,
+    # and a grid of whole XCD rounds covering every 64-row tile
+    for m in (17, 65, 100, 333, 1000, 1536, 2048, 4096, 8192):
+        for n in (1, 16, 640, 2000, 2560, 6912, 8192, 28672):
+            for k in (1, 256, 2560, 6912, 28672):
+                p = bl.forward_plan(m, n, k)
+                if p["kernel"] != "prefill":
+                    assert m <= 64, (m, n, k, p)
+                    continue
+                assert p["tile_m"] == 64 and p["tile_n"] in (192, 256), (m, n, k, p)
+                assert p["k_groups"] in (1, 2) and p["threads"] == 256 * p["k_groups"], (m, n, k, p)
+                tiles = -(-m // 64) * -(-n // p["tile_n"])
+                assert p["workgroups"] == 8 * -(-tiles // 8), (m, n, k, p)
+                if p["k_groups"] == 2:
+                    assert tiles <= 512, (m, n, k, p)
+
+
 def test_launch_plans_cover_every_tile():
     # host-only sweep of every planner: a plan's waves x tiles per wave must cover all K
     # tiles, and its workgroups all row blocks, or outputs would silently go missing
