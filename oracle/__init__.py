@@ -2,8 +2,9 @@
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
 may import this package.  The product path (``bitlinear_fwd_amd``) never imports it,
-and the two share no code: the oracle is plain scalar C (``bitlinear_oracle.c``) plus
-the exact-arithmetic mean below, written from the pages:
+and the two share no code: the oracle is plain scalar C (``bitlinear_oracle.c``) with a
+thin ctypes layer and the exact rational rounding of the mean below, written from the
+pages:
 
 * aratech.ae, "BitNet b1.58: Microsoft's 1-bit LLM that runs a 100B model on one CPU",
   section "The solution: BitNet b1.58", sub-sections "Ternary weights {-1, 0, +1}"
@@ -59,6 +60,10 @@ def _load():
         lib.orc_k_pad.argtypes = [i64]
         lib.orc_packed_bytes.restype = i64
         lib.orc_packed_bytes.argtypes = [i64, i64]
+        lib.orc_sum_limbs.restype = ctypes.c_int
+        lib.orc_sum_limbs.argtypes = []
+        lib.orc_abs_sum_fixed.restype = ctypes.c_int
+        lib.orc_abs_sum_fixed.argtypes = [p, i64, p]
         lib.orc_ternarise.restype = None
         lib.orc_ternarise.argtypes = [p, i64, ctypes.c_float, p]
         lib.orc_pack.restype = ctypes.c_int
@@ -143,28 +148,15 @@ def exact_abs_sum_scaled(w: np.ndarray) -> int:
     """Sum of |w| over all entries as an exact integer in units of 2**-149.
 
     Every finite fp32 is an integer multiple of 2**-149, so the sum is an integer in
-    those units.  Entries are grouped by exponent field; inside a group the 24-bit
-    significands are summed as two 12-bit halves with float64 bincount, which is exact
-    while each bin stays below 2**53 (guaranteed for fewer than 2**40 entries)."""
+    those units.  orc_abs_sum_fixed adds each weight, in index order, into a fixed-point
+    accumulator wide enough that nothing is ever rounded; its limbs become one Python
+    integer here."""
     a = np.ascontiguousarray(w, dtype=np.float32).ravel()
-    if a.size >= 1 << 40:
-        raise ValueError("tensor too large for the exact bin sums")
-    total = 0
-    step = 1 << 24  # exact integer partial sums add associatively; chunks bound the memory
-    for start in range(0, a.size, step):
-        bits = a[start:start + step].view(np.uint32) & np.uint32(0x7FFFFFFF)
-        expo = (bits >> np.uint32(23)).astype(np.int64)
-        if np.any(expo == 255):
-            raise ValueError("non-finite weight")
-        frac = (bits & np.uint32(0x7FFFFF)).astype(np.int64)
-        sig = np.where(expo > 0, frac | (1 << 23), frac)  # value = sig * 2**(max(expo,1) - 150)
-        eff = np.maximum(expo, 1)
-        lo = np.bincount(eff, weights=(sig & 0xFFF).astype(np.float64), minlength=256)
-        hi = np.bincount(eff, weights=(sig >> 12).astype(np.float64), minlength=256)
-        for e in range(1, 255):
-            s = int(hi[e]) * 4096 + int(lo[e])
-            total += s << (e - 1)  # sig * 2**(e-150) in units of 2**-149
-    return total
+    lib = _load()
+    limbs = np.zeros(int(lib.orc_sum_limbs()), dtype=np.uint32)
+    if lib.orc_abs_sum_fixed(_ptr(a), a.size, _ptr(limbs)) != 0:
+        raise ValueError("non-finite weight, or more than 2**40 weights")
+    return sum(int(v) << (32 * i) for i, v in enumerate(limbs))
 
 
 def gamma_absmean(w: np.ndarray) -> np.float32:

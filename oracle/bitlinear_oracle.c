@@ -18,7 +18,8 @@
  * Numeric conventions (the readings these functions follow):
  *   - The ternarise decision is taken in fp32, as the kernel takes it:
  *     t = fl32(W * s_w) with s_w = fl32(1 / gamma); q = clamp(rint(t), -1, 1) with
- *     round-half-to-even.  gamma itself comes from the exact mean (oracle/__init__.py).
+ *     round-half-to-even.  gamma is the exact mean: orc_abs_sum_fixed forms the exact sum
+ *     of |W|, and the caller divides by the count and rounds once to fp32.
  *   - Activation quantisation per row: a = max |x| (exact), s = fl32(127 / a),
  *     xq = clamp(rint(fl32(x * s)), -127, 127); a row of zeros gives xq = 0.
  *   - Contraction is exact integer arithmetic (int64, checked to fit int32).
@@ -46,6 +47,42 @@
 int64_t orc_n_pad(int64_t n) { return (n + 15) / 16 * 16; }
 int64_t orc_k_pad(int64_t k) { return (k + 255) / 256 * 256; }
 int64_t orc_packed_bytes(int64_t n, int64_t k) { return orc_n_pad(n) * orc_k_pad(k) / 4; }
+
+/* [AT] "Ternary weights {-1, 0, +1}": gamma is the mean magnitude taken over the whole
+ * weight tensor.  This forms the sum of |w| exactly.  Every finite fp32 is an integer
+ * multiple of 2^-149, so the sum is an integer in those units; it is kept in a plain
+ * fixed-point accumulator of ORC_SUM_LIMBS 32-bit limbs, least significant first.  A
+ * weight with exponent field e and 23-bit fraction f is sig * 2^(e - 150) with
+ * sig = f + 2^23 (e >= 1), or f * 2^-149 (e = 0, subnormal): in units of 2^-149 that is
+ * sig shifted left by max(e, 1) - 1 bits.  Each weight is added on its own, in index
+ * order.  352 bits hold 2^40 weights of the largest fp32 (2^40 * 2^128 * 2^149 < 2^318).
+ * Returns ORC_ERR_RANGE for a non-finite weight or more than 2^40 of them.  The division
+ * by the count and the rounding to fp32 are done on the exact integer by the caller. */
+#define ORC_SUM_LIMBS 11
+int orc_sum_limbs(void) { return ORC_SUM_LIMBS; }
+
+int orc_abs_sum_fixed(const float* w, int64_t count, uint32_t* limbs) {
+  for (int i = 0; i < ORC_SUM_LIMBS; ++i) limbs[i] = 0;
+  if (count < 0 || count > ((int64_t)1 << 40)) return ORC_ERR_RANGE;
+  for (int64_t i = 0; i < count; ++i) {
+    uint32_t bits;
+    memcpy(&bits, &w[i], 4);
+    bits &= 0x7FFFFFFFu; /* |w| */
+    const uint32_t e = bits >> 23, f = bits & 0x7FFFFFu;
+    if (e == 255u) return ORC_ERR_RANGE;
+    const uint64_t sig = e ? (uint64_t)f | (1u << 23) : (uint64_t)f;
+    const uint32_t shift = e ? e - 1u : 0u; /* 0 .. 253 */
+    int li = (int)(shift / 32u);
+    uint64_t add = sig << (shift % 32u); /* at most 55 bits */
+    while (add != 0 && li < ORC_SUM_LIMBS) {
+      const uint64_t s = (uint64_t)limbs[li] + (add & 0xFFFFFFFFu);
+      limbs[li] = (uint32_t)s;
+      add = (add >> 32) + (s >> 32); /* carry into the next limb */
+      ++li;
+    }
+  }
+  return ORC_OK;
+}
 
 /* [AT] "Ternary weights": scale_w is the reciprocal of the mean magnitude; each
  * weight is multiplied by it, rounded, and clamped to [-1, 1].  gamma == 0 (an

@@ -87,6 +87,75 @@ def test_gamma_matches_float64_library_mean():
     assert g == np.float32(np.mean(np.abs(w), dtype=np.float64))
 
 
+def _is_nearest_f32(g, exact) -> bool:
+    """g (fp32) is at least as close to the rational `exact` as both fp32 neighbours."""
+    from fractions import Fraction
+    g = np.float32(g)
+    err = abs(Fraction(float(g)) - exact)
+    return all(err <= abs(Fraction(float(nb)) - exact)
+               for nb in (np.nextafter(g, np.float32(np.inf)), np.nextafter(g, np.float32(0))))
+
+
+BIG = (1 << 24) + (1 << 20) + 7  # above 2^24 weights, as the 2048-token and 100B-class matrices
+
+
+def test_gamma_above_2_24_weights_closed_forms():
+    from fractions import Fraction
+    # a constant tensor has mean |c| exactly, at any magnitude: subnormal, tiny, typical, the
+    # largest binade (the sum then needs the top limbs of the accumulator)
+    for c in (-0.375, 1.0e-40, -2.0 ** -126, 0.02, 3.0e38):
+        w = np.full(BIG, c, np.float32)
+        assert oracle.gamma_absmean(w) == np.abs(np.float32(c)), c
+    # two values, the switch placed on either side of index 2^24: the exact mean is the
+    # weighted rational, and gamma is the fp32 nearest to it
+    for a, b, n1 in ((0.02, -0.03, (1 << 24) - 1), (1.0e-3, 7.0e-41, 1 << 24), (-5.0, 1.0e30, (1 << 24) + 1)):
+        fa, fb = np.float32(a), np.float32(b)
+        w = np.empty(BIG, np.float32)
+        w[:n1], w[n1:] = fa, fb
+        exact = (n1 * Fraction(abs(float(fa))) + (BIG - n1) * Fraction(abs(float(fb)))) / BIG
+        assert _is_nearest_f32(oracle.gamma_absmean(w), exact), (a, b, n1)
+    # 3 * 2^24 + 3 copies of 1.0 and of 2^-24 split 1:2: mean (1 + 2 * 2^-24) / 3 exactly
+    n3 = 3 * ((1 << 24) + 1)
+    w = np.full(n3, 2.0 ** -24, np.float32)
+    w[: n3 // 3] = 1.0
+    assert _is_nearest_f32(oracle.gamma_absmean(w), (1 + 2 * Fraction(1, 1 << 24)) / 3)
+
+
+def test_gamma_large_tensor_exact_sum_matches_fsum():
+    # 2^25 + 5 Gaussian latents with values planted across the exponent range (subnormals,
+    # the smallest and largest binades, signs) scattered over the tensor and at the indices
+    # around 2^24.  math.fsum gives the correctly rounded fp64 sum of the same values, an
+    # independent routine: the exact integer sum must round to it.
+    from fractions import Fraction
+    n = (1 << 25) + 5
+    w = synth.latent_weights(1, n, seed=19).numpy().ravel().copy()
+    rng = _rng(8)
+    planted = np.array([1.0e-45, -3.0e-42, 1.17549435e-38, -2.0 ** -126, 3.4e38, -1.0e38, 0.5, -1.5, 1e-20, 7.0,
+                        2.0 ** 100, -2.0 ** -140], np.float32)
+    where = np.concatenate([rng.integers(0, n, 4000), np.arange((1 << 24) - 6, (1 << 24) + 6)])
+    w[where] = planted[np.arange(where.size) % planted.size]
+    s = oracle.exact_abs_sum_scaled(w)
+    ref = math.fsum(np.abs(w).astype(np.float64).tolist())
+    assert float(Fraction(s, 1 << 149)) == ref
+    # the Gaussian part alone, against the same routine
+    w2 = synth.latent_weights(1, n, seed=20).numpy().ravel()
+    s2 = oracle.exact_abs_sum_scaled(w2)
+    assert float(Fraction(s2, 1 << 149)) == math.fsum(np.abs(w2).astype(np.float64).tolist())
+    g2 = oracle.gamma_absmean(w2)
+    assert _is_nearest_f32(g2, Fraction(s2, n << 149))
+    # and gamma against the fp64 library mean: within half an fp32 ulp of fsum / n
+    half_ulp = (float(np.nextafter(g2, np.float32(np.inf))) - float(g2)) / 2
+    assert abs(float(g2) - math.fsum(np.abs(w2).astype(np.float64).tolist()) / n) <= half_ulp * (1 + 1e-9)
+
+
+def test_gamma_rejects_non_finite():
+    for bad in (np.inf, -np.inf, np.nan):
+        w = np.ones(10, np.float32)
+        w[7] = bad
+        with pytest.raises(ValueError):
+            oracle.gamma_absmean(w)
+
+
 def test_gamma_gaussian_expectation():
     # E|W| = sigma * sqrt(2/pi) for W ~ N(0, sigma^2); std error sigma*sqrt(1-2/pi)/sqrt(n)
     w = synth.latent_weights(512, 2048, seed=11).numpy()
@@ -342,10 +411,26 @@ def test_subln_matches_normalise_then_quantise():
     assert np.allclose(sc, amax, rtol=1e-7, atol=0)
     t = n * 127.0 / amax[:, None]
     lit = np.rint(t)
-    near_tie = np.abs(np.abs(t - np.trunc(t)) - 0.5) < 1e-4
+    # The oracle decides each code on r = fl32(fl32(x * g) * fl32(127 / max|fl32(x * g)|)):
+    # four roundings of relative size <= 2^-24 each, on a value of magnitude <= 127.  So
+    # |r - t| <= 127 * ((1 + 2^-24)^4 - 1) (plus the fp64 error of t, ~1e-13), and the two
+    # codes can differ only where t lies that close to a half-integer.
+    window = 127.0 * ((1.0 + 2.0 ** -24) ** 4 - 1.0) + 1e-12
+    near_tie = np.abs(np.abs(t - np.trunc(t)) - 0.5) <= window
     agree = lit == xq[:, :k]
     assert np.all(agree | near_tie)
-    assert np.count_nonzero(~agree) <= np.count_nonzero(near_tie)
+    assert np.all(np.abs(lit.astype(np.int64) - xq[:, :k]) <= 1)  # a near-tie moves a code by one step
+    # the same on many rows: every disagreement sits inside that window
+    x2 = synth.activations(256, 2048, seed=37, dtype=torch.float32, outlier_p=0.005, outlier_mult=30.0).numpy()
+    g2 = _rng(7).uniform(-1.5, 1.5, 2048).astype(np.float32)
+    xq2, _, sc2, _ = _subln(x2, gain=g2, eps=eps)
+    xd2 = x2.astype(np.float64)
+    n2 = xd2 * g2.astype(np.float64) / np.sqrt(np.mean(xd2 * xd2, axis=1, keepdims=True) + eps32)
+    a2 = np.max(np.abs(n2), axis=1)
+    assert np.allclose(sc2, a2, rtol=1e-7, atol=0)
+    t2 = n2 * 127.0 / a2[:, None]
+    off = np.rint(t2) != xq2[:, :2048]
+    assert np.all(np.abs(np.abs(t2[off] - np.trunc(t2[off])) - 0.5) <= window)
 
 
 # ------------------------------------------------------------------ squared-ReLU gating
