@@ -1,7 +1,7 @@
 """Benchmark of the BitLinear forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 1] [--legs 2,3,4]
-                    [--no-graph] [--no-cpu-baseline] [--copy-calibration MIB]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 4] [--legs 1,3,4i,...]
+                    [--graph] [--no-cpu-baseline] [--copy-calibration MIB]
 
 A step is one pass of the hot path over one batch of synthetic input: for every matrix of
 the workload, the per-token int8 activation quantiser and the forward (packed-ternary x
@@ -14,33 +14,42 @@ timed region is the GPU's back-to-back execution.  --graph replays one captured 
 per step instead; on this stack a graph adds about a microsecond per kernel node over
 back-to-back stream launches, so it is the slower of the two for microsecond kernels.
 
-Headline (default workload 1): 2B-class decode at M = 1, gate/up 2560->6912 and down
-6912->2560, cycling through 48 distinct weight sets (637 MB of packed weights, more than
-twice the 256 MB Infinity Cache) so every step streams its weights from HBM.  value =
-packed-weight bytes per step / step time, in GB/s.  The JSON line also carries:
+Headline (default workload 4, M = 1): the 100B-class decode sweep, 8192 -> 28672 and
+28672 -> 8192 over an 80-layer stack of distinct seeded weights (160 matrices, 9.4 GB of
+packed weights, far beyond the 256 MB Infinity Cache, so every launch streams its weights
+from HBM); this is the largest configuration that fits one GPU.  Exactly K steps are timed
+after W warm-up steps, with a HIP event after every step on the stream the kernels run
+on: value = packed-weight bytes per step / mean step time, in GB/s, and `trials` gives
+the median, min and max of the K per-step times.  The JSON line also carries:
   roofline     the dominant kernel: algorithmic bytes (decode) or int8 ops (prefill) per
                launch / mean launch duration, against 8 TB/s or 5.0 POPS.  The duration
-               comes from HIP events on the replay stream: the timed region over its
-               launches when the step is nothing but that kernel, else graph replays of the
+               comes from HIP events on the launch stream: the timed region over its
+               launches when the step is nothing but that kernel, else passes of the
                forward launches alone.  traffic: measured HBM bytes per launch (see TRAFFIC);
-  legs         the other workloads: M = 16 full layer, M = 2048 prefill (int8 TOPS vs
-               5.0 POPS dense int8 MFMA), 100B-class M = 1 and M = 8 sweeps, and the 2B
-               decode workloads with the projections of one input (gate/up, Q/K/V) grouped
-               into one bitlinear_forward_grouped call ("1g", "2g"), and the same
-               workloads behind the sub-layer RMS normalisation ("1s", "1gs", "2s"), and the
-               gate/up pair with the squared-ReLU gating epilogue in one launch ("1f", "1fs");
-               the two-kernel int8 path ("1i"), the table-lookup decode ("1l") and the 1-bit
-               sign-binary variant ("1b", "4b") for comparison with the ternary decode, and
-               one GPU's share of the 100B-class matrices split over 8 GPUs ("5": the up
-               projection's 3584 output rows, the down projection's 3584 input columns);
+  legs         the other workloads, each with at least 20 timed steps and 400 launches and
+               its own per-step statistics; the 2B-class M = 1 decode ("1"), the 2048-token
+               prefill ("3", int8 TOPS vs 5.0 POPS) and the int8-only decode of the
+               headline matrices ("4i") carry their own roofline block.  Also: the M = 16
+               2B-class layer ("2"), M = 8 on the headline matrices ("4"), the projections
+               of one input grouped into one call ("1g", "2g"), the same workloads behind the
+               sub-layer RMS normalisation ("1s", "1gs", "2s"), the gate/up pair with the
+               squared-ReLU gating epilogue in one launch ("1f", "1fs"), the two-kernel int8
+               path ("1i"), the table-lookup decode ("1l"), the 1-bit sign-binary variant
+               ("1b", "4b"), and one GPU's share of the 100B-class matrices split over 8
+               GPUs ("5");
   gpu_state    rocm-smi clock and power readings before and after the timed region;
   quantisers   the weight quantiser (2560 -> 6912 fp32 latents) and the activation quantiser
                (bf16, decode and prefill sizes) timed alone, in bytes moved per second;
-  ceilings     measured on this GPU by the library's probes: HBM read rate with the decode
-               access pattern at 58.7 MB and 4.4 MB per launch, and the int8 MFMA rate;
+  ceilings     measured on this GPU: a plain grid-stride HBM read (no access pattern of the
+               BitLinear kernels) at 58.7 MB and 4.4 MB per launch and at 1 GiB, the same
+               sizes read with the decode kernels' tile pattern, and the int8 MFMA rate;
                roofline.frac_of_measured_ceiling sets the dominant kernel against the
-               one that matches its size;
-  cpu_baseline the CPU oracle on the host, on a bounded sample of the same workload.
+               plain read of its launch size;
+  cpu_baseline the CPU oracle on the host cores, on the same workload: all physical cores of
+               this process's CPU set, each matrix's output rows split over them
+               (cpu_baseline), and one thread on 2 of the 80 layers, scaled to the sweep
+               (cpu_baseline_single_thread); with the CPU model, core counts and the
+               oracle's compile flags.
 """
 from __future__ import annotations
 
@@ -61,16 +70,17 @@ I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA (no sparsity)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=480)
-    ap.add_argument("--warmup", type=int, default=48)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4, 5])
-    ap.add_argument("--legs", default="1g,1s,1gs,1f,1fs,1i,1l,1b,2,2g,2s,3,4,4b,5",
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, choices=[0, 1, 2, 3, 4, 5])
+    ap.add_argument("--legs", default="1,1g,1s,1gs,1f,1fs,1i,1l,1b,2,2g,2s,3,4,4i,4b,5",
                     help="other workloads timed into 'legs' ('' for none); a trailing g times the workload "
                          "with the projections of one input grouped into one call")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph instead of pre-marshalled eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the all-cores oracle run (the single-thread run takes 2 layers)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device three times (the reference kernel of "
                          "known size for scaling FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -80,10 +90,13 @@ def parse():
 class Matrix:
     """One quantised weight matrix with its pre-drawn activations."""
 
-    def __init__(self, bl, synth, wl, layer, midx, k, n, m, dev, binary=False):
-        w = synth.latent_weights(n, k, seed=synth.weight_seed(wl.index, layer, midx), device=dev)
-        self.packed, self.gamma = bl.quantize_weights_binary(w) if binary else bl.quantize_weights(w)
-        del w
+    def __init__(self, bl, synth, wl, layer, midx, k, n, m, dev, binary=False, weights=None):
+        if weights is not None:  # the same seeded weights, already quantised for another M
+            self.packed, self.gamma = weights.packed, weights.gamma
+        else:
+            w = synth.latent_weights(n, k, seed=synth.weight_seed(wl.index, layer, midx), device=dev)
+            self.packed, self.gamma = bl.quantize_weights_binary(w) if binary else bl.quantize_weights(w)
+            del w
         self.x = synth.activations(m, k, seed=synth.act_seed(wl.index, layer, midx), dtype=wl.act_dtype,
                                    device=dev, outlier_p=wl.outlier_p, outlier_mult=wl.outlier_mult)
         self.n, self.k, self.m = n, k, m
@@ -95,7 +108,7 @@ SUBLN_EPS = 1e-5
 
 
 class Workload:
-    def __init__(self, bl, synth, idx, m, dev, subln=False, path="fused"):
+    def __init__(self, bl, synth, idx, m, dev, subln=False, path="fused", weights_from=None):
         import torch
 
         self.wl = synth.WORKLOADS[idx]
@@ -108,7 +121,10 @@ class Workload:
         self.path = path
         self.sweep = self.wl.layers > 1  # a step sweeps every layer instead of one set
         nsets = self.wl.layers if self.sweep else self.wl.rotate_sets
-        self.sets = [[Matrix(bl, synth, self.wl, s, i, k, n, m, dev, binary=path == "binary")
+        share = weights_from is not None and weights_from.wl.index == idx and path != "binary" and \
+            weights_from.path != "binary"
+        self.sets = [[Matrix(bl, synth, self.wl, s, i, k, n, m, dev, binary=path == "binary",
+                             weights=weights_from.sets[s][i] if share else None)
                       for i, (_, k, n) in enumerate(self.wl.matrices)] for s in range(nsets)]
         for s, st in enumerate(self.sets):
             for i, mat in enumerate(st):
@@ -385,53 +401,86 @@ def measure_quantisers(bl, synth, dev, reps: int = 20):
     return out
 
 
+def _time_calls(calls, reps: int, warm: int = 20) -> float:
+    """Mean µs per call of back-to-back pre-marshalled launches, HIP events on the stream."""
+    import torch
+
+    for i in range(warm):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        calls[i % len(calls)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
 def measure_ceilings(bl, dev):
     """Measured ceilings on this GPU (library probes, back-to-back launches timed with HIP
-    events): HBM read rate for the decode access pattern at the two matrix sizes (the
-    buffers rotate through 2 GiB, so every launch reads from HBM), and the int8 MFMA rate
-    with no memory traffic."""
+    events; the buffers rotate through a 2 GiB pool, so every launch reads from HBM):
+      * read_*: a plain grid-stride read (bitlinear_probe_read) with no access pattern of
+        the BitLinear kernels, at 58.7 MB and 4.4 MB per launch (the decode matrices'
+        sizes) and 1 GiB; workgroup counts and load kinds swept, the best kept;
+      * stream_*: the same sizes read with the decode kernels' tile pattern
+        (bitlinear_probe_stream);
+      * mfma_int8_TOPS: independent int8 MFMAs with no memory traffic."""
     import torch
 
     pool_bytes = 2 << 30
     pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
     pool.fill_(0x5A)
     stream = torch.cuda.current_stream().cuda_stream
-    out = {}
-    for name, nbytes in (("58.7MB", 58_720_256), ("4.4MB", 4_423_680)):
+    out, sweep = {}, {}
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    for name, nbytes in (("58.7MB", 58_720_256), ("4.4MB", 4_423_680), ("1GiB", 1 << 30)):
         copies = pool_bytes // nbytes
-        words = int(bl.lib().bitlinear_probe_stream_words(nbytes))
-        sink = torch.empty(words, dtype=torch.int32, device=dev)
-        calls = [bl.PreparedCall("bitlinear_probe_stream", pool.data_ptr() + i * nbytes, nbytes, sink.data_ptr(),
-                                 words, stream) for i in range(copies)]
-        reps = 400 if nbytes < 10_000_000 else 200
-        for i in range(20):
-            calls[i % copies]()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(reps):
-            calls[i % copies]()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        out[f"stream_{name}_us"] = round(us, 3)
-        out[f"stream_{name}_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        reps = 400 if nbytes < 10_000_000 else (200 if nbytes < 100_000_000 else 12)
+        best = None
+        for nt in (1, 0):
+            for groups in (1024, 2048, 4096, 8192):
+                calls = [bl.PreparedCall("bitlinear_probe_read", pool.data_ptr() + i * nbytes, nbytes, groups, nt,
+                                         sink.data_ptr(), stream) for i in range(copies)]
+                us = _time_calls(calls, reps, warm=min(20, 2 * copies))
+                gbs = nbytes / (us * 1e-6) / 1e9
+                sweep[f"read_{name}_wg{groups}_{'nt' if nt else 'plain'}_GBps"] = round(gbs, 1)
+                if best is None or us < best[0]:
+                    best = (us, gbs, groups, nt)
+        out[f"read_{name}_us"] = round(best[0], 3)
+        out[f"read_{name}_GBps"] = round(best[1], 1)
+        out[f"read_{name}_config"] = f"{best[2]} workgroups, {'non-temporal' if best[3] else 'ordinary'} loads"
+        if nbytes < (1 << 30):
+            words = int(bl.lib().bitlinear_probe_stream_words(nbytes))
+            tsink = torch.empty(words, dtype=torch.int32, device=dev)
+            calls = [bl.PreparedCall("bitlinear_probe_stream", pool.data_ptr() + i * nbytes, nbytes, tsink.data_ptr(),
+                                     words, stream) for i in range(copies)]
+            us = _time_calls(calls, reps)
+            out[f"stream_{name}_us"] = round(us, 3)
+            out[f"stream_{name}_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    out["read_sweep"] = sweep
     del pool
     torch.cuda.empty_cache()
     # about 5 ms per launch; the first launch brings the clocks up, the best of three counts
     groups, iters = 512, 16000
-    sink = torch.empty(groups, dtype=torch.int32, device=dev)
+    msink = torch.empty(groups, dtype=torch.int32, device=dev)
     best = 0.0
     for rep in range(4):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        bl.probe_mfma(iters, groups, sink)
+        bl.probe_mfma(iters, groups, msink)
         e1.record()
         torch.cuda.synchronize()
         if rep:
             best = max(best, 2.0 * 16 * 16 * 64 * 16 * iters * groups * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e12)
     out["mfma_int8_TOPS"] = round(best, 1)
     return out
+
+
+def read_ceiling(ceilings, launch_bytes: float) -> float:
+    """The plain-read ceiling of the probe size nearest the launch's bytes."""
+    return ceilings["read_58.7MB_GBps"] if launch_bytes >= 20e6 else ceilings["read_4.4MB_GBps"]
 
 
 def dominant_kernel(w: Workload) -> str:
@@ -478,18 +527,45 @@ def gpu_state():
 
 
 def time_steps(w: Workload, steps: int, warmup: int):
+    """W untimed warm-up steps, then exactly `steps` timed steps with a HIP event recorded
+    after each on the stream the kernels run on.  Returns (mean ms per step over the whole
+    timed region, the per-step times in ms)."""
     import torch
 
     for _ in range(warmup):
         w.run_step()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         w.run_step()
-    stop.record()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps  # ms per step
+    trials = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, trials
+
+
+def trial_stats(trials, bytes_per_step=None, ops_per_step=None):
+    """Median, min, max and mean of per-step times, and the rates at the median and the min."""
+    import statistics
+
+    med, lo = statistics.median(trials), min(trials)
+    out = {"n": len(trials), "median_ms": round(med, 5), "min_ms": round(lo, 5), "max_ms": round(max(trials), 5),
+           "mean_ms": round(sum(trials) / len(trials), 5)}
+    if bytes_per_step:
+        out["GBps_at_median"] = round(bytes_per_step / (med * 1e-3) / 1e9, 1)
+        out["GBps_at_min"] = round(bytes_per_step / (lo * 1e-3) / 1e9, 1)
+    if ops_per_step:
+        out["TOPS_at_median"] = round(ops_per_step / (med * 1e-3) / 1e12, 2)
+        out["TOPS_at_min"] = round(ops_per_step / (lo * 1e-3) / 1e12, 2)
+    return out
+
+
+def leg_steps(w: Workload, floor_steps: int = 20, floor_launches: int = 400):
+    """Timed steps of a leg: at least 20 (the trial count) and at least 400 launches."""
+    launches = max(1, len(w.calls[0]))
+    return max(floor_steps, -(-floor_launches // launches))
 
 
 def time_forward_only(w: Workload, reps: int):
@@ -533,22 +609,59 @@ def time_forward_only(w: Workload, reps: int):
             sum(m.ops for m in mats) / len(mats))
 
 
-def cpu_baseline(w: Workload, budget_s: float):
-    """The oracle on the host over a bounded sample of the same workload (one thread)."""
+def host_cpu_facts():
+    """The host the oracle baseline runs on: CPU model, logical CPUs of the machine and of
+    this process's CPU set, and the physical cores in that set (distinct (package, core)
+    pairs of sysfs topology; hyper-threads of one core count once)."""
+    aff = sorted(os.sched_getaffinity(0))
+    cores = set()
+    for c in aff:
+        try:
+            with open(f"/sys/devices/system/cpu/cpu{c}/topology/physical_package_id") as f:
+                pkg = f.read().strip()
+            with open(f"/sys/devices/system/cpu/cpu{c}/topology/core_id") as f:
+                core = f.read().strip()
+            cores.add((pkg, core))
+        except OSError:
+            cores.add(("cpu", c))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_in_affinity": len(aff),
+            "physical_cores_in_affinity": len(cores)}
+
+
+def _acts_host_f32(x):
     import numpy as np
     import torch
 
     import oracle
 
-    def acts_host_f32(x):
-        if x.dtype == torch.bfloat16:
-            return oracle.bf16_bits_to_f32(x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
-        return x.float().cpu().numpy()
+    if x.dtype == torch.bfloat16:
+        return oracle.bf16_bits_to_f32(x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+    return x.float().cpu().numpy()
 
-    done_bytes, done_ops, t_used, mats = 0, 0, 0.0, 0
-    for mat in sum(w.sets, []):
+
+def cpu_baseline_single(w: Workload, layers: int = 2):
+    """The oracle on one host thread over the matrices of the first `layers` layers of the
+    step (weight sets, for a one-set step): act quant, unpack, integer matmul and rescale
+    per matrix.  Returns (bytes, ops, seconds, matrices, matrices per step)."""
+    import numpy as np
+
+    import oracle
+
+    mats = sum(w.sets[:layers], [])
+    done_bytes = done_ops = 0
+    t_used = 0.0
+    for mat in mats:
         packed = mat.packed.cpu().numpy()
-        x = acts_host_f32(mat.x)
+        x = _acts_host_f32(mat.x)
         g = np.float32(mat.gamma.cpu().numpy()[0])
         t0 = time.perf_counter()
         xq, a = oracle.quant_acts(x)
@@ -557,57 +670,102 @@ def cpu_baseline(w: Workload, budget_s: float):
         t_used += time.perf_counter() - t0
         done_bytes += mat.bytes
         done_ops += mat.ops
-        mats += 1
-        if t_used >= budget_s:
-            break
-    return done_bytes, done_ops, t_used, mats
+    return done_bytes, done_ops, t_used, len(mats), w.matrices_per_step()
 
 
-def cpu_baseline_threads(w: Workload, budget_s: float, threads: int):
-    """The same oracle calls on `threads` host threads at once (the oracle's C routines run
-    outside the interpreter lock), each thread taking whole matrices of the workload in
-    turn until the wall-clock budget is spent: the oracle as it is, on more cores."""
-    import threading
+def cpu_baseline_cores(w: Workload, budget_s: float, threads: int):
+    """The oracle on `threads` host threads over the step's matrices in order, until the
+    wall-clock budget is spent or the step is done.  For each matrix the activation
+    quantiser runs once; then the 16-row blocks of the output rows are split into
+    `threads` contiguous slices, and each thread unpacks its slice of the packed bytes (a
+    row block is a contiguous byte range) and computes its columns of the output (the
+    oracle's C routines run outside the interpreter lock).  Host copies of the inputs are
+    made outside the timed part.  Returns (bytes, ops, seconds, matrices, matrices per step)."""
+    from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
-    import torch
 
     import oracle
 
-    def acts_host_f32(x):
-        if x.dtype == torch.bfloat16:
-            return oracle.bf16_bits_to_f32(x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
-        return x.float().cpu().numpy()
+    mats = w.step_groups()[0]
+    done_bytes = done_ops = 0
+    t_used = 0.0
+    n_done = 0
+    with ThreadPoolExecutor(threads) as pool:
+        for mat in mats:
+            if t_used >= budget_s:
+                break
+            packed = mat.packed.cpu().numpy()
+            x = _acts_host_f32(mat.x)
+            g = np.float32(mat.gamma.cpu().numpy()[0])
+            blocks = -(-mat.n // 16)
+            cuts = [blocks * i // threads for i in range(threads + 1)]
 
-    mats = sum(w.sets, [])[: 4 * threads]
-    inputs = [(m.packed.cpu().numpy(), acts_host_f32(m.x), np.float32(m.gamma.cpu().numpy()[0]), m) for m in mats]
-    lock = threading.Lock()
-    state = {"next": 0, "bytes": 0, "ops": 0, "mats": 0}
-    t0 = time.perf_counter()
+            def part(i, xq, a, packed=packed, mat=mat, g=g, cuts=cuts):
+                lo, hi = cuts[i], cuts[i + 1]
+                if lo == hi:
+                    return None
+                rows = min(mat.n, 16 * hi) - 16 * lo
+                sub = packed[oracle.packed_bytes(16 * lo, mat.k):oracle.packed_bytes(16 * hi, mat.k)]
+                q = oracle.unpack(np.ascontiguousarray(sub), rows, mat.k)
+                return oracle.forward(q, g, xq, a, mat.k)[1]
 
-    def worker():
-        while time.perf_counter() - t0 < budget_s:
-            with lock:
-                i = state["next"]
-                state["next"] += 1
-            packed, x, g, mat = inputs[i % len(inputs)]
+            t0 = time.perf_counter()
             xq, a = oracle.quant_acts(x)
-            q = oracle.unpack(packed, mat.n, mat.k)
-            oracle.forward(q, g, xq, a, mat.k)
-            with lock:
-                state["bytes"] += mat.bytes
-                state["ops"] += mat.ops
-                state["mats"] += 1
-
-    pool = [threading.Thread(target=worker) for _ in range(threads)]
-    for t in pool:
-        t.start()
-    for t in pool:
-        t.join()
-    return state["bytes"], state["ops"], time.perf_counter() - t0, state["mats"]
+            ys = [y for y in pool.map(lambda i: part(i, xq, a), range(threads)) if y is not None]
+            np.concatenate(ys, axis=1)
+            t_used += time.perf_counter() - t0
+            done_bytes += mat.bytes
+            done_ops += mat.ops
+            n_done += 1
+    return done_bytes, done_ops, t_used, n_done, len(mats)
 
 
-def leg_summary(w: Workload, ms: float, launch_ms, launch_bytes, launch_ops, ceilings=None):
+def roofline_block(w: Workload, launch_ms, launch_bytes, launch_ops, launch_timing, workload_idx, ceilings):
+    """The roofline of the step's dominant kernel: algorithmic bytes (decode, HBM-bound) or
+    int8 ops (prefill, MFMA-bound) per launch over the mean launch duration."""
+    kernel = dominant_kernel(w)
+    traffic = measured_traffic(kernel, workload_idx, w.m)
+    if w.m <= 16:
+        achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+                "launch_us": round(launch_ms * 1e3, 3), "launch_timing": launch_timing,
+                "algorithmic_bytes_per_launch": int(launch_bytes),
+                "note": "algorithmic bytes are the 2-bit packed weights; the information bound of ternary "
+                        "codes, log2(3) bits per weight, is 79 % of them"}
+        if ceilings:
+            c = read_ceiling(ceilings, launch_bytes)
+            roof["measured_ceiling"] = c
+            roof["measured_ceiling_kind"] = "plain grid-stride HBM read of the same bytes per launch"
+            roof["frac_of_measured_ceiling"] = round(achieved / c, 4)
+    else:
+        # int8 contraction: TOPS against the dense int8 MFMA peak (unit kept as the contract's)
+        achieved = launch_ops / (launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": I8_PEAK_TOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / I8_PEAK_TOPS, 4), "traffic": traffic, "kernel": kernel,
+                "launch_us": round(launch_ms * 1e3, 3), "launch_timing": launch_timing,
+                "algorithmic_ops_per_launch": int(launch_ops)}
+        if ceilings:
+            roof["measured_ceiling"] = ceilings["mfma_int8_TOPS"]
+            roof["measured_ceiling_kind"] = "independent int8 MFMAs, no memory traffic"
+            roof["frac_of_measured_ceiling"] = round(achieved / ceilings["mfma_int8_TOPS"], 4)
+    return roof
+
+
+def launch_timing_of(w: Workload, ms: float):
+    """Mean forward-launch duration: the timed region over its launches when the step holds
+    nothing but the fused kernel, else passes of the forward launches alone."""
+    mats = w.step_groups()[0]
+    if all(w.fused.values()) and not getattr(w, "grouping", None) and not getattr(w, "gated", False):
+        return (ms / len(mats), w.bytes_per_step() / len(mats), w.ops_per_step() / len(mats),
+                "timed region / launches (the step is only this kernel)")
+    reps = max(20, len(w.step_groups())) if w.sweep else max(400, 4 * len(w.sets))
+    l_ms, l_b, l_o = time_forward_only(w, reps)
+    return l_ms, l_b, l_o, "HIP events around back-to-back forward launches alone (activations quantised before)"
+
+
+def leg_summary(w: Workload, ms: float, trials, launch_ms, launch_bytes, launch_ops, ceilings=None):
     gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9
     tops = w.ops_per_step() / (ms * 1e-3) / 1e12
     out = {
@@ -617,6 +775,8 @@ def leg_summary(w: Workload, ms: float, launch_ms, launch_bytes, launch_ops, cei
         "allin_GBps": round(w.allin_bytes_per_step() / (ms * 1e-3) / 1e9, 1),
         "int8_TOPS": round(tops, 2), "mfma_frac": round(tops / I8_PEAK_TOPS, 4),
         "tokens_per_s_eq": round(w.m / (ms * 1e-3), 1),  # every matrix of the step applied once per token
+        "launches_per_step": len(w.calls[0]),
+        "trials": trial_stats(trials, w.bytes_per_step(), w.ops_per_step() if w.m > 16 else None),
     }
     if launch_ms is not None:
         out["forward_launch_us"] = round(launch_ms * 1e3, 3)
@@ -626,10 +786,14 @@ def leg_summary(w: Workload, ms: float, launch_ms, launch_bytes, launch_ops, cei
             if w.m > 16:
                 out["forward_frac_of_measured_mfma"] = round(out["forward_launch_TOPS"] / ceilings["mfma_int8_TOPS"], 4)
             else:
-                big = launch_bytes >= 20e6
-                c = ceilings["stream_58.7MB_GBps"] if big else ceilings["stream_4.4MB_GBps"]
-                out["forward_frac_of_measured_stream"] = round(out["forward_launch_GBps"] / c, 4)
+                out["forward_frac_of_plain_read"] = round(out["forward_launch_GBps"] / read_ceiling(ceilings,
+                                                                                                     launch_bytes), 4)
     return out
+
+
+# legs that carry their own roofline block: the 2B-class M = 1 decode, the 2048-token
+# prefill, and the int8-only decode of the 100B-class matrices
+ROOFLINE_LEGS = {"1", "3", "4i"}
 
 
 def main():
@@ -652,119 +816,101 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
     state_before = gpu_state()
-    ms = time_steps(head, args.steps, args.warmup)
+    progress(f"headline workload {args.workload} M={m_head} ready: {len(head.calls[0])} launches per step")
+    ms, trials = time_steps(head, args.steps, args.warmup)
     state_after = gpu_state()
+    progress(f"headline timed: {ms:.4f} ms per step")
     decode = m_head <= 16
-    mats = head.step_groups()[0]
-    if all(head.fused.values()):
-        # the step holds nothing but launches of the fused kernel: its mean launch duration
-        # is the timed region (HIP events on the replay stream) over the launches in it
-        launch_ms = ms / len(mats)
-        launch_bytes, launch_ops = head.bytes_per_step() / len(mats), head.ops_per_step() / len(mats)
-        launch_timing = "timed region / launches (the step is only this kernel)"
-    else:
-        launch_ms, launch_bytes, launch_ops = time_forward_only(head, 3 if head.sweep else max(40, 4 * len(head.sets)))
-        launch_timing = "graph replays of the forward launches alone"
+    launch_ms, launch_bytes, launch_ops, launch_timing = launch_timing_of(head, ms)
     value = head.bytes_per_step() / (ms * 1e-3) / 1e9 if decode else head.ops_per_step() / (ms * 1e-3) / 1e12
-    kernel = dominant_kernel(head)
-    traffic = measured_traffic(kernel, args.workload, m_head)
-    if decode:
-        achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kernel, "launch_us": round(launch_ms * 1e3, 3), "launch_timing": launch_timing,
-                "algorithmic_bytes_per_launch": int(launch_bytes)}
-    else:
-        # int8 contraction: TOPS against the dense int8 MFMA peak (unit kept as the contract's)
-        achieved = launch_ops / (launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": I8_PEAK_TOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / I8_PEAK_TOPS, 4), "traffic": traffic, "kernel": kernel,
-                "launch_us": round(launch_ms * 1e3, 3), "launch_timing": launch_timing,
-                "algorithmic_ops_per_launch": int(launch_ops)}
     ceilings = measure_ceilings(bl, dev)
+    progress("ceilings measured")
+    roof = roofline_block(head, launch_ms, launch_bytes, launch_ops, launch_timing, args.workload, ceilings)
     quantisers = measure_quantisers(bl, synth, dev)
-    if decode:
-        ceil = ceilings["stream_4.4MB_GBps"] if head.bytes_per_step() / len(mats) < 20e6 else ceilings["stream_58.7MB_GBps"]
-    else:
-        ceil = ceilings["mfma_int8_TOPS"]
-    roof["measured_ceiling"] = ceil
-    roof["frac_of_measured_ceiling"] = round(roof["achieved"] / ceil, 4)
-    if decode:
-        roof["note"] = ("algorithmic bytes are the 2-bit packed weights; the information bound of ternary "
-                        "codes, log2(3) bits per weight, is 79 % of them")
     legs = {}
     for tok in [t.strip() for t in args.legs.split(",") if t.strip()]:
         flags = tok.lstrip("0123456789")
         idx = int(tok[: len(tok) - len(flags)])
         grouped, subln, gated = "g" in flags, "s" in flags, "f" in flags
         path = "lut" if "l" in flags else ("int8" if "i" in flags else ("binary" if "b" in flags else "fused"))
-        if idx == args.workload and not flags:
-            continue
         if (grouped and idx not in GROUPINGS) or (gated and idx != 1):
             continue
         for m in synth.WORKLOADS[idx].m_list:
+            if idx == args.workload and not flags and m == m_head:
+                continue  # the headline itself
             plan_of = {"lut": bl.forward_lut_plan, "binary": bl.forward_binary_plan}.get(path)
             if plan_of and any(plan_of(m, n, k) is None for _, k, n in synth.WORKLOADS[idx].matrices):
                 continue
-            w = Workload(bl, synth, idx, m, dev, subln=subln, path=path)
+            w = Workload(bl, synth, idx, m, dev, subln=subln, path=path, weights_from=head)
             if grouped:
                 w.set_grouping(GROUPINGS[idx])
             if gated:
                 w.set_gated_pair()
             if args.graph:
                 w.capture()
-            steps = max(3, args.steps // (40 if w.sweep else 1))
-            lms = time_steps(w, steps, max(1, args.warmup // (40 if w.sweep else 4)))
+            lms, ltrials = time_steps(w, leg_steps(w), max(2, -(-100 // len(w.calls[0]))))
             key = f"w{idx}{flags}_m{m}"
-            if gated:
-                legs[key] = leg_summary(w, lms, None, None, None)
-                legs[key]["note"] = ("gate and up in one bitlinear_forward_gated_relu2 launch (squared-ReLU gating "
-                                     "epilogue), then down; per-step bytes as the three matrices")
-                if subln:
-                    legs[key]["note"] += "; sub-layer RMS normalisation in front of both quantisers"
-            elif grouped:
-                legs[key] = leg_summary(w, lms, None, None, None)
-                legs[key]["grouping"] = [[w.wl.matrices[i][0] for i in g] for g in GROUPINGS[idx]]
-                legs[key]["note"] = ("projections of one input in one grouped call (shared activation "
-                                     "quantisation); per-step bytes and ops as the ungrouped workload")
-                if subln:
+            progress(f"leg {key}: {lms:.4f} ms per step")
+            if gated or grouped or subln:
+                legs[key] = leg_summary(w, lms, ltrials, None, None, None)
+                if gated:
+                    legs[key]["note"] = ("gate and up in one bitlinear_forward_gated_relu2 launch (squared-ReLU "
+                                         "gating epilogue), then down; per-step bytes as the three matrices")
+                elif grouped:
+                    legs[key]["grouping"] = [[w.wl.matrices[i][0] for i in g] for g in GROUPINGS[idx]]
+                    legs[key]["note"] = ("projections of one input in one grouped call (shared activation "
+                                         "quantisation); per-step bytes and ops as the ungrouped workload")
+                else:
+                    legs[key]["kernel"] = dominant_kernel(w)
+                    legs[key]["note"] = ("sub-layer RMS normalisation (per-feature gain, eps 1e-5) in front of the "
+                                         "quantiser, in the same kernel where the plan fuses it")
+                if subln and (gated or grouped):
                     legs[key]["note"] += "; sub-layer RMS normalisation in front of the quantiser"
-            elif path != "fused":
-                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else max(40, 4 * len(w.sets)))
-                legs[key] = leg_summary(w, lms, l_ms, l_b, l_o, ceilings)
+            else:
+                l_ms, l_b, l_o, l_how = launch_timing_of(w, lms)
+                legs[key] = leg_summary(w, lms, ltrials, l_ms, l_b, l_o, ceilings)
                 legs[key]["kernel"] = {"lut": "k_gemv_lut (table-lookup decode)",
                                        "binary": "k_gemv_bin (1-bit sign-binary decode)"}.get(path) or dominant_kernel(w)
-                legs[key]["note"] = ("activation quantiser, then the " +
-                                     {"lut": "table-lookup forward (bitlinear_forward_lut)",
-                                      "binary": "1-bit sign-binary forward (bitlinear_forward_binary; "
-                                                "packed_GBps counts the 1-bit bytes)"}.get(
-                                         path, "int8 forward (bitlinear_forward)") +
-                                     "; forward_launch_* time the forward launches alone")
-            elif subln:
-                legs[key] = leg_summary(w, lms, None, None, None)
-                legs[key]["kernel"] = dominant_kernel(w)
-                legs[key]["note"] = ("sub-layer RMS normalisation (per-feature gain, eps 1e-5) in front of the "
-                                     "quantiser, in the same kernel where the plan fuses it")
-            else:
-                l_ms, l_b, l_o = time_forward_only(w, 3 if w.sweep else max(40, 4 * len(w.sets)))
-                legs[key] = leg_summary(w, lms, l_ms, l_b, l_o, ceilings)
-                legs[key]["kernel"] = dominant_kernel(w)
-                legs[key]["traffic_bytes_per_launch"] = measured_traffic(dominant_kernel(w), idx, m)
+                legs[key]["forward_launch_timing"] = l_how
+                if path == "fused":
+                    legs[key]["traffic_bytes_per_launch"] = measured_traffic(dominant_kernel(w), idx, m)
+                else:
+                    legs[key]["note"] = ("activation quantiser, then the " +
+                                         {"lut": "table-lookup forward (bitlinear_forward_lut)",
+                                          "binary": "1-bit sign-binary forward (bitlinear_forward_binary; "
+                                                    "packed_GBps counts the 1-bit bytes)"}.get(
+                                             path, "int8 forward (bitlinear_forward)") +
+                                         "; forward_launch_* time the forward launches alone")
+                if tok in ROOFLINE_LEGS and (m == synth.WORKLOADS[idx].m_list[0]):
+                    legs[key]["roofline"] = roofline_block(w, l_ms, l_b, l_o, l_how, idx, ceilings)
             del w
             torch.cuda.empty_cache()
-    cpu = None
+    cpu = cpu_single = None
+    host = host_cpu_facts()
     if not args.no_cpu_baseline:
-        b, o, t, n_cpu = cpu_baseline(head, args.cpu_seconds)
-        threads = min(16, len(os.sched_getaffinity(0)))
-        bm, om, tm, nm = cpu_baseline_threads(head, args.cpu_seconds / 2, threads)
-        cpu_mt = {"value": round(bm / tm / 1e9, 4) if decode else round(om / tm / 1e12, 6),
-                  "unit": "GB/s" if decode else "TOPS", "cores": threads, "kind": "oracle",
-                  "sample": f"{nm} matrices of the same workload on {threads} host threads at once, "
-                            f"{tm:.1f} s wall clock"}
-        cpu = {"value": round(b / t / 1e9, 4) if decode else round(o / t / 1e12, 6),
-               "unit": "GB/s" if decode else "TOPS", "cores": 1, "kind": "oracle",
-               "sample": f"{n_cpu} matrices of the same workload (act quant + unpack + int matmul + rescale), "
-                         f"{t:.1f} s, single-threaded scalar C"}
+        unit = "GB/s" if decode else "TOPS"
+        rate = (lambda b, o, t: round(b / t / 1e9, 4)) if decode else (lambda b, o, t: round(o / t / 1e12, 6))
+        threads = max(1, min(16, host["physical_cores_in_affinity"]))
+        b, o, t, n_done, per_step = cpu_baseline_cores(head, args.cpu_seconds, threads)
+        cpu = {"value": rate(b, o, t), "unit": unit, "cores": threads, "kind": "oracle",
+               "sample": (f"{n_done} of the step's {per_step} matrices in order "
+                          f"({'the whole step' if n_done == per_step else 'a leading sample'}), {t:.1f} s: act quant "
+                          f"once per matrix, then each matrix's 16-row blocks split into {threads} contiguous "
+                          f"slices (unpack + int matmul + rescale) on {threads} host threads, one per physical "
+                          "core of this process's CPU set"),
+               "step_s_scaled": round(t * per_step / n_done, 3),
+               "tokens_per_s_eq": round(m_head * n_done / (t * per_step), 3),
+               "host": host, "oracle_cflags": " ".join(oracle_cflags())}
+        progress(f"oracle on {threads} threads: {n_done} matrices in {t:.1f} s")
+        b1, o1, t1, n1, per_step = cpu_baseline_single(head, 2)
+        progress(f"oracle on one thread: {n1} matrices in {t1:.1f} s")
+        scaled = per_step / n1
+        cpu_single = {"value": rate(b1, o1, t1), "unit": unit, "cores": 1, "kind": "oracle",
+                      "sample": (f"{n1} matrices ({'2 layers' if head.sweep else '2 weight sets'}) on one thread, "
+                                 f"{t1:.1f} s; the step time is scaled by {per_step}/{n1} (SCALED, not measured "
+                                 "over the whole step)"),
+                      "step_s_scaled": round(t1 * scaled, 3),
+                      "tokens_per_s_eq_scaled": round(m_head / (t1 * scaled), 4)}
     out = {
         "metric": "BitLinear decode packed-weight GB/s (% HBM peak); prefill int8 TOPS (% MFMA)",
         "value": round(value, 1 if decode else 2),
@@ -775,24 +921,36 @@ def main():
         "dtype": "i8", "data": "synthetic",
         "config": {"workload": head.wl.name, "M": m_head,
                    "matrices": [list(x) for x in head.wl.matrices],
-                   "distinct_weight_sets": len(head.sets),
+                   "layers": head.wl.layers, "distinct_weight_sets": len(head.sets),
+                   "launches_per_step": len(head.calls[0]),
                    "packed_bytes_per_step": head.bytes_per_step(),
                    "allin_GBps": round(head.allin_bytes_per_step() / (ms * 1e-3) / 1e9, 1),
                    "us_per_matrix": round(ms * 1e3 / head.matrices_per_step(), 3),
                    "tokens_per_s_eq": round(m_head / (ms * 1e-3), 1),
-                   "seeds": "torch.Generator per tensor: 1000*workload + 10*set + matrix for weights, "
+                   "seeds": "torch.Generator per tensor: 1000*workload + 10*layer + matrix for weights, "
                             "+500 for activations, +700 for sub-layer gains",
                    "launch": "hip graph replay" if args.graph else "pre-marshalled eager C-ABI calls",
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None},
+        "trials": trial_stats(trials, head.bytes_per_step(), None if decode else head.ops_per_step()),
         "roofline": roof,
         "ceilings": ceilings,
         "quantisers": quantisers,
         "cpu_baseline": cpu,
-        "cpu_baseline_all_cores": cpu_mt if cpu else None,
+        "cpu_baseline_single_thread": cpu_single,
         "gpu_state": {"before_timed_region": state_before, "after_timed_region": state_after},
         "legs": legs,
     }
     print(json.dumps(out), flush=True)
+
+
+def progress(msg: str) -> None:
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def oracle_cflags():
+    import oracle
+
+    return ["gcc", *oracle._CFLAGS]
 
 
 if __name__ == "__main__":

@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_probe_stream_words.argtypes = [i64]
         L.bitlinear_probe_stream.restype = c_int
         L.bitlinear_probe_stream.argtypes = [p, i64, p, i64, p]
+        L.bitlinear_probe_read.restype = c_int
+        L.bitlinear_probe_read.argtypes = [p, i64, i64, c_int, p, p]
         L.bitlinear_probe_mfma.restype = c_int
         L.bitlinear_probe_mfma.argtypes = [i64, i64, p, p]
         L.bitlinear_forward_grouped.restype = c_int
@@ -109,7 +111,8 @@ EXPORTED_SYMBOLS = (
     "bitlinear_packed_bytes", "bitlinear_wq_workspace_bytes", "bitlinear_quantize_weights",
     "bitlinear_quantize_acts", "bitlinear_forward", "bitlinear_forward_fused", "bitlinear_forward_plan",
     "bitlinear_forward_fused_plan", "bitlinear_forward_grouped", "bitlinear_probe_stream_words",
-    "bitlinear_probe_stream", "bitlinear_probe_mfma", "bitlinear_subln_quantize_acts", "bitlinear_forward_subln",
+    "bitlinear_probe_stream", "bitlinear_probe_read", "bitlinear_probe_mfma", "bitlinear_subln_quantize_acts",
+    "bitlinear_forward_subln",
     "bitlinear_forward_grouped_subln", "bitlinear_forward_subln_plan", "bitlinear_gated_relu2_workspace_bytes",
     "bitlinear_forward_gated_relu2", "bitlinear_forward_gated_relu2_plan", "bitlinear_forward_lut",
     "bitlinear_forward_lut_plan", "bitlinear_kb_pad", "bitlinear_packed_bytes_binary",
@@ -608,6 +611,22 @@ def probe_stream(buf, out=None):
         out = torch.empty(words, dtype=torch.int32, device=buf.device)
     _check("bitlinear_probe_stream", lib().bitlinear_probe_stream(buf.data_ptr(), nbytes, out.data_ptr(),
                                                                   out.numel(), _stream(buf.device)))
+    return out
+
+
+def probe_read(buf, workgroups: int, nontemporal: bool = True, out=None):
+    """Read the device tensor ``buf`` with a plain grid-stride loop of ``workgroups`` x 256
+    lanes (measurement probe); returns the per-workgroup XOR checksums (int32 device tensor)."""
+    import torch
+
+    _require_cuda(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(workgroups, dtype=torch.int32, device=buf.device)
+    if out.numel() < workgroups:
+        raise ValueError("out needs one word per workgroup")
+    _check("bitlinear_probe_read", lib().bitlinear_probe_read(buf.data_ptr(), nbytes, workgroups, int(nontemporal),
+                                                              out.data_ptr(), _stream(buf.device)))
     return out
 
 

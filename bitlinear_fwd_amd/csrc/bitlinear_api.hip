@@ -283,6 +283,15 @@ int bitlinear_probe_stream(const void* buf, int64_t bytes, uint32_t* out, int64_
   return hip_status(bl::launch_probe_stream(buf, bytes, out, static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_probe_read(const void* buf, int64_t bytes, int64_t workgroups, int nontemporal, uint32_t* out,
+                         void* stream) {
+  if (!buf || !out || bytes < 16 || bytes % 16 || bytes >= (int64_t(1) << 40) || workgroups < 1 ||
+      workgroups > (int64_t(1) << 20) || (nontemporal != 0 && nontemporal != 1))
+    return BL_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || !aligned(out, 4)) return BL_ERR_INVALID_ARG;
+  return hip_status(bl::launch_probe_read(buf, bytes, workgroups, nontemporal != 0, out, static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_probe_mfma(int64_t iters, int64_t workgroups, uint32_t* out, void* stream) {
   if (!out || iters < 1 || iters > (int64_t(1) << 32) || workgroups < 1 || workgroups > (int64_t(1) << 20) ||
       !aligned(out, 4))

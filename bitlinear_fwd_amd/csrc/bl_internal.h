@@ -173,6 +173,8 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
 int64_t probe_stream_groups(int64_t bytes);
 hipError_t launch_probe_stream(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
 hipError_t launch_probe_mfma(int64_t iters, int64_t groups, uint32_t* out, hipStream_t s);
+hipError_t launch_probe_read(const void* buf, int64_t bytes, int64_t groups, bool nontemporal, uint32_t* out,
+                             hipStream_t s);
 
 inline int64_t n_pad(int64_t n) { return (n + kTileRows - 1) / kTileRows * kTileRows; }
 inline int64_t k_pad(int64_t k) { return (k + kTileCols - 1) / kTileCols * kTileCols; }

@@ -5,6 +5,10 @@
 //                   issued at once) and does nothing else with it: the HBM read ceiling
 //                   for that pattern at a given size.  Each workgroup (4 waves, 32 KiB)
 //                   stores the XOR of the 32-bit words it read, so the result is checkable.
+//   k_probe_read    a plain grid-stride read of a buffer, 16 bytes per lane, 8 loads in
+//                   flight per lane, as many workgroups as the caller asks for: the HBM
+//                   read ceiling of a launch of that size with no access pattern of the
+//                   BitLinear kernels.  Each workgroup stores the XOR of the words it read.
 //   k_probe_mfma    independent v_mfma_i32_16x16x64_i8 back to back, no memory traffic:
 //                   the int8 matrix-core ceiling.
 #include "bl_internal.h"
@@ -15,6 +19,42 @@ namespace {
 constexpr int kStreamRun = 8;         // tiles per wave
 constexpr int kStreamWaves = 4;       // waves per workgroup
 constexpr int kMfmaChains = 16;       // independent accumulators per wave
+constexpr int kReadUnroll = 8;        // loads in flight per lane in the plain read
+
+__device__ __forceinline__ uint32_t xor4(const uint4& v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+template <bool kNonTemporal>
+__device__ __forceinline__ uint4 read16(const uint4* p) {
+  if constexpr (kNonTemporal)
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p)));
+  else
+    return *p;
+}
+
+// Lane i of the grid reads 16-byte words i, i + S, i + 2S, ... (S = 256 x workgroups), eight
+// at a time; the loop bound keeps every access below n16.
+template <bool kNonTemporal>
+__global__ __launch_bounds__(256) void k_probe_read(const uint4* __restrict__ buf, int64_t n16,
+                                                    uint32_t* __restrict__ out) {
+  __shared__ uint32_t red[4];
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+    uint4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = read16<kNonTemporal>(buf + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) x ^= xor4(v[u]);
+  }
+  for (; i < n16; i += stride) x ^= xor4(read16<kNonTemporal>(buf + i));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
 
 __global__ __launch_bounds__(kStreamWaves * 64) void k_probe_stream(const uint4* __restrict__ buf, int64_t tiles,
                                                                     uint32_t* __restrict__ out) {
@@ -71,6 +111,16 @@ hipError_t launch_probe_stream(const void* buf, int64_t bytes, uint32_t* out, hi
   const int64_t tiles = bytes / kTileBytes;
   hipLaunchKernelGGL(k_probe_stream, dim3((unsigned)probe_stream_groups(bytes)), dim3(kStreamWaves * 64), 0, s,
                      static_cast<const uint4*>(buf), tiles, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void* buf, int64_t bytes, int64_t groups, bool nontemporal, uint32_t* out,
+                             hipStream_t s) {
+  const auto* p = static_cast<const uint4*>(buf);
+  if (nontemporal)
+    hipLaunchKernelGGL(k_probe_read<true>, dim3((unsigned)groups), dim3(256), 0, s, p, bytes / 16, out);
+  else
+    hipLaunchKernelGGL(k_probe_read<false>, dim3((unsigned)groups), dim3(256), 0, s, p, bytes / 16, out);
   return hipGetLastError();
 }
 

@@ -320,12 +320,22 @@ int bitlinear_forward_fused_plan(int64_t M, int64_t N, int64_t K, int dt, int32_
  * receives the XOR of the 32-bit words of the i-th 32 KiB block (the last block may be
  * shorter).  bitlinear_probe_stream_words returns -1 for an invalid size.
  *
+ * bitlinear_probe_read reads `bytes` (a multiple of 16, at least 16) of device memory at
+ * `buf` (16-byte aligned) with a plain grid-stride loop: `workgroups` (1 .. 2^20) of 256
+ * lanes, lane i of the grid taking the 16-byte words i, i + S, i + 2S, ... (S = 256 x
+ * workgroups), eight loads in flight per lane, non-temporal when `nontemporal` is 1 (0:
+ * ordinary loads).  It shares no access pattern with the BitLinear kernels: the plain HBM
+ * read ceiling for a launch of that size.  out[workgroups] (device, uint32) receives, per
+ * workgroup, the XOR of the 32-bit words it read.
+ *
  * bitlinear_probe_mfma runs `workgroups` x 4 waves, each issuing 16 independent
  * v_mfma_i32_16x16x64_i8 per iteration for `iters` iterations (32768 int8 operations
  * each), with no memory traffic; out[workgroups] (device) receives checksums.
  */
 int64_t bitlinear_probe_stream_words(int64_t bytes);
 int bitlinear_probe_stream(const void* buf, int64_t bytes, uint32_t* out, int64_t out_words, void* stream);
+int bitlinear_probe_read(const void* buf, int64_t bytes, int64_t workgroups, int nontemporal, uint32_t* out,
+                         void* stream);
 int bitlinear_probe_mfma(int64_t iters, int64_t workgroups, uint32_t* out, void* stream);
 
 #ifdef __cplusplus

@@ -3,6 +3,9 @@ exactly the bytes the GPU consumed, and the comparison bars.
 
 Bars: gamma, packed bytes, int8 codes, absmax and int32 accumulators bit-exact; y within
 1e-5 relative of the oracle's fp64 rescale, and exactly 0 where the oracle's is 0."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -45,3 +48,24 @@ def check_equal(a: np.ndarray, b: np.ndarray, what: str) -> None:
 
 def gamma_bits(g) -> int:
     return int(np.asarray(g, dtype=np.float32).reshape(-1)[0:1].view(np.uint32)[0])
+
+
+def host_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_forward_rows(q: np.ndarray, gamma, xq: np.ndarray, absmax: np.ndarray, k: int):
+    """oracle.forward on every token row, the rows split into contiguous slices computed
+    on host threads at once (the oracle's C routines run outside the interpreter lock).
+    Each row's result depends on that row alone, so the slices concatenate to the
+    single-call result."""
+    m = xq.shape[0]
+    parts = max(1, min(host_threads(), m))
+    bounds = [m * i // parts for i in range(parts + 1)]
+    def one(i):
+        lo, hi = bounds[i], bounds[i + 1]
+        return oracle.forward(q, gamma, np.ascontiguousarray(xq[lo:hi]), np.ascontiguousarray(absmax[lo:hi]), k)
+    with ThreadPoolExecutor(parts) as pool:
+        res = list(pool.map(one, range(parts)))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])

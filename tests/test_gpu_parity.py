@@ -13,7 +13,7 @@ import torch
 import bitlinear_fwd_amd as bl
 import oracle
 from bitlinear_fwd_amd import synth
-from gpu_helpers import acts_host_f32, check_equal, check_y, gamma_bits, host
+from gpu_helpers import acts_host_f32, check_equal, check_y, gamma_bits, host, oracle_forward_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -343,8 +343,8 @@ def test_forward_prefill(m, n, k):
     (1000, 3000, 777, 192, 2), (700, 2600, 1100, 192, 2), (500, 7000, 1100, 256, 2), (450, 8000, 6912, 256, 2)])
 def test_forward_prefill_tile_shapes(m, n, k, tile_n, k_groups):
     # the prefill tile shapes (64 x 256 or 64 x 192 by the last round's load, one or two K
-    # groups per tile) with ragged M, N and K; the oracle checks a sample of token rows
-    # covering tile edges
+    # groups per tile) with ragged M, N and K; every output is checked (the oracle's rows
+    # split over host threads)
     plan = bl.forward_plan(m, n, k)
     _announce("forward prefill tiles", m, n, k, plan)
     assert plan["kernel"] == "prefill" and plan["tile_m"] == 64 and plan["tile_n"] == tile_n
@@ -358,10 +358,9 @@ def test_forward_prefill_tile_shapes(m, n, k, tile_n, k_groups):
     y, acc = bl.forward(d(oracle.pack(q)), d(np.array([gamma], np.float32)), d(xq), d(a), n, k,
                         want_y=True, want_acc=True)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, m // 2, m - 2, m - 1], rng.integers(0, m, 12)]))
-    acc_ref, y_ref = oracle.forward(q, gamma, xq[rows], a[rows], k)
-    check_equal(host(acc)[rows], acc_ref, f"acc m={m} n={n} k={k}")
-    check_y(host(y)[rows], y_ref, f"y m={m} n={n} k={k}")
+    acc_ref, y_ref = oracle_forward_rows(q, gamma, xq, a, k)
+    check_equal(host(acc), acc_ref, f"acc m={m} n={n} k={k}")
+    check_y(host(y), y_ref, f"y m={m} n={n} k={k}")
 
 
 def test_forward_extreme_accumulators():
@@ -512,6 +511,28 @@ def test_forward_fused_lds_form(m, n, k, dtype):
     _announce("forward fused lds", m, n, k, dtype, plan)
     assert plan["kernel"] == "fused" and plan["acts"] == "lds"
     _fused_check(m, n, k, dtype, seed=m * 13 + n + k)
+
+
+# One token on many row blocks (257 .. 1875, several workgroups per compute unit), ragged
+# last rows (29999) and ragged K, int8 and fused: the 100B-class shapes and others.
+MANY_RB = [(28672, 8192), (8192, 28672), (4100, 296), (16400, 296), (6912, 2560), (29999, 4000), (8200, 12000),
+           (5000, 20000), (4200, 32000), (12288, 3000), (16000, 1104), (24576, 5000)]
+
+
+@pytest.mark.parametrize("n,k", MANY_RB)
+def test_forward_many_row_blocks(n, k):
+    plan = bl.forward_plan(1, n, k)
+    _announce("forward many row blocks", 1, n, k, plan)
+    assert plan["kernel"] == "decode"
+    _fwd_check(1, n, k, seed=n + 7 * k)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("n,k", MANY_RB)
+def test_forward_fused_many_row_blocks(n, k, dtype):
+    plan = bl.forward_fused_plan(1, n, k, "bf16" if dtype == torch.bfloat16 else "f32")
+    _announce("forward fused many row blocks", 1, n, k, dtype, plan)
+    _fused_check(1, n, k, dtype, seed=n + 11 * k)
 
 
 @pytest.mark.parametrize("m,n,k,dtype,unaligned", [(5, 64, 512, torch.bfloat16, False), (1, 64, 300, torch.bfloat16, False),
