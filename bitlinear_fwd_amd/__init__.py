@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).argtypes = [i64, i64]
         L.bitlinear_quantize_weights.restype = c_int
         L.bitlinear_quantize_weights.argtypes = [p, i64, i64, p, p, p, i64, p]
+        L.bitlinear_quantize_weights_noalloc.restype = c_int
+        L.bitlinear_quantize_weights_noalloc.argtypes = [p, i64, i64, p, p, p]
         L.bitlinear_quantize_acts.restype = c_int
         L.bitlinear_quantize_acts.argtypes = [p, c_int, i64, i64, p, p, p, p]
         L.bitlinear_forward_fused.restype = c_int
@@ -117,6 +119,7 @@ EXPORTED_SYMBOLS = (
     "bitlinear_forward_gated_relu2", "bitlinear_forward_gated_relu2_plan", "bitlinear_forward_lut",
     "bitlinear_forward_lut_plan", "bitlinear_kb_pad", "bitlinear_packed_bytes_binary",
     "bitlinear_quantize_weights_binary", "bitlinear_forward_binary", "bitlinear_forward_binary_plan",
+    "bitlinear_quantize_weights_noalloc",
 )
 
 MAX_GROUP = 8
@@ -245,6 +248,26 @@ def quantize_weights(W, packed=None, gamma=None, workspace=None):
     _check("bitlinear_quantize_weights", lib().bitlinear_quantize_weights(
         W.data_ptr(), n, k, packed.data_ptr(), gamma.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(dev)))
+    return packed, gamma
+
+
+def quantize_weights_noalloc(W, packed=None, gamma=None):
+    """bitlinear_quantize_weights_noalloc: the weight quantiser with the library's own static
+    scratch in place of a workspace (the C call allocates nothing; outputs not given here
+    are allocated by torch before it).  Returns ``(packed, gamma)``."""
+    import torch
+
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float32 tensor")
+    n, k = W.shape
+    dev = W.device
+    if packed is None:
+        packed = torch.empty(packed_bytes(n, k), dtype=torch.uint8, device=dev)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=dev)
+    _check("bitlinear_quantize_weights_noalloc", lib().bitlinear_quantize_weights_noalloc(
+        W.data_ptr(), n, k, packed.data_ptr(), gamma.data_ptr(), _stream(dev)))
     return packed, gamma
 
 

@@ -62,6 +62,15 @@ int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* pa
   return hip_status(bl::launch_weight_quant(W, N, K, packed, gamma, workspace, static_cast<hipStream_t>(stream)));
 }
 
+int bitlinear_quantize_weights_noalloc(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                                       void* stream) {
+  if (!W || !packed || !gamma) return BL_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim) return BL_ERR_INVALID_ARG;
+  if (N > kMaxCount / K) return BL_ERR_UNSUPPORTED;
+  if (!aligned(W, 4) || !aligned(packed, 16) || !aligned(gamma, 4)) return BL_ERR_INVALID_ARG;
+  return hip_status(bl::launch_weight_quant_noalloc(W, N, K, packed, gamma, static_cast<hipStream_t>(stream)));
+}
+
 int bitlinear_quantize_acts(const void* X, int dt, int64_t M, int64_t K, int8_t* Xq, float* absmax,
                             int32_t* rowsum, void* stream) {
   if (!X || !Xq || !absmax) return BL_ERR_INVALID_ARG;

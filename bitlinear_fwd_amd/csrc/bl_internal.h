@@ -125,6 +125,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 // C ABI before these are called.
 hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
                                void* workspace, hipStream_t s);
+// The same with the workspace in the library's per-device static scratch (allocates nothing).
+hipError_t launch_weight_quant_noalloc(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                                       hipStream_t s);
 // rowsum (nullable): int32 [M], the exact sum of each row's codes.
 hipError_t launch_act_quant(const void* X, int bf16, int64_t M, int64_t K, int8_t* Xq, float* absmax,
                             hipStream_t s, int32_t* rowsum = nullptr);

@@ -14,7 +14,15 @@
 #include "bl_internal.h"
 #include "binary.h"
 
+#include <mutex>
+
 namespace bl {
+
+// Scratch of the no-allocation weight quantiser (bitlinear_quantize_weights_noalloc): the
+// exponent bins and 1/gamma, one copy per GPU, held until the process ends.  Host code
+// never uses this name as an address: it is resolved per device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[kWqWorkspaceBytes];
+
 namespace {
 
 constexpr int kBinThreads = 256;
@@ -297,6 +305,31 @@ hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, uint8_t* pa
   hipLaunchKernelGGL(k_ternarise_pack, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, W, N, K,
                      n_tiles, chunks, vec4_rows, inv, packed);
   return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept; null if the lookup fails.
+static void* scratch_address() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex lock;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> guard(lock);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+hipError_t launch_weight_quant_noalloc(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                                       hipStream_t s) {
+  void* ws = scratch_address();
+  if (!ws) return hipErrorInvalidSymbol;
+  // the bins are cleared by k_wq_clear at the start of every call (a kernel, not a memset)
+  return launch_weight_quant(W, N, K, packed, gamma, ws, s);
 }
 
 }  // namespace bl

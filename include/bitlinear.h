@@ -93,6 +93,21 @@ int bitlinear_quantize_weights(const float* W, int64_t N, int64_t K, uint8_t* pa
                                void* workspace, int64_t ws_bytes, void* stream);
 
 /*
+ * Step 1 without any allocation, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same result as bitlinear_quantize_weights, with the quantiser's scratch (the exponent
+ * bins and 1/gamma, 2304 bytes) in a static device array of the library instead of a
+ * caller workspace.  Each GPU holds its own copy until the process ends; it is looked up
+ * on the first call on a device (that device current).  The call allocates nothing.
+ * Arguments and limits as bitlinear_quantize_weights (N * K < 2^40, else
+ * BL_ERR_UNSUPPORTED; the scratch does not grow with the shape).  The scratch is cleared
+ * by a kernel at the start of every call; calls that overlap on one GPU (other streams,
+ * other host threads) share it and race.
+ */
+int bitlinear_quantize_weights_noalloc(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                                       void* stream);
+
+/*
  * Step 2 - per-token absmax int8 activation quantiser (aratech.ae, "BitLinear: the
  * building block": the largest magnitude of each token maps to 127).
  *   X       [M][K] fp32 (dt = BL_F32) or bf16 (dt = BL_BF16), row-major, element-aligned.
