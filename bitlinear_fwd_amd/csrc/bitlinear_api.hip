@@ -398,6 +398,11 @@ int grouped_impl(const bl_matrix* mats, int count, const void* X, int dt, int64_
   const hipError_t eq = norm ? bl::launch_subln_quant(X, dt == BL_BF16 ? 1 : 0, M, K, gain, eps, Xq, absmax, s)
                              : bl::launch_act_quant(X, dt == BL_BF16 ? 1 : 0, M, K, Xq, absmax, s);
   if (eq != hipSuccess) return BL_ERR_HIP;
+  {
+    bool launched = false;
+    const hipError_t e = bl::launch_gemv_grouped_int8(gm, count, Xq, absmax, M, K, s, &launched);
+    if (launched || e != hipSuccess) return hip_status(e);
+  }
   for (int j = 0; j < count; ++j) {
     const int st = bitlinear_forward(mats[j].packed, mats[j].gamma, Xq, absmax, M, mats[j].N, K, mats[j].Y,
                                      mats[j].acc, stream);

@@ -160,6 +160,11 @@ struct GroupMat {
 hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, int bf16, int64_t M, int64_t K,
                                int8_t* Xq_out, float* absmax_out, hipStream_t s, bool* launched,
                                const NormArgs* norm = nullptr);
+// Matrices of one int8-quantised input, 5..16 tokens on rows of at most 16 K tiles, in one
+// launch of the 5..16-token register decode: *launched tells whether it did (nothing is
+// enqueued otherwise).
+hipError_t launch_gemv_grouped_int8(const GroupMat* mats, int count, const int8_t* Xq, const float* absmax, int64_t M,
+                                    int64_t K, hipStream_t s, bool* launched);
 // Gate / up pair with the squared-ReLU gating: one launch where gated_fused_ok (M <= 4,
 // register form of the fused decode kernel, runs of at most 8 tiles); otherwise
 // hipErrorInvalidConfiguration and nothing enqueued.

@@ -762,11 +762,10 @@ __global__ __launch_bounds__(1024) void k_gemv_dpp_group(const MatGroup grp, con
 // covers RB row blocks over its run of T tiles, so one set of activation registers
 // feeds RB weight tiles.
 template <int T, int MM, int RB>
-__global__ __launch_bounds__(1024) void k_gemv_dppm(const uint8_t* __restrict__ packed,
-                                                   const float* __restrict__ gamma, const int8_t* __restrict__ Xq,
-                                                   const float* __restrict__ absmax, int M, int N, int K_pad,
-                                                   int chunks, int rblocks, float* __restrict__ Y,
-                                                   int32_t* __restrict__ acc_out) {
+__device__ __forceinline__ void gemv_dppm_body(const uint8_t* __restrict__ packed, const float* __restrict__ gamma,
+                                               const int8_t* __restrict__ Xq, const float* __restrict__ absmax, int M,
+                                               int N, int K_pad, int chunks, int rblocks, float* __restrict__ Y,
+                                               int32_t* __restrict__ acc_out, int blk) {
   static_assert(MM == 8 || MM == 16, "token group of 8 or 16");
   constexpr int RA = MM / 4;
   __shared__ v4i red[16 * 64];  // W * RB <= 16 partial tiles
@@ -774,7 +773,7 @@ __global__ __launch_bounds__(1024) void k_gemv_dppm(const uint8_t* __restrict__ 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int rb0 = blockIdx.x * RB;
+  const int rb0 = blk * RB;
   const int c0 = wave * T;
   const uint4* wsrc[RB];
 #pragma unroll
@@ -837,6 +836,56 @@ __global__ __launch_bounds__(1024) void k_gemv_dppm(const uint8_t* __restrict__ 
       }
     }
   }
+}
+
+template <int T, int MM, int RB>
+__global__ __launch_bounds__(1024) void k_gemv_dppm(const uint8_t* __restrict__ packed,
+                                                   const float* __restrict__ gamma, const int8_t* __restrict__ Xq,
+                                                   const float* __restrict__ absmax, int M, int N, int K_pad,
+                                                   int chunks, int rblocks, float* __restrict__ Y,
+                                                   int32_t* __restrict__ acc_out) {
+  gemv_dppm_body<T, MM, RB>(packed, gamma, Xq, absmax, M, N, K_pad, chunks, rblocks, Y, acc_out, (int)blockIdx.x);
+}
+
+// Matrices that share one quantised input (the 5..16-token grouped call): workgroups
+// [wg_end[j-1], wg_end[j]) take the row blocks of matrix j, RB at a time.
+struct DppmGroup {
+  int count;
+  int wg_end[kMaxGroup];
+  int N[kMaxGroup];
+  int rblocks[kMaxGroup];
+  const uint8_t* packed[kMaxGroup];
+  const float* gamma[kMaxGroup];
+  float* Y[kMaxGroup];
+  int32_t* acc[kMaxGroup];
+};
+
+template <int T, int MM, int RB>
+__global__ __launch_bounds__(1024) void k_gemv_dppm_group(const DppmGroup grp, const int8_t* __restrict__ Xq,
+                                                         const float* __restrict__ absmax, int M, int K_pad,
+                                                         int chunks) {
+  int mat = 0;  // uniform
+#pragma unroll
+  for (int k = 0; k + 1 < kMaxGroup; ++k)
+    if (k + 1 < grp.count && (int)blockIdx.x >= grp.wg_end[k]) mat = k + 1;
+  const uint8_t* packed = grp.packed[0];
+  const float* gamma = grp.gamma[0];
+  float* Y = grp.Y[0];
+  int32_t* acc_out = grp.acc[0];
+  int N = grp.N[0], rblocks = grp.rblocks[0], wg_base = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxGroup; ++k)
+    if (mat == k) {
+      packed = grp.packed[k];
+      gamma = grp.gamma[k];
+      Y = grp.Y[k];
+      acc_out = grp.acc[k];
+      N = grp.N[k];
+      rblocks = grp.rblocks[k];
+      wg_base = grp.wg_end[k - 1];
+    }
+  gemv_dppm_body<T, MM, RB>(packed, gamma, Xq, absmax, M, N, K_pad, chunks, rblocks, Y, acc_out,
+                            (int)blockIdx.x - wg_base);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1062,6 +1111,15 @@ hipError_t launch_dppm(int W, const Args& a, hipStream_t s) {
   const unsigned groups = (unsigned)((a.rblocks + RB - 1) / RB);
   hipLaunchKernelGGL((k_gemv_dppm<T, MM, RB>), dim3(groups), dim3(W * 64), 0, s, a.packed, a.gamma,
                      static_cast<const int8_t*>(a.X), a.absmax, a.M, a.N, a.K_pad, a.chunks, a.rblocks, a.Y, a.acc);
+  return hipGetLastError();
+}
+
+template <int T, int MM, int RB>
+hipError_t launch_dppm_group(int W, const DppmGroup& g, const int8_t* Xq, const float* absmax, int M, int K_pad,
+                             int chunks, hipStream_t s) {
+  if (W * RB > 16 || (int64_t)W * T < chunks) return hipErrorInvalidConfiguration;  // LDS partials, coverage
+  hipLaunchKernelGGL((k_gemv_dppm_group<T, MM, RB>), dim3(g.wg_end[g.count - 1]), dim3(W * 64), 0, s, g, Xq, absmax, M,
+                     K_pad, chunks);
   return hipGetLastError();
 }
 
@@ -1294,6 +1352,39 @@ hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, i
     case 3: return launch_dpp_run<3>(p.run, (int)M, p.waves, a, s, &g);
     default: return launch_dpp_run<4>(p.run, (int)M, p.waves, a, s, &g);
   }
+}
+
+hipError_t launch_gemv_grouped_int8(const GroupMat* mats, int count, const int8_t* Xq, const float* absmax, int64_t M,
+                                    int64_t K, hipStream_t s, bool* launched) {
+  *launched = false;
+  const int64_t K_pad = k_pad(K), chunks = K_pad / kTileCols;
+  // 5..16 tokens on rows of at most 16 tiles: the register form of k_gemv_dppm for every
+  // matrix of the group, in one launch (the single-matrix planner takes the same form)
+  if (count < 2 || count > kMaxGroup || M < 5 || M > 16 || chunks > 16) return hipSuccess;
+  int64_t rb_total = 0;
+  for (int j = 0; j < count; ++j) rb_total += n_pad(mats[j].N) / kTileRows;
+  // two row blocks per workgroup once the group fills the chip (the single-matrix rule)
+  const int RB = rb_total >= 384 ? 2 : 1;
+  DppmGroup g{};
+  g.count = count;
+  int end = 0;
+  for (int j = 0; j < count; ++j) {
+    const int rb = (int)(n_pad(mats[j].N) / kTileRows);
+    end += (rb + RB - 1) / RB;
+    g.wg_end[j] = end;
+    g.N[j] = (int)mats[j].N;
+    g.rblocks[j] = rb;
+    g.packed[j] = mats[j].packed;
+    g.gamma[j] = mats[j].gamma;
+    g.Y[j] = mats[j].Y;
+    g.acc[j] = mats[j].acc;
+  }
+  const int W = (int)((chunks + 1) / 2);
+  *launched = true;
+  if (M > 8) return RB == 2 ? launch_dppm_group<2, 16, 2>(W, g, Xq, absmax, (int)M, (int)K_pad, (int)chunks, s)
+                            : launch_dppm_group<2, 16, 1>(W, g, Xq, absmax, (int)M, (int)K_pad, (int)chunks, s);
+  return RB == 2 ? launch_dppm_group<2, 8, 2>(W, g, Xq, absmax, (int)M, (int)K_pad, (int)chunks, s)
+                 : launch_dppm_group<2, 8, 1>(W, g, Xq, absmax, (int)M, (int)K_pad, (int)chunks, s);
 }
 
 bool gated_fused_ok(int64_t M, int64_t N, int64_t K, int src) {

@@ -576,11 +576,18 @@ def _grouped_check(m, ns, k, dtype, seed):
     (3, [16, 33, 48, 64, 80, 96, 112, 130], 512, torch.bfloat16),  # eight matrices
     (4, [700, 900], 4096, torch.float32),
     (1, [512], 256, torch.float32),                    # a group of one
-    (8, [300, 100], 2560, torch.bfloat16),             # more tokens: quantiser once, then forwards
+    (8, [300, 100], 2560, torch.bfloat16),             # more tokens: quantiser once, then one grouped forward
     (40, [130, 64], 1000, torch.float32),              # 17..64 tokens: token groups
     (100, [130, 64], 1000, torch.bfloat16),            # prefill sizes
     (1, [100, 200], 300, torch.bfloat16),              # K not a multiple of 8: quantiser path
     (2, [2560, 2560], 2560, torch.bfloat16),           # 320 row blocks: weights issued as activations land
+    # 5..16 tokens: the quantiser, then one launch of the 5..16-token decode for the group
+    (16, [2560, 640, 640], 2560, torch.bfloat16),      # Q, K, V of the 2B-class layer
+    (16, [6912, 6912], 2560, torch.bfloat16),          # gate + up (864 row blocks: two per workgroup)
+    (5, [17, 300, 1000, 33], 1000, torch.float32),     # ragged rows and columns, token group of 8
+    (12, [130, 2100], 3000, torch.bfloat16),           # token group of 16, ragged K
+    (9, [16, 32, 48, 64, 80, 96, 112, 6150], 4096, torch.float32),  # eight matrices, 16 K tiles
+    (16, [300, 500], 4097, torch.bfloat16),            # 17 K tiles: one forward per matrix
     (1, [4096, 2048], 4096, torch.float32),            # 384 row blocks
 ])
 def test_forward_grouped(m, ns, k, dtype):
