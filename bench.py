@@ -79,8 +79,14 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph instead of pre-marshalled eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-clock budget of the all-cores oracle run (the single-thread run takes 2 layers)")
+    ap.add_argument("--path", default="fused", choices=["fused", "int8"],
+                    help="headline path: the fused quantise + decode kernel where the library fuses the shape "
+                         "(default), or the activation quantiser then the int8 forward")
+    ap.add_argument("--skip-ceilings", action="store_true",
+                    help="profiling runs only: no probe ceilings and no quantiser timings (shorter traces); "
+                         "frac_of_measured_ceiling is then omitted")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device three times (the reference kernel of "
                          "known size for scaling FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -305,13 +311,15 @@ KERNEL_SOURCES = {
     "prefill": ("bitlinear_fwd_amd/csrc/gemm.hip", "bitlinear_fwd_amd/csrc/bl_internal.h"),
 }
 TRAFFIC = {
-    # (workload, M): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
-    # Copy calibration (256 MiB device copy): FETCH_SIZE read 131085.3 KiB (x1.99980),
-    # WRITE_SIZE 262144.0 KiB (x1.0).
-    (1, 1): {"bytes_per_launch": 4591108, "fetch_kib": 2229.34, "write_kib": 25.28, "sha": "61f7a96371860d6d"},
-    (2, 16): {"bytes_per_launch": 3160075, "fetch_kib": 1441.44, "write_kib": 203.43, "sha": "61f7a96371860d6d"},
-    (3, 2048): {"bytes_per_launch": 94794700, "fetch_kib": 27345.22, "write_kib": 37888.06, "sha": "85d7b679bf307030"},
-    (4, 1): {"bytes_per_launch": 59258200, "fetch_kib": 28892.26, "write_kib": 90.03, "sha": "61f7a96371860d6d"},
+    # (workload, M, path): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
+    # path: "fused" (quantise + decode in one kernel), "int8" (decode of quantised
+    # activations), "prefill".  Copy calibration (256 MiB device copy): FETCH_SIZE read
+    # 131083.83 KiB (x1.99982), WRITE_SIZE 262144.0 KiB (x1.0).
+    (4, 1, "fused"): {"bytes_per_launch": 59265254, "fetch_kib": 28895.71, "write_kib": 90.03, "sha": "8bbc7600b51c6e36"},
+    (4, 1, "int8"): {"bytes_per_launch": 59033040, "fetch_kib": 28791.33, "write_kib": 72.00, "sha": "8bbc7600b51c6e36"},
+    (1, 1, "fused"): {"bytes_per_launch": 4586719, "fetch_kib": 2227.17, "write_kib": 25.28, "sha": "8bbc7600b51c6e36"},
+    (2, 16, "int8"): {"bytes_per_launch": 3152349, "fetch_kib": 1437.65, "write_kib": 203.43, "sha": "8bbc7600b51c6e36"},
+    (3, 2048, "prefill"): {"bytes_per_launch": 94894111, "fetch_kib": 27393.45, "write_kib": 37888.09, "sha": "b5bffc76041e7afe"},
 }
 
 
@@ -331,11 +339,11 @@ def source_sha(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: int, m: int):
-    rec = TRAFFIC.get((workload, m))
+def measured_traffic(kernel: str, workload: int, m: int, path: str):
+    kind = "prefill" if kernel.startswith("k_gemm") else "decode"
+    rec = TRAFFIC.get((workload, m, "prefill" if kind == "prefill" else path))
     if rec is None:
         return None
-    kind = "prefill" if kernel.startswith("k_gemm") else "decode"
     return rec["bytes_per_launch"] if rec["sha"] == source_sha(kind) else None
 
 
@@ -725,7 +733,8 @@ def roofline_block(w: Workload, launch_ms, launch_bytes, launch_ops, launch_timi
     """The roofline of the step's dominant kernel: algorithmic bytes (decode, HBM-bound) or
     int8 ops (prefill, MFMA-bound) per launch over the mean launch duration."""
     kernel = dominant_kernel(w)
-    traffic = measured_traffic(kernel, workload_idx, w.m)
+    fused = w.path == "fused" and all(w.fused.values())
+    traffic = measured_traffic(kernel, workload_idx, w.m, "fused" if fused else "int8")
     if w.m <= 16:
         achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -810,7 +819,7 @@ def main():
     torch.cuda.set_device(dev)
     bl.lib()
     m_head = synth.WORKLOADS[args.workload].m_list[0]
-    head = Workload(bl, synth, args.workload, m_head, dev)
+    head = Workload(bl, synth, args.workload, m_head, dev, path=args.path)
     if args.graph:
         head.capture()
     if args.copy_calibration:
@@ -823,10 +832,10 @@ def main():
     decode = m_head <= 16
     launch_ms, launch_bytes, launch_ops, launch_timing = launch_timing_of(head, ms)
     value = head.bytes_per_step() / (ms * 1e-3) / 1e9 if decode else head.ops_per_step() / (ms * 1e-3) / 1e12
-    ceilings = measure_ceilings(bl, dev)
+    ceilings = None if args.skip_ceilings else measure_ceilings(bl, dev)
     progress("ceilings measured")
     roof = roofline_block(head, launch_ms, launch_bytes, launch_ops, launch_timing, args.workload, ceilings)
-    quantisers = measure_quantisers(bl, synth, dev)
+    quantisers = None if args.skip_ceilings else measure_quantisers(bl, synth, dev)
     legs = {}
     for tok in [t.strip() for t in args.legs.split(",") if t.strip()]:
         flags = tok.lstrip("0123456789")
@@ -873,7 +882,8 @@ def main():
                                        "binary": "k_gemv_bin (1-bit sign-binary decode)"}.get(path) or dominant_kernel(w)
                 legs[key]["forward_launch_timing"] = l_how
                 if path == "fused":
-                    legs[key]["traffic_bytes_per_launch"] = measured_traffic(dominant_kernel(w), idx, m)
+                    legs[key]["traffic_bytes_per_launch"] = measured_traffic(
+                        dominant_kernel(w), idx, m, "fused" if all(w.fused.values()) else "int8")
                 else:
                     legs[key]["note"] = ("activation quantiser, then the " +
                                          {"lut": "table-lookup forward (bitlinear_forward_lut)",
@@ -930,6 +940,7 @@ def main():
                    "seeds": "torch.Generator per tensor: 1000*workload + 10*layer + matrix for weights, "
                             "+500 for activations, +700 for sub-layer gains",
                    "launch": "hip graph replay" if args.graph else "pre-marshalled eager C-ABI calls",
+                   "path": args.path,
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None},
         "trials": trial_stats(trials, head.bytes_per_step(), None if decode else head.ops_per_step()),
         "roofline": roof,

@@ -23,7 +23,8 @@
 //     of four waves per tile where there are few tiles (plan_gemm);
 //   * the loop body is unrolled over lcm(D, 2 CB) half-stages so that every ring index is
 //     static; half-stages past the end of K are skipped whole (measured: 2048 x 6912 x 2560
-//     48.9 -> 46.9 us, 4096 x 6912 x 2560 87.6 -> 82.3 us, 48 x 30000 x 512 9.4 -> 7.6 us);
+//     48.9 -> 46.9 us, 4096 x 6912 x 2560 87.6 -> 82.3 us, 48 x 30000 x 512 9.4 -> 7.6 us),
+//     and the loop ends by waiting for every load still in flight;
 //   * tile order is XCD-aware: consecutive workgroup ids go to different XCDs, so each
 //     XCD gets a contiguous run of output tiles (sharing activation rows in its L2).
 #include "bl_internal.h"
@@ -237,6 +238,9 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_mfma(const uint8_t* __restric
     });
     base += kBody;
   } while (base < hstages);
+  // the refills of the last P half-stages (clamped re-reads of the last chunk, never
+  // computed) land before the epilogue reuses registers and the workgroup ends
+  wait_vmcnt<0>();
 
   const float gm = gamma[0];
   // store row block mi of the wave's tile, adding `other` (the other K group's partial of
@@ -286,8 +290,7 @@ __global__ __launch_bounds__(256 * KS) void k_gemm_mfma(const uint8_t* __restric
     // group's partial (int32, exact), which comes through LDS one row block per pass.
     // The accumulators are only read (no VALU writes to them), which keeps the register
     // count at the one-group kernel's.
-    wait_vmcnt<0>();  // ring refills past the last chunk have landed before the slots are reused
-    ring_barrier();
+    ring_barrier();  // every load has landed (the wait after the loop)
     v4i* out = reinterpret_cast<v4i*>(kg == 0 ? As0 : As1) + wave * NB * 64 + lane;
     const v4i* in = reinterpret_cast<const v4i*>(kg == 0 ? As1 : As0) + wave * NB * 64 + lane;
     static_for<MB / 2>([&](auto pc) {
