@@ -100,6 +100,8 @@ struct GemvPlan {
                         // loads issued before the activation barrier
   bool mid = false;     // fused dpp, up to two workgroups per unit and short runs: weight
                         // loads issued once the activation pieces have landed
+  bool prio = false;    // fused dpp, one token, more than two workgroups per unit: raised
+                        // wave priority while the activation loads are issued
   int stage = 0;        // LDS staging: 16-byte activation pieces per thread
   int tg = 1;           // token groups of 16 (17..64 tokens: 2..4)
   bool ok = true;       // the requested activation source is supported by this plan

@@ -409,12 +409,16 @@ __device__ __forceinline__ void lds_barrier() {
 // bf16 / fp32 x through the sub-layer normalisation.  kSrcEarly added to 1 / 2 selects the
 // fused form that issues its weight loads before the activation barrier; kSrcMid added to
 // 1..4 the form that issues them as soon as its own activation pieces have landed.
+// kSrcPrio added to 1 / 2 raises the waves' issue priority while they issue their
+// activation loads (weights after the barrier, as in the plain fused form).
 constexpr int kSrcEarly = 8;
 constexpr int kSrcMid = 32;
+constexpr int kSrcPrio = 64;
 constexpr bool src_bf16(int src) { return (src & 7) == 1 || (src & 7) == 3; }
 constexpr bool src_norm(int src) { return (src & 7) >= 3; }
 constexpr bool src_early(int src) { return (src & kSrcEarly) != 0; }
 constexpr bool src_mid(int src) { return (src & kSrcMid) != 0; }
+constexpr bool src_prio(int src) { return (src & kSrcPrio) != 0; }
 
 template <int MM, int kSrc>
 struct DppShape {
@@ -460,7 +464,16 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   auto own = [&](int j) { return pq < 4 * UA && j * UA + pu < T && c0 + j * UA + pu < chunks; };
 
   // every activation load first (their wait then does not wait for the weights), then
-  // every weight load of the run
+  // every weight load of the run.  A compute unit issues the memory instructions of its
+  // waves oldest first, so with several workgroups per unit the activation loads of the
+  // younger ones wait behind the weight loads of the older ones, and their barrier with
+  // them.  kSrcPrio lifts the wave's priority over the activation loads alone, so they
+  // go out ahead of weight loads that older waves have not yet issued.
+  if constexpr (src_prio(kSrc)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   uint4 raw[NA][kParts];
   static_for<NA>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
@@ -507,6 +520,11 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   // With up to two workgroups per unit and short runs (kSrcMid) each wave waits for its
   // own activation pieces and then issues its weights, which stream during the
   // conversion, the absmax barrier and the quantisation.
+  if constexpr (src_prio(kSrc)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   constexpr int kEarly = (kSrc == 0 || src_early(kSrc) || src_mid(kSrc)) ? T : 0;
   if constexpr (src_early(kSrc)) asm volatile("s_barrier" ::: "memory");
   if constexpr (src_mid(kSrc)) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters at their maxima
@@ -1043,6 +1061,25 @@ hipError_t launch_dpp_run(int T, int M, int W, const Args& a, hipStream_t s, con
   }
 }
 
+// One token only (the priority form is planned for M = 1).
+template <int kSrc>
+hipError_t launch_dpp_prio(int T, int W, const Args& a, hipStream_t s) {
+  switch (T) {
+    case 1: return launch_dpp<1, 1, kSrc>(W, a, s);
+    case 2: return launch_dpp<2, 1, kSrc>(W, a, s);
+    case 3: return launch_dpp<3, 1, kSrc>(W, a, s);
+    case 4: return launch_dpp<4, 1, kSrc>(W, a, s);
+    case 5: return launch_dpp<5, 1, kSrc>(W, a, s);
+    case 6: return launch_dpp<6, 1, kSrc>(W, a, s);
+    case 7: return launch_dpp<7, 1, kSrc>(W, a, s);
+    case 8: return launch_dpp<8, 1, kSrc>(W, a, s);
+    case 10: return launch_dpp<10, 1, kSrc>(W, a, s);
+    case 12: return launch_dpp<12, 1, kSrc>(W, a, s);
+    case 14: return launch_dpp<14, 1, kSrc>(W, a, s);
+    default: return launch_dpp<16, 1, kSrc>(W, a, s);
+  }
+}
+
 // Runs of at most four tiles (the forms the planner only picks for short runs).
 template <int kSrc>
 hipError_t launch_dpp_run4(int T, int M, int W, const Args& a, hipStream_t s, const MatGroup* grp = nullptr) {
@@ -1194,6 +1231,11 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
         // workgroups queue behind the weights (8192 x 16384 9.25 -> 9.38 us, 16384 x 8192
         // 9.16 -> 9.92 us, 28672 x 8192 14.1 -> 22.3 us)
         p.mid = src != 0 && !p.early && rblocks <= 512 && t <= 4;
+        // one token, more than two workgroups per unit (weights after the barrier):
+        // measured (bf16 x) 8192 x 28672 12.95 -> 12.19 us and 13.00 -> 12.35 us in two
+        // interleaved runs; no gain at two tokens (16.07 -> 16.12 us), and on 28672 x 8192
+        // (512 workgroups) 13.62 -> 14.10 and 13.71 -> 13.69 us, so not taken there
+        p.prio = (src == 1 || src == 2) && M == 1 && !p.early && !p.mid && rblocks > 512;
         return p;
       }
     }
@@ -1299,6 +1341,8 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const vo
   if (p.dpp && p.early)
     return bf16 ? launch_dpp_run<1 + kSrcEarly>(p.run, (int)M, p.waves, a, s)
                 : launch_dpp_run<2 + kSrcEarly>(p.run, (int)M, p.waves, a, s);
+  if (p.dpp && p.prio)
+    return bf16 ? launch_dpp_prio<1 + kSrcPrio>(p.run, p.waves, a, s) : launch_dpp_prio<2 + kSrcPrio>(p.run, p.waves, a, s);
   if (p.dpp) return bf16 ? launch_dpp_run<1>(p.run, (int)M, p.waves, a, s) : launch_dpp_run<2>(p.run, (int)M, p.waves, a, s);
   if (bf16) return launch_lds_w<1>(p.waves, p.stage, a, s);
   return launch_lds_w<2>(p.waves, p.stage, a, s);
