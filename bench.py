@@ -314,12 +314,12 @@ TRAFFIC = {
     # (workload, M, path): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
     # path: "fused" (quantise + decode in one kernel), "int8" (decode of quantised
     # activations), "prefill".  Copy calibration (256 MiB device copy): FETCH_SIZE read
-    # 131083.83 KiB (x1.99982), WRITE_SIZE 262144.0 KiB (x1.0).
-    (4, 1, "fused"): {"bytes_per_launch": 59265254, "fetch_kib": 28895.71, "write_kib": 90.03, "sha": "8bbc7600b51c6e36"},
-    (4, 1, "int8"): {"bytes_per_launch": 59033040, "fetch_kib": 28791.33, "write_kib": 72.00, "sha": "8bbc7600b51c6e36"},
-    (1, 1, "fused"): {"bytes_per_launch": 4586719, "fetch_kib": 2227.17, "write_kib": 25.28, "sha": "8bbc7600b51c6e36"},
-    (2, 16, "int8"): {"bytes_per_launch": 3152349, "fetch_kib": 1437.65, "write_kib": 203.43, "sha": "8bbc7600b51c6e36"},
-    (3, 2048, "prefill"): {"bytes_per_launch": 94894111, "fetch_kib": 27393.45, "write_kib": 37888.09, "sha": "b5bffc76041e7afe"},
+    # 131083.83-131086.77 KiB (x1.99977-1.99982, taken per run), WRITE_SIZE 262144.0 KiB (x1.0).
+    (4, 1, "fused"): {"bytes_per_launch": 59264128, "fetch_kib": 28895.15, "write_kib": 90.03, "sha": "c78c3601852b719e"},
+    (4, 1, "int8"): {"bytes_per_launch": 59027931, "fetch_kib": 28788.83, "write_kib": 72.00, "sha": "c78c3601852b719e"},
+    (1, 1, "fused"): {"bytes_per_launch": 4587635, "fetch_kib": 2227.67, "write_kib": 25.28, "sha": "c78c3601852b719e"},
+    (2, 16, "int8"): {"bytes_per_launch": 3161349, "fetch_kib": 1442.08, "write_kib": 203.43, "sha": "c78c3601852b719e"},
+    (3, 2048, "prefill"): {"bytes_per_launch": 94828227, "fetch_kib": 27361.58, "write_kib": 37888.08, "sha": "3f0e3b710aeabab9"},
 }
 
 
