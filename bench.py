@@ -37,6 +37,8 @@ the median, min and max of the K per-step times.  The JSON line also carries:
                path ("1i"), the table-lookup decode ("1l"), the 1-bit sign-binary variant
                ("1b", "4b"), and one GPU's share of the 100B-class matrices split over 8
                GPUs ("5");
+  host_us_per_launch (config and each leg) the host's time to issue one launch inside the
+               timed region: near the GPU's time per launch, the host sets the pace;
   gpu_state    rocm-smi clock and power readings before and after the timed region;
   quantisers   the weight quantiser (2560 -> 6912 fp32 latents) and the activation quantiser
                (bf16, decode and prefill sizes) timed alone, in bytes moved per second;
@@ -537,7 +539,8 @@ def gpu_state():
 def time_steps(w: Workload, steps: int, warmup: int):
     """W untimed warm-up steps, then exactly `steps` timed steps with a HIP event recorded
     after each on the stream the kernels run on.  Returns (mean ms per step over the whole
-    timed region, the per-step times in ms)."""
+    timed region, the per-step times in ms, the host's ms per step spent issuing them: where
+    that reaches the GPU's time the launches, not the kernels, set the pace)."""
     import torch
 
     for _ in range(warmup):
@@ -546,12 +549,14 @@ def time_steps(w: Workload, steps: int, warmup: int):
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
+    t0 = time.perf_counter()
     for i in range(steps):
         w.run_step()
         ev[i + 1].record(stream)
+    host_ms = (time.perf_counter() - t0) * 1e3 / steps
     torch.cuda.synchronize()
     trials = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    return ev[0].elapsed_time(ev[steps]) / steps, trials
+    return ev[0].elapsed_time(ev[steps]) / steps, trials, host_ms
 
 
 def trial_stats(trials, bytes_per_step=None, ops_per_step=None):
@@ -826,7 +831,7 @@ def main():
         copy_calibration(args.copy_calibration)
     state_before = gpu_state()
     progress(f"headline workload {args.workload} M={m_head} ready: {len(head.calls[0])} launches per step")
-    ms, trials = time_steps(head, args.steps, args.warmup)
+    ms, trials, host_ms = time_steps(head, args.steps, args.warmup)
     state_after = gpu_state()
     progress(f"headline timed: {ms:.4f} ms per step")
     decode = m_head <= 16
@@ -857,7 +862,7 @@ def main():
                 w.set_gated_pair()
             if args.graph:
                 w.capture()
-            lms, ltrials = time_steps(w, leg_steps(w), max(2, -(-100 // len(w.calls[0]))))
+            lms, ltrials, lhost = time_steps(w, leg_steps(w), max(2, -(-100 // len(w.calls[0]))))
             key = f"w{idx}{flags}_m{m}"
             progress(f"leg {key}: {lms:.4f} ms per step")
             if gated or grouped or subln:
@@ -893,6 +898,7 @@ def main():
                                          "; forward_launch_* time the forward launches alone")
                 if tok in ROOFLINE_LEGS and (m == synth.WORKLOADS[idx].m_list[0]):
                     legs[key]["roofline"] = roofline_block(w, l_ms, l_b, l_o, l_how, idx, ceilings)
+            legs[key]["host_us_per_launch"] = round(lhost * 1e3 / max(1, len(w.calls[0])), 3)
             del w
             torch.cuda.empty_cache()
     cpu = cpu_single = None
@@ -940,6 +946,7 @@ def main():
                    "seeds": "torch.Generator per tensor: 1000*workload + 10*layer + matrix for weights, "
                             "+500 for activations, +700 for sub-layer gains",
                    "launch": "hip graph replay" if args.graph else "pre-marshalled eager C-ABI calls",
+                   "host_us_per_launch": round(host_ms * 1e3 / max(1, len(head.calls[0])), 3),
                    "path": args.path,
                    "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None},
         "trials": trial_stats(trials, head.bytes_per_step(), None if decode else head.ops_per_step()),
