@@ -102,6 +102,8 @@ struct GemvPlan {
                         // loads issued once the activation pieces have landed
   bool prio = false;    // fused dpp, one token, more than two workgroups per unit: raised
                         // wave priority while the activation loads are issued
+  bool lead = false;    // fused dpp, one token, at most two workgroups per unit, runs of 14
+                        // or 16 tiles: raised priority and two weight tiles before the barrier
   int stage = 0;        // LDS staging: 16-byte activation pieces per thread
   int tg = 1;           // token groups of 16 (17..64 tokens: 2..4)
   bool ok = true;       // the requested activation source is supported by this plan

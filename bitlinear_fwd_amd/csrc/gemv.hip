@@ -410,15 +410,19 @@ __device__ __forceinline__ void lds_barrier() {
 // fused form that issues its weight loads before the activation barrier; kSrcMid added to
 // 1..4 the form that issues them as soon as its own activation pieces have landed.
 // kSrcPrio added to 1 / 2 raises the waves' issue priority while they issue their
-// activation loads (weights after the barrier, as in the plain fused form).
+// activation loads (weights after the barrier, as in the plain fused form); kSrcLead does
+// the same and also issues the first two weight tiles of each run ahead of the barrier.
 constexpr int kSrcEarly = 8;
 constexpr int kSrcMid = 32;
 constexpr int kSrcPrio = 64;
+constexpr int kSrcLead = 128;
+constexpr int kLeadTiles = 2;
 constexpr bool src_bf16(int src) { return (src & 7) == 1 || (src & 7) == 3; }
 constexpr bool src_norm(int src) { return (src & 7) >= 3; }
 constexpr bool src_early(int src) { return (src & kSrcEarly) != 0; }
 constexpr bool src_mid(int src) { return (src & kSrcMid) != 0; }
-constexpr bool src_prio(int src) { return (src & kSrcPrio) != 0; }
+constexpr bool src_prio(int src) { return (src & (kSrcPrio | kSrcLead)) != 0; }
+constexpr bool src_lead(int src) { return (src & kSrcLead) != 0; }
 
 template <int MM, int kSrc>
 struct DppShape {
@@ -468,7 +472,10 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
   // waves oldest first, so with several workgroups per unit the activation loads of the
   // younger ones wait behind the weight loads of the older ones, and their barrier with
   // them.  kSrcPrio lifts the wave's priority over the activation loads alone, so they
-  // go out ahead of weight loads that older waves have not yet issued.
+  // go out ahead of weight loads that older waves have not yet issued.  kSrcLead (long
+  // runs, at most two workgroups per unit) also issues the first weight tiles of the run
+  // right behind the activation loads, so the unit's weight stream starts before the
+  // barrier.
   if constexpr (src_prio(kSrc)) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(3);
@@ -525,7 +532,7 @@ __device__ __forceinline__ void gemv_dpp_body(const uint8_t* __restrict__ packed
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
   }
-  constexpr int kEarly = (kSrc == 0 || src_early(kSrc) || src_mid(kSrc)) ? T : 0;
+  constexpr int kEarly = (kSrc == 0 || src_early(kSrc) || src_mid(kSrc)) ? T : (src_lead(kSrc) ? (T < kLeadTiles ? T : kLeadTiles) : 0);
   if constexpr (src_early(kSrc)) asm volatile("s_barrier" ::: "memory");
   if constexpr (src_mid(kSrc)) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters at their maxima
   uint4 w[T];
@@ -1080,6 +1087,16 @@ hipError_t launch_dpp_prio(int T, int W, const Args& a, hipStream_t s) {
   }
 }
 
+// One token, runs of 14 or 16 tiles (the lead form's plan).
+template <int kSrc>
+hipError_t launch_dpp_lead(int T, int W, const Args& a, hipStream_t s) {
+  switch (T) {
+    case 14: return launch_dpp<14, 1, kSrc>(W, a, s);
+    case 16: return launch_dpp<16, 1, kSrc>(W, a, s);
+    default: return hipErrorInvalidConfiguration;
+  }
+}
+
 // Runs of at most four tiles (the forms the planner only picks for short runs).
 template <int kSrc>
 hipError_t launch_dpp_run4(int T, int M, int W, const Args& a, hipStream_t s, const MatGroup* grp = nullptr) {
@@ -1236,6 +1253,12 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int src) {
         // interleaved runs; no gain at two tokens (16.07 -> 16.12 us), and on 28672 x 8192
         // (512 workgroups) 13.62 -> 14.10 and 13.71 -> 13.69 us, so not taken there
         p.prio = (src == 1 || src == 2) && M == 1 && !p.early && !p.mid && rblocks > 512;
+        // one token, at most two workgroups per unit and runs of 14 or 16 tiles: the raised
+        // priority plus two weight tiles issued before the barrier (measured, bf16 x,
+        // interleaved: 8192 x 28672 13.80 -> 13.25 and 13.60 -> 13.22 us, 6144 x 28672
+        // 12.46 -> 12.23 us, 8192 x 32000 19.38 -> 18.95 us; with 8- and 12-tile runs it
+        // lost: 8192 x 16384 9.15 -> 9.53 us, 8192 x 24576 11.61 -> 11.83 us)
+        p.lead = (src == 1 || src == 2) && M == 1 && !p.early && !p.mid && !p.prio && t >= 14;
         return p;
       }
     }
@@ -1343,6 +1366,8 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const vo
                 : launch_dpp_run<2 + kSrcEarly>(p.run, (int)M, p.waves, a, s);
   if (p.dpp && p.prio)
     return bf16 ? launch_dpp_prio<1 + kSrcPrio>(p.run, p.waves, a, s) : launch_dpp_prio<2 + kSrcPrio>(p.run, p.waves, a, s);
+  if (p.dpp && p.lead)
+    return bf16 ? launch_dpp_lead<1 + kSrcLead>(p.run, p.waves, a, s) : launch_dpp_lead<2 + kSrcLead>(p.run, p.waves, a, s);
   if (p.dpp) return bf16 ? launch_dpp_run<1>(p.run, (int)M, p.waves, a, s) : launch_dpp_run<2>(p.run, (int)M, p.waves, a, s);
   if (bf16) return launch_lds_w<1>(p.waves, p.stage, a, s);
   return launch_lds_w<2>(p.waves, p.stage, a, s);
