@@ -63,6 +63,14 @@ def lib() -> ctypes.CDLL:
         L.bitlinear_forward_fused_plan.argtypes = [i64, i64, i64, c_int, p]
         L.bitlinear_forward.restype = c_int
         L.bitlinear_forward.argtypes = [p, p, p, p, i64, i64, i64, p, p, p]
+        L.bitlinear_forward_ws_bytes.restype = i64
+        L.bitlinear_forward_ws_bytes.argtypes = [i64, i64, i64]
+        L.bitlinear_forward_ws.restype = c_int
+        L.bitlinear_forward_ws.argtypes = [p, p, p, p, i64, i64, i64, p, p, p, i64, p]
+        L.bitlinear_probe_prefill_occupancy.restype = c_int
+        L.bitlinear_probe_prefill_occupancy.argtypes = [p]
+        L.bitlinear_forward_ws_plan.restype = c_int
+        L.bitlinear_forward_ws_plan.argtypes = [i64, i64, i64, p]
         L.bitlinear_probe_stream_words.restype = i64
         L.bitlinear_probe_stream_words.argtypes = [i64]
         L.bitlinear_probe_stream.restype = c_int
@@ -119,7 +127,8 @@ EXPORTED_SYMBOLS = (
     "bitlinear_forward_gated_relu2", "bitlinear_forward_gated_relu2_plan", "bitlinear_forward_lut",
     "bitlinear_forward_lut_plan", "bitlinear_kb_pad", "bitlinear_packed_bytes_binary",
     "bitlinear_quantize_weights_binary", "bitlinear_forward_binary", "bitlinear_forward_binary_plan",
-    "bitlinear_quantize_weights_noalloc",
+    "bitlinear_quantize_weights_noalloc", "bitlinear_forward_ws_bytes", "bitlinear_forward_ws",
+    "bitlinear_forward_ws_plan", "bitlinear_probe_prefill_occupancy",
 )
 
 MAX_GROUP = 8
@@ -176,8 +185,11 @@ def _plan_dict(out) -> dict:
         return {"kernel": "decode", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
                 "acts": acts, "lds_acts": out[4] == 1, "lds_bytes": out[5] if out[4] == 1 else 0,
                 "tiles_per_wave": out[5] if out[4] == 2 else 0}
-    return {"kernel": "prefill", "workgroups": out[1], "threads": out[2], "tile_m": out[3], "tile_n": out[4],
-            "k_groups": out[5]}
+    d = {"kernel": "prefill", "workgroups": out[1], "threads": out[2], "tile_m": out[3], "tile_n": out[4],
+         "k_groups": out[5]}
+    if out[0] == 6:
+        d.update(split_tail=True, rounds=out[6], split_tiles=out[7], k_ranges=out[8], chunks_per_range=out[9])
+    return d
 
 
 def forward_plan(m: int, n: int, k: int) -> dict:
@@ -185,6 +197,31 @@ def forward_plan(m: int, n: int, k: int) -> dict:
     out = (ctypes.c_int32 * 6)()
     _check("bitlinear_forward_plan", lib().bitlinear_forward_plan(m, n, k, out))
     return _plan_dict(out)
+
+
+def forward_ws_plan(m: int, n: int, k: int) -> dict:
+    """The launch bitlinear_forward_ws makes for (M, N, K), computed on the host."""
+    out = (ctypes.c_int32 * 10)()
+    _check("bitlinear_forward_ws_plan", lib().bitlinear_forward_ws_plan(m, n, k, out))
+    return _plan_dict(out)
+
+
+def forward_ws_bytes(m: int, n: int, k: int) -> int:
+    """Workspace bytes bitlinear_forward_ws needs for (M, N, K) (0: none)."""
+    v = int(lib().bitlinear_forward_ws_bytes(m, n, k))
+    if v < 0:
+        raise ValueError(f"invalid shape {(m, n, k)}")
+    return v
+
+
+def forward_workspace(m: int, n: int, k: int, device):
+    """A zero-filled workspace for bitlinear_forward_ws on (M, N, K) (None when it needs
+    none).  Every call returns its counters to zero, so one workspace serves later calls
+    of any shape it is large enough for."""
+    import torch
+
+    nb = forward_ws_bytes(m, n, k)
+    return torch.zeros(nb, dtype=torch.uint8, device=device) if nb > 0 else None
 
 
 def forward_fused_plan(m: int, n: int, k: int, dtype: str = "bf16") -> dict:
@@ -320,6 +357,32 @@ def forward(packed, gamma, xq, absmax, n: int, k: int, y=None, acc=None, want_y:
         packed.data_ptr(), gamma.data_ptr(), xq.data_ptr(), absmax.data_ptr(), m, n, k,
         y.data_ptr() if y is not None else None, acc.data_ptr() if acc is not None else None,
         _stream(dev)))
+    if want_y and want_acc:
+        return y, acc
+    return y if want_y else acc
+
+
+def forward_ws(packed, gamma, xq, absmax, n: int, k: int, workspace=None, y=None, acc=None, want_y: bool = True,
+               want_acc: bool = False):
+    """forward() through bitlinear_forward_ws: the same results, with the caller's
+    zero-filled workspace (forward_workspace) for the prefill GEMM's split tail tiles."""
+    import torch
+
+    for t, name in ((packed, "packed"), (gamma, "gamma"), (xq, "xq"), (absmax, "absmax")):
+        _require_cuda(t, name)
+    m = xq.shape[0]
+    dev = xq.device
+    if workspace is not None:
+        _require_cuda(workspace, "workspace")
+    if want_y and y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    if want_acc and acc is None:
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    _check("bitlinear_forward_ws", lib().bitlinear_forward_ws(
+        packed.data_ptr(), gamma.data_ptr(), xq.data_ptr(), absmax.data_ptr(), m, n, k,
+        y.data_ptr() if y is not None else None, acc.data_ptr() if acc is not None else None,
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev)))
     if want_y and want_acc:
         return y, acc
     return y if want_y else acc
@@ -662,6 +725,14 @@ def probe_mfma(iters: int, workgroups: int, out):
     return out
 
 
+def prefill_occupancy() -> dict:
+    """Resident workgroups per compute unit of the one-group prefill kernels, from the HIP
+    runtime: {"whole": {256: n, 192: n}, "split": {256: n, 192: n}} by tile width."""
+    out = (ctypes.c_int32 * 4)()
+    _check("bitlinear_probe_prefill_occupancy", lib().bitlinear_probe_prefill_occupancy(out))
+    return {"whole": {256: out[0], 192: out[1]}, "split": {256: out[2], 192: out[3]}}
+
+
 class PreparedCall:
     """One C-ABI call with its arguments marshalled once: raw device pointers, sizes and the
     stream handle, converted to ctypes values up front.  Calling it re-issues the same
@@ -780,6 +851,17 @@ def prepare_quantize_acts(x, xq, absmax) -> PreparedCall:
     dt = BL_BF16 if x.dtype == torch.bfloat16 else BL_F32
     return PreparedCall("bitlinear_quantize_acts", x.data_ptr(), dt, x.shape[0], x.shape[1], xq.data_ptr(),
                         absmax.data_ptr(), None, _stream(x.device))
+
+
+def prepare_forward_ws(packed, gamma, xq, absmax, n: int, k: int, y, workspace) -> PreparedCall:
+    """bitlinear_forward_ws on these tensors (y fp32 output), marshalled once."""
+    for t, name in ((packed, "packed"), (gamma, "gamma"), (xq, "xq"), (absmax, "absmax"), (y, "y")):
+        _require_cuda(t, name)
+    return PreparedCall("bitlinear_forward_ws", packed.data_ptr(), gamma.data_ptr(), xq.data_ptr(), absmax.data_ptr(),
+                        xq.shape[0], n, k, y.data_ptr(), None,
+                        workspace.data_ptr() if workspace is not None else None,
+                        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                        _stream(xq.device))
 
 
 def prepare_forward(packed, gamma, xq, absmax, n: int, k: int, y) -> PreparedCall:

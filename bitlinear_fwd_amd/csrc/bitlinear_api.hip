@@ -106,6 +106,54 @@ int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* X
   return hip_status(bl::launch_gemm(packed, gamma, Xq, absmax, M, N, K, Y, acc, s));
 }
 
+int64_t bitlinear_forward_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1 || M >= kMaxDim || N >= kMaxDim || K > kMaxK) return -1;
+  if (use_decode(M, N, K)) return 0;
+  return bl::plan_gemm_ws(M, N, K).ws_bytes;
+}
+
+int bitlinear_forward_ws(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
+                         int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* workspace, int64_t ws_bytes,
+                         void* stream) {
+  const int64_t need = bitlinear_forward_ws_bytes(M, N, K);
+  if (need <= 0) return bitlinear_forward(packed, gamma, Xq, absmax, M, N, K, Y, acc, stream);
+  if (!packed || !gamma || !Xq || !absmax || (!Y && !acc)) return BL_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return BL_ERR_INVALID_ARG;
+  if (!aligned(packed, 16) || !aligned(Xq, 16) || !aligned(gamma, 4) || !aligned(absmax, 4) ||
+      (Y && !aligned(Y, 4)) || (acc && !aligned(acc, 4)))
+    return BL_ERR_INVALID_ARG;
+  return hip_status(bl::launch_gemm_ws(packed, gamma, Xq, absmax, M, N, K, Y, acc, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int bitlinear_probe_prefill_occupancy(int32_t out[4]) {
+  if (!out) return BL_ERR_INVALID_ARG;
+  int v[4];
+  if (bl::gemm_occupancy(v) != hipSuccess) return BL_ERR_HIP;
+  for (int i = 0; i < 4; ++i) out[i] = v[i];
+  return BL_OK;
+}
+
+int bitlinear_forward_ws_plan(int64_t M, int64_t N, int64_t K, int32_t out[10]) {
+  if (!out) return BL_ERR_INVALID_ARG;
+  for (int i = 6; i < 10; ++i) out[i] = 0;
+  const int st = bitlinear_forward_plan(M, N, K, out);
+  if (st != BL_OK || use_decode(M, N, K)) return st;
+  const bl::GemmPlan p = bl::plan_gemm_ws(M, N, K);
+  if (!p.sk) return BL_OK;
+  out[0] = 6;
+  out[1] = (int32_t)p.groups;
+  out[2] = p.threads;
+  out[3] = p.bm;
+  out[4] = p.bn;
+  out[5] = 1;
+  out[6] = p.sk_rounds;
+  out[7] = p.sk_tail;
+  out[8] = p.sk_parts;
+  out[9] = p.sk_cpp;
+  return BL_OK;
+}
+
 int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const void* X, int dt, int64_t M, int64_t N,
                             int64_t K, float* Y, int32_t* acc, int8_t* Xq, float* absmax, void* stream) {
   if (!packed || !gamma || !X || !Xq || !absmax || (!Y && !acc)) return BL_ERR_INVALID_ARG;

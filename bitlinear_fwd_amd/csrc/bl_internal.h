@@ -122,8 +122,22 @@ struct GemmPlan {
   int ks = 1;              // K groups of four waves per tile (1 or 2)
   int threads = 256;
   int64_t groups = 0;
+  // split-tail form (plan_gemm_ws only): sk_rounds rounds of whole tiles over the resident
+  // slots, then the sk_tail tiles left split into sk_parts K ranges of sk_cpp chunks
+  bool sk = false;
+  int sk_rounds = 0, sk_tail = 0, sk_parts = 1, sk_cpp = 0;
+  int64_t ws_bytes = 0;    // workspace: the tail's int32 partial tiles
 };
+constexpr int kGemmCUs = 256;  // compute units of one MI355X
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+// The plan of the workspace form (bitlinear_forward_ws): the split tail where it evens
+// out a partial last round with at most 8 MiB of partial tiles, else plan_gemm's.
+GemmPlan plan_gemm_ws(int64_t M, int64_t N, int64_t K);
+int gemm_slots_per_cu(int bn);
+// Resident workgroups per compute unit the runtime reports for the one-group prefill
+// kernels: 64 x 256 and 64 x 192 whole-tile, then 64 x 256 and 64 x 192 split-tail.
+hipError_t gemm_occupancy(int out[4]);
+
 
 // Launchers (return hipSuccess or the launch error).  All sizes are validated by the
 // C ABI before these are called.
@@ -180,6 +194,8 @@ hipError_t launch_gemv_gated(const uint8_t* packed_gate, const float* gamma_gate
 hipError_t launch_gated_relu2(const float* y_gate, const float* y_up, int64_t count, float* h, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
                        int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, hipStream_t s);
+hipError_t launch_gemm_ws(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
+                          int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* workspace, hipStream_t s);
 
 // Measurement probes (probes.hip).
 int64_t probe_stream_groups(int64_t bytes);

@@ -138,6 +138,40 @@ int bitlinear_forward(const uint8_t* packed, const float* gamma, const int8_t* X
                       int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* stream);
 
 /*
+ * bitlinear_forward with a caller workspace (steps 3 + 4, as bitlinear_forward; the same
+ * arguments and results, bit for bit).  The workspace lets the prefill GEMM even out a
+ * partial last round of output tiles: where the tiles need more than one round of the
+ * GPU's resident workgroups, the whole rounds run as in bitlinear_forward, and the tiles
+ * left over are split along K (the contraction index) into ranges computed by different
+ * workgroups, each writing its exact int32 partial tile to the workspace; a second launch
+ * on the stream adds the partials (integer addition: the result does not depend on the
+ * order) and writes y / acc.  The planner takes the split only where the partial tiles
+ * stay within 8 MiB (their bytes are written and read once more, next to the fp32
+ * output); otherwise bitlinear_forward_ws_bytes returns 0 and the call is
+ * bitlinear_forward (workspace may then be null).
+ *   workspace  device memory of at least bitlinear_forward_ws_bytes(M, N, K) bytes,
+ *              256-byte aligned, owned by the caller; its contents on entry do not
+ *              matter and nothing in it carries over between calls.  Calls that share a
+ *              workspace must not overlap (one stream, or events between streams).
+ *   ws_bytes   its size in bytes.
+ * Errors: those of bitlinear_forward; BL_ERR_INVALID_ARG when the workspace is needed and
+ * is null, misaligned or smaller than required (nothing enqueued).
+ */
+int64_t bitlinear_forward_ws_bytes(int64_t M, int64_t N, int64_t K);
+int bitlinear_forward_ws(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax,
+                         int64_t M, int64_t N, int64_t K, float* Y, int32_t* acc, void* workspace, int64_t ws_bytes,
+                         void* stream);
+/*
+ * Host-only description of the launches bitlinear_forward_ws makes for (M, N, K); no
+ * device work.  out[0..5] as bitlinear_forward_plan; where the split tail runs, out[0] = 6,
+ * out[1] = workgroups of the first launch, out[2] = threads, out[3] / out[4] = output tile
+ * rows / columns, out[5] = 1, out[6] = rounds of whole tiles, out[7] = tiles split along K,
+ * out[8] = K ranges per split tile, out[9] = 256-column chunks per range (out[6..9] are 0
+ * otherwise).  Returns BL_OK or BL_ERR_INVALID_ARG (as bitlinear_forward_plan).
+ */
+int bitlinear_forward_ws_plan(int64_t M, int64_t N, int64_t K, int32_t out[10]);
+
+/*
  * Steps 2 + 3 + 4 in one call: per-token activation quantisation, contraction and
  * rescale, for inference on un-quantised activations.
  *   X       [M][K] fp32 (dt = BL_F32) or bf16 (dt = BL_BF16), row-major.
@@ -352,6 +386,14 @@ int bitlinear_probe_stream(const void* buf, int64_t bytes, uint32_t* out, int64_
 int bitlinear_probe_read(const void* buf, int64_t bytes, int64_t workgroups, int nontemporal, uint32_t* out,
                          void* stream);
 int bitlinear_probe_mfma(int64_t iters, int64_t workgroups, uint32_t* out, void* stream);
+/*
+ * bitlinear_probe_prefill_occupancy writes to out[4] (host memory) the workgroups per
+ * compute unit that the HIP runtime reports as resident at once for the one-group prefill
+ * kernels: 64 x 256 and 64 x 192 tiles of bitlinear_forward, then the same two of
+ * bitlinear_forward_ws's split-tail form.  The planner of bitlinear_forward_ws assumes 3
+ * and 4.  Needs a current HIP device; BL_ERR_HIP if the query fails.
+ */
+int bitlinear_probe_prefill_occupancy(int32_t out[4]);
 
 #ifdef __cplusplus
 }

@@ -302,6 +302,54 @@ def test_prefill_plans():
                     assert tiles <= 512, (m, n, k, p)
 
 
+def test_split_tail_plans_cover_every_tile_once():
+    # host-only sweep of the workspace planner (bitlinear_forward_ws): where it splits a tail,
+    # the blocks of the grid must cover every output tile exactly once, whole tiles by one
+    # block and each tail tile by K ranges that partition its 256-column chunks, with the
+    # workspace large enough for the counters and every range's partial tile.  The block ->
+    # work map below is the one the kernel documents: block b < rounds x slots takes whole
+    # tile (b % 8) x (rounds x slots / 8) + b / 8; block b past them, with s = (b - D) / 8,
+    # takes range s % parts of tail tile 8 (s / parts) + b % 8 (none when that is >= tail).
+    seen_split = 0
+    for m in (65, 333, 1000, 1061, 1536, 1571, 1600, 2048, 2098, 3000, 3074, 4096, 4721, 4904, 8192):
+        for n in (640, 2560, 2600, 4100, 6912, 8000, 8003, 9000, 10240, 12000, 28672):
+            for k in (256, 700, 1000, 2560, 3001, 6912, 8192):
+                p = bl.forward_ws_plan(m, n, k)
+                nbytes = bl.forward_ws_bytes(m, n, k)
+                if not p.get("split_tail"):
+                    assert nbytes == 0 and p == bl.forward_plan(m, n, k), (m, n, k, p)
+                    continue
+                seen_split += 1
+                assert p["tile_n"] == bl.forward_plan(m, n, k)["tile_n"] and nbytes <= 8 << 20, (m, n, k, p)
+                bn, chunks = p["tile_n"], bl.k_pad(k) // 256
+                tiles = -(-m // 64) * -(-n // bn)
+                slots = 256 * (3 if bn == 256 else 4)
+                rounds, tail, parts, cpp = p["rounds"], p["split_tiles"], p["k_ranges"], p["chunks_per_range"]
+                assert p["tile_m"] == 64 and p["threads"] == 256 and p["k_groups"] == 1, p
+                assert rounds == tiles // slots and tail == tiles - rounds * slots and 0 < tail < slots, (m, n, k, p)
+                assert parts >= 2 and (parts - 1) * cpp < chunks <= parts * cpp, (m, n, k, p)
+                assert nbytes == tail * parts * 64 * bn * 4, (m, n, k, p, nbytes)
+                dp = rounds * slots
+                assert dp % 8 == 0 and p["workgroups"] == dp + 8 * parts * -(-tail // 8), (m, n, k, p)
+                whole = [0] * tiles
+                ranges = {}
+                for b in range(p["workgroups"]):
+                    if b < dp:
+                        whole[(b % 8) * (dp // 8) + b // 8] += 1
+                        continue
+                    s_ = (b - dp) // 8
+                    i = 8 * (s_ // parts) + b % 8
+                    if i < tail:
+                        ranges.setdefault(dp + i, []).append(s_ % parts)
+                assert all(c == 1 for c in whole[:dp]) and not any(whole[dp:]), (m, n, k, p)
+                assert sorted(ranges) == list(range(dp, tiles)), (m, n, k, p)
+                for t, js in ranges.items():
+                    assert sorted(js) == list(range(parts)), (m, n, k, t, js)
+                    covered = sorted(c for j in js for c in range(j * cpp, min(chunks, (j + 1) * cpp)))
+                    assert covered == list(range(chunks)), (m, n, k, t)
+    assert seen_split > 20
+
+
 def test_launch_plans_cover_every_tile():
     # host-only sweep of every planner: a plan's waves x tiles per wave must cover all K
     # tiles, and its workgroups all row blocks, or outputs would silently go missing
