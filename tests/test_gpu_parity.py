@@ -516,10 +516,12 @@ def test_forward_fused_lds_form(m, n, k, dtype):
 # One token on many row blocks (257 .. 1875, several workgroups per compute unit), ragged
 # last rows (29999) and ragged K, int8 and fused: the 100B-class shapes and others.  Past
 # 512 row blocks the fused form issues its activation loads at raised wave priority; up to
-# 512 with runs of 14 or 16 tiles (8192 x 28672, 4200 x 32000, 6000 x 32504) it also issues
-# two weight tiles ahead of the barrier.
+# 512 with runs of 14 or 16 tiles (8192 x 28672, 4200 x 32000, 6000 x 32504, 8100 x 28000
+# with an odd number of row blocks, 7500 x 28504 with ragged K) it also issues two weight
+# tiles ahead of the barrier.
 MANY_RB = [(28672, 8192), (8192, 28672), (4100, 296), (16400, 296), (6912, 2560), (29999, 4000), (8200, 12000),
-           (5000, 20000), (4200, 32000), (12288, 3000), (16000, 1104), (24576, 5000), (6000, 32504)]
+           (5000, 20000), (4200, 32000), (12288, 3000), (16000, 1104), (24576, 5000), (6000, 32504), (8100, 28000),
+           (7500, 28504)]
 
 
 @pytest.mark.parametrize("n,k", MANY_RB)
