@@ -37,6 +37,10 @@
 //     before.  Before, every half-stage waited for the refills it had just issued
 //     (measured: 2048 x 6912 x 2560 47.7 -> 45.1 us, 2048 x 2560 x 6912 44.0 -> 41.5 us,
 //     8192^3 504 -> 478 us);
+//   * epilogue: the wave's 16 row scales are loaded together before the first store (one
+//     wait, not one memory round trip per row), and each row takes one address with the
+//     column blocks at constant offsets from it (measured: 2048 x 6912 x 2560 45.3 -> 42.2
+//     us, 4096 x 6912 x 2560 79.5 -> 73.4 us, 2048 x 2560 x 6912 42.6 -> 42.1 us);
 //   * split-tail form (bitlinear_forward_ws): the whole rounds of tiles as above, then the
 //     tiles left over split along K over the freed slots, their exact int32 partial tiles
 //     summed by a second launch (k_gemm_fixup).
@@ -300,8 +304,46 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(kSK ? 
   };
 
   const float gm = gamma[0];
-  // store row block mi of the wave's tile at (m0, n0): y = (acc + the sum of `np`
-  // partials at `other`, stride `pstride` v4i, lane-major per column block) * scale
+  // Row scales gamma * a[m] / 127 of the wave's rows 16 mi + 4 g + v, loaded together
+  // before any store (rows past M read row M-1; their outputs are never stored).
+  float sc[MB][4];
+  auto load_scales = [&](int m0) {
+    float am[MB][4];
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) am[mi][v] = absmax[min(m0 + wm * WM + 16 * mi + 4 * g + v, M - 1)];
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sc[mi][v] = gm * am[mi][v] * (1.0f / 127.0f);
+  };
+  // store row block mi of the wave's tile at (m0, n0) from its int32 values `part`: one
+  // row address per row, the column blocks at constant offsets from it, and the column
+  // bound checked only in a tile that crosses N
+  auto store_rows = [&](auto mc, int m0, int n0, const v4i (&part)[NB]) {
+    constexpr int mi = decltype(mc)::value;
+    const int nl = n0 + wn * WN + r;  // column of block j: nl + 16 j
+    const bool full_n = n0 + BN <= N;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + wm * WM + 16 * mi + 4 * g + v;
+      if (m >= M) continue;
+      const size_t off = (size_t)m * N + nl;
+      if (acc_out) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          if (full_n || nl + 16 * j < N) acc_out[off + 16 * j] = part[j][v];
+      }
+      if (Y) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          if (full_n || nl + 16 * j < N) Y[off + 16 * j] = (float)part[j][v] * sc[mi][v];
+      }
+    }
+  };
+  // store row block mi: (acc + the sum of `np` partials at `other`, stride `pstride` v4i,
+  // lane-major per column block) * scale
   auto store_block = [&](auto mc, int m0, int n0, const v4i* other, int np, size_t pstride) {
     constexpr int mi = decltype(mc)::value;
     v4i part[NB];
@@ -311,42 +353,12 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(kSK ? 
 #pragma unroll
       for (int j = 0; j < NB; ++j) part[j] += other[(size_t)q * pstride + j * 64];
     }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = m0 + wm * WM + 16 * mi + 4 * g + v;
-      if (m >= M) continue;
-      const float sc = gm * absmax[m] * (1.0f / 127.0f);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = n0 + wn * WN + 16 * j + r;
-        if (n < N) {
-          const int32_t a = part[j][v];
-          if (acc_out) acc_out[(size_t)m * N + n] = a;
-          if (Y) Y[(size_t)m * N + n] = (float)a * sc;
-        }
-      }
-    }
+    store_rows(mc, m0, n0, part);
   };
   // the whole tile, from the accumulators alone
   auto store_tile = [&](int m0, int n0) {
-#pragma unroll
-    for (int mi = 0; mi < MB; ++mi) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * WM + 16 * mi + 4 * g + v;
-        if (m >= M) continue;
-        const float sc = gm * absmax[m] * (1.0f / 127.0f);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int n = n0 + wn * WN + 16 * j + r;
-          if (n < N) {
-            const int32_t a = acc[mi][j][v];
-            if (acc_out) acc_out[(size_t)m * N + n] = a;
-            if (Y) Y[(size_t)m * N + n] = (float)a * sc;
-          }
-        }
-      }
-    }
+    load_scales(m0);
+    static_for<MB>([&](auto mc) { store_rows(mc, m0, n0, acc[decltype(mc)::value]); });
   };
 
   const int tiles = tiles_m * tiles_n;
@@ -367,6 +379,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(kSK ? 
     } else {
       // Group 0 stores row blocks mi < MB/2 and group 1 the rest, each adding the other
       // group's partial (int32, exact), which comes through LDS one row block per pass.
+      load_scales(m0);
       ring_barrier();  // every load has landed (the wait after the loop)
       v4i* out = reinterpret_cast<v4i*>(kg == 0 ? As0 : As1) + wave * NB * 64 + lane;
       const v4i* in = reinterpret_cast<const v4i*>(kg == 0 ? As1 : As0) + wave * NB * 64 + lane;
