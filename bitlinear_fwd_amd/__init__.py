@@ -176,6 +176,9 @@ def _plan_dict(out) -> dict:
     if out[0] == 4:
         return {"kernel": "lut", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
                 "tiles_per_wave": out[4], "lds_bytes": out[5]}
+    if out[0] == 3 and out[4] == 4:  # 5..16 tokens: every workgroup quantises the 16 token rows into LDS
+        return {"kernel": "fused", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
+                "acts": "lds16", "lds_acts": True, "lds_bytes": 0, "tiles_per_wave": out[5]}
     if out[0] == 3:
         return {"kernel": "fused", "workgroups": out[1], "threads": out[2], "row_blocks": out[3],
                 "acts": "registers" if out[4] == 2 else "lds", "lds_acts": out[4] == 1,

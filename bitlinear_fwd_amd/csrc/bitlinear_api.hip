@@ -169,6 +169,13 @@ int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const voi
     if ((p.lds_act || p.dpp) && p.ok)
       return hip_status(bl::launch_gemv_fused(packed, gamma, X, dt == BL_BF16, M, N, K, Y, acc, Xq, absmax, s));
   }
+  if (M >= 5 && M <= 16 && aligned(X, 16)) {
+    // 5..16 tokens: the fused form that quantises into LDS in every workgroup
+    const bl::GroupMat gm{packed, gamma, N, Y, acc};
+    bool launched = false;
+    const hipError_t e = bl::launch_gemv_fq16(&gm, 1, X, dt == BL_BF16, M, K, Xq, absmax, s, &launched);
+    if (launched || e != hipSuccess) return hip_status(e);
+  }
   // general case: the activation quantiser, then the forward, both on the stream
   hipError_t e = bl::launch_act_quant(X, dt == BL_BF16 ? 1 : 0, M, K, Xq, absmax, s);
   if (e != hipSuccess) return BL_ERR_HIP;
@@ -371,6 +378,19 @@ int bitlinear_forward_fused_plan(int64_t M, int64_t N, int64_t K, int dt, int32_
       return BL_OK;
     }
   }
+  {
+    const bl::Fq16Plan q = bl::plan_fq16(M, bl::n_pad(N) / bl::kTileRows, K, dt == BL_BF16 ? 1 : 2);
+    if (q.ok) {
+      const bl::GroupMat gm{nullptr, nullptr, N, nullptr, nullptr};
+      out[0] = 3;
+      out[1] = (int32_t)bl::fq16_groups(q, &gm, 1);
+      out[2] = q.W * 64;
+      out[3] = q.RB;
+      out[4] = 4;
+      out[5] = q.T;
+      return BL_OK;
+    }
+  }
   return bitlinear_forward_plan(M, N, K, out);
 }
 
@@ -440,6 +460,11 @@ int grouped_impl(const bl_matrix* mats, int count, const void* X, int dt, int64_
     bool launched = false;
     const hipError_t e =
         bl::launch_gemv_grouped(gm, count, X, dt == BL_BF16, M, K, Xq, absmax, s, &launched, norm ? &nargs : nullptr);
+    if (launched || e != hipSuccess) return hip_status(e);
+  }
+  if (!norm && aligned(X, 16)) {
+    bool launched = false;
+    const hipError_t e = bl::launch_gemv_fq16(gm, count, X, dt == BL_BF16, M, K, Xq, absmax, s, &launched);
     if (launched || e != hipSuccess) return hip_status(e);
   }
   // general case: one activation quantisation, then one forward per matrix

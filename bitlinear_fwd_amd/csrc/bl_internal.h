@@ -183,6 +183,22 @@ hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, i
 // enqueued otherwise).
 hipError_t launch_gemv_grouped_int8(const GroupMat* mats, int count, const int8_t* Xq, const float* absmax, int64_t M,
                                     int64_t K, hipStream_t s, bool* launched);
+// The fused 5..16-token form (bf16 x, K a multiple of 8 up to 4096, k_gemv_fq16): every
+// workgroup quantises the whole input into LDS and decodes RB row blocks with W waves,
+// runs of T tiles, KL 16-byte row pieces per lane.  ok false where it does not apply.
+struct Fq16Plan {
+  bool ok = false;
+  int W = 0, T = 0, RB = 1, KL = 0;
+  int64_t lds_bytes = 0;  // dynamic LDS: the codes of 16 token rows
+};
+// rb_total: row blocks of all the matrices of the call; src as plan_gemv's
+Fq16Plan plan_fq16(int64_t M, int64_t rb_total, int64_t K, int src);
+// Workgroups of the fused 5..16-token launch over these matrices' row blocks.
+int64_t fq16_groups(const Fq16Plan& p, const GroupMat* mats, int count);
+// The fused 5..16-token launch for a group of matrices (a single forward is a group of
+// one): *launched tells whether it did (nothing is enqueued otherwise).
+hipError_t launch_gemv_fq16(const GroupMat* mats, int count, const void* X, int bf16, int64_t M, int64_t K,
+                            int8_t* Xq_out, float* absmax_out, hipStream_t s, bool* launched);
 // Gate / up pair with the squared-ReLU gating: one launch where gated_fused_ok (M <= 4,
 // register form of the fused decode kernel, runs of at most 8 tiles); otherwise
 // hipErrorInvalidConfiguration and nothing enqueued.

@@ -37,12 +37,15 @@
 #include "decode_common.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace bl {
 namespace {
 
 constexpr int kMaxLdsActBytes = 48 * 1024;
 constexpr int64_t kMaxFusedElems = 8192;  // M*K limit of the one-kernel quantise + decode
+constexpr int kMaxFq16Lds = 80 * 1024;    // dynamic LDS of the fused 5..16-token kernel
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Sum the W waves' partial tiles (red[w][t][j][lane]) and write y / acc for token group t
 // (tokens 16 t .. 16 t + 15) of row block j.
@@ -914,6 +917,171 @@ __global__ __launch_bounds__(1024) void k_gemv_dppm_group(const DppmGroup grp, c
 }
 
 // ---------------------------------------------------------------------------------------
+// k_gemv_fq16: the fused form for 5..16 tokens (bf16 x): quantiser and decode in one
+// launch.  Every workgroup quantises the whole M x K input into LDS: token m belongs to
+// wave m % W, which loads its row with coalesced 16-byte pieces (lane l takes pieces
+// l, l + 64, ...), takes the absmax over them with a wave reduction (no barrier: the wave
+// holds the whole row) and writes the codes to LDS row m, with the standalone quantiser's
+// arithmetic.  The weights of the workgroup (RB row blocks, a run of T tiles per wave) are
+// issued right behind the row loads and stream in meanwhile.  One barrier, then the A operand of
+// step i of tile t comes from LDS (lane (r, g): token r, columns 256 t + 64 g + 16 i) and
+// the B operand from the weight registers, as in k_gemv_dppm.  Rows of tokens >= M are
+// never written or stored.  Workgroup 0 also stores xq (zero-padded to K_pad) and absmax.
+// KL = loads per lane per token row (16-byte pieces l + 64 k < K / 8).
+template <int W, int T, int RB, int KL>
+__global__ __launch_bounds__(W * 64) void k_gemv_fq16(const DppmGroup grp, const uint16_t* __restrict__ X, int M, int K,
+                                                     int K_pad, int chunks, int8_t* __restrict__ xq_out,
+                                                     float* __restrict__ absmax_out) {
+  constexpr int TPW = (16 + W - 1) / W;  // token rows per wave
+  extern __shared__ __attribute__((aligned(16))) uint8_t act[];  // [16][K_pad + 16] int8 codes
+  __shared__ v4i red[W * RB * 64];
+  __shared__ float amax_s[16];
+  int mat = 0;  // uniform
+#pragma unroll
+  for (int k = 0; k + 1 < kMaxGroup; ++k)
+    if (k + 1 < grp.count && (int)blockIdx.x >= grp.wg_end[k]) mat = k + 1;
+  const uint8_t* packed = grp.packed[0];
+  const float* gamma = grp.gamma[0];
+  float* Y = grp.Y[0];
+  int32_t* acc_out = grp.acc[0];
+  int N = grp.N[0], rblocks = grp.rblocks[0], wg_base = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxGroup; ++k)
+    if (mat == k) {
+      packed = grp.packed[k];
+      gamma = grp.gamma[k];
+      Y = grp.Y[k];
+      acc_out = grp.acc[k];
+      N = grp.N[k];
+      rblocks = grp.rblocks[k];
+      wg_base = grp.wg_end[k - 1];
+    }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int rb0 = ((int)blockIdx.x - wg_base) * RB;
+  const int c0 = wave * T;
+  const int stride = K_pad + 16;
+
+  // the wave's token rows first (L2 hits that return while the weights stream from HBM):
+  // pieces past the row are not loaded and stay zero
+  const int pieces = K / 8;
+  uint4 x[TPW][KL];
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int m = min(wave + W * q, M - 1);
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+      const int p = lane + 64 * k;
+      x[q][k] = p < pieces ? reinterpret_cast<const uint4*>(X + (size_t)m * K)[p] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // then every weight load of the wave's run, for its RB row blocks
+  uint4 w[T][RB];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+      w[t][j] = load_nt(reinterpret_cast<const uint4*>(packed) +
+                        ((size_t)min(rb0 + j, rblocks - 1) * chunks + min(c0 + t, chunks - 1)) * 64 + lane);
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int m = wave + W * q;
+    if (m >= M) continue;  // uniform across the wave
+    // absmax: the largest |x| bit pattern, two bf16 values per 32-bit word (for values that
+    // are not NaN the order of the patterns with the sign cleared is the order of |x|)
+    u16x2 mx = {0, 0};
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+      const uint32_t d[4] = {x[q][k].x, x[q][k].y, x[q][k].z, x[q][k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, d[e] & 0x7FFF7FFFu));
+    }
+    uint32_t mb = max((uint32_t)mx.x, (uint32_t)mx.y);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
+    float a = __uint_as_float(mb << 16);
+    if (mb > 0x7F80u) {
+      // a NaN in the row: the float maximum, which passes over NaN as the standalone
+      // quantiser's does
+      a = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KL; ++k) {
+        const uint32_t d[4] = {x[q][k].x, x[q][k].y, x[q][k].z, x[q][k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a = fmaxf(a, fmaxf(fabsf(__uint_as_float(d[e] << 16)), fabsf(__uint_as_float(d[e] & 0xFFFF0000u))));
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    }
+    const float sc = a > 0.0f ? 127.0f / a : 0.0f;
+    if (lane == 0) {
+      amax_s[m] = a;
+      if (blockIdx.x == 0) absmax_out[m] = a;
+    }
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+      const int p = lane + 64 * k;
+      if (p >= pieces) continue;
+      const uint32_t d[4] = {x[q][k].x, x[q][k].y, x[q][k].z, x[q][k].w};
+      const uint32_t lo = quant_code4(__uint_as_float(d[0] << 16), __uint_as_float(d[0] & 0xFFFF0000u),
+                                      __uint_as_float(d[1] << 16), __uint_as_float(d[1] & 0xFFFF0000u), sc);
+      const uint32_t hi = quant_code4(__uint_as_float(d[2] << 16), __uint_as_float(d[2] & 0xFFFF0000u),
+                                      __uint_as_float(d[3] << 16), __uint_as_float(d[3] & 0xFFFF0000u), sc);
+      *reinterpret_cast<uint2*>(act + m * stride + 8 * p) = make_uint2(lo, hi);
+      if (blockIdx.x == 0) *reinterpret_cast<uint2*>(xq_out + (size_t)m * K_pad + 8 * p) = make_uint2(lo, hi);
+    }
+    // padding columns K .. K_pad - 1 of xq are zero (the LDS copy needs none: the packed
+    // padding codes decode to 0)
+    if (blockIdx.x == 0)
+      for (int p = pieces + lane; p < K_pad / 8; p += 64)
+        *reinterpret_cast<uint2*>(xq_out + (size_t)m * K_pad + 8 * p) = make_uint2(0u, 0u);
+  }
+  lds_barrier();
+
+  v4i c[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) c[j] = (v4i){0, 0, 0, 0};
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int tile = min(c0 + t, chunks - 1);
+    const bool live = c0 + t < chunks;  // tiles past the matrix decode as 0
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v4i av = *reinterpret_cast<const v4i*>(act + r * stride + tile * kTileCols + 64 * g + 16 * i);
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        const uint32_t word = live ? word_of(w[t][j], i) : 0u;
+        c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, decode16(word), c[j], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < RB; ++j) red[(wave * RB + j) * 64 + lane] = c[j];
+  lds_barrier();
+  const float gm = gamma[0];
+  for (int j = wave; j < RB; j += W) {
+    if (rb0 + j >= rblocks) continue;
+    v4i sum = red[j * 64 + lane];
+    for (int w2 = 1; w2 < W; ++w2) sum += red[(w2 * RB + j) * 64 + lane];
+    const int n = (rb0 + j) * kTileRows + r;
+    if (n >= N) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 4 * g + v;
+      if (m < M) {
+        if (acc_out) acc_out[(size_t)m * N + n] = sum[v];
+        if (Y) Y[(size_t)m * N + n] = (float)sum[v] * gm * amax_s[m] * (1.0f / 127.0f);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 struct Args {
   const uint8_t* packed;
   const float* gamma;
@@ -1174,6 +1342,31 @@ hipError_t launch_dppm_group(int W, const DppmGroup& g, const int8_t* Xq, const 
   if (W * RB > 16 || (int64_t)W * T < chunks) return hipErrorInvalidConfiguration;  // LDS partials, coverage
   hipLaunchKernelGGL((k_gemv_dppm_group<T, MM, RB>), dim3(g.wg_end[g.count - 1]), dim3(W * 64), 0, s, g, Xq, absmax, M,
                      K_pad, chunks);
+  return hipGetLastError();
+}
+
+template <int W, int T, int RB, int KL>
+hipError_t launch_fq16_k(const DppmGroup& g, const void* X, int M, int K, int K_pad, int chunks, int8_t* xq_out,
+                         float* absmax_out, int64_t lds_bytes, hipStream_t s) {
+  if ((int64_t)W * T < chunks || (int64_t)KL * 512 < K) return hipErrorInvalidConfiguration;  // coverage
+  auto kern = k_gemv_fq16<W, T, RB, KL>;
+  // the LDS limit above 64 KiB is raised once per device for this kernel (a repeated set
+  // from a concurrent first call is harmless)
+  static std::atomic<uint64_t> raised{0};
+  if (lds_bytes > 64 * 1024) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = uint64_t(1) << (dev & 63);
+    if (!(raised.load(std::memory_order_relaxed) & bit)) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kMaxFq16Lds);
+      if (e != hipSuccess) return e;
+      raised.fetch_or(bit, std::memory_order_relaxed);
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3(g.wg_end[g.count - 1]), dim3(W * 64), (unsigned)lds_bytes, s, g,
+                     static_cast<const uint16_t*>(X), M, K, K_pad, chunks, xq_out, absmax_out);
   return hipGetLastError();
 }
 
@@ -1454,6 +1647,69 @@ hipError_t launch_gemv_grouped_int8(const GroupMat* mats, int count, const int8_
                             : launch_dppm_group<2, 16, 1>(W, g, Xq, absmax, (int)M, (int)K_pad, (int)chunks, s);
   return RB == 2 ? launch_dppm_group<2, 8, 2>(W, g, Xq, absmax, (int)M, (int)K_pad, (int)chunks, s)
                  : launch_dppm_group<2, 8, 1>(W, g, Xq, absmax, (int)M, (int)K_pad, (int)chunks, s);
+}
+
+Fq16Plan plan_fq16(int64_t M, int64_t rb_total, int64_t K, int src) {
+  Fq16Plan p;
+  // bf16 x in whole 16-byte pieces, 5..16 tokens, rows of at most 4096 columns.  Eight
+  // waves with two token rows each; row blocks shared per workgroup once there are more
+  // than about 1.25 workgroups per compute unit.  (Longer rows were measured slower than
+  // the quantiser plus the decode: 2560 x 6912 at M = 16, sixteen waves of one row each,
+  // 11.3 against 9.9 us: every workgroup quantises the whole input, 110 K values there.)
+  if (src != 1 || M < 5 || M > 16 || K % 8 != 0 || K > 4096) return p;
+  const int64_t K_pad = k_pad(K), chunks = K_pad / kTileCols;
+  p.W = 8;
+  p.T = (int)((chunks + 7) / 8);
+  p.KL = K <= 2048 ? 4 : 8;
+  p.RB = rb_total > 640 ? 4 : (rb_total > 320 ? 2 : 1);
+  p.lds_bytes = 16 * (K_pad + 16);
+  p.ok = p.lds_bytes <= kMaxFq16Lds && (int64_t)p.W * p.T >= chunks && (int64_t)p.KL * 512 >= K;
+  return p;
+}
+
+int64_t fq16_groups(const Fq16Plan& p, const GroupMat* mats, int count) {
+  int64_t groups = 0;
+  for (int j = 0; j < count; ++j) groups += (n_pad(mats[j].N) / kTileRows + p.RB - 1) / p.RB;
+  return groups;
+}
+
+hipError_t launch_gemv_fq16(const GroupMat* mats, int count, const void* X, int bf16, int64_t M, int64_t K,
+                            int8_t* Xq_out, float* absmax_out, hipStream_t s, bool* launched) {
+  *launched = false;
+  if (count < 1 || count > kMaxGroup) return hipSuccess;
+  int64_t rb_total = 0;
+  for (int j = 0; j < count; ++j) rb_total += n_pad(mats[j].N) / kTileRows;
+  const Fq16Plan p = plan_fq16(M, rb_total, K, bf16 ? 1 : 2);
+  if (!p.ok) return hipSuccess;
+  DppmGroup g{};
+  g.count = count;
+  int end = 0;
+  for (int j = 0; j < count; ++j) {
+    const int rb = (int)(n_pad(mats[j].N) / kTileRows);
+    end += (rb + p.RB - 1) / p.RB;
+    g.wg_end[j] = end;
+    g.N[j] = (int)mats[j].N;
+    g.rblocks[j] = rb;
+    g.packed[j] = mats[j].packed;
+    g.gamma[j] = mats[j].gamma;
+    g.Y[j] = mats[j].Y;
+    g.acc[j] = mats[j].acc;
+  }
+  const int K_pad = (int)k_pad(K), chunks = K_pad / kTileCols;
+  *launched = true;
+  auto go = [&](auto wc, auto tc, auto rc, auto kc) {
+    return launch_fq16_k<decltype(wc)::value, decltype(tc)::value, decltype(rc)::value, decltype(kc)::value>(
+        g, X, (int)M, (int)K, K_pad, chunks, Xq_out, absmax_out, p.lds_bytes, s);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  auto by_rb = [&](auto tc, auto kc) {
+    return p.RB == 4 ? go(I8{}, tc, I4{}, kc) : (p.RB == 2 ? go(I8{}, tc, I2{}, kc) : go(I8{}, tc, I1{}, kc));
+  };
+  if (p.T == 1) return p.KL == 4 ? by_rb(I1{}, I4{}) : by_rb(I1{}, I8{});
+  return p.KL == 4 ? by_rb(I2{}, I4{}) : by_rb(I2{}, I8{});
 }
 
 bool gated_fused_ok(int64_t M, int64_t N, int64_t K, int src) {

@@ -182,8 +182,11 @@ int bitlinear_forward_ws_plan(int64_t M, int64_t N, int64_t K, int32_t out[10]);
  * few tokens (M <= 4) with K a multiple of 8 (bf16) or 4 (fp32), a 16-byte aligned X and
  * K up to a size limit that depends on M and dt (at least 8192), one kernel launch does
  * all three steps: each workgroup computes the per-token absmax from the activation
- * pieces its waves hold, and each lane quantises its own pieces; otherwise the two
- * kernels run back to back (bitlinear_forward_fused_plan tells which).
+ * pieces its waves hold, and each lane quantises its own pieces.  For 5 to 16 tokens with
+ * bf16 X, K a multiple of 8 and at most 4096, one kernel launch does the same with the
+ * whole M x K input quantised into LDS by every workgroup (each token row held by one
+ * wave, so the row's absmax is a wave reduction).  Otherwise the two kernels run back to back
+ * (bitlinear_forward_fused_plan tells which).
  */
 int bitlinear_forward_fused(const uint8_t* packed, const float* gamma, const void* X, int dt, int64_t M, int64_t N,
                             int64_t K, float* Y, int32_t* acc, int8_t* Xq, float* absmax, void* stream);
@@ -206,7 +209,9 @@ typedef struct {
  * matrix.  For M <= 4 with a 16-byte aligned X, when bitlinear_forward_fused_plan(M,
  * sum of N_pad, K, dt) reports a fused kernel with activations in registers, the whole
  * group is one kernel launch (workgroups take the row blocks of the matrices in order);
- * otherwise the quantiser runs once, then one forward per matrix.
+ * likewise for 5..16 tokens under the conditions of the LDS form of
+ * bitlinear_forward_fused.  Otherwise the quantiser runs once, then one forward launch for
+ * the whole group (5..16 tokens, K up to 4096) or one per matrix.
  */
 int bitlinear_forward_grouped(const bl_matrix* mats, int count, const void* X, int dt, int64_t M, int64_t K,
                               int8_t* Xq, float* absmax, void* stream);
@@ -351,8 +356,9 @@ int bitlinear_forward_plan(int64_t M, int64_t N, int64_t K, int32_t out[6]);
  * Host-only description of what bitlinear_forward_fused does for (M, N, K) and activation
  * type dt, for a 16-byte aligned X; no device work.  out[0] = 3 when one fused kernel
  * quantises and contracts (out[1..3] as bitlinear_forward_plan; out[4] = 2 with out[5] =
- * K tiles per wave for the register form, or out[4] = 1 with out[5] = dynamic LDS bytes
- * for the LDS form); otherwise the activation quantiser runs first and out[] describes
+ * K tiles per wave for the register form, out[4] = 1 with out[5] = dynamic LDS bytes
+ * for the LDS form, or out[4] = 4 with out[5] = K tiles per wave for the 5..16-token LDS
+ * form); otherwise the activation quantiser runs first and out[] describes
  * the forward launch exactly as bitlinear_forward_plan.  Returns BL_OK,
  * BL_ERR_INVALID_ARG (as bitlinear_forward_plan) or BL_ERR_UNSUPPORTED (dt).
  */

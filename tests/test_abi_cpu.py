@@ -350,6 +350,11 @@ def test_split_tail_plans_cover_every_tile_once():
     assert seen_split > 20
 
 
+def dt_of(name, p):
+    # the 5..16-token LDS form reads bf16 x only
+    return name == "fused bf16"
+
+
 def test_launch_plans_cover_every_tile():
     # host-only sweep of every planner: a plan's waves x tiles per wave must cover all K
     # tiles, and its workgroups all row blocks, or outputs would silently go missing
@@ -363,7 +368,7 @@ def test_launch_plans_cover_every_tile():
                 rblocks = bl.n_pad(n) // 16
                 plans = [("forward", bl.forward_plan(m, n, k))]
                 for dt in ("bf16", "f32"):
-                    plans.append(("fused", bl.forward_fused_plan(m, n, k, dt)))
+                    plans.append(("fused " + dt, bl.forward_fused_plan(m, n, k, dt)))
                     plans.append(("subln", bl.forward_subln_plan(m, n, k, dt)))
                     plans.append(("gated", bl.forward_gated_relu2_plan(m, n, k, dt, True)))
                 for name, p in plans:
@@ -372,6 +377,14 @@ def test_launch_plans_cover_every_tile():
                         waves = p["threads"] // 64
                         assert waves * p["tiles_per_wave"] >= chunks, (name, m, n, k, p)
                         assert waves <= 16 and (waves - 1) * p["tiles_per_wave"] < chunks, (name, m, n, k, p)
+                        assert p["workgroups"] * p["row_blocks"] >= rblocks, (name, m, n, k, p)
+                    if p["kernel"] == "fused" and p["acts"] == "lds16":
+                        # 5..16 tokens, bf16, every workgroup quantises the input into LDS:
+                        # eight waves of two token rows each, runs cover K
+                        waves = p["threads"] // 64
+                        assert 5 <= m <= 16 and dt_of(name, p) and k % 8 == 0 and k <= 4096, (name, m, n, k, p)
+                        assert waves == 8 and waves * p["tiles_per_wave"] >= chunks, (name, m, n, k, p)
+                        assert p["row_blocks"] * waves <= 32, (name, m, n, k, p)
                         assert p["workgroups"] * p["row_blocks"] >= rblocks, (name, m, n, k, p)
                     if p["kernel"] == "decode" and p["acts"] == "per-tile loads":
                         # waves split the K tiles into contiguous runs; workgroups own row blocks
