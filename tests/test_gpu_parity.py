@@ -509,6 +509,50 @@ def test_forward_fused_5_to_16_tokens(m, n, k, dtype):
     _fused_check(m, n, k, dtype, seed=m * 41 + n + k)
 
 
+@pytest.mark.parametrize("m", [5, 16])
+def test_forward_fused_5_to_16_nonfinite_rows(m):
+    # rows holding a NaN (quiet, a signalling bit pattern, a negative one) or an infinity:
+    # the one-launch 5..16-token form takes the absmax over the bit patterns of |x| and
+    # falls back to the float maximum where a row holds a NaN.  The oracle's absmax passes
+    # over NaN (a comparison with NaN is false) and an infinite absmax gives a zero scale;
+    # the codes of the non-finite entries themselves are not defined by the oracle
+    # (rounding NaN to an integer), so only the finite entries' codes are compared.
+    n, k = 640, 2560
+    plan = bl.forward_fused_plan(m, n, k, "bf16")
+    _announce("forward fused 5..16 non-finite rows", m, n, k, plan)
+    assert plan["kernel"] == "fused" and plan["acts"] == "lds16"
+    q = np.random.default_rng(m).integers(-1, 2, (n, k)).astype(np.int8)
+    packed = torch.from_numpy(oracle.pack(q)).to(DEV)
+    x = synth.activations(m, k, seed=97 + m, dtype=torch.bfloat16, device=DEV, outlier_p=0.01, outlier_mult=20.0)
+    bits = x.view(torch.int16)
+    planted = [(0, 5, 0x7FC0), (1, k - 1, 0x7F81), (2, 100, 0xFFC0 - 0x10000), (3, 7, 0x7F80), (4, 9, 0xFF80 - 0x10000)]
+    for r, c, b in planted:
+        bits[r, c] = b
+    bits[4, 10] = 0x7FC1  # a NaN beside the negative infinity
+    (y, acc), xq, a = bl.forward_fused(packed, torch.tensor([0.02], device=DEV), x, n, k, want_y=True, want_acc=True)
+    torch.cuda.synchronize()
+    xf = acts_host_f32(x)
+    xq_ref, a_ref = oracle.quant_acts(np.where(np.isfinite(xf), xf, 0.0).astype(np.float32))
+    # the absmax over the row with its non-finite entries: NaN passes, infinity wins
+    a_exp = a_ref.copy()
+    for r in range(m):
+        if np.isinf(xf[r]).any():
+            a_exp[r] = np.inf
+    check_equal(host(a).view(np.uint32), a_exp.view(np.uint32), f"absmax m={m}")
+    finite = np.isfinite(xf)
+    got = host(xq)[:, :k]
+    for r in range(m):
+        if np.isinf(a_exp[r]):
+            # zero scale: every finite entry's code is 0
+            assert (got[r][finite[r]] == 0).all(), r
+        else:
+            assert np.array_equal(got[r][finite[r]], xq_ref[r, :k][finite[r]]), r
+    # rows without non-finite entries are unaffected: their outputs match the oracle
+    clean = [r for r in range(m) if finite[r].all()]
+    acc_ref, _ = oracle.forward(q, np.float32(0.02), xq_ref, a_ref, k)
+    check_equal(host(acc)[clean], acc_ref[clean], f"acc of the finite rows m={m}")
+
+
 @pytest.mark.parametrize("m,n,k,dtype", [(3, 65600, 768, torch.float32), (4, 70000, 1024, torch.float32)])
 def test_forward_fused_lds_form(m, n, k, dtype):
     # many row blocks leave one wave per block; where its pieces would not fit in
