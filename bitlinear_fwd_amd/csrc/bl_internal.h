@@ -183,7 +183,8 @@ hipError_t launch_gemv_grouped(const GroupMat* mats, int count, const void* X, i
 // enqueued otherwise).
 hipError_t launch_gemv_grouped_int8(const GroupMat* mats, int count, const int8_t* Xq, const float* absmax, int64_t M,
                                     int64_t K, hipStream_t s, bool* launched);
-// The fused 5..16-token form (bf16 x, K a multiple of 8 up to 4096, k_gemv_fq16): every
+// The fused 5..16-token form (bf16 x, K a multiple of 8 up to 7168, M K <= 65536,
+// k_gemv_fq16): every
 // workgroup quantises the whole input into LDS and decodes RB row blocks with W waves,
 // runs of T tiles, KL 16-byte row pieces per lane.  ok false where it does not apply.
 struct Fq16Plan {

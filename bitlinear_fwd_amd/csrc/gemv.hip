@@ -44,7 +44,7 @@ namespace {
 
 constexpr int kMaxLdsActBytes = 48 * 1024;
 constexpr int64_t kMaxFusedElems = 8192;  // M*K limit of the one-kernel quantise + decode
-constexpr int kMaxFq16Lds = 80 * 1024;    // dynamic LDS of the fused 5..16-token kernel
+constexpr int kMaxFq16Lds = 120 * 1024;   // dynamic LDS of the fused 5..16-token kernel
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Sum the W waves' partial tiles (red[w][t][j][lane]) and write y / acc for token group t
@@ -1651,17 +1651,24 @@ hipError_t launch_gemv_grouped_int8(const GroupMat* mats, int count, const int8_
 
 Fq16Plan plan_fq16(int64_t M, int64_t rb_total, int64_t K, int src) {
   Fq16Plan p;
-  // bf16 x in whole 16-byte pieces, 5..16 tokens, rows of at most 4096 columns.  Eight
-  // waves with two token rows each; row blocks shared per workgroup once there are more
-  // than about 1.25 workgroups per compute unit.  (Longer rows were measured slower than
-  // the quantiser plus the decode: 2560 x 6912 at M = 16, sixteen waves of one row each,
-  // 11.3 against 9.9 us: every workgroup quantises the whole input, 110 K values there.)
-  if (src != 1 || M < 5 || M > 16 || K % 8 != 0 || K > 4096) return p;
+  // bf16 x in whole 16-byte pieces, 5..16 tokens, rows of at most 7168 columns and at most
+  // 64 Ki values quantised by every workgroup.  Eight waves with two token rows each; row
+  // blocks shared per workgroup once there are more than about 1.25 workgroups per compute
+  // unit (rows up to 4096 columns).  Measured against the quantiser plus the decode
+  // (2B-class grouped calls): M = 16, K = 2560: 7.9 -> 6.7 us (Q/K/V), 8.1 -> 6.4 us (O),
+  // 9.6 -> 8.7 us (gate/up); M = 8, K = 6912: 8.9 -> 8.2 us; but M = 16, K = 6912 (110 K
+  // values per workgroup) 10.4 -> 10.7 us, so the bound on M K.
+  if (src != 1 || M < 5 || M > 16 || K % 8 != 0 || K > 7168 || M * K > 65536) return p;
   const int64_t K_pad = k_pad(K), chunks = K_pad / kTileCols;
   p.W = 8;
   p.T = (int)((chunks + 7) / 8);
-  p.KL = K <= 2048 ? 4 : 8;
-  p.RB = rb_total > 640 ? 4 : (rb_total > 320 ? 2 : 1);
+  if (K <= 4096) {
+    p.KL = K <= 2048 ? 4 : 8;
+    p.RB = rb_total > 640 ? 4 : (rb_total > 320 ? 2 : 1);
+  } else {
+    p.KL = 14;
+    p.RB = 1;
+  }
   p.lds_bytes = 16 * (K_pad + 16);
   p.ok = p.lds_bytes <= kMaxFq16Lds && (int64_t)p.W * p.T >= chunks && (int64_t)p.KL * 512 >= K;
   return p;
@@ -1708,6 +1715,10 @@ hipError_t launch_gemv_fq16(const GroupMat* mats, int count, const void* X, int 
   auto by_rb = [&](auto tc, auto kc) {
     return p.RB == 4 ? go(I8{}, tc, I4{}, kc) : (p.RB == 2 ? go(I8{}, tc, I2{}, kc) : go(I8{}, tc, I1{}, kc));
   };
+  if (p.KL == 14) {
+    using I14 = std::integral_constant<int, 14>;
+    return p.T == 3 ? go(I8{}, std::integral_constant<int, 3>{}, I1{}, I14{}) : go(I8{}, I4{}, I1{}, I14{});
+  }
   if (p.T == 1) return p.KL == 4 ? by_rb(I1{}, I4{}) : by_rb(I1{}, I8{});
   return p.KL == 4 ? by_rb(I2{}, I4{}) : by_rb(I2{}, I8{});
 }

@@ -183,7 +183,7 @@ int bitlinear_forward_ws_plan(int64_t M, int64_t N, int64_t K, int32_t out[10]);
  * K up to a size limit that depends on M and dt (at least 8192), one kernel launch does
  * all three steps: each workgroup computes the per-token absmax from the activation
  * pieces its waves hold, and each lane quantises its own pieces.  For 5 to 16 tokens with
- * bf16 X, K a multiple of 8 and at most 4096, one kernel launch does the same with the
+ * bf16 X, K a multiple of 8, K <= 7168 and M K <= 65536, one kernel launch does the same with the
  * whole M x K input quantised into LDS by every workgroup (each token row held by one
  * wave, so the row's absmax is a wave reduction).  Otherwise the two kernels run back to back
  * (bitlinear_forward_fused_plan tells which).

@@ -382,7 +382,8 @@ def test_launch_plans_cover_every_tile():
                         # 5..16 tokens, bf16, every workgroup quantises the input into LDS:
                         # eight waves of two token rows each, runs cover K
                         waves = p["threads"] // 64
-                        assert 5 <= m <= 16 and dt_of(name, p) and k % 8 == 0 and k <= 4096, (name, m, n, k, p)
+                        assert 5 <= m <= 16 and dt_of(name, p) and k % 8 == 0 and k <= 7168 and m * k <= 65536, \
+                            (name, m, n, k, p)
                         assert waves == 8 and waves * p["tiles_per_wave"] >= chunks, (name, m, n, k, p)
                         assert p["row_blocks"] * waves <= 32, (name, m, n, k, p)
                         assert p["workgroups"] * p["row_blocks"] >= rblocks, (name, m, n, k, p)

@@ -496,15 +496,17 @@ def test_forward_fused_single_kernel(m, n, k, dtype):
                                          (16, 2560, 6912, torch.bfloat16), (16, 2560, 2048, torch.bfloat16),
                                          (6, 1000, 4104, torch.bfloat16), (16, 520, 4096, torch.bfloat16),
                                          (11, 300, 4088, torch.bfloat16), (16, 11000, 1024, torch.bfloat16),
+                                         (8, 2560, 6912, torch.bfloat16), (9, 700, 7168, torch.bfloat16),
+                                         (5, 520, 7176, torch.bfloat16), (7, 2000, 5000, torch.bfloat16),
                                          (13, 6000, 2560, torch.bfloat16), (16, 300, 4097, torch.bfloat16)])
 def test_forward_fused_5_to_16_tokens(m, n, k, dtype):
     # 5..16 tokens: one launch where every workgroup quantises the 16 token rows into LDS
-    # (bf16 x, K a multiple of 8 up to 4096: eight waves of two rows; 1, 2 or 4 row blocks
-    # per workgroup); else the quantiser and the forward as two launches inside the one
-    # call (ragged K and N, fp32 x, long rows)
+    # (bf16 x, K a multiple of 8 up to 7168 and M K up to 64 Ki: eight waves of two rows; 1,
+    # 2 or 4 row blocks per workgroup up to K = 4096); else the quantiser and the forward as
+    # two launches inside the one call (ragged K and N, fp32 x, long rows)
     plan = bl.forward_fused_plan(m, n, k, "bf16" if dtype == torch.bfloat16 else "f32")
     _announce("forward fused 5..16", m, n, k, dtype, plan)
-    one_launch = dtype == torch.bfloat16 and k % 8 == 0 and k <= 4096
+    one_launch = dtype == torch.bfloat16 and k % 8 == 0 and k <= 7168 and m * k <= 65536
     assert (plan["kernel"] == "fused" and plan["acts"] == "lds16") == one_launch, plan
     _fused_check(m, n, k, dtype, seed=m * 41 + n + k)
 
@@ -590,7 +592,7 @@ def test_forward_fused_many_row_blocks(n, k, dtype):
     _fused_check(1, n, k, dtype, seed=n + 11 * k)
 
 
-@pytest.mark.parametrize("m,n,k,dtype,unaligned", [(5, 64, 5000, torch.bfloat16, False), (1, 64, 300, torch.bfloat16, False),
+@pytest.mark.parametrize("m,n,k,dtype,unaligned", [(5, 64, 7176, torch.bfloat16, False), (1, 64, 300, torch.bfloat16, False),
                                                    (2, 64, 1002, torch.float32, False), (3, 40, 512, torch.bfloat16, True),
                                                    (40, 72, 700, torch.float32, False), (100, 72, 700, torch.bfloat16, False),
                                                    (3, 40, 12000, torch.float32, False),
@@ -640,6 +642,7 @@ def _grouped_check(m, ns, k, dtype, seed):
     (16, [2560, 640, 640], 2560, torch.bfloat16),      # Q, K, V of the 2B-class layer
     (16, [6912, 6912], 2560, torch.bfloat16),          # gate + up (864 row blocks: four per workgroup)
     (7, [33, 500, 17, 1000], 4096, torch.bfloat16),    # ragged rows, 16 K tiles, 7 tokens
+    (8, [2560, 100], 6912, torch.bfloat16),            # 27 K tiles: runs of 4, one row block per workgroup
     (10, [4096, 4096, 100], 1000, torch.bfloat16),     # 520 row blocks: two per workgroup
     # 5..16 tokens otherwise: the quantiser, then one launch of the 5..16-token decode
     (16, [2560], 6912, torch.bfloat16),                # down: long rows, one forward
