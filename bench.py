@@ -316,12 +316,12 @@ TRAFFIC = {
     # (workload, M, path): scaled bytes per launch (fetch + write), raw KiB per launch, source hash.
     # path: "fused" (quantise + decode in one kernel), "int8" (decode of quantised
     # activations), "prefill".  Copy calibration (256 MiB device copy): FETCH_SIZE read
-    # 131083.8-131086.8 KiB (x1.99977-1.99982, taken per run), WRITE_SIZE 262144.0 KiB (x1.0).
-    (4, 1, "fused"): {"bytes_per_launch": 59263337, "fetch_kib": 28894.77, "write_kib": 90.03, "sha": "9f8707ebdbe55467"},
-    (4, 1, "int8"): {"bytes_per_launch": 59032887, "fetch_kib": 28791.25, "write_kib": 72.00, "sha": "9f8707ebdbe55467"},
-    (1, 1, "fused"): {"bytes_per_launch": 4589691, "fetch_kib": 2228.67, "write_kib": 25.28, "sha": "9f8707ebdbe55467"},
-    (2, 16, "int8"): {"bytes_per_launch": 3153302, "fetch_kib": 1438.15, "write_kib": 203.43, "sha": "9f8707ebdbe55467"},
-    (3, 2048, "prefill"): {"bytes_per_launch": 99964602, "fetch_kib": 29869.84, "write_kib": 37888.12, "sha": "44cd0403f297f1e4"},
+    # 131083.8-131086.5 KiB (x1.99978-1.99982, taken per run), WRITE_SIZE 262144.0 KiB (x1.0).
+    (4, 1, "fused"): {"bytes_per_launch": 59264290, "fetch_kib": 28895.23, "write_kib": 90.03, "sha": "9a60bae9175f079c"},
+    (4, 1, "int8"): {"bytes_per_launch": 59032887, "fetch_kib": 28791.25, "write_kib": 72.00, "sha": "9a60bae9175f079c"},
+    (1, 1, "fused"): {"bytes_per_launch": 4591156, "fetch_kib": 2229.34, "write_kib": 25.28, "sha": "9a60bae9175f079c"},
+    (2, 16, "int8"): {"bytes_per_launch": 3160685, "fetch_kib": 1441.72, "write_kib": 203.43, "sha": "9a60bae9175f079c"},
+    (3, 2048, "prefill"): {"bytes_per_launch": 103701990, "fetch_kib": 31694.53, "write_kib": 37888.13, "sha": "8802b9988ad4424c"},
 }
 
 
