@@ -26,6 +26,8 @@
 //                several matrices of one input in one launch;
 //   k_gemv_dppm  5..16 tokens on rows of at most 4096: the same register runs for a
 //                token group of 8 or 16, activation registers shared by 1 or 2 row blocks;
+//   k_gemv_fq16  the fused form for 5..16 tokens (bf16 x): every workgroup quantises the
+//                token rows into LDS, one wave per row, while its weights stream in;
 //   k_gemv_reg   other 5..16-token shapes: activation fragments loaded per tile with
 //                the weights of a ring of batches, shared by 1, 2 or 4 row blocks;
 //   k_gemv_lds   the fused form where its register pieces would not fit (many row
