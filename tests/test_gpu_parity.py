@@ -498,6 +498,8 @@ def test_forward_fused_single_kernel(m, n, k, dtype):
                                          (11, 300, 4088, torch.bfloat16), (16, 11000, 1024, torch.bfloat16),
                                          (8, 2560, 6912, torch.bfloat16), (9, 700, 7168, torch.bfloat16),
                                          (5, 520, 7176, torch.bfloat16), (7, 2000, 5000, torch.bfloat16),
+                                         (5, 1, 8, torch.bfloat16), (9, 1, 7168, torch.bfloat16),
+                                         (16, 1, 7168, torch.bfloat16),
                                          (13, 6000, 2560, torch.bfloat16), (16, 300, 4097, torch.bfloat16)])
 def test_forward_fused_5_to_16_tokens(m, n, k, dtype):
     # 5..16 tokens: one launch where every workgroup quantises the 16 token rows into LDS
@@ -649,6 +651,9 @@ def _grouped_check(m, ns, k, dtype, seed):
     (5, [17, 300, 1000, 33], 1000, torch.float32),     # ragged rows and columns, token group of 8
     (12, [130, 2100], 3000, torch.bfloat16),           # token group of 16, ragged K
     (9, [16, 32, 48, 64, 80, 96, 112, 6150], 4096, torch.float32),  # eight matrices, 16 K tiles
+    (16, [16, 33, 48, 700, 80, 96, 112, 6150], 4096, torch.bfloat16),  # eight matrices in the fused form, 2 row blocks per WG
+    (9, [2000, 17, 4100], 7168, torch.bfloat16),       # the longest fused rows (28 K tiles), M K = 64512
+    (5, [8200, 8], 8, torch.bfloat16),                 # K = 8: one K tile, mostly padding, 514 row blocks
     (16, [300, 500], 4097, torch.bfloat16),            # 17 K tiles: one forward per matrix
     (1, [4096, 2048], 4096, torch.float32),            # 384 row blocks
 ])
