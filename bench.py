@@ -321,7 +321,7 @@ TRAFFIC = {
     (4, 1, "int8"): {"bytes_per_launch": 59032887, "fetch_kib": 28791.25, "write_kib": 72.00, "sha": "9a60bae9175f079c"},
     (1, 1, "fused"): {"bytes_per_launch": 4591156, "fetch_kib": 2229.34, "write_kib": 25.28, "sha": "9a60bae9175f079c"},
     (2, 16, "int8"): {"bytes_per_launch": 3160685, "fetch_kib": 1441.72, "write_kib": 203.43, "sha": "9a60bae9175f079c"},
-    (3, 2048, "prefill"): {"bytes_per_launch": 103701990, "fetch_kib": 31694.53, "write_kib": 37888.13, "sha": "8802b9988ad4424c"},
+    (3, 2048, "prefill"): {"bytes_per_launch": 103728584, "fetch_kib": 31708.16, "write_kib": 37888.14, "sha": "0b835e9f806c2790"},
 }
 
 

@@ -5,7 +5,7 @@
 // bhfrc.com news 56965, section 1.1 (ternary x activation = add / subtract / skip) and
 // section 4.1 (2-bit codes); aratech.ae BitNet b1.58 article, "BitLinear".
 //
-// Structure (workgroup = 4 waves in a GM x GN grid, each wave a WM x WN block of 16 x 16
+// Structure (workgroup = 4 or 8 waves in a GM x GN grid, each wave a WM x WN block of 16 x 16
 // v_mfma_i32_16x16x64_i8 tiles; K advances half a 256-column packed chunk per stage):
 //   * activations (A): each half-stage's BM x 128-byte slab (the pieces two MFMA steps
 //     use) goes straight from global memory into LDS (direct global -> LDS loads, no
@@ -19,8 +19,10 @@
 //   * one 16-byte word of a slot feeds one MFMA step and serves WM / 16 MFMAs, which
 //     keeps the decode VALU below the matrix-core time;
 //   * shapes: 64 x 256 or 64 x 192 output tiles (waves 1 x 4 of 64 x 64 or 64 x 48,
-//     three-slot ring), whichever leaves the lighter last round of tiles, and two K groups
-//     of four waves per tile where there are few tiles (plan_gemm);
+//     three-slot ring), or 64 x 384 (eight waves 1 x 8 of 64 x 48, which share each
+//     activation slab over twice the columns: half the activation re-reads), whichever
+//     leaves the lighter last round of tiles, and two K groups of four waves per tile where
+//     there are few tiles (plan_gemm);
 //   * the loop body is unrolled over lcm(D, 2 CB) half-stages so that every ring index is
 //     static; half-stages past the end of K are skipped whole (measured: 2048 x 6912 x 2560
 //     48.9 -> 46.9 us, 4096 x 6912 x 2560 87.6 -> 82.3 us, 48 x 30000 x 512 9.4 -> 7.6 us),
@@ -120,19 +122,21 @@ struct SkArgs {
 };
 
 template <int GM, int GN, int WM, int WN, int D, int KS = 1, bool kSK = false>
-__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(kSK ? (WN == 64 ? 3 : 4) : 1))) void k_gemm_mfma(const uint8_t* __restrict__ packed, const float* __restrict__ gamma,
+__global__ __launch_bounds__(64 * GM * GN * KS) __attribute__((amdgpu_waves_per_eu(kSK ? (WN == 64 ? 3 : 4) : 1))) void k_gemm_mfma(const uint8_t* __restrict__ packed, const float* __restrict__ gamma,
                                                    const int8_t* __restrict__ Xq, const float* __restrict__ absmax,
                                                    int M, int N, int n_blocks, int K_pad, int chunks, int tiles_m,
                                                    int tiles_n, float* __restrict__ Y, int32_t* __restrict__ acc_out,
                                                    SkArgs sk) {
-  static_assert(GM * GN == 4, "four waves");
+  constexpr int NW = GM * GN;  // waves per K group
+  static_assert(NW == 4 || (NW == 8 && KS == 1 && !kSK), "four waves, or eight in one K group");
   static_assert(D >= 2, "at least two ring slots");
   static_assert(KS == 1 || KS == 2, "one or two K groups");
   static_assert(!kSK || KS == 1, "the split-tail form runs one K group per tile");
   constexpr int BM = GM * WM, BN = GN * WN;
   constexpr int MB = WM / 16, NB = WN / 16;
   constexpr int kHalf = kTileCols / 2;        // bytes per activation row in a half-stage
-  constexpr int kDma = BM / 32;               // direct loads per wave per half-stage (8 rows each, 4 waves)
+  constexpr int kDma = BM / (8 * NW);        // direct loads per wave per half-stage (8 rows each)
+  static_assert(kDma >= 1 && BM % (8 * NW) == 0, "the waves share the activation slab's rows evenly");
   constexpr int P = D - 1;                    // prefetch distance in half-stages
   constexpr int CB = (P + 1) / 2 + 1;         // weight register ring (chunks live at once)
   constexpr int kBody = std::lcm(D, 2 * CB);  // half-stages per trip: both ring indices static
@@ -209,12 +213,12 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(kSK ? 
       else return min(c_lo + (min(h, hstages - 1) >> 1), ce - 1);
     };
 
-    // this lane's source for each direct load: row 8 (4 j + wave) + lane / 8, LDS slot
+    // this lane's source for each direct load: row 8 (NW j + wave) + lane / 8, LDS slot
     // lane % 8 holding local piece lp = slot ^ swizzle, global piece 4 (lp >> 1) + 2h + (lp & 1)
     // (rows past M repeat row M-1: their outputs are never stored)
 #pragma unroll
     for (int j = 0; j < kDma; ++j) {
-      const int row = 8 * (4 * j + wave) + (lane >> 3);
+      const int row = 8 * (NW * j + wave) + (lane >> 3);
       const int lp = a_slot(row, lane & 7);
       asrc[j] = Xq + (size_t)min(m0 + row, M - 1) * K_pad + 16 * (4 * (lp >> 1) + (lp & 1));
     }
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(kSK ? 
       uint8_t* dst = slab(std::integral_constant<int, hs>{}) + kgoff;
 #pragma unroll
       for (int j = 0; j < kDma; ++j)
-        load_g2lds16(asrc[j] + (size_t)c * kTileCols + 32 * (min(hs, hstages - 1) & 1), &dst[8 * (4 * j + wave) * kHalf]);
+        load_g2lds16(asrc[j] + (size_t)c * kTileCols + 32 * (min(hs, hstages - 1) & 1), &dst[8 * (NW * j + wave) * kHalf]);
       if constexpr ((hs & 1) == 0) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) bw[(hs / 2) % CB][j] = bsrc[j][(size_t)c * 64];
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(kSK ? 
           uint8_t* dst = slab(std::integral_constant<int, (k + P) % D>{}) + kgoff;
 #pragma unroll
           for (int j = 0; j < kDma; ++j)
-            load_g2lds16(asrc[j] + (size_t)c * kTileCols + 32 * (hc & 1), &dst[8 * (4 * j + wave) * kHalf]);
+            load_g2lds16(asrc[j] + (size_t)c * kTileCols + 32 * (hc & 1), &dst[8 * (NW * j + wave) * kHalf]);
           if constexpr (((k + P) & 1) == 0) {
 #pragma unroll
             for (int j = 0; j < NB; ++j) bw[((k + P) / 2) % CB][j] = bsrc[j][(size_t)c * 64];
@@ -486,7 +490,7 @@ hipError_t launch(const uint8_t* packed, const float* gamma, const int8_t* Xq, c
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   const int tiles = tiles_m * tiles_n;
   const int grid = 8 * ((tiles + 7) / 8);
-  hipLaunchKernelGGL((k_gemm_mfma<GM, GN, WM, WN, D, KS>), dim3(grid), dim3(256 * KS), 0, s, packed, gamma, Xq, absmax, (int)M,
+  hipLaunchKernelGGL((k_gemm_mfma<GM, GN, WM, WN, D, KS>), dim3(grid), dim3(64 * GM * GN * KS), 0, s, packed, gamma, Xq, absmax, (int)M,
                      (int)N, n_blocks, (int)K_pad, chunks, tiles_m, tiles_n, Y, acc, SkArgs{});
   return hipGetLastError();
 }
@@ -527,7 +531,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   //   64 x 256: waves of 64 x 64 side by side (three-slot ring, 24 KiB of LDS, 152
   //             registers, three workgroups per CU): the most work per operand byte;
   //   64 x 192: waves of 64 x 48 (118 registers, four per CU): the same structure, for
-  //             column counts that 256 would leave a ragged last round on.
+  //             column counts that 256 would leave a ragged last round on;
+  //   64 x 384: eight waves of 64 x 48 in one K group (two workgroups per CU): the
+  //             64 x 192 waves with each activation slab shared by twice the columns.
   // Where the tiles do not fill the chip, two K groups of four waves share each tile (eight
   // waves, each group half the chunks, partials summed through LDS): twice the waves per
   // tile at the same operand bytes per tile.  64 x 256 tiles when that gives 193..256 of
@@ -539,13 +545,20 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   // 22.5 -> 20.4 us at K = 2560; the one shape measured slower, 512 x 2560 x 6912, by 3 %
   // (25.2 -> 25.9 us).  With more tiles the split costs more than it gives (2048 x 6912 x
   // 2560: 45.2 -> 47.8 us; 4096 x 2560 x 6912: 72.5 -> 78.2 us).
-  // Otherwise, between 64 x 256 and 64 x 192, the cost of the last round decides: rounds of
-  // 256 tiles times the tile width, the 48-column waves counted at 0.976 of the 64-column
-  // rate (measured 8192^3: 486 vs 474 us).  Measured at M = 2048 x 6912 columns: 46.8 us
-  // (64 x 256) -> 45.9 us (64 x 192); 8192^3, 4096 x 2560 x 6912 and 2048 x 28672 x 8192
-  // stay on 64 x 256.
+  // Otherwise, between 64 x 256, 64 x 192 and 64 x 384, the cost of the last round decides:
+  // rounds of 256 tiles times the tile width, the 48-column waves counted at 0.976 of the
+  // 64-column rate (measured 8192^3: 486 vs 474 us) and the eight-wave 384-column tiles at
+  // 1.14 of it (half the activation re-reads; fitted to interleaved A/B runs, 64 x 384 against
+  // the four-wave tile the rule chose before, outputs identical, M x K x N: 1536 x 2560 x
+  // 6912 33.9 -> 31.5 us, 1792 x 2560 x 6912 35.9 -> 33.0, 2560 x 2560 x 6912 49.5 -> 47.3,
+  // 3584 x 2560 x 6912 64.8 -> 61.0, 4096 x 6912 x 2560 76.2 -> 72.0, 3000 x 700 x 9000 37.2
+  // -> 36.4, 8192^3 457 -> 446, 4096 x 2560 x 6912 75.7 -> 76.2, 2048 x 8192 x 28672 402 ->
+  // 402, 4000 x 1000 x 8190 47.9 -> 48.3; where the 384-column tiles leave a light last
+  // round the rule keeps the narrower tile: 2048 x 2560 x 6912 41.6 -> 42.5 us, 3072 x 2560
+  // x 6912 57.8 -> 56.8).  Measured at M = 2048 x 6912 columns: 46.8 us (64 x 256) -> 45.9 us
+  // (64 x 192).
   const int64_t tm = (M + 63) / 64;
-  const int64_t t256 = tm * ((N + 255) / 256), t192 = tm * ((N + 191) / 192);
+  const int64_t t256 = tm * ((N + 255) / 256), t192 = tm * ((N + 191) / 192), t384 = tm * ((N + 383) / 384);
   p.bm = 64;
   p.ks = 1;
   if (t256 > 192 && t256 <= 256) {
@@ -557,9 +570,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
   } else {
     const double c256 = (double)((t256 + 255) / 256) * 256.0;
     const double c192 = (double)((t192 + 255) / 256) * 192.0 / 0.976;
+    const double c384 = N >= 384 ? (double)((t384 + 255) / 256) * 384.0 / 1.14 : 1e300;
     p.bn = c192 < c256 ? 192 : 256;
+    if (c384 < std::min(c192, c256)) p.bn = 384;
   }
-  p.threads = 256 * p.ks;
+  p.threads = (p.bn == 384 ? 512 : 256) * p.ks;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   p.groups = 8 * ((tiles + 7) / 8);
   return p;
@@ -572,6 +587,7 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
     if (p.bn == 256) return launch<1, 4, 64, 64, 3, 2>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
     return launch<1, 4, 64, 48, 3, 2>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
   }
+  if (p.bn == 384) return launch<1, 8, 64, 48, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
   if (p.bn == 256) return launch<1, 4, 64, 64, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
   return launch<1, 4, 64, 48, 3>(packed, gamma, Xq, absmax, M, N, K, Y, acc, s);
 }
@@ -583,7 +599,7 @@ int gemm_slots_per_cu(int bn) { return bn == 256 ? 3 : 4; }
 
 GemmPlan plan_gemm_ws(int64_t M, int64_t N, int64_t K) {
   GemmPlan p = plan_gemm(M, N, K);
-  if (p.ks != 1) return p;
+  if (p.ks != 1 || p.bn == 384) return p;  // the split-tail form runs four-wave tiles
   // With plan_gemm's tile, where the tiles need more than one round of the resident slots
   // and the last round is partial: every slot takes `rounds` whole tiles, and the tiles
   // left over are split along K so that every slot carries the same work to within one K

@@ -285,8 +285,9 @@ def test_token_group_routing():
 
 
 def test_prefill_plans():
-    # host-only sweep of the prefill planner: a supported tile shape, 256 threads per K group,
-    # and a grid of whole XCD rounds covering every 64-row tile
+    # host-only sweep of the prefill planner: a supported tile shape, 256 threads per K group
+    # (512 for the eight-wave 64 x 384 tile, one K group), and a grid of whole XCD rounds
+    # covering every 64-row tile
     for m in (17, 65, 100, 333, 1000, 1536, 2048, 4096, 8192):
         for n in (1, 16, 640, 2000, 2560, 6912, 8192, 28672):
             for k in (1, 256, 2560, 6912, 28672):
@@ -294,8 +295,12 @@ def test_prefill_plans():
                 if p["kernel"] != "prefill":
                     assert m <= 64, (m, n, k, p)
                     continue
-                assert p["tile_m"] == 64 and p["tile_n"] in (192, 256), (m, n, k, p)
-                assert p["k_groups"] in (1, 2) and p["threads"] == 256 * p["k_groups"], (m, n, k, p)
+                assert p["tile_m"] == 64 and p["tile_n"] in (192, 256, 384), (m, n, k, p)
+                assert p["k_groups"] in (1, 2), (m, n, k, p)
+                if p["tile_n"] == 384:
+                    assert p["k_groups"] == 1 and p["threads"] == 512 and n >= 384, (m, n, k, p)
+                else:
+                    assert p["threads"] == 256 * p["k_groups"], (m, n, k, p)
                 tiles = -(-m // 64) * -(-n // p["tile_n"])
                 assert p["workgroups"] == 8 * -(-tiles // 8), (m, n, k, p)
                 if p["k_groups"] == 2:
@@ -311,8 +316,9 @@ def test_split_tail_plans_cover_every_tile_once():
     # tile (b % 8) x (rounds x slots / 8) + b / 8; block b past them, with s = (b - D) / 8,
     # takes range s % parts of tail tile 8 (s / parts) + b % 8 (none when that is >= tail).
     seen_split = 0
-    for m in (65, 333, 1000, 1061, 1536, 1571, 1600, 2048, 2098, 3000, 3074, 4096, 4721, 4904, 8192):
-        for n in (640, 2560, 2600, 4100, 6912, 8000, 8003, 9000, 10240, 12000, 28672):
+    for m in (65, 333, 614, 1000, 1037, 1061, 1345, 1536, 1571, 1600, 2048, 2098, 2961, 3000, 3074, 4096, 4721, 4904,
+              8192):
+        for n in (640, 2560, 2600, 4100, 6912, 8000, 8003, 9000, 10240, 12000, 19968, 28672):
             for k in (256, 700, 1000, 2560, 3001, 6912, 8192):
                 p = bl.forward_ws_plan(m, n, k)
                 nbytes = bl.forward_ws_bytes(m, n, k)

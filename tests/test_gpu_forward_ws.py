@@ -40,15 +40,17 @@ def _run_ws(q, xq, a, gamma, n, k, ws):
     return host(y), host(acc)
 
 
-# (M, N, K, tile_n, split tiles, K ranges): M, N and K ragged against the 64-row tiles,
-# the tile widths and the 256-column chunks; three to twelve K ranges per split tile, one
-# to four whole-tile rounds before the tail, both tile widths
+# (M, N, K, tile_n, split tiles, K ranges): M, N and K ragged against the 64-row tiles and
+# the 256-column chunks; three to twelve K ranges per split tile.  Where the tiles take more
+# than one round or 64 x 256 tiles would leave a tail, the planner now takes the eight-wave
+# 64 x 384 tiles instead (no split), so every split it makes follows one round of 64 x 192
+# tiles.
 SPLIT_CASES = [
     (1600, 8000, 1000, 192, 26, 4),     # 1050 tiles of 64 x 192: one round, 26 tiles in 4 ranges
     (4721, 2600, 3001, 192, 12, 12),    # 12 ranges of one chunk, K ragged
-    (3074, 8000, 2560, 192, 10, 10),    # two rounds, 10 tiles in 10 ranges
-    (2098, 12000, 700, 192, 31, 3),     # two rounds, 31 tiles in 3 ranges (K ragged)
-    (4904, 10240, 3001, 256, 8, 12),    # 64 x 256 tiles: four rounds, 8 tiles in 12 ranges
+    (2961, 4100, 2560, 192, 10, 10),    # 10 tiles in 10 ranges
+    (1037, 12000, 700, 192, 47, 3),     # 47 tiles in 3 ranges (K ragged)
+    (614, 19968, 700, 192, 16, 3),      # 1040 tiles from ten 64-row blocks: 16 tiles in 3 ranges
 ]
 
 

@@ -336,19 +336,20 @@ def test_forward_prefill(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k,tile_n,k_groups", [
-    (2048, 4100, 1000, 192, 1), (333, 24000, 2600, 192, 1), (4000, 8190, 1000, 256, 1), (3000, 9000, 700, 192, 1),
-    (4096, 2560, 6912, 256, 1), (2048, 2560, 6912, 192, 2), (1500, 2000, 777, 192, 2),
+    (2048, 4100, 1000, 192, 1), (333, 24000, 2600, 192, 1), (2000, 4090, 1000, 256, 1), (3000, 9000, 700, 384, 1),
+    (4096, 2560, 6912, 384, 1), (1792, 6912, 2560, 384, 1), (4000, 8190, 1000, 384, 1), (2048, 2560, 6912, 192, 2),
+    (1500, 2000, 777, 192, 2),
     # two K groups per tile where the tiles do not fill the chip; odd chunk counts (K = 1100:
     # 5 chunks, 6912: 27) leave the second group one chunk short
     (1000, 3000, 777, 192, 2), (700, 2600, 1100, 192, 2), (500, 7000, 1100, 256, 2), (450, 8000, 6912, 256, 2)])
 def test_forward_prefill_tile_shapes(m, n, k, tile_n, k_groups):
-    # the prefill tile shapes (64 x 256 or 64 x 192 by the last round's load, one or two K
-    # groups per tile) with ragged M, N and K; every output is checked (the oracle's rows
-    # split over host threads)
+    # the prefill tile shapes (64 x 256, 64 x 192 or the eight-wave 64 x 384 by the last
+    # round's load, one or two K groups per tile) with ragged M, N and K; every output is
+    # checked (the oracle's rows split over host threads)
     plan = bl.forward_plan(m, n, k)
     _announce("forward prefill tiles", m, n, k, plan)
     assert plan["kernel"] == "prefill" and plan["tile_m"] == 64 and plan["tile_n"] == tile_n
-    assert plan["k_groups"] == k_groups and plan["threads"] == 256 * k_groups
+    assert plan["k_groups"] == k_groups and plan["threads"] == (512 if tile_n == 384 else 256 * k_groups)
     rng = np.random.default_rng(m + n + k)
     q = rng.integers(-1, 2, (n, k)).astype(np.int8)
     x = synth.activations(m, k, seed=m + k, dtype=torch.float32, outlier_p=0.01, outlier_mult=20.0).numpy()
