@@ -218,9 +218,9 @@ def forward_ws_bytes(m: int, n: int, k: int) -> int:
 
 
 def forward_workspace(m: int, n: int, k: int, device):
-    """A zero-filled workspace for bitlinear_forward_ws on (M, N, K) (None when it needs
-    none).  Every call returns its counters to zero, so one workspace serves later calls
-    of any shape it is large enough for."""
+    """A workspace for bitlinear_forward_ws on (M, N, K) (None when it needs none).  Its
+    contents on entry do not matter and nothing carries over between calls, so one
+    workspace serves later calls of any shape it is large enough for."""
     import torch
 
     nb = forward_ws_bytes(m, n, k)

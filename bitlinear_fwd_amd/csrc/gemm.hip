@@ -496,7 +496,7 @@ hipError_t launch(const uint8_t* packed, const float* gamma, const int8_t* Xq, c
 }
 
 // The split-tail form (one K group) with the plan's rounds and tail; the workspace holds
-// the tail tiles' counters (zero at rest) and then their partial tiles.
+// the tail tiles' partial tiles, written by the first launch and summed by the second.
 template <int GM, int GN, int WM, int WN, int D>
 hipError_t launch_sk(const uint8_t* packed, const float* gamma, const int8_t* Xq, const float* absmax, int64_t M,
                      int64_t N, int64_t K, float* Y, int32_t* acc, const GemmPlan& p, void* workspace, hipStream_t s) {
