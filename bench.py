@@ -1,6 +1,6 @@
 """Benchmark of the BitLinear forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 4] [--legs 1,3,4i,...]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 4] [--legs 1,3,4i,...] [--prefill-shapes MxKxN,...]
                     [--graph] [--no-cpu-baseline] [--copy-calibration MIB]
 
 A step is one pass of the hot path over one batch of synthetic input: for every matrix of
@@ -92,6 +92,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device three times (the reference kernel of "
                          "known size for scaling FETCH_SIZE / WRITE_SIZE counter runs)")
+    ap.add_argument("--prefill-shapes", default="", metavar="MxKxN,...",
+                    help="also time bitlinear_forward alone on these prefill shapes (tokens x in x out; "
+                         "seeded synthetic inputs as the 2048-token workload's) and report them apart "
+                         "from the legs")
     return ap.parse_args()
 
 
@@ -622,6 +626,52 @@ def time_forward_only(w: Workload, reps: int):
             sum(m.ops for m in mats) / len(mats))
 
 
+def time_prefill_shapes(bl, synth, dev, spec: str, reps: int = 40):
+    """bitlinear_forward alone on each M x K x N of `spec`: the plan's tile, and the launch
+    time as the fastest and the median of five windows of `reps` back-to-back launches (HIP
+    events on the kernels' stream), with the int8 TOPS and the fraction of the 5 POPS peak."""
+    import statistics
+
+    import torch
+
+    out = {}
+    wl = synth.WORKLOADS[3]
+    for tok in [t for t in spec.split(",") if t.strip()]:
+        m, k, n = (int(v) for v in tok.lower().split("x"))
+        w = synth.latent_weights(n, k, seed=synth.weight_seed(3, 90, 0), device=dev)
+        packed, gamma = bl.quantize_weights(w)
+        del w
+        x = synth.activations(m, k, seed=synth.act_seed(3, 90, 0), dtype=wl.act_dtype, device=dev,
+                              outlier_p=wl.outlier_p, outlier_mult=wl.outlier_mult)
+        xq, a = bl.quantize_acts(x)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        call = bl.prepare_forward(packed, gamma, xq, a, n, k, y)
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        wins = []
+        for _ in range(5):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            for _ in range(reps):
+                call()
+            e.record(stream)
+            torch.cuda.synchronize()
+            wins.append(s.elapsed_time(e) * 1e3 / reps)
+        med, lo = statistics.median(wins), min(wins)
+        plan = bl.forward_plan(m, n, k)
+        ops = 2 * m * n * k
+        out[tok] = {"tile": f"{plan.get('tile_m')}x{plan.get('tile_n')}", "k_groups": plan.get("k_groups"),
+                    "threads": plan.get("threads"), "launch_us_median": round(med, 3), "launch_us_min": round(lo, 3),
+                    "TOPS_at_median": round(ops / (med * 1e-6) / 1e12, 2),
+                    "mfma_frac_at_median": round(ops / (med * 1e-6) / 1e12 / I8_PEAK_TOPS, 4)}
+        progress(f"prefill shape {tok}: {med:.2f} us per launch")
+        del packed, gamma, x, xq, a, y, call
+        torch.cuda.empty_cache()
+    return out
+
+
 def host_cpu_facts():
     """The host the oracle baseline runs on: CPU model, logical CPUs of the machine and of
     this process's CPU set, and the physical cores in that set (distinct (package, core)
@@ -904,6 +954,7 @@ def main():
             legs[key]["host_us_per_launch"] = round(lhost * 1e3 / max(1, len(w.calls[0])), 3)
             del w
             torch.cuda.empty_cache()
+    shapes = time_prefill_shapes(bl, synth, dev, args.prefill_shapes) if args.prefill_shapes else None
     cpu = cpu_single = None
     host = host_cpu_facts()
     if not args.no_cpu_baseline:
@@ -960,6 +1011,7 @@ def main():
         "cpu_baseline_single_thread": cpu_single,
         "gpu_state": {"before_timed_region": state_before, "after_timed_region": state_after},
         "legs": legs,
+        "prefill_shapes": shapes,
     }
     print(json.dumps(out), flush=True)
 
