@@ -337,7 +337,8 @@ def test_forward_prefill(m, n, k):
 
 @pytest.mark.parametrize("m,n,k,tile_n,k_groups", [
     (2048, 4100, 1000, 192, 1), (333, 24000, 2600, 192, 1), (2000, 4090, 1000, 256, 1), (3000, 9000, 700, 384, 1),
-    (4096, 2560, 6912, 384, 1), (1792, 6912, 2560, 384, 1), (4000, 8190, 1000, 384, 1), (2048, 2560, 6912, 192, 2),
+    (4096, 2560, 6912, 384, 1), (1792, 6912, 2560, 384, 1), (4000, 8190, 1000, 384, 1), (4096, 8192, 200, 384, 1),
+    (2048, 2560, 6912, 192, 2),
     (1500, 2000, 777, 192, 2),
     # two K groups per tile where the tiles do not fill the chip; odd chunk counts (K = 1100:
     # 5 chunks, 6912: 27) leave the second group one chunk short
