@@ -265,17 +265,20 @@ class Workload:
         return calls
 
     def capture(self):
+        """Record each step group's launches into a HIP graph: the same calls the eager steps
+        make (grouped and gated calls included), prepared inside the capture so that they
+        record onto the capture stream."""
         import torch
 
         self.graphs = []
-        for group in self.step_groups():
-            for mat in group:  # warm the kernels once outside capture
-                self.launch(mat)
+        for i, group in enumerate(self.step_groups()):
+            for call in self.calls[i]:  # warm the kernels once outside capture
+                call()
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for mat in group:
-                    self.launch(mat)
+                for call in self.prepared(group, False):
+                    call()
             self.graphs.append(g)
         torch.cuda.synchronize()
 
@@ -966,6 +969,19 @@ def main():
                 if tok in ROOFLINE_LEGS and (m == synth.WORKLOADS[idx].m_list[0]):
                     legs[key]["roofline"] = roofline_block(w, l_ms, l_b, l_o, l_how, idx, ceilings)
             legs[key]["host_us_per_launch"] = round(lhost * 1e3 / max(1, len(w.calls[0])), 3)
+            if not args.graph and lhost >= 0.9 * lms:
+                # the host's issue rate sets this leg's pace: the same step as HIP graph replays,
+                # reported beside it (the eager figures above stay the leg's record; measured, graph
+                # replay is faster on the one-GPU-shard legs and slower on the short 2B-class ones)
+                w.capture()
+                g_ms, g_trials, _ = time_steps(w, leg_steps(w), max(2, -(-100 // len(w.calls[0]))))
+                w.graphs = None
+                legs[key]["graph_replay"] = {
+                    "ms_per_step": round(g_ms, 5), "us_per_matrix": round(g_ms * 1e3 / w.matrices_per_step(), 3),
+                    "packed_GBps": round(w.bytes_per_step() / (g_ms * 1e-3) / 1e9, 1),
+                    "allin_GBps": round(w.allin_bytes_per_step() / (g_ms * 1e-3) / 1e9, 1),
+                    "trials": trial_stats(g_trials, w.bytes_per_step(), w.ops_per_step() if w.m > 16 else None)}
+                progress(f"leg {key} as graph replays: {g_ms:.4f} ms per step")
             del w
             torch.cuda.empty_cache()
     shapes = time_prefill_shapes(bl, synth, dev, args.prefill_shapes) if args.prefill_shapes else None
